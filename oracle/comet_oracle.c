@@ -1,0 +1,442 @@
+/*
+ * CPU oracle for the W4Ax fine-grained mixed-precision GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's
+ * CPU-baseline leg are the only code that may load or call this library. The
+ * product library never links, loads or calls it, and shares no code with it.
+ *
+ * What it computes, step by step, in the order the pages describe it:
+ *
+ *  1. Channel order (offline). Channels are ranked by a calibration score and
+ *     permuted so that the outlier channels share 128-channel blocks; the
+ *     highest-scoring blocks are stored in 8 bits, the rest in 4 bits.
+ *     COMET article (mmssai.com/?p=43269), section "1.离群点分布规律的重定义";
+ *     QUIK blog (deep-paper.org/paper/2310.09259), section "第一步: 识别与重排"
+ *     (outlier columns go to the end of W); QoQ/QServe article
+ *     (youleyou.com/wenzhang/3078652.html), section "通用量化优化技巧", item 3
+ *     (channels of similar saliency share a quantization group).
+ *  2. Weight quantization (offline). Symmetric INT4 per output channel per
+ *     128-channel group, with an fp16 scale per group (QUIK blog, section
+ *     "反量化背后的数学": weights are quantized symmetrically; QoQ/QServe
+ *     article, section "背景": an fp16 scale shared per group). The per-group
+ *     weight sum is precomputed here (QUIK blog, same section: the term that
+ *     involves the sum of the weights depends on the weights only).
+ *  3. Activation quantization (online). Per token and per block, absmax
+ *     scaling to INT4 ([-7, 7]) or INT8 ([-127, 127]); QoQ/QServe article,
+ *     section "保护量化范围", names the symmetric 8-bit range [-127, 127].
+ *  4. Block partials. The exact INT32 dot product of each 128-channel block.
+ *     A second form uses the zero-extended 4-bit code u = q + 8 and removes
+ *     the offset with the precomputed weight sum (COMET article, section
+ *     "3.硬件指令集的极限挖掘": zero extension instead of sign extension,
+ *     compensated through the scales).
+ *  5. Epilogue. Y = fp16( sum over blocks of (s_x * s_w) * P ), in FP32, in
+ *     block order (QUIK blog, section "核融合": the integer result is
+ *     dequantized to fp16 while still in registers).
+ *
+ * Readings of points the pages leave open (INT4 range, rounding mode, scale
+ * form, all-zero blocks, tie-breaking of the channel sort) are listed with the
+ * design notes at the repository root; each is stated where it is used below.
+ *
+ * Precision. Built with -O2 -ffp-contract=off and without fast-math, so every
+ * float operation below is a single IEEE-754 binary32 operation rounded to
+ * nearest-even, and rintf() rounds half-way cases to even.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BLOCK 128
+
+enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_NONFINITE = 2 };
+
+/* ------------------------------------------------------------------------ */
+/* IEEE-754 binary16, written from the format's definition.                 */
+/* ------------------------------------------------------------------------ */
+
+/* Exact conversion of a binary16 bit pattern to binary32. */
+float orc_half_to_float(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);                 /* zero / subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even; overflow gives +-Inf. */
+uint16_t orc_float_to_half(float f)
+{
+    if (isnan(f))
+        return 0x7E00;
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs((double)f);                    /* exact */
+    if (isinf(f))
+        return sign | 0x7C00;
+    if (a < ldexp(1.0, -14)) {
+        /* Subnormal range: the quantum is 2^-24. A result of 1024 quanta is
+         * the smallest normal number, whose bit pattern is also 1024. */
+        double q = nearbyint(a * 16777216.0);
+        return sign | (uint16_t)q;
+    }
+    int e2;
+    frexp(a, &e2);                                 /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;                                /* unbiased exponent */
+    double q = nearbyint(ldexp(a, 10 - E));        /* significand in quanta, [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7C00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)q - 1024);
+}
+
+/* Array forms of the two conversions (used by the exhaustive checks). */
+void orc_half_to_float_array(const uint16_t *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_half_to_float(in[i]);
+}
+
+void orc_float_to_half_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_float_to_half(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1. Channel order                                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float score;
+    int32_t index;
+} orc_ranked;
+
+/* Ascending score; equal scores keep the original channel order. */
+static int orc_rank_cmp(const void *pa, const void *pb)
+{
+    const orc_ranked *a = (const orc_ranked *)pa, *b = (const orc_ranked *)pb;
+    if (a->score < b->score) return -1;
+    if (a->score > b->score) return 1;
+    return (a->index > b->index) - (a->index < b->index);
+}
+
+/* perm[k'] = original channel stored at permuted position k'; block b holds
+ * positions [128 b, 128 b + 128). The nb8 highest-scoring blocks, which are the
+ * last ones, are the 8-bit blocks: is_int8[b] = (b >= nb - nb8). */
+int orc_channel_order(int K, const float *score, int nb8, int32_t *perm, uint8_t *is_int8)
+{
+    if (K <= 0 || K % ORC_BLOCK != 0)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    if (nb8 < 0 || nb8 > nb)
+        return ORC_ERR_ARG;
+    orc_ranked *r = (orc_ranked *)malloc(sizeof(orc_ranked) * (size_t)K);
+    if (!r)
+        return ORC_ERR_ARG;
+    for (int k = 0; k < K; ++k) {
+        if (!isfinite(score[k])) {
+            free(r);
+            return ORC_ERR_NONFINITE;
+        }
+        r[k].score = score[k];
+        r[k].index = k;
+    }
+    qsort(r, (size_t)K, sizeof(orc_ranked), orc_rank_cmp);
+    for (int k = 0; k < K; ++k)
+        perm[k] = r[k].index;
+    for (int b = 0; b < nb; ++b)
+        is_int8[b] = (uint8_t)(b >= nb - nb8);
+    free(r);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Shared element rule: round half to even, then clamp to [-qmax, qmax].     */
+/* ------------------------------------------------------------------------ */
+
+static int orc_round_clamp(float v, int qmax)
+{
+    float r = rintf(v);
+    if (r > (float)qmax) r = (float)qmax;
+    if (r < (float)-qmax) r = (float)-qmax;
+    return (int)r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2. Weight quantization: symmetric INT4, fp16 scale per (channel, group)   */
+/* ------------------------------------------------------------------------ */
+
+/* Scale of one weight group with absmax a > 0: fp16(a / 7). A scale that
+ * rounds to zero (a below 3.5 * 2^-24) becomes the smallest fp16 subnormal,
+ * 2^-24, so that the division below stays finite. Returns the fp16 bits. */
+uint16_t orc_weight_scale(float a)
+{
+    float s = a / 7.0f;
+    uint16_t h = orc_float_to_half(s);
+    if (h == 0)
+        h = 1;
+    return h;
+}
+
+/* qw: [N][K] in permuted channel order, values in [-7, 7].
+ * sw16: [N][nb] fp16 bits. wsum: [N][nb], sum of the group's qw. */
+int orc_quantize_weights(const uint16_t *W, int N, int K, const int32_t *perm,
+                         int8_t *qw, uint16_t *sw16, int32_t *wsum)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int n = 0; n < N; ++n) {
+        const uint16_t *wrow = W + (size_t)n * K;
+        for (int b = 0; b < nb; ++b) {
+            float a = 0.0f;
+            for (int k = 0; k < ORC_BLOCK; ++k) {
+                float v = orc_half_to_float(wrow[perm[b * ORC_BLOCK + k]]);
+                if (!isfinite(v))
+                    bad = 1;
+                float av = fabsf(v);
+                if (av > a)
+                    a = av;
+            }
+            int32_t sum = 0;
+            int8_t *q = qw + (size_t)n * K + (size_t)b * ORC_BLOCK;
+            if (a == 0.0f) {
+                sw16[(size_t)n * nb + b] = 0;
+                for (int k = 0; k < ORC_BLOCK; ++k)
+                    q[k] = 0;
+            } else {
+                uint16_t h = orc_weight_scale(a);
+                float s = orc_half_to_float(h);
+                sw16[(size_t)n * nb + b] = h;
+                for (int k = 0; k < ORC_BLOCK; ++k) {
+                    float v = orc_half_to_float(wrow[perm[b * ORC_BLOCK + k]]);
+                    float d = v / s;
+                    q[k] = (int8_t)orc_round_clamp(d, 7);
+                    sum += q[k];
+                }
+            }
+            wsum[(size_t)n * nb + b] = sum;
+        }
+    }
+    return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3. Activation quantization: per token, per block, symmetric absmax        */
+/* ------------------------------------------------------------------------ */
+
+/* Reciprocal and scale of one (token, block) with absmax a > 0:
+ * inv = qmax / a and s = a / qmax, each one correctly rounded division. */
+void orc_act_scale(float a, int qmax, float *inv, float *s)
+{
+    *inv = (float)qmax / a;
+    *s = a / (float)qmax;
+}
+
+/* One element: round(x * inv) clamped to [-qmax, qmax]; the product is a
+ * single rounded multiply, never fused with anything. */
+int orc_act_quantize_value(float x, float inv, int qmax)
+{
+    float p = x * inv;
+    return orc_round_clamp(p, qmax);
+}
+
+/* qa: [M][K] in permuted channel order. sa: [M][nb].
+ * An all-zero block gets scale 0 and codes 0. */
+int orc_quantize_activations(const uint16_t *X, int M, int K, int ldx, const int32_t *perm,
+                             const uint8_t *is_int8, int8_t *qa, float *sa)
+{
+    if (M <= 0 || K <= 0 || K % ORC_BLOCK != 0 || ldx < K)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xrow = X + (size_t)m * ldx;
+        for (int b = 0; b < nb; ++b) {
+            int qmax = is_int8[b] ? 127 : 7;
+            float a = 0.0f;
+            for (int k = 0; k < ORC_BLOCK; ++k) {
+                float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                if (!isfinite(v))
+                    bad = 1;
+                float av = fabsf(v);
+                if (av > a)
+                    a = av;
+            }
+            int8_t *q = qa + (size_t)m * K + (size_t)b * ORC_BLOCK;
+            if (a == 0.0f) {
+                sa[(size_t)m * nb + b] = 0.0f;
+                for (int k = 0; k < ORC_BLOCK; ++k)
+                    q[k] = 0;
+                continue;
+            }
+            float inv, s;
+            orc_act_scale(a, qmax, &inv, &s);
+            sa[(size_t)m * nb + b] = s;
+            for (int k = 0; k < ORC_BLOCK; ++k) {
+                float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                q[k] = (int8_t)orc_act_quantize_value(v, inv, qmax);
+            }
+        }
+    }
+    return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 4. Block partials                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* P[m - m0][n][b] = sum over the block of qa[m][k'] * qw[n][k'], exact. */
+int orc_block_partials(const int8_t *qa, const int8_t *qw, int M, int N, int K, int m0, int m1,
+                       int32_t *P)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0 || m0 < 0 || m1 > M || m0 >= m1)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int m = m0; m < m1; ++m) {
+        const int8_t *a = qa + (size_t)m * K;
+        for (int n = 0; n < N; ++n) {
+            const int8_t *w = qw + (size_t)n * K;
+            int32_t *out = P + ((size_t)(m - m0) * N + n) * nb;
+            for (int b = 0; b < nb; ++b) {
+                int32_t acc = 0;
+                for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k)
+                    acc += (int32_t)a[k] * (int32_t)w[k];
+                out[b] = acc;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* The same partials through the zero-extended 4-bit code: on a 4-bit block the
+ * activation enters as u = q + 8 in [1, 15] and the offset is removed with the
+ * precomputed weight sum, P = sum(u * qw) - 8 * wsum. 8-bit blocks are signed. */
+int orc_block_partials_zero_extend(const int8_t *qa, const int8_t *qw, const int32_t *wsum,
+                                   const uint8_t *is_int8, int M, int N, int K, int m0, int m1,
+                                   int32_t *P)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0 || m0 < 0 || m1 > M || m0 >= m1)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int m = m0; m < m1; ++m) {
+        const int8_t *a = qa + (size_t)m * K;
+        for (int n = 0; n < N; ++n) {
+            const int8_t *w = qw + (size_t)n * K;
+            int32_t *out = P + ((size_t)(m - m0) * N + n) * nb;
+            for (int b = 0; b < nb; ++b) {
+                int32_t acc = 0;
+                if (is_int8[b]) {
+                    for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k)
+                        acc += (int32_t)a[k] * (int32_t)w[k];
+                } else {
+                    for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k) {
+                        uint32_t u = (uint32_t)(a[k] + 8);          /* 1 .. 15 */
+                        acc += (int32_t)u * (int32_t)w[k];
+                    }
+                    acc -= 8 * wsum[(size_t)n * nb + b];
+                }
+                out[b] = acc;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 5. Epilogue                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* For rows r of P ([rows][N][nb]) with scales sa ([rows][nb]) and sw16
+ * ([N][nb]):
+ *   y32 = 0;  for b in order:  y32 = y32 + (sa * sw) * float(P)
+ *   Y16 = fp16(y32)
+ * and, in double, yexact = sum_b sa * sw * P (each product is exact in
+ * double: 24 + 11 + 17 significant bits). Any output pointer may be NULL. */
+int orc_epilogue(const int32_t *P, const float *sa, const uint16_t *sw16, int rows, int N, int nb,
+                 float *y32, uint16_t *Y16, double *yexact)
+{
+    if (rows <= 0 || N <= 0 || nb <= 0)
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        for (int n = 0; n < N; ++n) {
+            const int32_t *p = P + ((size_t)r * N + n) * nb;
+            float y = 0.0f;
+            double ye = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                float s_x = sa[(size_t)r * nb + b];
+                float s_w = orc_half_to_float(sw16[(size_t)n * nb + b]);
+                float t = s_x * s_w;
+                float u = t * (float)p[b];
+                y = y + u;
+                ye += (double)s_x * (double)s_w * (double)p[b];
+            }
+            size_t o = (size_t)r * N + n;
+            if (y32) y32[o] = y;
+            if (Y16) Y16[o] = orc_float_to_half(y);
+            if (yexact) yexact[o] = ye;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Online forward for a row range (steps 3-5), for timing on the host        */
+/* ------------------------------------------------------------------------ */
+
+/* Quantizes rows [m0, m1) of X, forms their block partials against the
+ * already-quantized weights and applies the epilogue. Y16 and yexact are
+ * [(m1-m0)][N]; either may be NULL. */
+int orc_forward_rows(const uint16_t *X, int M, int K, int ldx, const int32_t *perm,
+                     const uint8_t *is_int8, const int8_t *qw, const uint16_t *sw16, int N,
+                     int m0, int m1, uint16_t *Y16, double *yexact)
+{
+    if (M <= 0 || K <= 0 || K % ORC_BLOCK != 0 || m0 < 0 || m1 > M || m0 >= m1 || N <= 0)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    int rows = m1 - m0;
+    int8_t *qa = (int8_t *)malloc((size_t)rows * K);
+    float *sa = (float *)malloc(sizeof(float) * (size_t)rows * nb);
+    int32_t *P = (int32_t *)malloc(sizeof(int32_t) * (size_t)rows * N * nb);
+    int rc = ORC_ERR_ARG;
+    if (qa && sa && P) {
+        rc = orc_quantize_activations(X + (size_t)m0 * ldx, rows, K, ldx, perm, is_int8, qa, sa);
+        if (rc == ORC_OK)
+            rc = orc_block_partials(qa, qw, rows, N, K, 0, rows, P);
+        if (rc == ORC_OK)
+            rc = orc_epilogue(P, sa, sw16, rows, N, nb, NULL, Y16, yexact);
+    }
+    free(qa);
+    free(sa);
+    free(P);
+    return rc;
+}
+
+/* Threads an OpenMP parallel region of this library uses. */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

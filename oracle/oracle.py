@@ -1,0 +1,238 @@
+"""ctypes front end of the CPU oracle (comet_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The product library never imports it.
+
+Logical arrays (no GPU layout here):
+  perm   int32 [K]        original channel at permuted position k'
+  flags  uint8 [nb]       1 for the 8-bit blocks (the last nb8)
+  qw     int8  [N, K]     weight codes in permuted order, [-7, 7]
+  sw16   uint16 [N, nb]   fp16 bits of the weight scales
+  wsum   int32 [N, nb]    per-group sums of qw
+  qa     int8  [M, K]     activation codes in permuted order
+  sa     f32   [M, nb]    activation scales
+  P      int32 [rows, N, nb] exact block partials
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "comet_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-fPIC", "-shared",
+          "-fopenmp", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.orc_half_to_float.restype = ctypes.c_float
+        L.orc_half_to_float.argtypes = [ctypes.c_uint16]
+        L.orc_float_to_half.restype = ctypes.c_uint16
+        L.orc_float_to_half.argtypes = [ctypes.c_float]
+        L.orc_weight_scale.restype = ctypes.c_uint16
+        L.orc_weight_scale.argtypes = [ctypes.c_float]
+        L.orc_act_scale.restype = None
+        L.orc_act_scale.argtypes = [ctypes.c_float, I, P, P]
+        L.orc_act_quantize_value.restype = I
+        L.orc_act_quantize_value.argtypes = [ctypes.c_float, ctypes.c_float, I]
+        L.orc_channel_order.argtypes = [I, P, I, P, P]
+        L.orc_quantize_weights.argtypes = [P, I, I, P, P, P, P]
+        L.orc_quantize_activations.argtypes = [P, I, I, I, P, P, P, P]
+        L.orc_block_partials.argtypes = [P, P, I, I, I, I, I, P]
+        L.orc_block_partials_zero_extend.argtypes = [P, P, P, P, I, I, I, I, I, P]
+        L.orc_epilogue.argtypes = [P, P, P, I, I, I, P, P, P]
+        L.orc_forward_rows.argtypes = [P, I, I, I, P, P, P, P, I, I, I, P, P]
+        L.orc_threads.restype = I
+        L.orc_half_to_float_array.restype = None
+        L.orc_half_to_float_array.argtypes = [P, P, ctypes.c_int64]
+        L.orc_float_to_half_array.restype = None
+        L.orc_float_to_half_array.argtypes = [P, P, ctypes.c_int64]
+        for f in ("orc_channel_order", "orc_quantize_weights", "orc_quantize_activations",
+                  "orc_block_partials", "orc_block_partials_zero_extend", "orc_epilogue",
+                  "orc_forward_rows"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def half_to_float(h: int) -> float:
+    return lib().orc_half_to_float(int(h))
+
+
+def float_to_half(f: float) -> int:
+    return lib().orc_float_to_half(float(f))
+
+
+def half_to_float_array(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.zeros(h.shape, np.float32)
+    lib().orc_half_to_float_array(_p(h), _p(out), h.size)
+    return out
+
+
+def float_to_half_array(f: np.ndarray) -> np.ndarray:
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.zeros(f.shape, np.uint16)
+    lib().orc_float_to_half_array(_p(f), _p(out), f.size)
+    return out
+
+
+def weight_scale(a: float) -> int:
+    return lib().orc_weight_scale(float(a))
+
+
+def act_scale(a: float, qmax: int) -> tuple[float, float]:
+    inv = np.zeros(1, np.float32)
+    s = np.zeros(1, np.float32)
+    lib().orc_act_scale(float(a), int(qmax), _p(inv), _p(s))
+    return float(inv[0]), float(s[0])
+
+
+def act_quantize_value(x: float, inv: float, qmax: int) -> int:
+    return lib().orc_act_quantize_value(float(x), float(inv), int(qmax))
+
+
+def channel_order(score: np.ndarray, nb8: int) -> tuple[np.ndarray, np.ndarray]:
+    score = np.ascontiguousarray(score, dtype=np.float32)
+    K = score.shape[0]
+    perm = np.zeros(K, np.int32)
+    flags = np.zeros(max(K // 128, 1), np.uint8)
+    _check(lib().orc_channel_order(K, _p(score), int(nb8), _p(perm), _p(flags)), "channel_order")
+    return perm, flags[: K // 128]
+
+
+def quantize_weights(W16: np.ndarray, perm: np.ndarray):
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    N, K = W16.shape
+    nb = K // 128
+    qw = np.zeros((N, K), np.int8)
+    sw16 = np.zeros((N, nb), np.uint16)
+    wsum = np.zeros((N, nb), np.int32)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    _check(lib().orc_quantize_weights(_p(W16), N, K, _p(perm), _p(qw), _p(sw16), _p(wsum)),
+           "quantize_weights")
+    return qw, sw16, wsum
+
+
+def quantize_activations(X16: np.ndarray, perm: np.ndarray, flags: np.ndarray):
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    M, K = X16.shape
+    nb = K // 128
+    qa = np.zeros((M, K), np.int8)
+    sa = np.zeros((M, nb), np.float32)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    _check(lib().orc_quantize_activations(_p(X16), M, K, K, _p(perm), _p(flags), _p(qa), _p(sa)),
+           "quantize_activations")
+    return qa, sa
+
+
+def block_partials(qa: np.ndarray, qw: np.ndarray, rows: tuple[int, int] | None = None):
+    qa = np.ascontiguousarray(qa, dtype=np.int8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    P = np.zeros((m1 - m0, N, K // 128), np.int32)
+    _check(lib().orc_block_partials(_p(qa), _p(qw), M, N, K, m0, m1, _p(P)), "block_partials")
+    return P
+
+
+def block_partials_zero_extend(qa, qw, wsum, flags, rows=None):
+    qa = np.ascontiguousarray(qa, dtype=np.int8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    wsum = np.ascontiguousarray(wsum, dtype=np.int32)
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    P = np.zeros((m1 - m0, N, K // 128), np.int32)
+    _check(lib().orc_block_partials_zero_extend(_p(qa), _p(qw), _p(wsum), _p(flags), M, N, K,
+                                                m0, m1, _p(P)), "block_partials_zero_extend")
+    return P
+
+
+def epilogue(P: np.ndarray, sa_rows: np.ndarray, sw16: np.ndarray):
+    """(y32 [rows, N] f32, Y16 [rows, N] fp16 bits, yexact [rows, N] f64)."""
+    P = np.ascontiguousarray(P, dtype=np.int32)
+    sa_rows = np.ascontiguousarray(sa_rows, dtype=np.float32)
+    sw16 = np.ascontiguousarray(sw16, dtype=np.uint16)
+    rows, N, nb = P.shape
+    y32 = np.zeros((rows, N), np.float32)
+    Y16 = np.zeros((rows, N), np.uint16)
+    ye = np.zeros((rows, N), np.float64)
+    _check(lib().orc_epilogue(_p(P), _p(sa_rows), _p(sw16), rows, N, nb, _p(y32), _p(Y16),
+                              _p(ye)), "epilogue")
+    return y32, Y16, ye
+
+
+def forward_rows(X16, perm, flags, qw, sw16, rows):
+    """Steps 3-5 for rows [m0, m1) of X: (Y16 [rows, N], yexact [rows, N])."""
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    M, K = X16.shape
+    N = qw.shape[0]
+    m0, m1 = rows
+    Y16 = np.zeros((m1 - m0, N), np.uint16)
+    ye = np.zeros((m1 - m0, N), np.float64)
+    _check(lib().orc_forward_rows(_p(X16), M, K, K, _p(np.ascontiguousarray(perm, np.int32)),
+                                  _p(np.ascontiguousarray(flags, np.uint8)),
+                                  _p(np.ascontiguousarray(qw, np.int8)),
+                                  _p(np.ascontiguousarray(sw16, np.uint16)), N, m0, m1,
+                                  _p(Y16), _p(ye)), "forward_rows")
+    return Y16, ye
+
+
+def threads() -> int:
+    return lib().orc_threads()
+
+
+def quantize_layer(X16, W16, score, nb8):
+    """Every logical array of one layer (all rows): a dict."""
+    perm, flags = channel_order(score, nb8)
+    qw, sw16, wsum = quantize_weights(W16, perm)
+    qa, sa = quantize_activations(X16, perm, flags)
+    return {"perm": perm, "flags": flags, "qw": qw, "sw16": sw16, "wsum": wsum,
+            "qa": qa, "sa": sa}
+
+
+def reference(X16, W16, score, nb8, rows=None):
+    """Full oracle result for rows (default all): quantized arrays plus P, y32, Y16, yexact."""
+    d = quantize_layer(X16, W16, score, nb8)
+    M = X16.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    P = block_partials(d["qa"], d["qw"], (m0, m1))
+    y32, Y16, ye = epilogue(P, d["sa"][m0:m1], d["sw16"])
+    d.update({"P": P, "y32": y32, "Y16": Y16, "yexact": ye, "rows": (m0, m1)})
+    return d

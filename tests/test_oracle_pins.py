@@ -1,0 +1,543 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each check compares the oracle with something it does not compute the same
+way: a library routine (numpy's IEEE fp16 cast, Python's sort, a float64
+matmul), exact rational arithmetic, a closed form, an invariant, a brute-force
+enumeration, or a hand-derived worked example (tests/golden/). The aim is that
+a plausible slip anywhere in the oracle (a dropped term, a wrong sign or index,
+a transposed operand, the permutation applied the wrong way round, the wrong
+rounding mode) fails at least one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from gen import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+ALL_POS_FP16 = np.arange(1, 0x7C00, dtype=np.uint16)   # every positive finite fp16
+
+
+def f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def small_layer(M, K, N, seed, nb8, outliers=True):
+    cfg = synth.LayerConfig("t", M, K, N, seed, x_kind="planted" if outliers else "student_t")
+    X = synth.make_x(cfg)
+    W = synth.make_w(cfg)
+    s = synth.make_scores(cfg)
+    return X, W, s, nb8
+
+
+def dequant_product(d):
+    """sum_k (s_x q_a)(s_w q_w) as a float64 matmul of the dequantized operands."""
+    K = d["qa"].shape[1]
+    blk = np.arange(K) // 128
+    A = d["qa"].astype(np.float64) * d["sa"].astype(np.float64)[:, blk]
+    B = d["qw"].astype(np.float64) * f16(d["sw16"])[:, blk]
+    return A @ B.T, np.abs(A) @ np.abs(B).T
+
+
+# --------------------------------------------------------------------------
+# IEEE binary16 conversions
+# --------------------------------------------------------------------------
+
+def test_half_to_float_exhaustive(orc):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.half_to_float_array(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_float_to_half_matches_numpy(orc):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    # plus every fp16 value, every midpoint between neighbours, and nudges around them
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    extra = np.concatenate([v.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+                            np.nextafter(mids, np.float32(np.inf)), [65504, 65519.99, 65520,
+                                                                    1e9, 2.0**-25, 2.0**-26]])
+    f = np.concatenate([f, extra.astype(np.float32), -extra.astype(np.float32)])
+    got = orc.float_to_half_array(f)
+    with np.errstate(over="ignore"):
+        ref = f.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# 1. Channel order
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,nb8", [(128, 0), (128, 1), (512, 1), (1024, 3), (4096, 4)])
+def test_channel_order_against_python_sort(orc, K, nb8):
+    rng = np.random.default_rng(K + nb8)
+    score = rng.integers(0, 40, size=K).astype(np.float32)  # many ties
+    perm, flags = orc.channel_order(score, nb8)
+    ref = sorted(range(K), key=lambda k: (float(score[k]), k))
+    assert perm.tolist() == ref
+    assert sorted(perm.tolist()) == list(range(K))           # bijection
+    assert np.all(np.diff(score[perm]) >= 0)                  # non-decreasing scores
+    nb = K // 128
+    assert flags.tolist() == [0] * (nb - nb8) + [1] * nb8    # 8-bit blocks last
+
+
+def test_channel_order_closed_form(orc):
+    # score(c) = 37 c mod 256 is a bijection of [0, 256); 37 * 173 = 1 (mod 256),
+    # so the channel at sorted position k' is 173 k' mod 256.
+    K = 256
+    score = ((37 * np.arange(K)) % K).astype(np.float32)
+    perm, flags = orc.channel_order(score, 1)
+    assert perm.tolist() == [(173 * k) % K for k in range(K)]
+    assert flags.tolist() == [0, 1]
+
+
+def test_channel_order_rejects(orc):
+    with pytest.raises(ValueError):
+        orc.channel_order(np.zeros(100, np.float32), 0)      # K not a multiple of 128
+    with pytest.raises(ValueError):
+        orc.channel_order(np.zeros(256, np.float32), 3)      # nb8 > nb
+    with pytest.raises(ValueError):
+        orc.channel_order(np.zeros(256, np.float32), -1)
+    s = np.zeros(256, np.float32)
+    s[5] = np.nan
+    with pytest.raises(ValueError):
+        orc.channel_order(s, 0)
+
+
+def test_outliers_land_in_int8_blocks(orc):
+    cfg = synth.CONFIGS["q_proj_7b"]
+    score = synth.make_scores(cfg)
+    ch, _ = synth.outlier_plan(cfg)
+    perm, flags = orc.channel_order(score, cfg.nb8)
+    int8_channels = set(perm[(cfg.nb - cfg.nb8) * 128:].tolist())
+    # every planted outlier channel (x20..x100) outranks every normal channel
+    assert set(ch.tolist()) <= int8_channels
+
+
+# --------------------------------------------------------------------------
+# 2. Weight quantization
+# --------------------------------------------------------------------------
+
+def test_weight_scale_exhaustive(orc):
+    """Every positive finite fp16 absmax: the scale is an fp16 value nearest a/7."""
+    a = f16(ALL_POS_FP16)
+    got = np.array([orc.weight_scale(float(x)) for x in a], dtype=np.uint16)
+    s = f16(got)
+    assert np.all(s > 0)
+    exact = a / 7.0
+    tiny = exact < 2.0 ** -25          # a/7 rounds to zero in fp16 -> smallest subnormal
+    assert np.all(got[tiny] == 1)
+    # nearest fp16: no other fp16 value is closer to a/7 (ties within the fp32 rounding
+    # of the intermediate quotient are allowed either way)
+    up = f16(got.astype(np.uint32) + 1)
+    dn = f16(np.maximum(got.astype(np.int64) - 1, 0).astype(np.uint16))
+    ok = tiny | ((np.abs(s - exact) <= np.abs(up - exact) * (1 + 2**-22)) &
+                 (np.abs(s - exact) <= np.abs(dn - exact) * (1 + 2**-22)))
+    assert np.all(ok)
+
+
+def brute_nearest(v, s, qmax):
+    """argmin over j in [-qmax, qmax] of |v - j s|, exact, ties to the even j."""
+    v = v if isinstance(v, Fraction) else Fraction(float(v))
+    s = s if isinstance(s, Fraction) else Fraction(float(s))
+    best = None
+    for j in range(-qmax, qmax + 1):
+        d = abs(v - j * s)
+        if best is None or d < best[0] or (d == best[0] and j % 2 == 0):
+            best = (d, j)
+    return best[1]
+
+
+def test_weight_quantization_brute_force(orc):
+    X, W, score, _ = small_layer(4, 256, 6, 11, 0)
+    # make one group all-zero and one a single tiny value (subnormal scale)
+    W = W.copy()
+    W[2, :] = 0
+    W[3, :] = 0
+    W[3, 17] = 2  # fp16 bits 2 = 2 * 2^-24
+    # a/7 = (10/7) 2^-24 rounds to the smallest subnormal, so the code -10 is clamped to -7
+    W[4, 128:] = 0
+    W[4, 130] = 0x800A  # -10 * 2^-24
+    perm = np.arange(256, dtype=np.int32)
+    qw, sw16, wsum = orc.quantize_weights(W, perm)
+    wv = f16(W)
+    for n in range(6):
+        for b in range(2):
+            s = f16(sw16[n, b])
+            blk = wv[n, b * 128:(b + 1) * 128]
+            if np.all(blk == 0):
+                assert sw16[n, b] == 0 and np.all(qw[n, b * 128:(b + 1) * 128] == 0)
+                continue
+            for k in range(128):
+                assert qw[n, b * 128 + k] == brute_nearest(blk[k], s, 7)
+            assert wsum[n, b] == int(qw[n, b * 128:(b + 1) * 128].astype(np.int64).sum())
+            # the absmax element lands on +-7
+            kk = int(np.argmax(np.abs(blk)))
+            if s > 2.0 ** -24:
+                assert abs(int(qw[n, b * 128 + kk])) == 7
+    assert sw16[3, 0] == 1 and qw[3, 17] == 2     # 2 * 2^-24 / 2^-24 = 2
+    assert sw16[4, 1] == 1 and qw[4, 130] == -7   # clamped
+
+
+def test_weight_round_trip_bound(orc):
+    cfg = synth.CONFIGS["q_proj_7b"]
+    W = synth.make_w(cfg)[:256]
+    score = synth.make_scores(cfg)
+    perm, _ = orc.channel_order(score, cfg.nb8)
+    qw, sw16, wsum = orc.quantize_weights(W, perm)
+    wp = f16(W)[:, perm]
+    s = f16(sw16)[:, np.arange(cfg.K) // 128]
+    err = np.abs(wp - qw * s)
+    assert np.all(err <= s / 2 * (1 + 2**-20))
+    assert np.all(np.abs(qw) <= 7)
+    assert np.array_equal(wsum, qw.reshape(256, -1, 128).astype(np.int64).sum(-1))
+
+
+# --------------------------------------------------------------------------
+# 3. Activation quantization
+# --------------------------------------------------------------------------
+
+def _correctly_rounded_f32(x: Fraction, got: float) -> bool:
+    g = Fraction(float(np.float32(got)))
+    lo = Fraction(float(np.nextafter(np.float32(got), np.float32(-np.inf))))
+    hi = Fraction(float(np.nextafter(np.float32(got), np.float32(np.inf))))
+    d = abs(g - x)
+    if d > abs(lo - x) or d > abs(hi - x):
+        return False
+    if d == abs(lo - x) or d == abs(hi - x):       # exact tie: even significand wins
+        return (np.float32(got).view(np.uint32) & 1) == 0
+    return True
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_act_scale_exhaustive(orc, qmax):
+    """Every positive finite fp16 absmax: inv = qmax/a and s = a/qmax correctly rounded,
+    s * qmax within one fp32 ulp of a, and the absmax element itself codes to qmax."""
+    a = f16(ALL_POS_FP16)
+    for x in a:
+        inv, s = orc.act_scale(float(x), qmax)
+        fx = Fraction(float(x))
+        assert _correctly_rounded_f32(Fraction(qmax) / fx, inv)
+        assert _correctly_rounded_f32(fx / qmax, s)
+        ulp = float(np.spacing(np.float32(x)))
+        assert abs(float(s) * qmax - float(x)) <= ulp
+        assert orc.act_quantize_value(float(x), inv, qmax) == qmax
+        assert orc.act_quantize_value(-float(x), inv, qmax) == -qmax
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_act_element_every_fp16(orc, qmax):
+    """Every fp16 x in [-a, a] at a few absmax values: the code is a nearest integer of
+    the exact t = x qmax / a up to the fp32 error of inv and of the product
+    (|q - t| <= 1/2 + 2^-22 |t|), it is the nearest integer away from half-way points,
+    and exact half-way products round to even."""
+    allv = f16(np.arange(0, 0x7C00, dtype=np.uint16))
+    for a in (7.0, 1.0, 0.3330078125, 100.0, 2.0 ** -20, 60000.0):
+        inv, s = orc.act_scale(a, qmax)
+        xs = allv[allv <= a]
+        xs = np.concatenate([xs, -xs])
+        for x in xs[:: max(1, len(xs) // 4000)]:
+            q = orc.act_quantize_value(float(x), inv, qmax)
+            t = Fraction(float(x)) * qmax / Fraction(a)
+            assert abs(q) <= qmax
+            assert abs(Fraction(q) - t) <= Fraction(1, 2) + abs(t) * Fraction(1, 2**22)
+            fl = t.numerator // t.denominator
+            if abs((t - fl) - Fraction(1, 2)) > abs(t) * Fraction(1, 2**21):
+                assert q == (fl + 1 if t - fl > Fraction(1, 2) else fl)
+            p32 = np.float32(x) * np.float32(inv)
+            if float(p32) - np.floor(float(p32)) == 0.5:
+                assert q % 2 == 0
+
+
+def test_activation_round_trip_and_gather(orc):
+    """X[m, perm[k']] ~ s_x q_a within s_x/2: catches a gather applied the wrong way."""
+    cfg = synth.CONFIGS["q_proj_7b"]
+    X = synth.make_x(cfg)
+    score = synth.make_scores(cfg)
+    perm, flags = orc.channel_order(score, cfg.nb8)
+    qa, sa = orc.quantize_activations(X, perm, flags)
+    xp = f16(X)[:, perm]
+    s = sa.astype(np.float64)[:, np.arange(cfg.K) // 128]
+    err = np.abs(xp - qa * s)
+    assert np.all(err <= s / 2 + 2.0**-22 * np.abs(xp) + 1e-30)
+    qmax = np.where(flags[np.arange(cfg.K) // 128] == 1, 127, 7)
+    assert np.all(np.abs(qa) <= qmax[None, :])
+    # each (token, block) reaches its range end at the absmax element
+    assert np.all(np.abs(qa).reshape(cfg.M, cfg.nb, 128).max(-1) ==
+                  np.where(flags == 1, 127, 7)[None, :])
+    # and the gather in the wrong direction does not satisfy the bound
+    inv_perm = np.argsort(perm)
+    assert not np.all(np.abs(f16(X)[:, inv_perm] - qa * s) <= s / 2 + 1e-30)
+
+
+# --------------------------------------------------------------------------
+# 4-5. Partials and epilogue
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nb8", [0, 1, 2, 4])
+def test_dequantize_then_matmul(orc, nb8):
+    """sum_b s_x s_w P equals a float64 matmul of the dequantized operands; nb8 = 0 is
+    plain W4A4 and nb8 = nb plain W4A8 (per-token per-128-group INT8 A, INT4 W)."""
+    X, W, score, _ = small_layer(24, 512, 40, 21, nb8)
+    d = orc.reference(X, W, score, nb8)
+    ref, mag = dequant_product(d)
+    assert np.all(np.abs(d["yexact"] - ref) <= 1e-12 * mag + 1e-300)
+    # y32 is an fp32 sum of nb rounded terms
+    nb = 4
+    t = np.abs(d["sa"].astype(np.float64)[:, None, :] * f16(d["sw16"])[None, :, :] * d["P"])
+    bound = (nb + 2) * 2.0**-24 * t.sum(-1) * (1 + 2**-10) + 2.0**-140
+    assert np.all(np.abs(d["y32"] - d["yexact"]) <= bound)
+    # Y16 is the fp16 rounding of y32 (library cast)
+    assert np.array_equal(d["Y16"], d["y32"].astype(np.float16).view(np.uint16))
+
+
+def test_error_bound_vs_unquantized(orc):
+    """A-priori bound of the quantization error against X W^T in float64."""
+    for name in ("tiny", "q_proj_7b"):
+        cfg = synth.CONFIGS[name]
+        X, W, score = synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg)
+        rows = (0, min(cfg.M, 32))
+        d = orc.reference(X, W, score, cfg.nb8, rows=rows)
+        xp = f16(X)[rows[0]:rows[1]][:, d["perm"]]
+        wp = f16(W)[:, d["perm"]]
+        exact = xp @ wp.T
+        nb = cfg.nb
+        sa = d["sa"][rows[0]:rows[1]].astype(np.float64)
+        sw = f16(d["sw16"])
+        axb = np.abs(xp).reshape(-1, nb, 128).sum(-1)          # [m, b]
+        awb = np.abs(wp).reshape(-1, nb, 128).sum(-1)          # [n, b]
+        bound = (0.5 * sa @ awb.T + 0.5 * axb @ sw.T + 0.25 * 128 * sa @ sw.T
+                 + 1e-6 * np.abs(xp) @ np.abs(wp).T)
+        assert np.all(np.abs(d["yexact"] - exact) <= bound)
+
+
+def test_error_statistics_vs_unquantized(orc):
+    """Rounding to the nearest code leaves errors close to independent and uniform on
+    [-s/2, s/2], so the mean squared error of y against X W^T is predicted by
+    sum_k (s_x^2 / 12) w'^2 + x'^2 (s_w^2 / 12). The observed value must agree within
+    a factor of two; dropping the dominant block or flipping its sign must not."""
+    for name in ("tiny", "q_proj_7b"):
+        cfg = synth.CONFIGS[name]
+        X, W, score = synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg)
+        rows = (0, min(cfg.M, 32))
+        d = orc.reference(X, W, score, cfg.nb8, rows=rows)
+        xp = f16(X)[rows[0]:rows[1]][:, d["perm"]]
+        wp = f16(W)[:, d["perm"]]
+        exact = xp @ wp.T
+        nb = cfg.nb
+        sa = d["sa"][rows[0]:rows[1]].astype(np.float64)
+        sw = f16(d["sw16"])
+        w2 = (wp ** 2).reshape(-1, nb, 128).sum(-1)           # [n, b]
+        x2 = (xp ** 2).reshape(-1, nb, 128).sum(-1)           # [m, b]
+        pred = ((sa ** 2) @ w2.T + x2 @ (sw ** 2).T) / 12.0
+        ratio = np.mean((d["yexact"] - exact) ** 2) / np.mean(pred)
+        assert 0.5 < ratio < 2.0, (name, ratio)
+        tb = (sa[:, None, :] * sw[None, :, :] * d["P"])
+        big = int(np.argmax(np.sqrt((tb ** 2).mean(axis=(0, 1)))))
+        for wrong in (d["yexact"] - tb[:, :, big], d["yexact"] - 2 * tb[:, :, big]):
+            assert np.mean((wrong - exact) ** 2) / np.mean(pred) > 4.0
+
+
+def test_single_block_closed_form(orc):
+    """K = 128: one term, y32 = fl(fl(s_x s_w) P) and yexact = s_x s_w P exactly."""
+    X, W, score, _ = small_layer(8, 128, 16, 31, 0)
+    for nb8 in (0, 1):
+        d = orc.reference(X, W, score, nb8)
+        sx = d["sa"][:, 0].astype(np.float64)
+        sw = f16(d["sw16"][:, 0])
+        P = d["P"][:, :, 0].astype(np.float64)
+        assert np.array_equal(d["yexact"], sx[:, None] * sw[None, :] * P)
+
+
+def test_one_hot_weights(orc):
+    """One nonzero weight c per group: q_w = sign(c) 7 there, s_w = fp16(|c| / 7),
+    so y is the sum over blocks of s_x q_a[k*] * 7 s_w sign(c), close to sum x[k*] c."""
+    M, K, N = 6, 384, 5
+    X, _, score, _ = small_layer(M, K, N, 41, 1)
+    rng = np.random.default_rng(3)
+    W = np.zeros((N, K), np.float32)
+    picks = {}
+    for n in range(N):
+        for b in range(3):
+            k = b * 128 + int(rng.integers(128))
+            W[n, k] = rng.choice([-1, 1]) * rng.uniform(0.01, 0.05)
+            picks[(n, b)] = k
+    W16 = synth.to_fp16(W)
+    score = np.zeros(K, np.float32)          # identity permutation
+    d = orc.reference(X, W16, score, 1)
+    wv, xv = f16(W16), f16(X)
+    for n in range(N):
+        for b in range(3):
+            k = picks[(n, b)]
+            assert d["qw"][n, k] == 7 * np.sign(wv[n, k])
+            assert d["sw16"][n, b] == synth.to_fp16(np.float32(abs(wv[n, k])) / np.float32(7))
+            assert np.count_nonzero(d["qw"][n, b * 128:(b + 1) * 128]) == 1
+    for m in range(M):
+        for n in range(N):
+            approx = sum(xv[m, picks[(n, b)]] * wv[n, picks[(n, b)]] for b in range(3))
+            tol = sum(d["sa"][m, b] / 2 * abs(wv[n, picks[(n, b)]]) * 1.001 for b in range(3))
+            assert abs(d["yexact"][m, n] - approx) <= tol + 1e-12
+
+
+def test_brute_force_tiny(orc):
+    """M, N <= 4, K = 256: every step by enumeration with exact rationals."""
+    X, W, score, _ = small_layer(3, 256, 4, 51, 1)
+    d = orc.reference(X, W, score, 1)
+    K, nb = 256, 2
+    perm = sorted(range(K), key=lambda k: (float(score[k]), k))
+    xv, wv = f16(X), f16(W)
+    for m in range(3):
+        for b in range(nb):
+            qmax = 127 if b == 1 else 7
+            blk = [xv[m, perm[b * 128 + k]] for k in range(128)]
+            a = max(abs(v) for v in blk)
+            s = float(np.float32(a) / np.float32(qmax))
+            assert d["sa"][m, b] == np.float32(s)
+            for k in range(128):
+                # x * inv carries two fp32 roundings; away from half-way points the code
+                # is the exact nearest integer of x * qmax / a
+                t = Fraction(blk[k]) * qmax / Fraction(a)
+                q = d["qa"][m, b * 128 + k]
+                frac = t - (t.numerator // t.denominator)
+                if abs(frac - Fraction(1, 2)) > Fraction(1, 10**5):
+                    assert q == brute_nearest(t, 1, qmax), (m, b, k)
+    for n in range(4):
+        for b in range(nb):
+            blk = [wv[n, perm[b * 128 + k]] for k in range(128)]
+            s = f16(d["sw16"][n, b])
+            for k in range(128):
+                assert d["qw"][n, b * 128 + k] == brute_nearest(blk[k], s, 7)
+    for m in range(3):
+        for n in range(4):
+            for b in range(nb):
+                p = sum(int(d["qa"][m, b * 128 + k]) * int(d["qw"][n, b * 128 + k])
+                        for k in range(128))
+                assert d["P"][m, n, b] == p
+            ye = sum(Fraction(float(d["sa"][m, b])) * Fraction(float(f16(d["sw16"][n, b])))
+                     * int(d["P"][m, n, b]) for b in range(nb))
+            assert abs(Fraction(float(d["yexact"][m, n])) - ye) <= abs(ye) * Fraction(1, 2**50)
+
+
+def test_joint_permutation_invariance(orc):
+    """Relabelling the channels of X, W and the scores with one permutation leaves
+    every result bit-identical (scores are tie-free across block boundaries)."""
+    X, W, _, _ = small_layer(16, 512, 32, 61, 1)
+    score = np.random.default_rng(61).permutation(512).astype(np.float32) * 0.25
+    srt = np.sort(score)
+    for b in range(1, 4):    # no tie straddles a block boundary
+        assert srt[128 * b - 1] != srt[128 * b]
+    d0 = orc.reference(X, W, score, 1)
+    pi = np.random.default_rng(5).permutation(512)
+    d1 = orc.reference(X[:, pi], W[:, pi], score[pi], 1)
+    for key in ("sa", "sw16", "wsum", "P", "y32", "Y16", "yexact"):
+        assert np.array_equal(d0[key], d1[key]), key
+
+
+def test_within_block_shuffle_invariance(orc):
+    """Reordering channels inside each block changes no scale, sum, partial or output."""
+    X, W, score, _ = small_layer(12, 512, 24, 71, 2)
+    d0 = orc.reference(X, W, score, 2)
+    rng = np.random.default_rng(9)
+    perm2 = d0["perm"].copy()
+    for b in range(4):
+        perm2[b * 128:(b + 1) * 128] = rng.permutation(perm2[b * 128:(b + 1) * 128])
+    qw, sw16, wsum = orc.quantize_weights(W, perm2)
+    qa, sa = orc.quantize_activations(X, perm2, d0["flags"])
+    P = orc.block_partials(qa, qw)
+    y32, Y16, ye = orc.epilogue(P, sa, sw16)
+    assert np.array_equal(sa, d0["sa"]) and np.array_equal(sw16, d0["sw16"])
+    assert np.array_equal(wsum, d0["wsum"]) and np.array_equal(P, d0["P"])
+    assert np.array_equal(Y16, d0["Y16"]) and np.array_equal(ye, d0["yexact"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "q_proj_7b", "down_7b"])
+def test_zero_extend_equals_sign_extend(orc, name):
+    """For 4-bit blocks, sum((q+8) w) - 8 sum(w) == sum(q w) exactly, every block."""
+    cfg = synth.CONFIGS[name]
+    X, W, score = synth.make_x(cfg, rows=min(cfg.M, 16)), synth.make_w(cfg), synth.make_scores(cfg)
+    d = orc.quantize_layer(X, W[:256], score, cfg.nb8)
+    P = orc.block_partials(d["qa"], d["qw"])
+    Pz = orc.block_partials_zero_extend(d["qa"], d["qw"], d["wsum"], d["flags"])
+    assert np.array_equal(P, Pz)
+
+
+def test_zero_extend_identity_random_nibbles():
+    rng = np.random.default_rng(1)
+    q = rng.integers(-7, 8, size=(2000, 128))
+    w = rng.integers(-7, 8, size=(2000, 128))
+    lhs = ((q + 8) * w).sum(1) - 8 * w.sum(1)
+    assert np.array_equal(lhs, (q * w).sum(1))
+
+
+def test_partials_extremes(orc):
+    """|P| <= 127 * 7 * 128 = 113792, reached by an all-max block."""
+    K = 128
+    X = synth.to_fp16(np.ones((2, K), np.float32))
+    X[1] = synth.to_fp16(-np.ones(K, np.float32))
+    W = synth.to_fp16(np.full((2, K), 0.5, np.float32))
+    W[1] = synth.to_fp16(np.full(K, -0.5, np.float32))
+    d = orc.reference(X, W, np.zeros(K, np.float32), 1)
+    assert d["P"][:, :, 0].tolist() == [[113792, -113792], [-113792, 113792]]
+
+
+# --------------------------------------------------------------------------
+# Hand-derived worked examples
+# --------------------------------------------------------------------------
+
+def _expand(spec, K):
+    out = np.zeros(K)
+    for seg in spec:
+        if "from" in seg:
+            out[seg["from"]:seg["to"]] = seg["value"]
+        elif seg["parity"] == "even":
+            out[0::2] = seg["value"]
+        elif seg["parity"] == "odd":
+            out[1::2] = seg["value"]
+        else:
+            out[:] = seg["value"]
+    return out
+
+
+def test_golden_worked_examples(orc):
+    ex = json.load(open(GOLDEN))["examples"]
+    for e in ex:
+        K = e["K"]
+        X = synth.to_fp16(np.tile(_expand(e["X"], K), (e["M"], 1)))
+        score = np.full(K, e["score"]["all"], np.float32)
+        perm, flags = orc.channel_order(score, e["nb8"])
+        exp = e["expect"]
+        assert np.array_equal(perm, np.arange(K))
+        qa, sa = orc.quantize_activations(X, perm, flags)
+        if "flags" in exp:
+            assert flags.tolist() == exp["flags"], e["name"]
+        assert np.array_equal(qa[0], _expand(exp["qa"], K).astype(np.int8)), e["name"]
+        sa_exp = [np.float32(1) / np.float32(127) if v == "fp32(1/127)" else v
+                  for v in exp["sa"]]
+        assert np.array_equal(sa[0], np.array(sa_exp, np.float32)), e["name"]
+        if "W" not in e:
+            continue
+        W = synth.to_fp16(np.tile(_expand(e["W"], K), (e["N"], 1)))
+        qw, sw16, wsum = orc.quantize_weights(W, perm)
+        assert sw16[0].tolist() == exp["sw16"], e["name"]
+        assert np.array_equal(qw[0], _expand(exp["qw"], K).astype(np.int8)), e["name"]
+        assert wsum[0].tolist() == exp["wsum"], e["name"]
+        P = orc.block_partials(qa, qw)
+        assert P[0, 0].tolist() == exp["P"], e["name"]
+        y32, Y16, ye = orc.epilogue(P, sa, sw16)
+        if "y32" in exp:
+            assert y32[0].tolist() == exp["y32"] and Y16[0].tolist() == exp["Y16"]
+            assert ye[0].tolist() == exp["yexact"]
+        if "P_zero_extend_raw" in exp:
+            Pz = orc.block_partials_zero_extend(qa, qw, wsum, flags)
+            assert Pz[0, 0, 0] + 8 * wsum[0, 0] == exp["P_zero_extend_raw"][0]
