@@ -1,0 +1,246 @@
+"""Benchmark of the W4Ax mixed-precision linear layer on one MI355X.
+
+A step is one pass of the online path over one batch of synthetic input:
+comet_quant_act then comet_w4ax_gemm, for every layer of the workload. The
+offline steps (channel ranking, weight quantization and packing) run once
+before timing, as the method prescribes for static weights.
+
+Default workload: the LLaMA-70B prefill pair, 4096 tokens, down_proj
+(K = 28672 -> N = 8192, 30% 8-bit blocks) and up_proj (K = 8192 -> N = 28672,
+7 of 64 blocks 8-bit). `--workload decode_70b` times the decode sweep
+(M in {1, 4, 16, 64} x N in {10240, 8192, 28672}, K = 8192).
+
+Prints one JSON line. `value` is effective TOPS: 2 M N K per layer, summed,
+over the measured step time. The roofline object is for comet_w4ax_gemm, the
+dominant kernel, from HIP events recorded around its launches on the stream
+they run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+
+WORKLOADS = {
+    "prefill_70b": ["prefill_down_70b", "prefill_up_70b"],
+    "decode_70b": [f"decode_70b_n{n}_m{m}" for n in (10240, 8192, 28672) for m in (1, 4, 16, 64)],
+    "q_proj_7b": ["q_proj_7b"],
+    "mlp_7b": ["up_gate_7b", "down_7b"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_bytes(M, N, K, nb8):
+    """Bytes the method must move for one GEMM: packed weights, weight scales and
+    sums, activation codes and scales, fp16 output."""
+    nb = K // 128
+    nb4 = nb - nb8
+    return N * K // 2 + 2 * N * nb + 2 * N * nb4 + M * (64 * nb4 + 128 * nb8) + 4 * M * nb + 2 * M * N
+
+
+def quant_bytes(M, K, nb8):
+    nb = K // 128
+    nb4 = nb - nb8
+    return 2 * M * K + 4 * K + M * (64 * nb4 + 128 * nb8) + 4 * M * nb
+
+
+class Layer:
+    def __init__(self, name, copies, torch, comet, synth):
+        cfg = synth.CONFIGS[name]
+        self.cfg = cfg
+        self.name = name
+        t0 = time.time()
+        X, W, score = synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg)
+        self.host = {"X": X, "W": W, "score": score}
+        pk = comet.comet_pack_weights(W, score, cfg.nb8)
+        self.pk = pk
+        w = comet.upload_weights(pk)
+        self.w = [w] + [{k: (v.clone() if hasattr(v, "clone") else v) for k, v in w.items()}
+                        for _ in range(copies - 1)]
+        self.X = torch.from_numpy(X.view(np.float16)).cuda()
+        M, K, N = cfg.M, cfg.K, cfg.N
+        self.Xq = torch.empty(comet.xq_bytes(M, K, cfg.nb8), dtype=torch.uint8, device="cuda")
+        self.xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+        self.Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        need = comet.workspace_bytes(M, N, K, cfg.nb8)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
+        self.ops = 2.0 * M * N * K
+        self.gbytes = gemm_bytes(M, N, K, cfg.nb8)
+        self.qbytes = quant_bytes(M, K, cfg.nb8)
+        log(f"[bench] {name}: M={M} K={K} N={N} nb8={cfg.nb8} ready in {time.time() - t0:.1f}s "
+            f"({copies} weight copies)")
+
+
+def copies_for(cfg, target_bytes=1 << 30):
+    per = cfg.N * cfg.K // 2
+    return int(max(1, min(32, -(-target_bytes // per))))
+
+
+def run_gpu(layers, steps, warmup, torch, comet):
+    """Warm up, then time exactly `steps` steps between two synchronizations.
+    Events recorded on the launch stream around every launch give the per-kernel
+    durations inside the same timed region."""
+    ev = {l.name: [] for l in layers}
+    qev = {l.name: [] for l in layers}
+
+    def step(i, record):
+        for l in layers:
+            w = l.w[i % len(l.w)]
+            if record:
+                a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                a.record()
+            comet.comet_quant_act(l.X, w["perm"], l.cfg.nb8, Xq=l.Xq, x_scale=l.xs)
+            if record:
+                b.record()
+            comet.comet_w4ax_gemm(l.Xq, l.xs, w, l.cfg.M, Y=l.Y, workspace=l.ws)
+            if record:
+                c.record()
+                qev[l.name].append((a, b))
+                ev[l.name].append((b, c))
+
+    for i in range(warmup):
+        step(i, False)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    per = {}
+    for l in layers:
+        g = [a.elapsed_time(b) for a, b in ev[l.name]]
+        q = [a.elapsed_time(b) for a, b in qev[l.name]]
+        per[l.name] = {"gemm_ms": float(np.mean(g)), "gemm_ms_p10": float(np.percentile(g, 10)),
+                       "gemm_ms_p90": float(np.percentile(g, 90)), "quant_ms": float(np.mean(q))}
+    return step_ms, per
+
+
+def cpu_baseline(layers, budget_s):
+    """The oracle as it stands, on a bounded sample of rows of every layer: host
+    time of steps 3-5 (activation quantization, block partials, epilogue) with
+    the weights quantized beforehand, like the GPU path."""
+    from oracle import oracle as O
+    O.build(force=False)
+    done_ops, spent, desc = 0.0, 0.0, []
+    prep = []
+    for l in layers:
+        perm, flags = O.channel_order(l.host["score"], l.cfg.nb8)
+        qw, sw16, _ = O.quantize_weights(l.host["W"], perm)
+        prep.append((l, perm, flags, qw, sw16))
+    per_layer = budget_s / len(layers)
+    for l, perm, flags, qw, sw16 in prep:
+        M, N, K = l.cfg.M, l.cfg.N, l.cfg.K
+        rows, t_layer, chunk = 0, 0.0, 4
+        while rows < M and t_layer < per_layer:
+            c = min(chunk, M - rows)
+            t = time.perf_counter()
+            O.forward_rows(l.host["X"], perm, flags, qw, sw16, (rows, rows + c))
+            dt = time.perf_counter() - t
+            t_layer += dt
+            rows += c
+            done_ops += 2.0 * c * N * K
+            if dt < 1.0:
+                chunk = min(chunk * 2, 256)
+        spent += t_layer
+        desc.append(f"{l.name}: rows 0..{rows - 1} of {M}")
+    return {"value": done_ops / spent / 1e12, "unit": "TOPS", "cores": O.threads(),
+            "kind": "oracle", "sample": "; ".join(desc) + f" ({spent:.1f} s of host time)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_70b", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import w4ax_mixed_precision_amd as comet
+    from gen import synth
+    comet.lib()
+    assert torch.cuda.is_available(), "bench needs a GPU"
+
+    layers = [Layer(n, copies_for(synth.CONFIGS[n]), torch, comet, synth)
+              for n in WORKLOADS[args.workload]]
+    step_ms, per = run_gpu(layers, args.steps, args.warmup, torch, comet)
+    ops = sum(l.ops for l in layers)
+    value = ops / (step_ms * 1e-3) / 1e12
+
+    gemm_ms = sum(per[l.name]["gemm_ms"] for l in layers)
+    gemm_ops = sum(l.ops for l in layers)
+    gemm_bytes_total = sum(l.gbytes for l in layers)
+    achieved_tops = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    achieved_gbs = gemm_bytes_total / (gemm_ms * 1e-3) / 1e9
+    t_mfma = gemm_ops / (PEAK_INT8_TOPS * 1e12)
+    t_hbm = gemm_bytes_total / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": achieved_tops, "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": achieved_tops / PEAK_INT8_TOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS}
+    roof["traffic"] = None
+    roof["kernel"] = "comet_w4ax_gemm"
+
+    kernels = {}
+    for l in layers:
+        p = per[l.name]
+        kernels[l.name] = {
+            "gemm_us": p["gemm_ms"] * 1e3, "gemm_us_p10": p["gemm_ms_p10"] * 1e3,
+            "gemm_us_p90": p["gemm_ms_p90"] * 1e3,
+            "gemm_tops": l.ops / (p["gemm_ms"] * 1e-3) / 1e12,
+            "gemm_frac_int8_peak": l.ops / (p["gemm_ms"] * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            "gemm_gbs": l.gbytes / (p["gemm_ms"] * 1e-3) / 1e9,
+            "quant_us": p["quant_ms"] * 1e3,
+            "quant_gbs": l.qbytes / (p["quant_ms"] * 1e-3) / 1e9,
+            "weight_copies": len(l.w)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(layers, args.cpu_seconds)
+
+    out = {
+        "metric": "W4Ax GEMM effective TOPS + % INT8-MFMA/HBM roofline, LLaMA-70B layer shapes",
+        "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded LLaMA-shaped activations with planted outlier channels, "
+                "N(0,0.02) weights)",
+        "config": {"workload": args.workload,
+                   "layers": [{"name": l.name, "M": l.cfg.M, "K": l.cfg.K, "N": l.cfg.N,
+                               "int8_blocks": l.cfg.nb8, "blocks": l.cfg.nb} for l in layers],
+                   "step": "comet_quant_act + comet_w4ax_gemm per layer"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * comet_w4ax.h -- C ABI of the W4Ax fine-grained mixed-precision GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (COMET, ASPLOS 2025; FMPQ quantization plus the W4Ax kernel):
+ *   - the input channels of a linear layer are split into 128-channel blocks;
+ *     activation outliers concentrate in about a tenth of the channels, so a
+ *     channel permutation gathers them into a few blocks, which are quantized
+ *     to 8 bits while every other block is quantized to 4 bits
+ *     (COMET article, mmssai.com/?p=43269, section "1.离群点分布规律的重定义");
+ *   - weights are quantized to symmetric INT4 per output channel per block,
+ *     offline (QUIK blog, deep-paper.org/paper/2310.09259, section
+ *     "反量化背后的数学"); activations are quantized online, per token and per
+ *     block, in one fused pass (QUIK blog, section "核融合");
+ *   - the GEMM forms exact integer partial sums per block on the matrix
+ *     units and dequantizes them in an FP32 epilogue that writes fp16
+ *     (COMET summary, paperbot-e5f.pages.dev/papers/10460.html, abstract;
+ *     QUIK blog, section "核融合").
+ *
+ * Three calls follow that statement of the problem: comet_pack_weights
+ * (offline, host memory), comet_quant_act and comet_w4ax_gemm (online,
+ * device memory, asynchronous on a HIP stream).
+ *
+ * Shared rules
+ *   - Every function returns a comet_status. Nothing throws across the ABI.
+ *   - The caller owns every buffer. The online calls never allocate; the GEMM
+ *     uses only the workspace the caller passes.
+ *   - All argument checks run before any HIP call, so a rejected call has no
+ *     effect on the device and needs no GPU.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. The
+ *     online calls are asynchronous on it and never synchronize; errors of the
+ *     kernels themselves surface at the caller's next synchronization.
+ *   - Calls on different streams with disjoint outputs may run concurrently.
+ *     Two GEMM calls that share one workspace must be ordered by the caller.
+ *   - Device pointers must be 16-byte aligned.
+ *
+ * Notation: nb = K / 128 blocks; nb8 = n_int8_blocks; nb4 = nb - nb8. The
+ * 8-bit blocks are always the LAST nb8 blocks of the permuted channel order
+ * (comet_pack_weights ranks channels by ascending score, so the outlier
+ * channels fill the highest blocks).
+ *
+ * Layouts (all little-endian):
+ *   Xq, activation codes, device, M * (64 * nb4 + 128 * nb8) bytes,
+ *     block-major. 4-bit block b (b < nb4) lives at byte b*M*64, row m at
+ *     + m*64; byte 16g + j (g in 0..3, j in 0..15) of a row holds the code of
+ *     block position 32g + j in its low nibble and of position 32g + 16 + j
+ *     in its high nibble. A 4-bit code is the zero-extended value u = q + 8,
+ *     q in [-7, 7]. 8-bit block b (b >= nb4) lives at byte
+ *     nb4*M*64 + (b - nb4)*M*128, row m at + m*128, byte k = int8 code q of
+ *     block position k, q in [-127, 127].
+ *   x_scale, activation scales, device, float [nb][M] (block-major).
+ *   Wq, weight codes, N * K / 2 bytes, fragment-ordered: the 16 output
+ *     channels 16c .. 16c+15 and block b form the 1024-byte fragment at byte
+ *     (c*nb + b) * 1024. Byte 16l + j of a fragment (l in 0..63, j in 0..15)
+ *     belongs to channel 16c + (l mod 16) and holds, as 4-bit two's
+ *     complement, q_w of block position 32(l/16) + j in its low nibble and of
+ *     position 32(l/16) + 16 + j in its high nibble.
+ *   w_scale, fp16 bit patterns [N][nb]; w_sum, int16 [N][nb] (sum of the
+ *     group's q_w, in [-896, 896]).
+ *   Block position p of block b is permuted channel 128b + p, i.e. original
+ *   channel perm[128b + p].
+ */
+#ifndef COMET_W4AX_H
+#define COMET_W4AX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    COMET_OK = 0,
+    COMET_ERR_NULL = 1,        /* a required pointer is NULL */
+    COMET_ERR_SHAPE = 2,       /* M < 1, N < 1, K < 128, K % 128 != 0, ldx < K or ldy < N */
+    COMET_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+    COMET_ERR_ARG = 4,         /* n_int8_blocks outside [0, K/128]; non-finite score or weight */
+    COMET_ERR_WORKSPACE = 5,   /* workspace smaller than comet_w4ax_gemm_workspace_bytes() */
+    COMET_ERR_HIP = 6,         /* a HIP launch or query failed */
+    COMET_ERR_UNSUPPORTED = 7  /* N % 128 != 0, or a size beyond the 32-bit index range */
+} comet_status;
+
+/*
+ * Offline: rank channels, quantize W to INT4 and pack it. Host memory only;
+ * touches no device.
+ *
+ * Channel order (COMET article, section "1.离群点分布规律的重定义", channel
+ * permutation; QUIK blog, section "第一步: 识别与重排", outlier columns moved
+ * to the end; QoQ/QServe article, youleyou.com/wenzhang/3078652.html,
+ * section "通用量化优化技巧", item 3): perm sorts the channels by ascending
+ * chan_score, ties in original order; block_is_int8[b] = (b >= nb - nb8).
+ * chan_score is a per-channel outlier statistic from calibration, e.g. the
+ * per-channel absmax of a calibration batch.
+ *
+ * Weights (QUIK blog, section "反量化背后的数学", symmetric weights; QoQ/QServe
+ * article, section "背景", fp16 group scales): for output channel n and block
+ * b with absmax a over the block's permuted channels, s = fp16(a / 7)
+ * (the smallest fp16 subnormal if that rounds to 0; 0 if a = 0) and
+ * q_w = clamp(round_half_even(w / s), -7, 7); w_sum = sum of the block's q_w.
+ *
+ *   W_fp16        in   [N][K] row-major fp16 bit patterns
+ *   chan_score    in   [K] float, finite
+ *   n_int8_blocks in   nb8, 0 <= nb8 <= K/128
+ *   perm          out  int32 [K]
+ *   block_is_int8 out  uint8 [K/128]
+ *   Wq_packed     out  N*K/2 bytes, layout above
+ *   w_scale_fp16  out  uint16 [N][K/128]
+ *   w_sum         out  int16 [N][K/128]
+ * Errors: NULL, SHAPE (N < 1, K % 128 != 0), UNSUPPORTED (N % 128 != 0),
+ * ARG (nb8 range, non-finite score or weight).
+ */
+int comet_pack_weights(const uint16_t* W_fp16, int N, int K, const float* chan_score,
+                       int n_int8_blocks, int32_t* perm, uint8_t* block_is_int8,
+                       uint8_t* Wq_packed, uint16_t* w_scale_fp16, int16_t* w_sum);
+
+/*
+ * Online, one kernel: gather the permuted channels of X, take the absmax of
+ * every (token, block), and write INT4 codes for the 4-bit blocks and INT8
+ * codes for the last nb8 blocks, with their scales (QUIK blog, section
+ * "核融合": one fused pass reads the input, takes the statistics and
+ * quantizes; COMET article, section "1.离群点分布规律的重定义": 8 bits for
+ * the outlier blocks, 4 bits elsewhere).
+ * For a (token, block) with absmax a > 0 and qmax = 7 or 127:
+ *   inv = qmax / a, s = a / qmax (IEEE float divisions),
+ *   q = clamp(round_half_even(x * inv), -qmax, qmax);
+ * an all-zero block gets s = 0 and q = 0.
+ *
+ *   X_fp16        in   device, [M][ldx] fp16, ldx >= K (elements)
+ *   perm          in   device, int32 [K], a permutation of 0..K-1
+ *   n_int8_blocks in   nb8
+ *   Xq            out  device, M * (64 nb4 + 128 nb8) bytes, layout above
+ *   x_scale       out  device, float [nb][M]
+ * Errors: NULL, SHAPE, ALIGN, ARG, HIP. perm must be a permutation and X
+ * finite; neither is checked (the result is then unspecified).
+ */
+int comet_quant_act(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                    int n_int8_blocks, void* Xq, float* x_scale, void* stream);
+
+/*
+ * Online: Y = X W^T from the quantized operands. For every output (m, n) and
+ * block b the exact INT32 partial P = sum over the block of q_a q_w is formed
+ * on INT8 matrix cores (4-bit operands are widened to 8 bits in registers;
+ * 4-bit activation codes enter zero-extended, u = q + 8, and the offset is
+ * removed through the precomputed weight sum: COMET article, section
+ * "3.硬件指令集的极限挖掘"; QUIK blog, section "反量化背后的数学"), then
+ *   y = sum over blocks of (x_scale[b][m] * w_scale[n][b]) * P   in FP32,
+ *   Y[m][n] = fp16(y) (round to nearest even; overflow gives +-Inf).
+ * Summation order over blocks is not fixed (split-K reorders it), but the
+ * result of one configuration is deterministic: no floating-point atomics.
+ *
+ *   Xq, x_scale       in   from comet_quant_act
+ *   Wq_packed, w_scale_fp16, w_sum  in  from comet_pack_weights, on device
+ *   n_int8_blocks     in   nb8, the same value as for the other two calls
+ *   Y_fp16            out  device, [M][ldy] fp16, ldy >= N (elements)
+ *   workspace         in/out device scratch of workspace_bytes bytes; may be
+ *                     NULL when comet_w4ax_gemm_workspace_bytes() is 0
+ * Errors: NULL, SHAPE, ALIGN, ARG, WORKSPACE, UNSUPPORTED, HIP.
+ */
+int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
+                     const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks,
+                     int M, int N, int K, void* Y_fp16, int ldy, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes comet_w4ax_gemm needs for this shape (0 if none). */
+size_t comet_w4ax_gemm_workspace_bytes(int M, int N, int K, int n_int8_blocks);
+
+/*
+ * Debug variant of the GEMM: writes the exact INT32 block partials of rows
+ * [m_begin, m_begin + m_count) instead of Y, as P[m - m_begin][n][b] (int32,
+ * [m_count][N][K/128], device). The partials do not depend on tiling, so any
+ * row range gives the values the full GEMM uses. Same inputs and errors as
+ * comet_w4ax_gemm (no workspace); SHAPE also covers a row range outside [0, M).
+ */
+int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* Wq_packed,
+                             const uint16_t* w_scale_fp16, const int16_t* w_sum,
+                             int n_int8_blocks, int M, int N, int K, int m_begin, int m_count,
+                             int32_t* P, void* stream);
+
+/* Static description of a status code. */
+const char* comet_status_string(int status);
+
+/* Library version string. */
+const char* comet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMET_W4AX_H */

@@ -1,0 +1,99 @@
+"""Shared pieces of the GPU tests: cached layer inputs, oracle results, device
+uploads and the output gates."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+from gen import synth
+
+# Full-size layers are compared on these row samples (first, last, and a
+# spread in between); smaller layers on every row.
+FULL_ROWS_LIMIT = 1024
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def sample_rows(M: int) -> np.ndarray:
+    if M <= FULL_ROWS_LIMIT:
+        return np.arange(M)
+    rng = np.random.default_rng(M)
+    mid = rng.choice(np.arange(16, M - 16), size=32, replace=False)
+    return np.unique(np.concatenate([np.arange(16), mid, np.arange(M - 16, M)]))
+
+
+_WCACHE: dict = {}
+
+
+def _weights(cfg):
+    """Weight-side inputs, oracle quantization and library pack of a layer: shared
+    by every configuration with the same seed, shape and 8-bit block count (the
+    decode sweep). One entry is kept."""
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    key = (cfg.seed, cfg.N, cfg.K, cfg.nb8)
+    if key in _WCACHE:
+        return _WCACHE[key]
+    _WCACHE.clear()
+    W, score = synth.make_w(cfg), synth.make_scores(cfg)
+    perm, flags = O.channel_order(score, cfg.nb8)
+    qw, sw16, wsum = O.quantize_weights(W, perm)
+    pk = comet.comet_pack_weights(W, score, cfg.nb8)
+    _WCACHE[key] = {"W": W, "score": score, "perm": perm, "flags": flags, "qw": qw,
+                    "sw16": sw16, "wsum": wsum, "pk": pk}
+    return _WCACHE[key]
+
+
+@functools.lru_cache(maxsize=1)
+def host_layer(name: str):
+    """Inputs and oracle-quantized operands of one configuration (host)."""
+    from oracle import oracle as O
+    cfg = synth.CONFIGS[name]
+    log(f"[layer] generating {name} M={cfg.M} K={cfg.K} N={cfg.N} nb8={cfg.nb8}")
+    wd = _weights(cfg)
+    X = synth.make_x(cfg)
+    qa, sa = O.quantize_activations(X, wd["perm"], wd["flags"])
+    d = dict(wd)
+    d.update({"X": X, "qa": qa, "sa": sa, "cfg": cfg})
+    return d
+
+
+def oracle_rows(d: dict, rows: np.ndarray):
+    """P, y32 and yexact of selected rows, plus sum_b |t_b| for the Y2 gate."""
+    from oracle import oracle as O
+    qa = d["qa"][rows]
+    P = O.block_partials(qa, d["qw"])
+    y32, Y16, ye = O.epilogue(P, d["sa"][rows], d["sw16"])
+    tabs = (np.abs(d["sa"][rows].astype(np.float64)[:, None, :] * f16(d["sw16"])[None, :, :]
+                   * P)).sum(-1)
+    return P, y32, Y16, ye, tabs
+
+
+def gate_y(yhat: np.ndarray, ye: np.ndarray, tabs: np.ndarray, nb: int):
+    """Gate Y1 (relative error with a floor) and gate Y2 (a per-element bound that
+    any FP32 epilogue over nb terms in any order, then fp16 rounding, meets)."""
+    rms = float(np.sqrt(np.mean(ye ** 2)))
+    err = np.abs(yhat - ye)
+    rel = err / np.maximum(np.abs(ye), 1e-2 * rms)
+    y1 = float(rel.max())
+    bound = (2.0 ** -11 * np.abs(ye) * (1 + 2.0 ** -10)
+             + (nb + 2) * 2.0 ** -24 * (1 + 2.0 ** -10) * (1 + 2.0 ** -11) * tabs + 2.0 ** -25)
+    y2_ok = bool(np.all(err <= bound))
+    return y1, y2_ok, float((err / bound).max())
+
+
+def device_layer(d: dict, pk: dict):
+    import torch
+    import w4ax_mixed_precision_amd as comet
+    w = comet.upload_weights(pk)
+    X = torch.from_numpy(d["X"].view(np.float16)).cuda()
+    return X, w

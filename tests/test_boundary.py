@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import w4ax_mixed_precision_amd as comet
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "comet_w4ax.h")
+
+OK, NULL, SHAPE, ALIGN, ARG, WORKSPACE, HIP, UNSUP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(comet_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = comet.lib()
+    names = declared_functions()
+    assert set(names) >= {"comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(comet.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    L = comet.lib()
+    for s in range(8):
+        assert L.comet_status_string(s)
+    assert L.comet_status_string(99) == b"unknown status"
+    assert comet.version().startswith("comet-w4ax")
+
+
+A = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced
+MIS = A + 4          # misaligned
+
+
+def qa(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, Xq=A, xs=A):
+    return comet.lib().comet_quant_act(X, M, K, ldx, perm, nb8, Xq, xs, None)
+
+
+def gm(Xq=A, xs=A, Wq=A, ws=A, wsum=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512,
+       work=None, wbytes=0):
+    return comet.lib().comet_w4ax_gemm(Xq, xs, Wq, ws, wsum, nb8, M, N, K, Y, ldy, work, wbytes,
+                                       None)
+
+
+def gp(Xq=A, xs=A, Wq=A, ws=A, wsum=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A):
+    return comet.lib().comet_w4ax_gemm_partials(Xq, xs, Wq, ws, wsum, nb8, M, N, K, m0, mc, P,
+                                                None)
+
+
+def test_quant_act_rejections():
+    assert qa(X=None) == NULL and qa(perm=None) == NULL and qa(Xq=None) == NULL
+    assert qa(xs=None) == NULL
+    assert qa(M=0) == SHAPE and qa(K=100) == SHAPE and qa(K=0) == SHAPE
+    assert qa(ldx=511) == SHAPE
+    assert qa(nb8=-1) == ARG and qa(nb8=5) == ARG
+    assert qa(X=MIS) == ALIGN and qa(perm=MIS) == ALIGN and qa(Xq=MIS) == ALIGN
+    assert qa(xs=MIS) == ALIGN
+
+
+def test_gemm_rejections():
+    assert gm(Xq=None) == NULL and gm(Y=None) == NULL and gm(wsum=None) == NULL
+    assert gm(M=0) == SHAPE and gm(N=0) == SHAPE and gm(K=384 + 1) == SHAPE
+    assert gm(ldy=500) == SHAPE
+    assert gm(nb8=5) == ARG and gm(nb8=-2) == ARG
+    assert gm(N=200, ldy=200) == UNSUP
+    assert gm(Wq=MIS) == ALIGN and gm(Y=MIS) == ALIGN and gm(ws=MIS) == ALIGN
+    assert gm(M=1 << 20, N=1 << 12, ldy=1 << 12) == UNSUP       # M*N beyond int32
+
+
+def test_gemm_workspace_contract():
+    L = comet.lib()
+    for M, N, K in ((1, 8192, 8192), (16, 28672, 8192), (4096, 8192, 28672), (16, 512, 512)):
+        need = L.comet_w4ax_gemm_workspace_bytes(M, N, K, 1)
+        if need:
+            assert gm(M=M, N=N, K=K, ldy=N, work=None) == NULL
+            assert gm(M=M, N=N, K=K, ldy=N, work=A, wbytes=need - 1) == WORKSPACE
+            assert gm(M=M, N=N, K=K, ldy=N, work=MIS, wbytes=need) == ALIGN
+    assert L.comet_w4ax_gemm_workspace_bytes(0, 512, 512, 0) == 0
+
+
+def test_partials_rejections():
+    assert gp(P=None) == NULL
+    assert gp(m0=-1) == SHAPE and gp(mc=0) == SHAPE and gp(m0=10, mc=7) == SHAPE
+    assert gp(P=MIS) == ALIGN
+
+
+def test_pack_rejections():
+    W = np.zeros((128, 256), np.uint16)
+    s = np.zeros(256, np.float32)
+    with pytest.raises(comet.CometError) as e:
+        comet.comet_pack_weights(np.zeros((128, 200), np.uint16), np.zeros(200, np.float32), 0)
+    assert e.value.status == SHAPE
+    with pytest.raises(comet.CometError) as e:
+        comet.comet_pack_weights(W, s, 3)
+    assert e.value.status == ARG
+    with pytest.raises(comet.CometError) as e:
+        comet.comet_pack_weights(np.zeros((100, 256), np.uint16), s, 0)
+    assert e.value.status == UNSUP
+    bad = s.copy()
+    bad[3] = np.inf
+    with pytest.raises(comet.CometError) as e:
+        comet.comet_pack_weights(W, bad, 0)
+    assert e.value.status == ARG
+    Wn = W.copy()
+    Wn[5, 7] = 0x7E00                      # NaN weight
+    with pytest.raises(comet.CometError) as e:
+        comet.comet_pack_weights(Wn, s, 0)
+    assert e.value.status == ARG
+    L = comet.lib()
+    p = ctypes.c_void_p(A)
+    assert L.comet_pack_weights(None, 128, 256, p, 0, p, p, p, p, p) == NULL

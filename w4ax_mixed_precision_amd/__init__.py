@@ -1,0 +1,189 @@
+"""Python binding of libcomet_w4ax.so (the W4Ax mixed-precision GEMM for gfx950).
+
+Argument marshalling only: every step of the online path runs in the
+library's HIP kernels. PyTorch supplies device memory and the current HIP
+stream; numpy carries the host arrays of the offline packing step.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python w4ax_mixed_precision_amd/build.py``); importing the binding without
+it raises immediately, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcomet_w4ax.so")
+
+COMET_OK = 0
+STATUS_NAMES = {0: "COMET_OK", 1: "COMET_ERR_NULL", 2: "COMET_ERR_SHAPE", 3: "COMET_ERR_ALIGN",
+                4: "COMET_ERR_ARG", 5: "COMET_ERR_WORKSPACE", 6: "COMET_ERR_HIP",
+                7: "COMET_ERR_UNSUPPORTED"}
+
+
+class CometError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} -> {STATUS_NAMES.get(status, status)}: "
+                         f"{lib().comet_status_string(status).decode()}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library, with argument types declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.comet_pack_weights.argtypes = [P, I, I, P, I, P, P, P, P, P]
+    L.comet_quant_act.argtypes = [P, I, I, I, P, I, P, P, P]
+    L.comet_w4ax_gemm.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P, Z, P]
+    L.comet_w4ax_gemm_partials.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
+    L.comet_w4ax_gemm_workspace_bytes.argtypes = [I, I, I, I]
+    L.comet_w4ax_gemm_workspace_bytes.restype = Z
+    L.comet_status_string.argtypes = [I]
+    L.comet_status_string.restype = ctypes.c_char_p
+    L.comet_version.restype = ctypes.c_char_p
+    for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
+              "comet_w4ax_gemm_partials"):
+        getattr(L, f).restype = I
+    _lib = L
+    return L
+
+
+EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
+           "comet_w4ax_gemm_workspace_bytes", "comet_w4ax_gemm_partials",
+           "comet_status_string", "comet_version")
+
+
+def _check(call: str, rc: int):
+    if rc != COMET_OK:
+        raise CometError(call, rc)
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def nblocks(K: int) -> int:
+    return K // 128
+
+
+def xq_bytes(M: int, K: int, nb8: int) -> int:
+    nb = K // 128
+    return M * (64 * (nb - nb8) + 128 * nb8)
+
+
+# ----------------------------------------------------------------------------
+# Offline (host)
+# ----------------------------------------------------------------------------
+
+def comet_pack_weights(W16: np.ndarray, score: np.ndarray, nb8: int) -> dict:
+    """Rank channels, quantize and pack W. Host numpy in, host numpy out:
+    perm int32 [K], flags uint8 [nb], Wq uint8 [N*K/2], w_scale uint16 [N, nb],
+    w_sum int16 [N, nb]."""
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    score = np.ascontiguousarray(score, dtype=np.float32)
+    N, K = W16.shape
+    if score.shape != (K,):
+        raise ValueError("score must have K entries")
+    nb = max(K // 128, 1)
+    out = {"perm": np.zeros(K, np.int32), "flags": np.zeros(nb, np.uint8),
+           "Wq": np.zeros(N * K // 2, np.uint8), "w_scale": np.zeros((N, nb), np.uint16),
+           "w_sum": np.zeros((N, nb), np.int16)}
+    rc = lib().comet_pack_weights(_np_ptr(W16), N, K, _np_ptr(score), int(nb8),
+                                  _np_ptr(out["perm"]), _np_ptr(out["flags"]), _np_ptr(out["Wq"]),
+                                  _np_ptr(out["w_scale"]), _np_ptr(out["w_sum"]))
+    _check("comet_pack_weights", rc)
+    out["N"], out["K"], out["nb8"] = N, K, int(nb8)
+    return out
+
+
+def upload_weights(packed: dict, device="cuda") -> dict:
+    """Copy the packed weight bundle to device tensors (torch only as memory)."""
+    import torch
+    d = {"perm": torch.from_numpy(packed["perm"]).to(device),
+         "Wq": torch.from_numpy(packed["Wq"]).to(device),
+         "w_scale": torch.from_numpy(packed["w_scale"].view(np.int16)).to(device),
+         "w_sum": torch.from_numpy(packed["w_sum"]).to(device)}
+    d.update({k: packed[k] for k in ("N", "K", "nb8")})
+    return d
+
+
+# ----------------------------------------------------------------------------
+# Online (device)
+# ----------------------------------------------------------------------------
+
+def comet_quant_act(X, perm, nb8: int, Xq=None, x_scale=None, stream=None):
+    """X: fp16 cuda tensor [M, ldx] (uses the first K = len(perm) columns).
+    Returns (Xq uint8 [xq_bytes], x_scale float32 [nb, M])."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    if Xq is None:
+        Xq = torch.empty(xq_bytes(M, K, nb8), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty((K // 128, M), dtype=torch.float32, device=X.device)
+    rc = lib().comet_quant_act(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(perm), int(nb8),
+                               _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
+    _check("comet_quant_act", rc)
+    return Xq, x_scale
+
+
+def workspace_bytes(M: int, N: int, K: int, nb8: int) -> int:
+    return int(lib().comet_w4ax_gemm_workspace_bytes(M, N, K, nb8))
+
+
+def comet_w4ax_gemm(Xq, x_scale, w: dict, M: int, Y=None, workspace=None, stream=None):
+    """Y fp16 [M, N] = dequant(Xq) dequant(Wq)^T for the uploaded weight bundle `w`."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    need = workspace_bytes(M, N, K, nb8)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    ws_ptr = _dev_ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    rc = lib().comet_w4ax_gemm(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["Wq"]),
+                               _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]), int(nb8), M, N, K,
+                               _dev_ptr(Y), Y.stride(0), ws_ptr, ws_bytes, _stream(stream))
+    _check("comet_w4ax_gemm", rc)
+    return Y
+
+
+def comet_w4ax_gemm_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
+                             m_count: int | None = None, P=None, stream=None):
+    """Exact INT32 block partials of rows [m_begin, m_begin + m_count): [m_count, N, nb]."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    m_count = M - m_begin if m_count is None else m_count
+    if P is None:
+        P = torch.empty((m_count, N, K // 128), dtype=torch.int32, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_partials(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["Wq"]),
+                                        _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]), int(nb8),
+                                        M, N, K, m_begin, m_count, _dev_ptr(P), _stream(stream))
+    _check("comet_w4ax_gemm_partials", rc)
+    return P
+
+
+def version() -> str:
+    return lib().comet_version().decode()

@@ -1,0 +1,152 @@
+// The C entry points: argument validation (before any HIP call, so a rejected
+// call needs no GPU and has no device effect), then the launchers.
+#include <cstdint>
+#include <limits>
+
+#include "comet_internal.h"
+
+namespace {
+
+using comet::kBlock;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common shape checks of the online calls. Sizes must keep every byte offset
+// the kernels form inside size_t and every element index of one buffer
+// inside int32 where the kernels use 32-bit products.
+int check_online_shape(int M, int N, int K, int nb8) {
+    if (M < 1 || N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (nb8 < 0 || nb8 > K / kBlock) return COMET_ERR_ARG;
+    if (N % 128 != 0) return COMET_ERR_UNSUPPORTED;
+    const int64_t mk = static_cast<int64_t>(M) * K;
+    const int64_t nk = static_cast<int64_t>(N) * K;
+    const int64_t mn = static_cast<int64_t>(M) * N;
+    const int64_t lim = std::numeric_limits<int32_t>::max();
+    if (mk > lim || nk > lim || mn > lim) return COMET_ERR_UNSUPPORTED;
+    return COMET_OK;
+}
+
+int hip_status(int e) { return e == 0 ? COMET_OK : COMET_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int comet_pack_weights(const uint16_t* W_fp16, int N, int K, const float* chan_score,
+                       int n_int8_blocks, int32_t* perm, uint8_t* block_is_int8,
+                       uint8_t* Wq_packed, uint16_t* w_scale_fp16, int16_t* w_sum) {
+    if (!W_fp16 || !chan_score || !perm || !block_is_int8 || !Wq_packed || !w_scale_fp16 || !w_sum)
+        return COMET_ERR_NULL;
+    if (N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return COMET_ERR_ARG;
+    if (N % 128 != 0) return COMET_ERR_UNSUPPORTED;
+    return comet::pack_weights(W_fp16, N, K, chan_score, n_int8_blocks, perm, block_is_int8,
+                               Wq_packed, w_scale_fp16, w_sum);
+}
+
+int comet_quant_act(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                    int n_int8_blocks, void* Xq, float* x_scale, void* stream) {
+    if (!X_fp16 || !perm || !Xq || !x_scale) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return COMET_ERR_ARG;
+    if (!aligned16(X_fp16) || !aligned16(perm) || !aligned16(Xq) || !aligned16(x_scale))
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_quant_act(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
+                                              n_int8_blocks, static_cast<uint8_t*>(Xq), x_scale,
+                                              stream));
+}
+
+size_t comet_w4ax_gemm_workspace_bytes(int M, int N, int K, int n_int8_blocks) {
+    if (check_online_shape(M, N, K, n_int8_blocks) != COMET_OK) return 0;
+    return comet::gemm_workspace_bytes(M, N, K, n_int8_blocks);
+}
+
+int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
+                     const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks,
+                     int M, int N, int K, void* Y_fp16, int ldy, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (!Xq || !x_scale || !Wq_packed || !w_scale_fp16 || !w_sum || !Y_fp16) return COMET_ERR_NULL;
+    int st = check_online_shape(M, N, K, n_int8_blocks);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(Wq_packed) || !aligned16(w_scale_fp16) ||
+        !aligned16(w_sum) || !aligned16(Y_fp16))
+        return COMET_ERR_ALIGN;
+    const size_t need = comet::gemm_workspace_bytes(M, N, K, n_int8_blocks);
+    if (need > 0) {
+        if (!workspace) return COMET_ERR_NULL;
+        if (workspace_bytes < need) return COMET_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return COMET_ERR_ALIGN;
+    }
+    comet::GemmProblem p{};
+    p.Xq = static_cast<const uint8_t*>(Xq);
+    p.x_scale = x_scale;
+    p.Wq = static_cast<const uint8_t*>(Wq_packed);
+    p.w_scale = w_scale_fp16;
+    p.w_sum = w_sum;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.nb = K / kBlock;
+    p.nb4 = p.nb - n_int8_blocks;
+    p.Y = static_cast<uint16_t*>(Y_fp16);
+    p.ldy = ldy;
+    p.P = nullptr;
+    p.m_begin = 0;
+    p.m_count = M;
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    return hip_status(comet::launch_w4ax_gemm(p, stream));
+}
+
+int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* Wq_packed,
+                             const uint16_t* w_scale_fp16, const int16_t* w_sum,
+                             int n_int8_blocks, int M, int N, int K, int m_begin, int m_count,
+                             int32_t* P, void* stream) {
+    if (!Xq || !x_scale || !Wq_packed || !w_scale_fp16 || !w_sum || !P) return COMET_ERR_NULL;
+    int st = check_online_shape(M, N, K, n_int8_blocks);
+    if (st != COMET_OK) return st;
+    if (m_begin < 0 || m_count < 1 || m_begin > M - m_count) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(m_count) * N * (K / kBlock) > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(Wq_packed) || !aligned16(w_scale_fp16) ||
+        !aligned16(w_sum) || !aligned16(P))
+        return COMET_ERR_ALIGN;
+    comet::GemmProblem p{};
+    p.Xq = static_cast<const uint8_t*>(Xq);
+    p.x_scale = x_scale;
+    p.Wq = static_cast<const uint8_t*>(Wq_packed);
+    p.w_scale = w_scale_fp16;
+    p.w_sum = w_sum;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.nb = K / kBlock;
+    p.nb4 = p.nb - n_int8_blocks;
+    p.Y = nullptr;
+    p.ldy = N;
+    p.P = P;
+    p.m_begin = m_begin;
+    p.m_count = m_count;
+    return hip_status(comet::launch_w4ax_gemm(p, stream));
+}
+
+const char* comet_status_string(int status) {
+    switch (status) {
+        case COMET_OK: return "ok";
+        case COMET_ERR_NULL: return "a required pointer is NULL";
+        case COMET_ERR_SHAPE: return "invalid shape or leading dimension";
+        case COMET_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case COMET_ERR_ARG: return "invalid argument (n_int8_blocks range or non-finite input)";
+        case COMET_ERR_WORKSPACE: return "workspace too small";
+        case COMET_ERR_HIP: return "HIP launch or query failed";
+        case COMET_ERR_UNSUPPORTED: return "unsupported shape (N % 128 != 0 or size beyond 32-bit indexing)";
+        default: return "unknown status";
+    }
+}
+
+const char* comet_version(void) { return "comet-w4ax-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/comet_w4ax.h"
+
+namespace comet {
+
+constexpr int kBlock = 128;          // channels per quantization block
+constexpr int kFragBytes = 1024;     // packed weight fragment: 16 channels x 128 positions
+
+// Bytes of the activation code buffer for M rows.
+inline size_t xq_bytes(int M, int nb4, int nb8) {
+    return static_cast<size_t>(M) * (64u * static_cast<size_t>(nb4) + 128u * static_cast<size_t>(nb8));
+}
+
+// Launchers (device code lives in the .hip files). Arguments were validated by
+// the C entry points; each returns a hipError_t value as int.
+int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                     uint8_t* Xq, float* x_scale, void* stream);
+
+struct GemmProblem {
+    const uint8_t* Xq;
+    const float* x_scale;
+    const uint8_t* Wq;
+    const uint16_t* w_scale;
+    const int16_t* w_sum;
+    int M, N, K, nb, nb4;
+    uint16_t* Y;
+    int ldy;
+    int32_t* P;              // debug partials output, or nullptr
+    int m_begin, m_count;    // row range of the partials output
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+size_t gemm_workspace_bytes(int M, int N, int K, int nb8);
+int launch_w4ax_gemm(const GemmProblem& p, void* stream);
+
+// Host packer (pack_weights.cpp).
+int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
+                 uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum);
+
+}  // namespace comet

@@ -1,0 +1,124 @@
+// Offline weight preparation: channel ranking, symmetric INT4 quantization per
+// (output channel, 128-channel block) with an fp16 scale, the per-block weight
+// sums, and the nibble pack in MFMA fragment order.
+//
+// Channel ranking: COMET article (mmssai.com/?p=43269), section
+// "1.离群点分布规律的重定义" (permute so that outlier channels share blocks);
+// QUIK blog (deep-paper.org/paper/2310.09259), section "第一步: 识别与重排"
+// (outlier columns go to the end of W); QoQ/QServe article
+// (youleyou.com/wenzhang/3078652.html), section "通用量化优化技巧", item 3.
+// Quantization: QUIK blog, section "反量化背后的数学" (symmetric weights, the
+// weight sum is a weight-only quantity computed offline); QoQ/QServe article,
+// section "背景" (fp16 scale per group).
+// Fragment order: QoQ/QServe article, section "W4A8 GEMM的核心设计" (store the
+// weights in the order the matrix instructions consume them, one wide load per
+// lane); here the consumer is the gfx950 16x16x64 INT8 MFMA, see the Wq layout
+// in comet_w4ax.h.
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+#include "comet_internal.h"
+
+namespace comet {
+namespace {
+
+inline float half_bits_to_float(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return static_cast<float>(v);
+}
+
+inline uint16_t float_to_half_bits(float f) {
+    _Float16 v = static_cast<_Float16>(f);   // IEEE round to nearest even
+    uint16_t h;
+    __builtin_memcpy(&h, &v, 2);
+    return h;
+}
+
+// One output channel: quantize every block and scatter its nibbles into the
+// channel's lane of each fragment. Returns false on a non-finite weight.
+bool pack_row(const uint16_t* wrow, int K, const int32_t* perm, int n, uint8_t* Wq,
+              uint16_t* w_scale, int16_t* w_sum) {
+    const int nb = K / kBlock;
+    const int frag_col = n / 16;
+    const int lane_col = n % 16;
+    int8_t q[kBlock];
+    for (int b = 0; b < nb; ++b) {
+        float v[kBlock];
+        float a = 0.0f;
+        for (int p = 0; p < kBlock; ++p) {
+            v[p] = half_bits_to_float(wrow[perm[b * kBlock + p]]);
+            if (!std::isfinite(v[p])) return false;
+            a = std::max(a, std::fabs(v[p]));
+        }
+        int sum = 0;
+        if (a == 0.0f) {
+            w_scale[static_cast<size_t>(n) * nb + b] = 0;
+            std::fill(q, q + kBlock, 0);
+        } else {
+            uint16_t hs = float_to_half_bits(a / 7.0f);
+            if (hs == 0) hs = 1;                      // keep the divisor nonzero
+            const float s = half_bits_to_float(hs);
+            w_scale[static_cast<size_t>(n) * nb + b] = hs;
+            for (int p = 0; p < kBlock; ++p) {
+                float r = std::rint(v[p] / s);
+                r = std::min(7.0f, std::max(-7.0f, r));
+                q[p] = static_cast<int8_t>(r);
+                sum += q[p];
+            }
+        }
+        w_sum[static_cast<size_t>(n) * nb + b] = static_cast<int16_t>(sum);
+        uint8_t* frag = Wq + (static_cast<size_t>(frag_col) * nb + b) * kFragBytes;
+        for (int g = 0; g < 4; ++g) {
+            uint8_t* dst = frag + 16 * (16 * g + lane_col);
+            for (int j = 0; j < 16; ++j) {
+                const uint8_t lo = static_cast<uint8_t>(q[32 * g + j]) & 0xF;
+                const uint8_t hi = static_cast<uint8_t>(q[32 * g + 16 + j]) & 0xF;
+                dst[j] = static_cast<uint8_t>(lo | (hi << 4));
+            }
+        }
+    }
+    return true;
+}
+
+}  // namespace
+
+int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
+                 uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum) {
+    const int nb = K / kBlock;
+    for (int k = 0; k < K; ++k)
+        if (!std::isfinite(score[k])) return COMET_ERR_ARG;
+
+    std::vector<int32_t> order(K);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [score](int32_t x, int32_t y) { return score[x] < score[y]; });
+    std::copy(order.begin(), order.end(), perm);
+    for (int b = 0; b < nb; ++b) flags[b] = static_cast<uint8_t>(b >= nb - nb8);
+
+    unsigned hw = std::thread::hardware_concurrency();
+    const int threads = static_cast<int>(std::max(1u, std::min(hw ? hw : 1u, 32u)));
+    const int per = (N + threads - 1) / threads;
+    std::vector<char> ok(threads, 1);
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t) {
+        const int n0 = t * per, n1 = std::min(N, n0 + per);
+        if (n0 >= n1) break;
+        pool.emplace_back([=, &ok] {
+            for (int n = n0; n < n1; ++n)
+                if (!pack_row(W + static_cast<size_t>(n) * K, K, perm, n, Wq, w_scale, w_sum)) {
+                    ok[t] = 0;
+                    return;
+                }
+        });
+    }
+    for (auto& th : pool) th.join();
+    for (char c : ok)
+        if (!c) return COMET_ERR_ARG;
+    return COMET_OK;
+}
+
+}  // namespace comet
