@@ -55,8 +55,9 @@
  *     belongs to channel 16c + (l mod 16) and holds, as 4-bit two's
  *     complement, q_w of block position 32(l/16) + j in its low nibble and of
  *     position 32(l/16) + 16 + j in its high nibble.
- *   w_scale, fp16 bit patterns [N][nb]; w_sum, int16 [N][nb] (sum of the
- *     group's q_w, in [-896, 896]).
+ *   w_scale, fp16 bit patterns [nb][N]; w_sum, int16 [nb][N] (sum of the
+ *     group's q_w, in [-896, 896]); block-major like x_scale, so the scales of
+ *     one block are one contiguous row.
  *   Block position p of block b is permuted channel 128b + p, i.e. original
  *   channel perm[128b + p].
  */
@@ -105,8 +106,8 @@ typedef enum {
  *   perm          out  int32 [K]
  *   block_is_int8 out  uint8 [K/128]
  *   Wq_packed     out  N*K/2 bytes, layout above
- *   w_scale_fp16  out  uint16 [N][K/128]
- *   w_sum         out  int16 [N][K/128]
+ *   w_scale_fp16  out  uint16 [K/128][N]
+ *   w_sum         out  int16 [K/128][N]
  * Errors: NULL, SHAPE (N < 1, K % 128 != 0), UNSUPPORTED (N % 128 != 0),
  * ARG (nb8 range, non-finite score or weight).
  */
@@ -144,7 +145,7 @@ int comet_quant_act(const void* X_fp16, int M, int K, int ldx, const int32_t* pe
  * 4-bit activation codes enter zero-extended, u = q + 8, and the offset is
  * removed through the precomputed weight sum: COMET article, section
  * "3.硬件指令集的极限挖掘"; QUIK blog, section "反量化背后的数学"), then
- *   y = sum over blocks of (x_scale[b][m] * w_scale[n][b]) * P   in FP32,
+ *   y = sum over blocks of (x_scale[b][m] * w_scale[b][n]) * P   in FP32,
  *   Y[m][n] = fp16(y) (round to nearest even; overflow gives +-Inf).
  * Summation order over blocks is not fixed (split-K reorders it), but the
  * result of one configuration is deterministic: no floating-point atomics.

@@ -21,8 +21,8 @@ def test_pack_matches_oracle(orc, name):
     qw, sw16, wsum = orc.quantize_weights(W, perm)
     assert np.array_equal(pk["perm"], perm)
     assert np.array_equal(pk["flags"], flags)
-    assert np.array_equal(pk["w_scale"], sw16)
-    assert np.array_equal(pk["w_sum"].astype(np.int32), wsum)
+    assert np.array_equal(pk["w_scale"].T, sw16)
+    assert np.array_equal(pk["w_sum"].T.astype(np.int32), wsum)
     assert np.array_equal(decode_wq(pk["Wq"], N, K), qw)
 
 
@@ -41,6 +41,6 @@ def test_pack_edge_values(orc):
         perm, flags = orc.channel_order(score, nb8)
         qw, sw16, wsum = orc.quantize_weights(W, perm)
         assert np.array_equal(pk["perm"], perm) and np.array_equal(pk["flags"], flags)
-        assert np.array_equal(pk["w_scale"], sw16)
-        assert np.array_equal(pk["w_sum"].astype(np.int32), wsum)
+        assert np.array_equal(pk["w_scale"].T, sw16)
+        assert np.array_equal(pk["w_sum"].T.astype(np.int32), wsum)
         assert np.array_equal(decode_wq(pk["Wq"], N, K), qw)

@@ -98,8 +98,8 @@ def xq_bytes(M: int, K: int, nb8: int) -> int:
 
 def comet_pack_weights(W16: np.ndarray, score: np.ndarray, nb8: int) -> dict:
     """Rank channels, quantize and pack W. Host numpy in, host numpy out:
-    perm int32 [K], flags uint8 [nb], Wq uint8 [N*K/2], w_scale uint16 [N, nb],
-    w_sum int16 [N, nb]."""
+    perm int32 [K], flags uint8 [nb], Wq uint8 [N*K/2], w_scale uint16 [nb, N],
+    w_sum int16 [nb, N]."""
     W16 = np.ascontiguousarray(W16, dtype=np.uint16)
     score = np.ascontiguousarray(score, dtype=np.float32)
     N, K = W16.shape
@@ -107,8 +107,8 @@ def comet_pack_weights(W16: np.ndarray, score: np.ndarray, nb8: int) -> dict:
         raise ValueError("score must have K entries")
     nb = max(K // 128, 1)
     out = {"perm": np.zeros(K, np.int32), "flags": np.zeros(nb, np.uint8),
-           "Wq": np.zeros(N * K // 2, np.uint8), "w_scale": np.zeros((N, nb), np.uint16),
-           "w_sum": np.zeros((N, nb), np.int16)}
+           "Wq": np.zeros(N * K // 2, np.uint8), "w_scale": np.zeros((nb, N), np.uint16),
+           "w_sum": np.zeros((nb, N), np.int16)}
     rc = lib().comet_pack_weights(_np_ptr(W16), N, K, _np_ptr(score), int(nb8),
                                   _np_ptr(out["perm"]), _np_ptr(out["flags"]), _np_ptr(out["Wq"]),
                                   _np_ptr(out["w_scale"]), _np_ptr(out["w_sum"]))

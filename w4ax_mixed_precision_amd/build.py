@@ -21,6 +21,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
+    # MFMA accumulators in VGPRs: the epilogue reads them with plain VALU ops
+    # instead of an extra v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

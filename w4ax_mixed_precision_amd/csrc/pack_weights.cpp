@@ -40,7 +40,7 @@ inline uint16_t float_to_half_bits(float f) {
 
 // One output channel: quantize every block and scatter its nibbles into the
 // channel's lane of each fragment. Returns false on a non-finite weight.
-bool pack_row(const uint16_t* wrow, int K, const int32_t* perm, int n, uint8_t* Wq,
+bool pack_row(const uint16_t* wrow, int N, int K, const int32_t* perm, int n, uint8_t* Wq,
               uint16_t* w_scale, int16_t* w_sum) {
     const int nb = K / kBlock;
     const int frag_col = n / 16;
@@ -56,13 +56,13 @@ bool pack_row(const uint16_t* wrow, int K, const int32_t* perm, int n, uint8_t* 
         }
         int sum = 0;
         if (a == 0.0f) {
-            w_scale[static_cast<size_t>(n) * nb + b] = 0;
+            w_scale[static_cast<size_t>(b) * N + n] = 0;
             std::fill(q, q + kBlock, 0);
         } else {
             uint16_t hs = float_to_half_bits(a / 7.0f);
             if (hs == 0) hs = 1;                      // keep the divisor nonzero
             const float s = half_bits_to_float(hs);
-            w_scale[static_cast<size_t>(n) * nb + b] = hs;
+            w_scale[static_cast<size_t>(b) * N + n] = hs;
             for (int p = 0; p < kBlock; ++p) {
                 float r = std::rint(v[p] / s);
                 r = std::min(7.0f, std::max(-7.0f, r));
@@ -70,7 +70,7 @@ bool pack_row(const uint16_t* wrow, int K, const int32_t* perm, int n, uint8_t* 
                 sum += q[p];
             }
         }
-        w_sum[static_cast<size_t>(n) * nb + b] = static_cast<int16_t>(sum);
+        w_sum[static_cast<size_t>(b) * N + n] = static_cast<int16_t>(sum);
         uint8_t* frag = Wq + (static_cast<size_t>(frag_col) * nb + b) * kFragBytes;
         for (int g = 0; g < 4; ++g) {
             uint8_t* dst = frag + 16 * (16 * g + lane_col);
@@ -109,7 +109,7 @@ int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, i
         if (n0 >= n1) break;
         pool.emplace_back([=, &ok] {
             for (int n = n0; n < n1; ++n)
-                if (!pack_row(W + static_cast<size_t>(n) * K, K, perm, n, Wq, w_scale, w_sum)) {
+                if (!pack_row(W + static_cast<size_t>(n) * K, N, K, perm, n, Wq, w_scale, w_sum)) {
                     ok[t] = 0;
                     return;
                 }

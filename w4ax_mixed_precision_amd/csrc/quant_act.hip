@@ -27,6 +27,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxLdsRowChannels = 32768;     // 64 KB of fp16 per staged row
 
+// Integer minimum by value (a reference-returning min leaves stack slots behind).
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
 __device__ inline float h2f(uint16_t h) {
     return __half2float(__ushort_as_half(h));
 }
