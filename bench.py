@@ -13,11 +13,16 @@ Default workload: the LLaMA-70B prefill pair, 4096 tokens, down_proj
 Prints one JSON line. `value` is effective TOPS: 2 M N K per layer, summed,
 over the measured step time. The roofline object is for comet_w4ax_gemm, the
 dominant kernel, from HIP events recorded around its launches on the stream
-they run on.
+they run on. Its `traffic` is the HBM bytes of one step's GEMM launches taken
+from hardware counters (FETCH_SIZE and WRITE_SIZE, scaled by what the same
+counters read for a device copy of known size), read from the counter summary
+under profiles/ when that summary was taken on the current kernel sources,
+otherwise null. `--copy-calibration` runs only that known-size copy.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +42,46 @@ WORKLOADS = {
     "q_proj_7b": ["q_proj_7b"],
     "mlp_7b": ["up_gate_7b", "down_7b"],
 }
+
+
+# Sources whose change invalidates counter data taken on the GEMM kernel.
+KERNEL_SOURCES = ["w4ax_mixed_precision_amd/csrc/w4ax_gemm.hip",
+                  "w4ax_mixed_precision_amd/csrc/comet_internal.h",
+                  "w4ax_mixed_precision_amd/build.py"]
+COPY_CAL_BYTES = 1 << 30
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per step of the GEMM launches from the committed counter summary
+    of this workload, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"w4ax_gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None, "kernel changed since the counters were taken"
+    return float(rec["hbm_bytes_per_step"]), path
+
+
+def copy_calibration(torch):
+    """A plain device copy of COPY_CAL_BYTES, three times, for counter scaling."""
+    n = COPY_CAL_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "copies": 3}), flush=True)
 
 
 def log(msg):
@@ -171,6 +216,7 @@ def main():
     ap.add_argument("--workload", default="prefill_70b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -178,6 +224,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import w4ax_mixed_precision_amd as comet
     from gen import synth
@@ -203,7 +253,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS}
-    roof["traffic"] = None
+    traffic, traffic_src = measured_traffic(args.workload)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = traffic_src
+    roof["algorithmic_bytes"] = gemm_bytes_total
     roof["kernel"] = "comet_w4ax_gemm"
 
     kernels = {}

@@ -73,26 +73,35 @@ __device__ inline v4i mfma_i8(v4i a, v4i b, v4i c) {
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (prefill shapes): 128 x 128 output tile per workgroup of four
-// waves in a 2 x 2 arrangement, 64 x 64 per wave. The packed A and B tiles of
-// a block go from HBM straight into LDS (global_load_lds_dwordx4: each lane's
-// 16 bytes land at LDS base + 16 * lane, so one wave instruction fills one
-// 1 KB piece and no registers are spent on staging). Two LDS stages: the
-// loads of block b+1 are in flight while block b computes; one barrier per
-// block.
+// waves in a 2 x 2 arrangement, 64 x 64 per wave, one workgroup per CU.
 //
-// LDS pieces (1 KB each) of a stage:
+// Everything a block needs goes from HBM straight into LDS with direct loads
+// (global_load_lds: each lane's 16 or 4 bytes land at LDS base + lane * size,
+// no registers spent on staging) into a ring of four LDS stages, issued three
+// blocks ahead of the compute. Each wave issues the same number of loads per
+// block (5 for a 4-bit block, 7 for an 8-bit one), so at the end of block b a
+// partial wait (s_waitcnt vmcnt = loads of blocks b+2, b+3) plus a plain
+// s_barrier make block b+1 visible while b+2 and b+3 stay in flight.
+//
+// LDS stage (25.6 KB):
 //   A, 4-bit block: 8 pieces of 16 rows x 64 B. Slot s = 4 r + (j ^ ((r >> 2) & 3))
 //     holds 16-byte chunk j of row r, so the 16 lanes of one MFMA k-group
 //     (16 rows, same chunk) hit 16 different bank groups.
 //   A, 8-bit block: 16 pieces of 8 rows x 128 B. Slot s = 8 r + (j ^ f), with
 //     f = ((r >> 1) & 3) | ((piece & 1) << 2), same purpose.
 //   B: 8 fragments in their stored (lane) order.
-// plus the block's 128 activation scales, 128 weight scales (pre-divided by
-// 16) and 128 weight-sum corrections.
+//   the block's 128 activation scales (f32), 128 weight scales (fp16 bits) and
+//   128 weight sums (int16), converted when read.
 // ---------------------------------------------------------------------------
 
+// Three LDS stages (76.8 KB) and a 256-register budget let two workgroups
+// share a CU, i.e. two waves per SIMD, which hides the dependency latencies
+// of the widen -> MFMA -> convert -> FMA chain far better than one.
+#ifndef COMET_TILED_STAGES
+#define COMET_TILED_STAGES 3
+#endif
 #ifndef COMET_TILED_WG_PER_CU
-#define COMET_TILED_WG_PER_CU 1   // workgroups per CU the register budget is sized for
+#define COMET_TILED_WG_PER_CU 2
 #endif
 
 constexpr int kTM = 128;
@@ -100,15 +109,17 @@ constexpr int kTN = 128;
 constexpr int kLdsA = kTM * 128;                 // room for an 8-bit block
 constexpr int kLdsB = (kTN / 16) * kFragBytes;
 constexpr int kLdsSa = kTM * 4;
-constexpr int kLdsSw = kTN * 4;
-constexpr int kLdsCorr = kTN * 4;
-constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSw + kLdsCorr;
+constexpr int kLdsSw = kTN * 2;
+constexpr int kLdsWs = kTN * 2;
+constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSw + kLdsWs;
+constexpr int kStages = COMET_TILED_STAGES;
+static_assert(kStages == 3 || kStages == 4, "the unrolled ring below is written for three or four stages");
 
 // Tile of a workgroup. Workgroups are dispatched round-robin over the eight
 // XCDs (workgroup w runs on XCD w mod 8); each XCD gets a contiguous range of
 // the tile order, and the tile order walks 8-row-tile groups column by
-// column, so the ~64 workgroups an XCD runs at once cover about an 8 x 8 patch
-// and share their A and B stripes in that XCD's L2.
+// column, so the workgroups an XCD runs at once cover a compact patch and
+// share their A and B stripes in that XCD's L2.
 __device__ inline bool tile_of(int w, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + 7) / 8;
@@ -129,67 +140,68 @@ __device__ __forceinline__ void lds_load16(const void* g, uint8_t* lds_piece) {
                                             reinterpret_cast<uintptr_t>(lds_piece)),
                                      16, 0, 0);
 }
+__device__ __forceinline__ void lds_load4(const void* g, uint8_t* lds_piece) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(lds_piece)),
+                                     4, 0, 0);
+}
 
-// Per-lane byte offsets of the direct-to-LDS loads, fixed for a tile: the
-// block only moves the (wave-uniform) base pointers.
+// Per-lane byte offsets of the direct loads, fixed for a tile: the block only
+// moves the (wave-uniform) base pointers.
 struct IssueOffsets {
-    uint32_t a4[2];   // 4-bit A pieces 2w, 2w+1: row * 64 + 16 * swizzled chunk
-    uint32_t a8[4];   // 8-bit A pieces 4w .. 4w+3: row * 128 + 16 * swizzled piece
-    uint32_t sa;      // activation-scale row (threads 0..127)
+    uint32_t a4_0, a4_1;               // 4-bit A pieces 2w, 2w+1
+    uint32_t a8_0, a8_1, a8_2, a8_3;   // 8-bit A pieces 4w .. 4w+3
+    uint32_t sc;                        // scale words: wave 0/1 activation scales, 2 weight scales, 3 sums
 };
 
-__device__ __forceinline__ IssueOffsets issue_offsets(int M, int m0, int wave, int lane, int tid) {
+__device__ __forceinline__ IssueOffsets issue_offsets(int M, int m0, int wave, int lane) {
     IssueOffsets o;
     {
         const int r = lane >> 2;
         const int j = (lane & 3) ^ ((r >> 2) & 3);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int row = imin(m0 + 16 * (2 * wave + k) + r, M - 1);
-            o.a4[k] = static_cast<uint32_t>(row) * 64u + 16u * j;
-        }
+        o.a4_0 = static_cast<uint32_t>(imin(m0 + 16 * (2 * wave + 0) + r, M - 1)) * 64u + 16u * j;
+        o.a4_1 = static_cast<uint32_t>(imin(m0 + 16 * (2 * wave + 1) + r, M - 1)) * 64u + 16u * j;
     }
     {
         const int r = lane >> 3;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int piece = 4 * wave + k;
-            const int j = (lane & 7) ^ (((r >> 1) & 3) | ((piece & 1) << 2));
-            const int row = imin(m0 + 8 * piece + r, M - 1);
-            o.a8[k] = static_cast<uint32_t>(row) * 128u + 16u * j;
-        }
+        const int j0 = (lane & 7) ^ (((r >> 1) & 3) | 0);
+        const int j1 = (lane & 7) ^ (((r >> 1) & 3) | 4);
+        o.a8_0 = static_cast<uint32_t>(imin(m0 + 8 * (4 * wave + 0) + r, M - 1)) * 128u + 16u * j0;
+        o.a8_1 = static_cast<uint32_t>(imin(m0 + 8 * (4 * wave + 1) + r, M - 1)) * 128u + 16u * j1;
+        o.a8_2 = static_cast<uint32_t>(imin(m0 + 8 * (4 * wave + 2) + r, M - 1)) * 128u + 16u * j0;
+        o.a8_3 = static_cast<uint32_t>(imin(m0 + 8 * (4 * wave + 3) + r, M - 1)) * 128u + 16u * j1;
     }
-    o.sa = static_cast<uint32_t>(imin(m0 + (tid & (kTM - 1)), M - 1));
+    // waves 0 and 1: activation scales of rows 64w + lane (clamped into [0, M));
+    // waves 2 and 3: two weight scales / sums per lane
+    o.sc = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, M - 1)) * 4u : 4u * lane;
     return o;
 }
 
-// Issue the direct-to-LDS loads of block b's A and B pieces (wave `wave`, a
-// wave-uniform value, loads its share) and fetch this thread's scale words.
+// Direct loads of block b into stage `st`: every wave issues 1 scale word
+// load, 2 (4-bit) or 4 (8-bit) A pieces and 2 B fragments, in that order.
 __device__ __forceinline__ void tiled_issue(const GemmProblem& p, int b, int n0, int wave, int lane,
-                                            int tid, const IssueOffsets& o, uint8_t* st, float& sa,
-                                            uint32_t& hs, int32_t& ws) {
+                                            const IssueOffsets& o, uint8_t* st) {
     const int M = p.M, N = p.N, nb = p.nb, nb4 = p.nb4;
-    // Scale words first (every thread, no branch), all 32-bit: threads 0..127
-    // take an activation scale, 128..191 two weight scales, 192..255 two weight
-    // sums. Waiting for them later then leaves the younger LDS loads in flight.
-    {
-        sa = (p.x_scale + static_cast<size_t>(b) * M)[o.sa];
-        const uint32_t* wsc = reinterpret_cast<const uint32_t*>(p.w_scale + static_cast<size_t>(b) * N + n0);
-        const uint32_t* wsm = reinterpret_cast<const uint32_t*>(p.w_sum + static_cast<size_t>(b) * N + n0);
-        hs = wsc[tid & 63];
-        ws = static_cast<int32_t>(wsm[tid & 63]);
+    if (wave < 2) {
+        lds_load4(reinterpret_cast<const uint8_t*>(p.x_scale + static_cast<size_t>(b) * M) + o.sc,
+                  st + kLdsA + kLdsB + 256 * wave);
+    } else if (wave == 2) {
+        lds_load4(reinterpret_cast<const uint8_t*>(p.w_scale + static_cast<size_t>(b) * N + n0) + o.sc,
+                  st + kLdsA + kLdsB + kLdsSa);
+    } else {
+        lds_load4(reinterpret_cast<const uint8_t*>(p.w_sum + static_cast<size_t>(b) * N + n0) + o.sc,
+                  st + kLdsA + kLdsB + kLdsSa + kLdsSw);
     }
-    // (written out: an array indexed in a loop would be left on the stack)
     if (b < nb4) {
         const uint8_t* slab = p.Xq + static_cast<size_t>(b) * M * 64;
-        lds_load16(slab + o.a4[0], st + (2 * wave + 0) * kFragBytes);
-        lds_load16(slab + o.a4[1], st + (2 * wave + 1) * kFragBytes);
+        lds_load16(slab + o.a4_0, st + (2 * wave + 0) * kFragBytes);
+        lds_load16(slab + o.a4_1, st + (2 * wave + 1) * kFragBytes);
     } else {
         const uint8_t* slab = p.Xq + static_cast<size_t>(nb4) * M * 64 + static_cast<size_t>(b - nb4) * M * 128;
-        lds_load16(slab + o.a8[0], st + (4 * wave + 0) * kFragBytes);
-        lds_load16(slab + o.a8[1], st + (4 * wave + 1) * kFragBytes);
-        lds_load16(slab + o.a8[2], st + (4 * wave + 2) * kFragBytes);
-        lds_load16(slab + o.a8[3], st + (4 * wave + 3) * kFragBytes);
+        lds_load16(slab + o.a8_0, st + (4 * wave + 0) * kFragBytes);
+        lds_load16(slab + o.a8_1, st + (4 * wave + 1) * kFragBytes);
+        lds_load16(slab + o.a8_2, st + (4 * wave + 2) * kFragBytes);
+        lds_load16(slab + o.a8_3, st + (4 * wave + 3) * kFragBytes);
     }
     const uint8_t* frag = p.Wq + (static_cast<size_t>(n0 / 16 + 2 * wave) * nb + b) * kFragBytes +
                           16u * static_cast<uint32_t>(lane);
@@ -197,52 +209,46 @@ __device__ __forceinline__ void tiled_issue(const GemmProblem& p, int b, int n0,
     lds_load16(frag + static_cast<size_t>(nb) * kFragBytes, st + kLdsA + (2 * wave + 1) * kFragBytes);
 }
 
-// Scales of a staged block into LDS: s_w / 16 as f32 and the weight-sum
-// correction -128 w_sum (4-bit blocks) or 0 (8-bit blocks) as int32.
-__device__ __forceinline__ void tiled_store_scales(uint8_t* st, int tid, bool is4, float sa,
-                                                   uint32_t hs, int32_t ws) {
-    // Opaque redefinition: keeps the compiler from hoisting the conversions
-    // (and so the wait for these loads, which would also wait for the
-    // in-flight LDS loads) up to where the loads are issued.
-    asm volatile("" : "+v"(sa), "+v"(hs), "+v"(ws));
-    float* sa_l = reinterpret_cast<float*>(st + kLdsA + kLdsB);
-    float* sw_l = reinterpret_cast<float*>(st + kLdsA + kLdsB + kLdsSa);
-    int* corr_l = reinterpret_cast<int*>(st + kLdsA + kLdsB + kLdsSa + kLdsSw);
-    if (tid < kTM) {
-        sa_l[tid] = sa;
-    } else if (tid < kTM + 64) {
-        const int c = 2 * (tid - kTM);
-        sw_l[c] = h2f(static_cast<uint16_t>(hs & 0xFFFFu)) * 0.0625f;
-        sw_l[c + 1] = h2f(static_cast<uint16_t>(hs >> 16)) * 0.0625f;
-    } else {
-        const int c = 2 * (tid - kTM - 64);
-        const int lo = static_cast<int16_t>(static_cast<uint32_t>(ws) & 0xFFFFu);
-        const int hi = ws >> 16;
-        corr_l[c] = is4 ? -128 * lo : 0;
-        corr_l[c + 1] = is4 ? -128 * hi : 0;
+// Loads one wave issues for block b (0 past the last block).
+__device__ __forceinline__ int issued_loads(int b, int nb, int nb4) {
+    return b >= nb ? 0 : (b < nb4 ? 5 : 7);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define COMET_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Wait until at most `younger` of this wave's direct loads are outstanding.
+__device__ __forceinline__ void wait_loads(int younger) {
+    switch (younger) {
+        case 0: COMET_VMCNT(0); break;
+        case 5: COMET_VMCNT(5); break;
+        case 7: COMET_VMCNT(7); break;
+        case 10: COMET_VMCNT(10); break;
+        case 12: COMET_VMCNT(12); break;
+        default: COMET_VMCNT(14); break;
     }
 }
 
-// One block of the tiled kernel: compute from stage `st` while block b+1
-// streams into stage `nxt`.
+// One block of the tiled kernel: issue block b+3 into `nxt`, compute block b
+// from `st`, then make block b+1 visible.
 template <bool kDump>
 __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0, int n0, int row_lo,
-                                            int row_hi, int wave, int lane, int tid,
-                                            const IssueOffsets& ioff, int a4_base, int a8_base,
-                                            const uint8_t* st, uint8_t* nxt, float (&y)[4][4][4]) {
+                                            int row_hi, int wave, int lane, const IssueOffsets& ioff,
+                                            int a4_base, int a8_base, const uint8_t* st, uint8_t* nxt,
+                                            float (&y)[4][4][4]) {
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 4, l16 = lane & 15;
     const int nb = p.nb, nb4 = p.nb4, N = p.N;
-    float gsa = 0.0f;
-    uint32_t ghs = 0;
-    int32_t gws = 0;
-    if (b + 1 < nb) tiled_issue(p, b + 1, n0, wave, lane, tid, ioff, nxt, gsa, ghs, gws);
+    if (b + kStages - 1 < nb) tiled_issue(p, b + kStages - 1, n0, wave, lane, ioff, nxt);
 
     const bool is4 = b < nb4;
     const float* sa_l = reinterpret_cast<const float*>(st + kLdsA + kLdsB);
-    const float* sw_l = reinterpret_cast<const float*>(st + kLdsA + kLdsB + kLdsSa);
-    const int* corr_l = reinterpret_cast<const int*>(st + kLdsA + kLdsB + kLdsSa + kLdsSw);
-    const float sa_lane = sa_l[64 * wr + lane];
+    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(st + kLdsA + kLdsB + kLdsSa);
+    const int16_t* ws_l = reinterpret_cast<const int16_t*>(st + kLdsA + kLdsB + kLdsSa + kLdsSw);
+    // s_x / 16 of this lane's row: the outer product then gives s_x * s_w / 16
+    const float sa_lane = sa_l[64 * wr + lane] * 0.0625f;
+    const int corr_factor = is4 ? -128 : 0;
 
     // A operands of the four row tiles: row tile r is 1 KB (4-bit) or 2 KB
     // (8-bit) further into the stage; the second half of an 8-bit row is the
@@ -264,15 +270,16 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
     // 16-register t vectors are ever live; their latency hides under the next
     // tile's MFMAs.
     v16f t = {};
-    if constexpr (!kDump) t = __builtin_amdgcn_mfma_f32_16x16x1f32(sa_lane, sw_l[64 * wc + l16], t, 0, 0, 0);
+    if constexpr (!kDump)
+        t = __builtin_amdgcn_mfma_f32_16x16x1f32(sa_lane, h2f(sw_l[64 * wc + l16]), t, 0, 0, 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int col = 64 * wc + 16 * c + l16;
-        float sw_next = c < 3 ? sw_l[col + 16] : 0.0f;
+        float sw_next = c < 3 ? h2f(sw_l[col + 16]) : 0.0f;
         const uint4 pk = *reinterpret_cast<const uint4*>(st + kLdsA + (4 * wc + c) * kFragBytes + 16 * lane);
         const v4i B0 = widen_weights_lo(pk);
         const v4i B1 = widen_weights_hi(pk);
-        const int corr = corr_l[col];
+        const int corr = corr_factor * static_cast<int>(ws_l[col]);
         const v4i cinit = {corr, corr, corr, corr};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -299,16 +306,21 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
                 t = __builtin_amdgcn_mfma_f32_16x16x1f32(sa_lane, sw_next, t, 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
-    if (b + 1 < nb) tiled_store_scales(nxt, tid, b + 1 < nb4, gsa, ghs, gws);
-    __syncthreads();    // this thread's direct-to-LDS loads have landed, and everyone is done with st
+    // block b+1's loads are done (only b+2 and b+3 may still be in flight),
+    // and every wave is finished with stage `st` before it is refilled
+    wait_loads(issued_loads(b + 2, nb, nb4) + (kStages == 4 ? issued_loads(b + 3, nb, nb4) : 0));
+    __builtin_amdgcn_s_barrier();
 }
 
 template <bool kDump>
 __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_kernel(GemmProblem p) {
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStage];
+#if COMET_TILED_STAGES == 4
+    __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStage];
+#endif
 
     const int row_lo = kDump ? p.m_begin : 0;
     const int row_hi = kDump ? p.m_begin + p.m_count : p.M;
@@ -319,13 +331,12 @@ __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_ke
     const int m0 = row_lo + tm * kTM;
     const int n0 = tn * kTN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 4, l16 = lane & 15;
-    const int nb = p.nb;
-    const IssueOffsets ioff = issue_offsets(p.M, m0, wave, lane, tid);
+    const int nb = p.nb, nb4 = p.nb4;
+    const IssueOffsets ioff = issue_offsets(p.M, m0, wave, lane);
 
     float y[4][4][4];
 #pragma unroll
@@ -341,21 +352,32 @@ __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_ke
     const int a8_base = (8 * wr + (l16 >> 3)) * kFragBytes +
                         16 * (8 * (l16 & 7) + ((2 * g) ^ ((((l16 & 7) >> 1) & 3) | (((l16 >> 3) & 1) << 2))));
 
-    {
-        float sa = 0.0f;
-        uint32_t hs = 0;
-        int32_t ws = 0;
-        tiled_issue(p, 0, n0, wave, lane, tid, ioff, stage0, sa, hs, ws);
-        tiled_store_scales(stage0, tid, 0 < p.nb4, sa, hs, ws);
-        __syncthreads();
-    }
-    for (int b = 0; b < nb; b += 2) {
-        tiled_block<kDump>(p, b, m0, n0, row_lo, row_hi, wave, lane, tid, ioff, a4_base, a8_base, stage0,
-                           stage1, y);
+    // prologue: blocks 0 .. kStages-2 in flight; wait for block 0
+    tiled_issue(p, 0, n0, wave, lane, ioff, stage0);
+    if (1 < nb) tiled_issue(p, 1, n0, wave, lane, ioff, stage1);
+    if (kStages == 4 && 2 < nb) tiled_issue(p, 2, n0, wave, lane, ioff, stage2);
+    wait_loads(issued_loads(1, nb, nb4) + (kStages == 4 ? issued_loads(2, nb, nb4) : 0));
+    __builtin_amdgcn_s_barrier();
+
+#if COMET_TILED_STAGES == 3
+    for (int b = 0; b < nb; b += 3) {
+        tiled_block<kDump>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage2, y);
         if (b + 1 < nb)
-            tiled_block<kDump>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, tid, ioff, a4_base, a8_base,
-                               stage1, stage0, y);
+            tiled_block<kDump>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
+        if (b + 2 < nb)
+            tiled_block<kDump>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
     }
+#else
+    for (int b = 0; b < nb; b += 4) {
+        tiled_block<kDump>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage3, y);
+        if (b + 1 < nb)
+            tiled_block<kDump>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
+        if (b + 2 < nb)
+            tiled_block<kDump>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
+        if (b + 3 < nb)
+            tiled_block<kDump>(p, b + 3, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage3, stage2, y);
+    }
+#endif
 
     if constexpr (!kDump) {
 #pragma unroll
@@ -374,105 +396,91 @@ __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_ke
 
 // ---------------------------------------------------------------------------
 // Streaming kernel (decode shapes, M <= 64): weight-bandwidth bound. A
-// workgroup owns one group of 16 output channels; its four waves split the
-// blocks four ways (split-K inside the workgroup) and stream their weight
-// fragments with everything else a block needs (activation codes, activation
-// scale, weight scale and sum) fetched a batch of kU blocks ahead, double
-// buffered. The four partial tiles are summed through LDS in wave order, so
-// the result is deterministic, and no global atomics or device-scope fences
-// are needed (on a multi-XCD part those write back and invalidate L2).
+// workgroup owns one group of 16 output channels; its kSplit waves split the
+// blocks (split-K inside the workgroup). Each wave keeps kD blocks in flight
+// with a rolling prefetch: register slot u is consumed and immediately refilled
+// with the block kD further on, everything a block needs in one slot (weight
+// word, activation words, activation scale, weight scale and sum). The kSplit
+// partial tiles are summed through LDS in wave order, so the result is
+// deterministic, and no global atomics or device-scope fences are needed (on
+// a multi-XCD part those write back and invalidate L2).
 // ---------------------------------------------------------------------------
 
-constexpr int kSplitWaves = 4;
-
-// One batch of kU blocks in registers: weight word, activation words (the
-// second only for 8-bit blocks), activation scale, weight scale bits, weight sum.
-template <int MR, int kU>
-struct StreamBatch {
-    uint4 w[kU];
-    uint4 a0[kU][MR];
-    uint4 a1[kU][MR];
-    float sa[kU];
-    uint32_t hs[kU];
-    int32_t ws[kU];
+template <int MR>
+struct StreamSlot {
+    uint4 w;          // weight fragment word of this lane
+    uint4 a0[MR];     // activation words (a1 only used by 8-bit blocks)
+    uint4 a1[MR];
+    float sa;         // activation scale of row `srow`
+    uint32_t hs;      // weight scale bits of column `ncol`
+    int32_t ws;       // weight sum of column `ncol`
 };
 
-template <int MR, int kU>
-__device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b0, int b_end, int grp, int lane,
-                                             int srow, const int (&arow)[MR], StreamBatch<MR, kU>& sb) {
+template <int MR>
+__device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b, int grp, int lane, int srow,
+                                             const int (&arow)[MR], StreamSlot<MR>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
     const int M = p.M, N = p.N, nb = p.nb, nb4 = p.nb4;
     const int ncol = grp * 16 + l16;
+    sl.w = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * nb + b) * kFragBytes + 16 * lane);
+    sl.sa = p.x_scale[static_cast<size_t>(b) * M + srow];
+    sl.hs = p.w_scale[static_cast<size_t>(b) * N + ncol];
+    sl.ws = p.w_sum[static_cast<size_t>(b) * N + ncol];
+    // branch-free: 4-bit rows are 64 bytes at 16g, 8-bit rows 128 bytes at
+    // 32g (+16 for the second word); a 4-bit block reloads its one word
+    const bool is4 = b < nb4;
+    const uint8_t* slab = is4 ? p.Xq + static_cast<size_t>(b) * M * 64
+                              : p.Xq + static_cast<size_t>(nb4) * M * 64 + static_cast<size_t>(b - nb4) * M * 128;
+    const uint32_t rstride = is4 ? 64u : 128u;
+    const uint32_t cofs = is4 ? 16u * g : 32u * g;
+    const uint32_t second = is4 ? 0u : 16u;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const int b = imin(b0 + u, b_end - 1);
-        sb.w[u] = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * nb + b) * kFragBytes +
-                                                  16 * lane);
-        sb.sa[u] = p.x_scale[static_cast<size_t>(b) * M + srow];
-        sb.hs[u] = p.w_scale[static_cast<size_t>(b) * N + ncol];
-        sb.ws[u] = p.w_sum[static_cast<size_t>(b) * N + ncol];
-        // branch-free: 4-bit rows are 64 bytes at 16g, 8-bit rows 128 bytes at
-        // 32g (+16 for the second word); a 4-bit block reloads its one word
-        const bool is4 = b < nb4;
-        const uint8_t* slab = is4 ? p.Xq + static_cast<size_t>(b) * M * 64
-                                  : p.Xq + static_cast<size_t>(nb4) * M * 64 + static_cast<size_t>(b - nb4) * M * 128;
-        const uint32_t rstride = is4 ? 64u : 128u;
-        const uint32_t cofs = is4 ? 16u * g : 32u * g;
-        const uint32_t second = is4 ? 0u : 16u;
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const uint8_t* src = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
-            sb.a0[u][r] = *reinterpret_cast<const uint4*>(src);
-            sb.a1[u][r] = *reinterpret_cast<const uint4*>(src + second);
-        }
+    for (int r = 0; r < MR; ++r) {
+        const uint8_t* src = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
+        sl.a0[r] = *reinterpret_cast<const uint4*>(src);
+        sl.a1[r] = *reinterpret_cast<const uint4*>(src + second);
     }
 }
 
-// Blocks past b_end (the tail of the last batch) were fetched clamped to a
-// valid block; they get a zero scale product, which adds exactly zero.
-template <int MR, int kU>
-__device__ __forceinline__ void stream_compute(int b0, int b_end, int nb4, const StreamBatch<MR, kU>& sb,
+// One block from a slot. `valid` is false for the clamped refetches past the
+// wave's last block: they get a zero scale product, which adds exactly zero.
+template <int MR>
+__device__ __forceinline__ void stream_compute(bool valid, bool is4, const StreamSlot<MR>& sl,
                                                float (&y)[MR][4]) {
+    const v4i B0 = widen_weights_lo(sl.w);
+    const v4i B1 = widen_weights_hi(sl.w);
+    const float sw = valid ? h2f(static_cast<uint16_t>(sl.hs)) * 0.0625f : 0.0f;
+    const int corr = is4 ? -128 * sl.ws : 0;
+    const v4i cinit = {corr, corr, corr, corr};
+    // t[4r + i] = s_x[row 16r + 4g + i] * s_w[col] / 16 for the MR row tiles
+    v16f t = {};
+    t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const int b = b0 + u;
-        const bool valid = b < b_end;
-        const bool is4 = imin(b, b_end - 1) < nb4;
-        const v4i B0 = widen_weights_lo(sb.w[u]);
-        const v4i B1 = widen_weights_hi(sb.w[u]);
-        const float sw = valid ? h2f(static_cast<uint16_t>(sb.hs[u])) * 0.0625f : 0.0f;
-        const int corr = is4 ? -128 * sb.ws[u] : 0;
-        const v4i cinit = {corr, corr, corr, corr};
-        // t[4r + i] = s_x[row 16r + 4g + i] * s_w[col] / 16 for the MR row tiles
-        v16f t = {};
-        t = __builtin_amdgcn_mfma_f32_16x16x1f32(sb.sa[u], sw, t, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            v4i A0, A1;
-            if (is4) {
-                A0 = widen_act_lo(sb.a0[u][r]);
-                A1 = widen_act_hi(sb.a0[u][r]);
-            } else {
-                A0 = as_v4i(sb.a0[u][r]);
-                A1 = as_v4i(sb.a1[u][r]);
-            }
-            v4i acc = mfma_i8(A0, B0, cinit);
-            acc = mfma_i8(A1, B1, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[r][i]);
+    for (int r = 0; r < MR; ++r) {
+        v4i A0, A1;
+        if (is4) {
+            A0 = widen_act_lo(sl.a0[r]);
+            A1 = widen_act_hi(sl.a0[r]);
+        } else {
+            A0 = as_v4i(sl.a0[r]);
+            A1 = as_v4i(sl.a1[r]);
         }
+        v4i acc = mfma_i8(A0, B0, cinit);
+        acc = mfma_i8(A1, B1, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[r][i]);
     }
 }
 
-template <int MR, int kU>
-__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmProblem p) {
-    __shared__ float red[kSplitWaves][MR * 4][64];
+template <int MR, int kD, int kSplit>
+__global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p) {
+    __shared__ float red[kSplit][MR * 4][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
     const int grp = blockIdx.x;                    // 16-channel group
-    const int nb = p.nb, M = p.M;
-    const int bps = (nb + kSplitWaves - 1) / kSplitWaves;
+    const int nb = p.nb, nb4 = p.nb4, M = p.M;
+    const int bps = (nb + kSplit - 1) / kSplit;
     const int b_begin = imin(nb, wave * bps);
     const int b_end = imin(nb, b_begin + bps);
 
@@ -487,13 +495,18 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmProblem p) {
         for (int i = 0; i < 4; ++i) y[r][i] = 0.0f;
 
     if (b_begin < b_end) {
-        StreamBatch<MR, kU> s0, s1;
-        stream_fetch<MR, kU>(p, b_begin, b_end, grp, lane, srow, arow, s0);
-        for (int b0 = b_begin; b0 < b_end; b0 += 2 * kU) {
-            stream_fetch<MR, kU>(p, b0 + kU, b_end, grp, lane, srow, arow, s1);
-            stream_compute<MR, kU>(b0, b_end, p.nb4, s0, y);
-            stream_fetch<MR, kU>(p, b0 + 2 * kU, b_end, grp, lane, srow, arow, s0);
-            stream_compute<MR, kU>(b0 + kU, b_end, p.nb4, s1, y);
+        const int last = b_end - 1;
+        StreamSlot<MR> slot[kD];
+#pragma unroll
+        for (int u = 0; u < kD; ++u) stream_fetch<MR>(p, imin(b_begin + u, last), grp, lane, srow, arow, slot[u]);
+        for (int b0 = b_begin; b0 < b_end; b0 += kD) {
+#pragma unroll
+            for (int u = 0; u < kD; ++u) {
+                const int b = b0 + u;
+                stream_compute<MR>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                if (b0 + kD < b_end)
+                    stream_fetch<MR>(p, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
+            }
         }
     }
 
@@ -502,10 +515,12 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmProblem p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[wave][4 * r + i][lane] = y[r][i];
     __syncthreads();
-    // each wave finishes MR*4/4 of the (row tile, i) slots, summing the four
-    // K-quarters in wave order
-    for (int q = wave; q < MR * 4; q += kSplitWaves) {
-        const float v = ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
+    // the (row tile, i) slots are shared out over the waves; each sums the
+    // K-parts in wave order
+    for (int q = wave; q < MR * 4; q += kSplit) {
+        float v = red[0][q][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < kSplit; ++w2) v += red[w2][q][lane];
         const int row = 16 * (q >> 2) + 4 * g + (q & 3);
         if (row < M) p.Y[static_cast<size_t>(row) * p.ldy + grp * 16 + l16] = __half_as_ushort(__float2half_rn(v));
     }
@@ -513,10 +528,32 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmProblem p) {
 
 bool use_stream(int M) { return M <= 64; }
 
+#ifndef COMET_STREAM_TARGET_WAVES
+#define COMET_STREAM_TARGET_WAVES 4096
+#endif
+#ifndef COMET_STREAM_DEPTH
+#define COMET_STREAM_DEPTH 4
+#endif
+
+// Widest in-workgroup split whose register budget (512 / waves per SIMD) holds
+// the kernel without spills at the default depth: 120, 187, 249 and 306 VGPRs
+// for 1..4 row tiles.
+template <int MR>
+constexpr int max_stream_split() { return MR == 1 ? 16 : (MR <= 3 ? 8 : 4); }
+
 template <int MR>
 int launch_stream(const GemmProblem& p, hipStream_t st) {
-    constexpr int kU = MR <= 1 ? 4 : 2;
-    gemm_stream_kernel<MR, kU><<<p.N / 16, kThreads, 0, st>>>(p);
+    constexpr int kD = COMET_STREAM_DEPTH;
+    constexpr int kMax = max_stream_split<MR>();
+    // split the blocks of a channel group over enough waves to keep many
+    // weight fragments in flight across the chip
+    const int groups = p.N / 16;
+    if (kMax == 4 || groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD)
+        gemm_stream_kernel<MR, kD, 4><<<groups, 256, 0, st>>>(p);
+    else if (kMax == 8 || groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD)
+        gemm_stream_kernel<MR, kD, (kMax >= 8 ? 8 : 4)><<<groups, 64 * (kMax >= 8 ? 8 : 4), 0, st>>>(p);
+    else
+        gemm_stream_kernel<MR, kD, (kMax >= 16 ? 16 : 4)><<<groups, 64 * (kMax >= 16 ? 16 : 4), 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
