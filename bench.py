@@ -34,7 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
+PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+STREAM_MAX_M = 64            # the library's INT4-layout GEMM streams weights up to this M
 
 WORKLOADS = {
     "prefill_70b": ["prefill_down_70b", "prefill_up_70b"],
@@ -88,18 +90,37 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemm_bytes(M, N, K, nb8):
-    """Bytes the method must move for one GEMM: packed weights, weight scales and
-    sums, activation codes and scales, fp16 output."""
-    nb = K // 128
-    nb4 = nb - nb8
-    return N * K // 2 + 2 * N * nb + 2 * N * nb4 + M * (64 * nb4 + 128 * nb8) + 4 * M * nb + 2 * M * N
+def layout_of(M):
+    """INT4 layout (weight streaming) for decode shapes, FP6 layout above."""
+    return "int4" if M <= STREAM_MAX_M else "fp6"
 
 
-def quant_bytes(M, K, nb8):
+def gemm_bytes(M, N, K, nb8, layout):
+    """Bytes one GEMM must move in its layout: weight codes, weight scales (and
+    sums on the INT4 layout), activation codes and scales, fp16 output."""
     nb = K // 128
     nb4 = nb - nb8
-    return 2 * M * K + 4 * K + M * (64 * nb4 + 128 * nb8) + 4 * M * nb
+    if layout == "int4":
+        return N * K // 2 + 2 * N * nb + 2 * N * nb4 + M * (64 * nb4 + 128 * nb8) + 4 * M * nb + 2 * M * N
+    return N * (96 * nb4 + 64 * nb8) + 2 * N * nb + M * (96 * nb4 + 128 * nb8) + 4 * M * nb + 2 * M * N
+
+
+def gemm_peak_tops(M, N, K, nb8, layout):
+    """Dense matrix-unit peak for this GEMM's instruction mix: INT8 for every
+    block on the INT4 layout; FP6 for the 4-bit blocks and INT8 for the 8-bit
+    blocks on the FP6 layout."""
+    nb = K // 128
+    if layout == "int4":
+        return PEAK_INT8_TOPS
+    nb4 = nb - nb8
+    return 1.0 / ((nb4 / PEAK_FP6_TOPS + nb8 / PEAK_INT8_TOPS) / nb)
+
+
+def quant_bytes(M, K, nb8, layout):
+    nb = K // 128
+    nb4 = nb - nb8
+    per4 = 64 if layout == "int4" else 96
+    return 2 * M * K + 4 * K + M * (per4 * nb4 + 128 * nb8) + 4 * M * nb
 
 
 class Layer:
@@ -110,27 +131,48 @@ class Layer:
         t0 = time.time()
         X, W, score = synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg)
         self.host = {"X": X, "W": W, "score": score}
+        self.layout = layout_of(cfg.M)
         pk = comet.comet_pack_weights(W, score, cfg.nb8)
+        if self.layout == "fp6":
+            comet.comet_repack_weights_fp6(pk)
+            pk.pop("Wq")                        # keep only the layout this layer runs
         self.pk = pk
         w = comet.upload_weights(pk)
         self.w = [w] + [{k: (v.clone() if hasattr(v, "clone") else v) for k, v in w.items()}
                         for _ in range(copies - 1)]
         self.X = torch.from_numpy(X.view(np.float16)).cuda()
         M, K, N = cfg.M, cfg.K, cfg.N
-        self.Xq = torch.empty(comet.xq_bytes(M, K, cfg.nb8), dtype=torch.uint8, device="cuda")
+        nxq = comet.xq_bytes(M, K, cfg.nb8) if self.layout == "int4" else comet.xq_fp6_bytes(M, K, cfg.nb8)
+        self.Xq = torch.empty(nxq, dtype=torch.uint8, device="cuda")
         self.xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
         self.Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         need = comet.workspace_bytes(M, N, K, cfg.nb8)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
         self.ops = 2.0 * M * N * K
-        self.gbytes = gemm_bytes(M, N, K, cfg.nb8)
-        self.qbytes = quant_bytes(M, K, cfg.nb8)
-        log(f"[bench] {name}: M={M} K={K} N={N} nb8={cfg.nb8} ready in {time.time() - t0:.1f}s "
-            f"({copies} weight copies)")
+        self.gbytes = gemm_bytes(M, N, K, cfg.nb8, self.layout)
+        self.qbytes = quant_bytes(M, K, cfg.nb8, self.layout)
+        self.peak = gemm_peak_tops(M, N, K, cfg.nb8, self.layout)
+        log(f"[bench] {name}: M={M} K={K} N={N} nb8={cfg.nb8} {self.layout} layout, ready in "
+            f"{time.time() - t0:.1f}s ({copies} weight copies)")
+
+    def quant(self, w):
+        import w4ax_mixed_precision_amd as comet
+        if self.layout == "int4":
+            comet.comet_quant_act(self.X, w["perm"], self.cfg.nb8, Xq=self.Xq, x_scale=self.xs)
+        else:
+            comet.comet_quant_act_fp6(self.X, w["perm"], self.cfg.nb8, Xq=self.Xq, x_scale=self.xs)
+
+    def gemm(self, w):
+        import w4ax_mixed_precision_amd as comet
+        if self.layout == "int4":
+            comet.comet_w4ax_gemm(self.Xq, self.xs, w, self.cfg.M, Y=self.Y, workspace=self.ws)
+        else:
+            comet.comet_w4ax_gemm_fp6(self.Xq, self.xs, w, self.cfg.M, Y=self.Y)
 
 
 def copies_for(cfg, target_bytes=1 << 30):
-    per = cfg.N * cfg.K // 2
+    nb = cfg.K // 128
+    per = gemm_bytes(0, cfg.N, cfg.K, cfg.nb8, layout_of(cfg.M)) - 2 * cfg.N * nb
     return int(max(1, min(32, -(-target_bytes // per))))
 
 
@@ -147,10 +189,10 @@ def run_gpu(layers, steps, warmup, torch, comet):
             if record:
                 a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                 a.record()
-            comet.comet_quant_act(l.X, w["perm"], l.cfg.nb8, Xq=l.Xq, x_scale=l.xs)
+            l.quant(w)
             if record:
                 b.record()
-            comet.comet_w4ax_gemm(l.Xq, l.xs, w, l.cfg.M, Y=l.Y, workspace=l.ws)
+            l.gemm(w)
             if record:
                 c.record()
                 qev[l.name].append((a, b))
@@ -245,11 +287,15 @@ def main():
     gemm_bytes_total = sum(l.gbytes for l in layers)
     achieved_tops = gemm_ops / (gemm_ms * 1e-3) / 1e12
     achieved_gbs = gemm_bytes_total / (gemm_ms * 1e-3) / 1e9
-    t_mfma = gemm_ops / (PEAK_INT8_TOPS * 1e12)
+    t_mfma = sum(l.ops / (l.peak * 1e12) for l in layers)
+    peak_tops = gemm_ops / t_mfma / 1e12
     t_hbm = gemm_bytes_total / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": achieved_tops, "peak": PEAK_INT8_TOPS,
-                "unit": "TFLOP/s", "frac": achieved_tops / PEAK_INT8_TOPS}
+        roof = {"bound": "mfma", "achieved": achieved_tops, "peak": peak_tops,
+                "unit": "TFLOP/s", "frac": achieved_tops / peak_tops,
+                "peak_basis": "dense MFMA peak of the instruction mix: FP6 10.1 POPS for 4-bit "
+                              "blocks, INT8 5.0 POPS for 8-bit blocks (and for every block on "
+                              "the INT4 layout)"}
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS}
@@ -266,10 +312,11 @@ def main():
             "gemm_us": p["gemm_ms"] * 1e3, "gemm_us_p10": p["gemm_ms_p10"] * 1e3,
             "gemm_us_p90": p["gemm_ms_p90"] * 1e3,
             "gemm_tops": l.ops / (p["gemm_ms"] * 1e-3) / 1e12,
-            "gemm_frac_int8_peak": l.ops / (p["gemm_ms"] * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            "gemm_frac_peak": l.ops / (p["gemm_ms"] * 1e-3) / 1e12 / l.peak,
             "gemm_gbs": l.gbytes / (p["gemm_ms"] * 1e-3) / 1e9,
             "quant_us": p["quant_ms"] * 1e3,
             "quant_gbs": l.qbytes / (p["quant_ms"] * 1e-3) / 1e9,
+            "layout": l.layout, "gemm_peak_tops": l.peak,
             "weight_copies": len(l.w)}
 
     cpu = None
@@ -286,7 +333,8 @@ def main():
         "config": {"workload": args.workload,
                    "layers": [{"name": l.name, "M": l.cfg.M, "K": l.cfg.K, "N": l.cfg.N,
                                "int8_blocks": l.cfg.nb8, "blocks": l.cfg.nb} for l in layers],
-                   "step": "comet_quant_act + comet_w4ax_gemm per layer"},
+                   "step": "comet_quant_act + comet_w4ax_gemm per layer (the *_fp6 pair on "
+                           "the FP6 layout when M > 64)"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

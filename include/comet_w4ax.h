@@ -19,7 +19,10 @@
  *
  * Three calls follow that statement of the problem: comet_pack_weights
  * (offline, host memory), comet_quant_act and comet_w4ax_gemm (online,
- * device memory, asynchronous on a HIP stream).
+ * device memory, asynchronous on a HIP stream). The *_fp6 calls are the same
+ * three steps on a second operand layout (FP6-encoded 4-bit codes) that the
+ * prefill GEMM kernel consumes directly; the INT4 layout is the smaller one
+ * and serves the weight-bandwidth-bound decode shapes.
  *
  * Shared rules
  *   - Every function returns a comet_status. Nothing throws across the ABI.
@@ -60,6 +63,25 @@
  *     one block are one contiguous row.
  *   Block position p of block b is permuted channel 128b + p, i.e. original
  *   channel perm[128b + p].
+ *
+ * FP6 layout (the *_fp6 calls; the same codes, stored as the gfx950 FP6 matrix
+ * instruction consumes them). A 4-bit code q in [-7, 7] is stored as FP6 E2M3
+ * (bit 5 sign, bits 4..3 exponent with bias 1, bits 2..0 mantissa; |q| = 0..7
+ * encode as 0, 8, 16, 20, 24, 26, 28, 30), which represents it exactly. The 32
+ * codes of block positions 32g .. 32g+31 form a 192-bit little-endian string,
+ * code j at bits 6j .. 6j+5; its bytes 0..15 are the group's head, bytes
+ * 16..23 its tail.
+ *   Xq_fp6, device, M * (96 * nb4 + 128 * nb8) bytes, block-major. 4-bit
+ *     block b lives at byte b*M*96, row m at + m*96: the heads of groups 0..3
+ *     at row bytes 16g, then their tails at 64 + 8g. 8-bit block b lives at
+ *     byte nb4*M*96 + (b - nb4)*M*128, row m at + m*128, as in Xq.
+ *   Wq_fp6, N * (96 * nb4 + 64 * nb8) bytes, block-major: for a 4-bit block b
+ *     the N/16 fragments of 1536 bytes start at byte b*(N/16)*1536; fragment c
+ *     (channels 16c .. 16c+15) holds, for lane l in 0..63 (channel
+ *     16c + (l mod 16), group l/16), the head at byte 16l and the tail at
+ *     1024 + 8l. For an 8-bit block b the N/16 INT4 fragments of 1024 bytes
+ *     (the Wq fragment format) start at byte (N/16)*(1536*nb4 + 1024*(b - nb4)).
+ *   x_scale and w_scale as above; no weight sums (the codes are signed).
  */
 #ifndef COMET_W4AX_H
 #define COMET_W4AX_H
@@ -177,6 +199,64 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
                              const uint16_t* w_scale_fp16, const int16_t* w_sum,
                              int n_int8_blocks, int M, int N, int K, int m_begin, int m_count,
                              int32_t* P, void* stream);
+
+/*
+ * FP6 layout, sizes: bytes of Xq_fp6 for M rows and of Wq_fp6 for N output
+ * channels (0 for an invalid shape).
+ */
+size_t comet_xq_fp6_bytes(int M, int K, int n_int8_blocks);
+size_t comet_wq_fp6_bytes(int N, int K, int n_int8_blocks);
+
+/*
+ * Offline, host memory: re-encode comet_pack_weights' Wq into the FP6 layout
+ * (4-bit blocks as FP6 E2M3 fragments, 8-bit blocks copied). The codes are
+ * unchanged, so w_scale applies as is.
+ *
+ *   Wq_packed      in   N*K/2 bytes from comet_pack_weights
+ *   n_int8_blocks  in   nb8 of that call
+ *   Wq_fp6         out  comet_wq_fp6_bytes(N, K, nb8) bytes, layout above
+ * Errors: NULL, SHAPE (N < 1, K % 128 != 0), ARG (nb8 range), UNSUPPORTED
+ * (N % 128 != 0).
+ */
+int comet_repack_weights_fp6(const uint8_t* Wq_packed, int N, int K, int n_int8_blocks,
+                             uint8_t* Wq_fp6);
+
+/*
+ * comet_quant_act writing the FP6 layout: the same codes and scales (QUIK
+ * blog, section "核融合"; COMET article, section "1.离群点分布规律的重定义"),
+ * 4-bit codes as FP6 E2M3. Arguments and errors as comet_quant_act; Xq_fp6
+ * has comet_xq_fp6_bytes(M, K, nb8) bytes.
+ */
+int comet_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                        int n_int8_blocks, void* Xq_fp6, float* x_scale, void* stream);
+
+/*
+ * comet_w4ax_gemm on the FP6 layout, for prefill shapes (any M >= 1 is
+ * valid; it pays off from a few hundred rows). The same result definition
+ * (COMET summary, abstract; QUIK blog, section "核融合"): exact block
+ * partials P (4-bit blocks on the FP6 matrix instruction, whose FP32 result
+ * is exact for these integer products; 8-bit blocks on the INT8 one), then
+ * y = sum over blocks of (x_scale * w_scale) * P in FP32 and Y = fp16(y).
+ * Needs no workspace and no weight sums.
+ *
+ *   Xq_fp6, x_scale   in   from comet_quant_act_fp6
+ *   Wq_fp6            in   from comet_repack_weights_fp6, on device
+ *   w_scale_fp16      in   from comet_pack_weights, on device
+ *   Y_fp16            out  device, [M][ldy] fp16, ldy >= N
+ * Errors: NULL, SHAPE, ALIGN, ARG, UNSUPPORTED, HIP.
+ */
+int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                        const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                        void* Y_fp16, int ldy, void* stream);
+
+/*
+ * Debug variant of comet_w4ax_gemm_fp6: the exact INT32 block partials of rows
+ * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], like
+ * comet_w4ax_gemm_partials.
+ */
+int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                                 const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N,
+                                 int K, int m_begin, int m_count, int32_t* P, void* stream);
 
 /* Static description of a status code. */
 const char* comet_status_string(int status);

@@ -47,7 +47,7 @@ def _weights(cfg):
     W, score = synth.make_w(cfg), synth.make_scores(cfg)
     perm, flags = O.channel_order(score, cfg.nb8)
     qw, sw16, wsum = O.quantize_weights(W, perm)
-    pk = comet.comet_pack_weights(W, score, cfg.nb8)
+    pk = comet.comet_repack_weights_fp6(comet.comet_pack_weights(W, score, cfg.nb8))
     _WCACHE[key] = {"W": W, "score": score, "perm": perm, "flags": flags, "qw": qw,
                     "sw16": sw16, "wsum": wsum, "pk": pk}
     return _WCACHE[key]

@@ -42,3 +42,64 @@ def zero_extended_codes_valid(Xq: np.ndarray, M: int, K: int, nb8: int) -> bool:
     nb4 = K // 128 - nb8
     s4 = np.asarray(Xq, dtype=np.uint8)[: nb4 * M * 64]
     return bool(np.all((s4 & 0xF) >= 1) and np.all((s4 >> 4) >= 1))
+
+
+def e2m3_value(code: np.ndarray) -> np.ndarray:
+    """Value of FP6 E2M3 codes from the format's definition: bit 5 sign, bits
+    4..3 exponent (bias 1), bits 2..0 mantissa; exponent 0 is subnormal."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c >> 5 & 1, -1.0, 1.0)
+    e = c >> 3 & 3
+    m = c & 7
+    return s * np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * 2.0 ** (e - 1))
+
+
+def _codes_from_groups(groups: np.ndarray) -> np.ndarray:
+    """[..., 24] bytes of a group string -> [..., 32] 6-bit codes (code j at bits 6j)."""
+    bits = np.unpackbits(np.asarray(groups, dtype=np.uint8), axis=-1, bitorder="little")
+    bits = bits.reshape(bits.shape[:-1] + (32, 6)).astype(np.int64)
+    return (bits << np.arange(6)).sum(-1)
+
+
+def _fp6_ints(codes: np.ndarray) -> np.ndarray:
+    v = e2m3_value(codes)
+    assert np.all(v == np.round(v)) and np.all(np.abs(v) <= 7), "FP6 code is not a 4-bit integer"
+    assert not np.any(codes == 32), "negative zero code"
+    return v.astype(np.int8)
+
+
+def decode_xq_fp6(Xq: np.ndarray, M: int, K: int, nb8: int) -> np.ndarray:
+    """Xq_fp6 bytes -> q_a int8 [M, K] in permuted channel order."""
+    nb = K // 128
+    nb4 = nb - nb8
+    Xq = np.asarray(Xq, dtype=np.uint8)
+    q = np.empty((M, K), np.int8)
+    rows = Xq[: nb4 * M * 96].reshape(nb4, M, 96)
+    groups = np.concatenate([rows[:, :, :64].reshape(nb4, M, 4, 16),
+                             rows[:, :, 64:].reshape(nb4, M, 4, 8)], axis=-1)      # [b, m, g, 24]
+    vals = _fp6_ints(_codes_from_groups(groups)).reshape(nb4, M, 128)
+    q[:, : nb4 * 128] = vals.transpose(1, 0, 2).reshape(M, nb4 * 128)
+    s8 = Xq[nb4 * M * 96:].view(np.int8).reshape(nb8, M, 128)
+    q[:, nb4 * 128:] = s8.transpose(1, 0, 2).reshape(M, nb8 * 128)
+    return q
+
+
+def decode_wq_fp6(WqF: np.ndarray, N: int, K: int, nb8: int) -> np.ndarray:
+    """Wq_fp6 bytes -> q_w int8 [N, K] in permuted channel order."""
+    nb = K // 128
+    nb4 = nb - nb8
+    G = N // 16
+    WqF = np.asarray(WqF, dtype=np.uint8)
+    q = np.empty((N, K), np.int8)
+    f = WqF[: nb4 * G * 1536].reshape(nb4, G, 1536)
+    groups = np.concatenate([f[:, :, :1024].reshape(nb4, G, 64, 16),
+                             f[:, :, 1024:].reshape(nb4, G, 64, 8)], axis=-1)      # [b, c, lane, 24]
+    vals = _fp6_ints(_codes_from_groups(groups))                                   # [b, c, lane, 32]
+    vals = vals.reshape(nb4, G, 4, 16, 32)                                          # [b, c, g, n16, j]
+    q[:, : nb4 * 128] = vals.transpose(1, 3, 0, 2, 4).reshape(N, nb4 * 128)
+    f8 = WqF[nb4 * G * 1536:].reshape(nb8, G, 4, 16, 16)                            # [b, c, g, n16, j]
+    lo = _sext4(f8 & 0xF)
+    hi = _sext4(f8 >> 4)
+    blk = np.stack([lo, hi], axis=4)                                                # [b, c, g, n16, half, j]
+    q[:, nb4 * 128:] = blk.transpose(1, 3, 0, 2, 4, 5).reshape(N, nb8 * 128)
+    return q

@@ -57,6 +57,38 @@ def gp(Xq=A, xs=A, Wq=A, ws=A, wsum=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P
                                                 None)
 
 
+def qf(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, Xq=A, xs=A):
+    return comet.lib().comet_quant_act_fp6(X, M, K, ldx, perm, nb8, Xq, xs, None)
+
+
+def gf(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512):
+    return comet.lib().comet_w4ax_gemm_fp6(Xq, xs, Wq, ws, nb8, M, N, K, Y, ldy, None)
+
+
+def gfp(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A):
+    return comet.lib().comet_w4ax_gemm_fp6_partials(Xq, xs, Wq, ws, nb8, M, N, K, m0, mc, P, None)
+
+
+def test_fp6_rejections():
+    assert qf(X=None) == NULL and qf(Xq=None) == NULL and qf(M=0) == SHAPE
+    assert qf(ldx=511) == SHAPE and qf(nb8=5) == ARG and qf(Xq=MIS) == ALIGN
+    assert gf(Xq=None) == NULL and gf(Wq=None) == NULL and gf(ws=None) == NULL and gf(Y=None) == NULL
+    assert gf(M=0) == SHAPE and gf(K=100) == SHAPE and gf(ldy=500) == SHAPE
+    assert gf(nb8=5) == ARG and gf(N=200, ldy=200) == UNSUP
+    assert gf(Wq=MIS) == ALIGN and gf(Y=MIS) == ALIGN and gf(xs=MIS) == ALIGN
+    assert gf(M=1 << 20, N=1 << 12, ldy=1 << 12) == UNSUP
+    assert gfp(P=None) == NULL and gfp(m0=10, mc=7) == SHAPE and gfp(P=MIS) == ALIGN
+    L = comet.lib()
+    assert L.comet_xq_fp6_bytes(16, 512, 1) == comet.xq_fp6_bytes(16, 512, 1) == 16 * (96 * 3 + 128)
+    assert L.comet_wq_fp6_bytes(256, 512, 1) == comet.wq_fp6_bytes(256, 512, 1) == 256 * (96 * 3 + 64)
+    assert L.comet_xq_fp6_bytes(16, 500, 1) == 0 and L.comet_wq_fp6_bytes(256, 512, 9) == 0
+    p = ctypes.c_void_p(A)
+    assert L.comet_repack_weights_fp6(None, 128, 256, 0, p) == NULL
+    assert L.comet_repack_weights_fp6(p, 128, 200, 0, p) == SHAPE
+    assert L.comet_repack_weights_fp6(p, 128, 256, 3, p) == ARG
+    assert L.comet_repack_weights_fp6(p, 100, 256, 0, p) == UNSUP
+
+
 def test_quant_act_rejections():
     assert qa(X=None) == NULL and qa(perm=None) == NULL and qa(Xq=None) == NULL
     assert qa(xs=None) == NULL

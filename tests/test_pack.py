@@ -44,3 +44,33 @@ def test_pack_edge_values(orc):
         assert np.array_equal(pk["w_scale"].T, sw16)
         assert np.array_equal(pk["w_sum"].T.astype(np.int32), wsum)
         assert np.array_equal(decode_wq(pk["Wq"], N, K), qw)
+
+
+def test_e2m3_codes_of_the_header():
+    """The header's E2M3 codes of |q| = 0..7 decode, by the format's definition,
+    to exactly 0..7, and their sign-bit twins to -0..-7."""
+    from tests.layout import e2m3_value
+    codes = np.array([0, 8, 16, 20, 24, 26, 28, 30])
+    assert np.array_equal(e2m3_value(codes), np.arange(8.0))
+    assert np.array_equal(e2m3_value(codes | 32), -np.arange(8.0))
+    # every other code is not an integer in [-7, 7] or is a duplicate zero
+    other = np.setdiff1d(np.arange(64), np.concatenate([codes, codes | 32]))
+    v = e2m3_value(other)
+    assert not np.any((v == np.round(v)) & (np.abs(v) <= 7) & (v != 0))
+
+
+@pytest.mark.parametrize("name,nb8", [("tiny", 1), ("q_proj_7b", 4), ("down_7b", 22), ("tiny", 0),
+                                      ("tiny", 4)])
+def test_repack_fp6_matches_oracle(orc, name, nb8):
+    from tests.layout import decode_wq_fp6
+    cfg = synth.CONFIGS[name]
+    W = synth.make_w(cfg)
+    score = synth.make_scores(cfg)
+    if cfg.N * cfg.K > 20e6:
+        W = W[:512]
+    N, K = W.shape
+    pk = comet.comet_repack_weights_fp6(comet.comet_pack_weights(W, score, nb8))
+    assert pk["WqF"].size == comet.wq_fp6_bytes(N, K, nb8)
+    perm, _ = orc.channel_order(score, nb8)
+    qw, _, _ = orc.quantize_weights(W, perm)
+    assert np.array_equal(decode_wq_fp6(pk["WqF"], N, K, nb8), qw)

@@ -49,11 +49,20 @@ def lib() -> ctypes.CDLL:
     L.comet_w4ax_gemm_partials.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
     L.comet_w4ax_gemm_workspace_bytes.argtypes = [I, I, I, I]
     L.comet_w4ax_gemm_workspace_bytes.restype = Z
+    L.comet_xq_fp6_bytes.argtypes = [I, I, I]
+    L.comet_xq_fp6_bytes.restype = Z
+    L.comet_wq_fp6_bytes.argtypes = [I, I, I]
+    L.comet_wq_fp6_bytes.restype = Z
+    L.comet_repack_weights_fp6.argtypes = [P, I, I, I, P]
+    L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
+    L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P]
     L.comet_status_string.argtypes = [I]
     L.comet_status_string.restype = ctypes.c_char_p
     L.comet_version.restype = ctypes.c_char_p
     for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
-              "comet_w4ax_gemm_partials"):
+              "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
+              "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -61,6 +70,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_w4ax_gemm_workspace_bytes", "comet_w4ax_gemm_partials",
+           "comet_xq_fp6_bytes", "comet_wq_fp6_bytes", "comet_repack_weights_fp6",
+           "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
            "comet_status_string", "comet_version")
 
 
@@ -92,6 +103,16 @@ def xq_bytes(M: int, K: int, nb8: int) -> int:
     return M * (64 * (nb - nb8) + 128 * nb8)
 
 
+def xq_fp6_bytes(M: int, K: int, nb8: int) -> int:
+    nb = K // 128
+    return M * (96 * (nb - nb8) + 128 * nb8)
+
+
+def wq_fp6_bytes(N: int, K: int, nb8: int) -> int:
+    nb = K // 128
+    return N * (96 * (nb - nb8) + 64 * nb8)
+
+
 # ----------------------------------------------------------------------------
 # Offline (host)
 # ----------------------------------------------------------------------------
@@ -117,13 +138,27 @@ def comet_pack_weights(W16: np.ndarray, score: np.ndarray, nb8: int) -> dict:
     return out
 
 
+def comet_repack_weights_fp6(packed: dict) -> dict:
+    """Add the FP6-layout weights (key "WqF") to a bundle from comet_pack_weights."""
+    N, K, nb8 = packed["N"], packed["K"], packed["nb8"]
+    WqF = np.zeros(wq_fp6_bytes(N, K, nb8), np.uint8)
+    rc = lib().comet_repack_weights_fp6(_np_ptr(np.ascontiguousarray(packed["Wq"])), N, K, int(nb8),
+                                        _np_ptr(WqF))
+    _check("comet_repack_weights_fp6", rc)
+    packed["WqF"] = WqF
+    return packed
+
+
 def upload_weights(packed: dict, device="cuda") -> dict:
     """Copy the packed weight bundle to device tensors (torch only as memory)."""
     import torch
     d = {"perm": torch.from_numpy(packed["perm"]).to(device),
-         "Wq": torch.from_numpy(packed["Wq"]).to(device),
          "w_scale": torch.from_numpy(packed["w_scale"].view(np.int16)).to(device),
          "w_sum": torch.from_numpy(packed["w_sum"]).to(device)}
+    if "Wq" in packed:
+        d["Wq"] = torch.from_numpy(packed["Wq"]).to(device)
+    if "WqF" in packed:
+        d["WqF"] = torch.from_numpy(packed["WqF"]).to(device)
     d.update({k: packed[k] for k in ("N", "K", "nb8")})
     return d
 
@@ -182,6 +217,50 @@ def comet_w4ax_gemm_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
                                         _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]), int(nb8),
                                         M, N, K, m_begin, m_count, _dev_ptr(P), _stream(stream))
     _check("comet_w4ax_gemm_partials", rc)
+    return P
+
+
+def comet_quant_act_fp6(X, perm, nb8: int, Xq=None, x_scale=None, stream=None):
+    """comet_quant_act with FP6 codes for the 4-bit blocks.
+    Returns (Xq uint8 [xq_fp6_bytes], x_scale float32 [nb, M])."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    if Xq is None:
+        Xq = torch.empty(xq_fp6_bytes(M, K, nb8), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty((K // 128, M), dtype=torch.float32, device=X.device)
+    rc = lib().comet_quant_act_fp6(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(perm), int(nb8),
+                                   _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
+    _check("comet_quant_act_fp6", rc)
+    return Xq, x_scale
+
+
+def comet_w4ax_gemm_fp6(Xq, x_scale, w: dict, M: int, Y=None, stream=None):
+    """Y fp16 [M, N] from FP6-layout activations and the bundle's FP6 weights."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_fp6(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
+                                   _dev_ptr(w["w_scale"]), int(nb8), M, N, K, _dev_ptr(Y), Y.stride(0),
+                                   _stream(stream))
+    _check("comet_w4ax_gemm_fp6", rc)
+    return Y
+
+
+def comet_w4ax_gemm_fp6_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
+                                 m_count: int | None = None, P=None, stream=None):
+    """Exact block partials of the FP6-layout GEMM, [m_count, N, nb] int32."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    m_count = M - m_begin if m_count is None else m_count
+    if P is None:
+        P = torch.empty((m_count, N, K // 128), dtype=torch.int32, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_fp6_partials(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
+                                            _dev_ptr(w["w_scale"]), int(nb8), M, N, K, m_begin,
+                                            m_count, _dev_ptr(P), _stream(stream))
+    _check("comet_w4ax_gemm_fp6_partials", rc)
     return P
 
 

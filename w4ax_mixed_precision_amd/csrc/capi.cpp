@@ -133,6 +133,99 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
     return hip_status(comet::launch_w4ax_gemm(p, stream));
 }
 
+size_t comet_xq_fp6_bytes(int M, int K, int n_int8_blocks) {
+    if (M < 1 || K < kBlock || K % kBlock != 0 || n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return 0;
+    return comet::xq_fp6_bytes(M, K / kBlock - n_int8_blocks, n_int8_blocks);
+}
+
+size_t comet_wq_fp6_bytes(int N, int K, int n_int8_blocks) {
+    if (N < 1 || K < kBlock || K % kBlock != 0 || n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return 0;
+    return comet::wq_fp6_bytes(N, K / kBlock - n_int8_blocks, n_int8_blocks);
+}
+
+int comet_repack_weights_fp6(const uint8_t* Wq_packed, int N, int K, int n_int8_blocks, uint8_t* Wq_fp6) {
+    if (!Wq_packed || !Wq_fp6) return COMET_ERR_NULL;
+    if (N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return COMET_ERR_ARG;
+    if (N % 128 != 0) return COMET_ERR_UNSUPPORTED;
+    comet::repack_fp6(Wq_packed, N, K, n_int8_blocks, Wq_fp6);
+    return COMET_OK;
+}
+
+int comet_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                        int n_int8_blocks, void* Xq_fp6, float* x_scale, void* stream) {
+    if (!X_fp16 || !perm || !Xq_fp6 || !x_scale) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return COMET_ERR_ARG;
+    if (!aligned16(X_fp16) || !aligned16(perm) || !aligned16(Xq_fp6) || !aligned16(x_scale))
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_quant_act_fp6(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
+                                                  n_int8_blocks, static_cast<uint8_t*>(Xq_fp6), x_scale,
+                                                  stream));
+}
+
+int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                        const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                        void* Y_fp16, int ldy, void* stream) {
+    if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !Y_fp16) return COMET_ERR_NULL;
+    int st = check_online_shape(M, N, K, n_int8_blocks);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Xq_fp6) || !aligned16(x_scale) || !aligned16(Wq_fp6) || !aligned16(w_scale_fp16) ||
+        !aligned16(Y_fp16))
+        return COMET_ERR_ALIGN;
+    comet::GemmProblem p{};
+    p.Xq = static_cast<const uint8_t*>(Xq_fp6);
+    p.x_scale = x_scale;
+    p.Wq = static_cast<const uint8_t*>(Wq_fp6);
+    p.w_scale = w_scale_fp16;
+    p.w_sum = nullptr;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.nb = K / kBlock;
+    p.nb4 = p.nb - n_int8_blocks;
+    p.Y = static_cast<uint16_t*>(Y_fp16);
+    p.ldy = ldy;
+    p.P = nullptr;
+    p.m_begin = 0;
+    p.m_count = M;
+    return hip_status(comet::launch_w4ax_gemm_fp6(p, stream));
+}
+
+int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                                 const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                                 int m_begin, int m_count, int32_t* P, void* stream) {
+    if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !P) return COMET_ERR_NULL;
+    int st = check_online_shape(M, N, K, n_int8_blocks);
+    if (st != COMET_OK) return st;
+    if (m_begin < 0 || m_count < 1 || m_begin > M - m_count) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(m_count) * N * (K / kBlock) > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Xq_fp6) || !aligned16(x_scale) || !aligned16(Wq_fp6) || !aligned16(w_scale_fp16) ||
+        !aligned16(P))
+        return COMET_ERR_ALIGN;
+    comet::GemmProblem p{};
+    p.Xq = static_cast<const uint8_t*>(Xq_fp6);
+    p.x_scale = x_scale;
+    p.Wq = static_cast<const uint8_t*>(Wq_fp6);
+    p.w_scale = w_scale_fp16;
+    p.w_sum = nullptr;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.nb = K / kBlock;
+    p.nb4 = p.nb - n_int8_blocks;
+    p.Y = nullptr;
+    p.ldy = N;
+    p.P = P;
+    p.m_begin = m_begin;
+    p.m_count = m_count;
+    return hip_status(comet::launch_w4ax_gemm_fp6(p, stream));
+}
+
 const char* comet_status_string(int status) {
     switch (status) {
         case COMET_OK: return "ok";

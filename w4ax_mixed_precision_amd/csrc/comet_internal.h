@@ -16,10 +16,21 @@ inline size_t xq_bytes(int M, int nb4, int nb8) {
     return static_cast<size_t>(M) * (64u * static_cast<size_t>(nb4) + 128u * static_cast<size_t>(nb8));
 }
 
+// Bytes of the FP6-layout activation and weight buffers.
+inline size_t xq_fp6_bytes(int M, int nb4, int nb8) {
+    return static_cast<size_t>(M) * (96u * static_cast<size_t>(nb4) + 128u * static_cast<size_t>(nb8));
+}
+inline size_t wq_fp6_bytes(int N, int nb4, int nb8) {
+    return static_cast<size_t>(N) * (96u * static_cast<size_t>(nb4) + 64u * static_cast<size_t>(nb8));
+}
+
 // Launchers (device code lives in the .hip files). Arguments were validated by
 // the C entry points; each returns a hipError_t value as int.
 int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                      uint8_t* Xq, float* x_scale, void* stream);
+
+int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                         uint8_t* Xq, float* x_scale, void* stream);
 
 struct GemmProblem {
     const uint8_t* Xq;
@@ -38,9 +49,12 @@ struct GemmProblem {
 
 size_t gemm_workspace_bytes(int M, int N, int K, int nb8);
 int launch_w4ax_gemm(const GemmProblem& p, void* stream);
+int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream);   // FP6 layout; w_sum unused
 
 // Host packer (pack_weights.cpp).
 int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
                  uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum);
+// INT4 fragments to the FP6 layout (pack_weights.cpp).
+void repack_fp6(const uint8_t* Wq, int N, int K, int nb8, uint8_t* WqF);
 
 }  // namespace comet

@@ -84,7 +84,66 @@ bool pack_row(const uint16_t* wrow, int N, int K, const int32_t* perm, int n, ui
     return true;
 }
 
+// FP6 E2M3 bits of an integer code q in [-7, 7] (sign bit 5, exponent bits
+// 4..3 with bias 1, mantissa bits 2..0): |q| = 0..7 -> 0, 8, 16, 20, 24, 26, 28, 30.
+inline uint8_t fp6_code(int q) {
+    static const uint8_t mag[8] = {0, 8, 16, 20, 24, 26, 28, 30};
+    return static_cast<uint8_t>(mag[q < 0 ? -q : q] | (q < 0 ? 32 : 0));
+}
+
+inline int sext4(int v) { return v >= 8 ? v - 16 : v; }
+
+// One INT4 fragment (1024 B) of a 4-bit block to its FP6 fragment (1536 B):
+// lane l's 32 codes (positions 32(l/16) + j) become a 192-bit string, code j
+// at bits 6j; bytes 0..15 go to the head at 16l, bytes 16..23 to the tail at
+// 1024 + 8l.
+void fragment_to_fp6(const uint8_t* src, uint8_t* dst) {
+    for (int l = 0; l < 64; ++l) {
+        uint8_t bits[24] = {};
+        for (int j = 0; j < 32; ++j) {
+            const uint8_t byte = src[16 * l + (j & 15)];
+            const int q = sext4(j < 16 ? (byte & 0xF) : (byte >> 4));
+            const uint32_t code = fp6_code(q);
+            const int bit = 6 * j;
+            bits[bit / 8] |= static_cast<uint8_t>(code << (bit % 8));
+            if (bit % 8 > 2) bits[bit / 8 + 1] |= static_cast<uint8_t>(code >> (8 - bit % 8));
+        }
+        std::copy(bits, bits + 16, dst + 16 * l);
+        std::copy(bits + 16, bits + 24, dst + 1024 + 8 * l);
+    }
+}
+
 }  // namespace
+
+void repack_fp6(const uint8_t* Wq, int N, int K, int nb8, uint8_t* WqF) {
+    const int nb = K / kBlock;
+    const int nb4 = nb - nb8;
+    const int groups = N / 16;
+    unsigned hw = std::thread::hardware_concurrency();
+    const int threads = static_cast<int>(std::max(1u, std::min(hw ? hw : 1u, 32u)));
+    const int per = (groups + threads - 1) / threads;
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t) {
+        const int f0 = t * per, f1 = std::min(groups, f0 + per);
+        if (f0 >= f1) break;
+        pool.emplace_back([=] {
+            for (int f = f0; f < f1; ++f)
+                for (int b = 0; b < nb; ++b) {
+                    const uint8_t* src = Wq + (static_cast<size_t>(f) * nb + b) * kFragBytes;
+                    if (b < nb4) {
+                        uint8_t* dst = WqF + static_cast<size_t>(b) * groups * 1536 + static_cast<size_t>(f) * 1536;
+                        fragment_to_fp6(src, dst);
+                    } else {
+                        uint8_t* dst = WqF + static_cast<size_t>(groups) * (1536u * static_cast<size_t>(nb4) +
+                                                                            1024u * static_cast<size_t>(b - nb4)) +
+                                       static_cast<size_t>(f) * kFragBytes;
+                        std::copy(src, src + kFragBytes, dst);
+                    }
+                }
+        });
+    }
+    for (auto& th : pool) th.join();
+}
 
 int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
                  uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum) {

@@ -16,6 +16,13 @@
 // butterfly inside the 16-lane group. Each lane quantizes 8 channels and
 // writes one packed dword (4-bit block) or 8 bytes (8-bit block), so the
 // stores of a block row are one coalesced 64- or 128-byte segment.
+//
+// The FP6 variant writes the codes of the 4-bit blocks as FP6 E2M3 values
+// (every integer in [-7, 7] is exact in that format), the operand format of
+// the gfx950 FP6 matrix instruction; 8-bit blocks are the same in both. There a
+// lane codes block positions 32g + 8s .. 32g + 8s + 7 (g = group, s = quarter
+// of the group), i.e. 48 bits of the group's 192-bit code string, and
+// neighbouring lanes trade 16 bits so that every store is a whole dword.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -42,7 +49,15 @@ __device__ inline int quantize(float x, float inv, float qmax) {
     return static_cast<int>(r);
 }
 
-template <bool kRowInLds>
+// FP6 E2M3 (sign, 2 exponent bits with bias 1, 3 mantissa bits) of an
+// integer q in [-7, 7]: |q| = 0..7 encode as 0, 8, 16, 20, 24, 26, 28, 30.
+__device__ inline uint32_t fp6_code(int q) {
+    const uint32_t a = static_cast<uint32_t>(q < 0 ? -q : q);
+    const uint32_t mag = static_cast<uint32_t>((0x1E1C1A1814100800ull >> (8u * a)) & 0xFFu);
+    return mag | (q < 0 ? 32u : 0u);
+}
+
+template <bool kRowInLds, bool kFp6>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
     int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
@@ -75,7 +90,11 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 
         // The 8 block positions this lane codes (see the Xq layout).
         int4 p0, p1;
-        if (!is8) {
+        if (!is8 && kFp6) {
+            const int g = i >> 2, s8 = (i & 3) * 8;
+            p0 = *reinterpret_cast<const int4*>(pb + 32 * g + s8);
+            p1 = *reinterpret_cast<const int4*>(pb + 32 * g + s8 + 4);
+        } else if (!is8) {
             const int g = i >> 2, j0 = (i & 3) * 4;
             p0 = *reinterpret_cast<const int4*>(pb + 32 * g + j0);
             p1 = *reinterpret_cast<const int4*>(pb + 32 * g + 16 + j0);
@@ -105,8 +124,39 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = a > 0.0f ? quantize(v[e], inv, qmax) : 0;
 
+        // FP6: this lane's 48 code bits (element e at bits 6e), and the low
+        // dword of the neighbouring quarter, taken with every lane active
+        uint32_t f_lo = 0, f_hi = 0, f_nlo = 0;
+        if constexpr (kFp6) {
+            uint64_t f = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f |= static_cast<uint64_t>(fp6_code(q[e])) << (6 * e);
+            f_lo = static_cast<uint32_t>(f);
+            f_hi = static_cast<uint32_t>(f >> 32);
+            f_nlo = __shfl_xor(f_lo, 1);
+        }
+
         if (valid) {
-            if (!is8) {
+            if (!is8 && kFp6) {
+                // group string: head = bits 0..127 at row byte 16g, tail = bits
+                // 128..191 at row byte 64 + 8g; quarter s holds bits 48s..48s+47
+                const int g = i >> 2, sq = i & 3;
+                uint8_t* row = Xq + static_cast<size_t>(bc) * M * 96 + static_cast<size_t>(m) * 96;
+                uint8_t* head = row + 16 * g;
+                uint8_t* tail = row + 64 + 8 * g;
+                const uint32_t joined = (f_hi & 0xFFFFu) | (f_nlo << 16);   // bits 32..47 + next 0..15
+                const uint32_t upper = (f_lo >> 16) | (f_hi << 16);         // bits 16..47
+                if (sq == 0) {
+                    *reinterpret_cast<uint2*>(head) = make_uint2(f_lo, joined);
+                } else if (sq == 1) {
+                    *reinterpret_cast<uint32_t*>(head + 8) = upper;
+                } else if (sq == 2) {
+                    *reinterpret_cast<uint32_t*>(head + 12) = f_lo;
+                    *reinterpret_cast<uint32_t*>(tail) = joined;
+                } else {
+                    *reinterpret_cast<uint32_t*>(tail + 4) = upper;
+                }
+            } else if (!is8) {
                 uint32_t w = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -123,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
                     w0 |= (static_cast<uint32_t>(q[e]) & 0xFF) << (8 * e);
                     w1 |= (static_cast<uint32_t>(q[4 + e]) & 0xFF) << (8 * e);
                 }
-                uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * 64 +
+                const size_t slab4 = kFp6 ? 96 : 64;
+                uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * slab4 +
                                static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128;
                 *reinterpret_cast<uint2*>(dst + 8 * i) = make_uint2(w0, w1);
             }
@@ -132,10 +183,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     }
 }
 
-}  // namespace
-
-int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
-                     uint8_t* Xq, float* x_scale, void* stream) {
+template <bool kFp6>
+int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8, uint8_t* Xq,
+           float* x_scale, void* stream) {
     const int nb = K / kBlock;
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
@@ -148,13 +198,25 @@ int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* pe
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K <= kMaxLdsRowChannels) {
         const size_t lds = static_cast<size_t>(K) * sizeof(uint16_t);
-        quant_act_kernel<true><<<grid, kThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                           x_scale);
+        quant_act_kernel<true, kFp6><<<grid, kThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
+                                                                 x_scale);
     } else {
-        quant_act_kernel<false><<<grid, kThreads, 0, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                          x_scale);
+        quant_act_kernel<false, kFp6><<<grid, kThreads, 0, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
+                                                                x_scale);
     }
     return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                     uint8_t* Xq, float* x_scale, void* stream) {
+    return launch<false>(X, M, K, ldx, perm, nb8, Xq, x_scale, stream);
+}
+
+int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                         uint8_t* Xq, float* x_scale, void* stream) {
+    return launch<true>(X, M, K, ldx, perm, nb8, Xq, x_scale, stream);
 }
 
 }  // namespace comet

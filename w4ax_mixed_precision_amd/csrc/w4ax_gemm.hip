@@ -29,47 +29,13 @@
 // products t of four 16x16 tiles come from one v_mfma_f32_16x16x1_4b_f32
 // (outer products of s_x and s_w on the matrix unit), accumulators stay in
 // VGPRs, and 64x64 wave tiles amortize the widening.
-#include <hip/hip_runtime.h>
-#include <hip/hip_fp16.h>
-
 #include "comet_internal.h"
+#include "device_util.h"
 
 namespace comet {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
 constexpr int kThreads = 256;
-
-// Integer minimum by value (a reference-returning min leaves stack slots behind).
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
-
-__device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-
-__device__ inline v4i widen_weights_lo(uint4 p) {   // block positions 32g + j
-    return v4i{static_cast<int>((p.x << 4) & 0xF0F0F0F0u), static_cast<int>((p.y << 4) & 0xF0F0F0F0u),
-               static_cast<int>((p.z << 4) & 0xF0F0F0F0u), static_cast<int>((p.w << 4) & 0xF0F0F0F0u)};
-}
-__device__ inline v4i widen_weights_hi(uint4 p) {   // block positions 32g + 16 + j
-    return v4i{static_cast<int>(p.x & 0xF0F0F0F0u), static_cast<int>(p.y & 0xF0F0F0F0u),
-               static_cast<int>(p.z & 0xF0F0F0F0u), static_cast<int>(p.w & 0xF0F0F0F0u)};
-}
-__device__ inline v4i widen_act_lo(uint4 p) {
-    return v4i{static_cast<int>(p.x & 0x0F0F0F0Fu), static_cast<int>(p.y & 0x0F0F0F0Fu),
-               static_cast<int>(p.z & 0x0F0F0F0Fu), static_cast<int>(p.w & 0x0F0F0F0Fu)};
-}
-__device__ inline v4i widen_act_hi(uint4 p) {
-    return v4i{static_cast<int>((p.x >> 4) & 0x0F0F0F0Fu), static_cast<int>((p.y >> 4) & 0x0F0F0F0Fu),
-               static_cast<int>((p.z >> 4) & 0x0F0F0F0Fu), static_cast<int>((p.w >> 4) & 0x0F0F0F0Fu)};
-}
-__device__ inline v4i as_v4i(uint4 p) {
-    return v4i{static_cast<int>(p.x), static_cast<int>(p.y), static_cast<int>(p.z), static_cast<int>(p.w)};
-}
-
-__device__ inline v4i mfma_i8(v4i a, v4i b, v4i c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (prefill shapes): 128 x 128 output tile per workgroup of four
@@ -114,37 +80,6 @@ constexpr int kLdsWs = kTN * 2;
 constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSw + kLdsWs;
 constexpr int kStages = COMET_TILED_STAGES;
 static_assert(kStages == 3 || kStages == 4, "the unrolled ring below is written for three or four stages");
-
-// Tile of a workgroup. Workgroups are dispatched round-robin over the eight
-// XCDs (workgroup w runs on XCD w mod 8); each XCD gets a contiguous range of
-// the tile order, and the tile order walks 8-row-tile groups column by
-// column, so the workgroups an XCD runs at once cover a compact patch and
-// share their A and B stripes in that XCD's L2.
-__device__ inline bool tile_of(int w, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + 7) / 8;
-    const int t = (w & 7) * per_xcd + (w >> 3);
-    if (t >= total) return false;
-    constexpr int G = 8;
-    const int group = t / (G * tiles_n);
-    const int first = group * G;
-    const int gh = imin(G, tiles_m - first);
-    const int in = t - group * G * tiles_n;
-    tn = in / gh;
-    tm = first + in % gh;
-    return true;
-}
-
-__device__ __forceinline__ void lds_load16(const void* g, uint8_t* lds_piece) {
-    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(lds_piece)),
-                                     16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* g, uint8_t* lds_piece) {
-    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(lds_piece)),
-                                     4, 0, 0);
-}
 
 // Per-lane byte offsets of the direct loads, fixed for a tile: the block only
 // moves the (wave-uniform) base pointers.
@@ -213,10 +148,6 @@ __device__ __forceinline__ void tiled_issue(const GemmProblem& p, int b, int n0,
 __device__ __forceinline__ int issued_loads(int b, int nb, int nb4) {
     return b >= nb ? 0 : (b < nb4 ? 5 : 7);
 }
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-#define COMET_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Wait until at most `younger` of this wave's direct loads are outstanding.
 __device__ __forceinline__ void wait_loads(int younger) {
