@@ -71,10 +71,14 @@
  * codes of block positions 32g .. 32g+31 form a 192-bit little-endian string,
  * code j at bits 6j .. 6j+5; its bytes 0..15 are the group's head, bytes
  * 16..23 its tail.
- *   Xq_fp6, device, M * (96 * nb4 + 128 * nb8) bytes, block-major. 4-bit
- *     block b lives at byte b*M*96, row m at + m*96: the heads of groups 0..3
- *     at row bytes 16g, then their tails at 64 + 8g. 8-bit block b lives at
- *     byte nb4*M*96 + (b - nb4)*M*128, row m at + m*128, as in Xq.
+ *   Xq_fp6, device, Mp * (96 * nb4 + 128 * nb8) bytes with Mp = M rounded up
+ *     to a multiple of 16, block-major, in 16-row tiles (rows M .. Mp-1 are
+ *     padding, never written and never used). 4-bit block b lives at byte
+ *     b*Mp*96; its tile t (rows 16t .. 16t+15) at + t*1536 holds the head of
+ *     group g of row 16t + r at byte 256g + 16r and its tail at
+ *     1024 + 128g + 8r. 8-bit block b lives at byte nb4*Mp*96 + (b - nb4)*Mp*128;
+ *     its tile t at + t*2048 holds the int8 codes of block positions
+ *     32g + 16h .. 32g + 16h + 15 of row 16t + r at byte 1024h + 256g + 16r.
  *   Wq_fp6, N * (96 * nb4 + 64 * nb8) bytes, block-major: for a 4-bit block b
  *     the N/16 fragments of 1536 bytes start at byte b*(N/16)*1536; fragment c
  *     (channels 16c .. 16c+15) holds, for lane l in 0..63 (channel
@@ -201,8 +205,8 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
                              int32_t* P, void* stream);
 
 /*
- * FP6 layout, sizes: bytes of Xq_fp6 for M rows and of Wq_fp6 for N output
- * channels (0 for an invalid shape).
+ * FP6 layout, sizes: bytes of Xq_fp6 for M rows (padded to a multiple of 16)
+ * and of Wq_fp6 for N output channels (0 for an invalid shape).
  */
 size_t comet_xq_fp6_bytes(int M, int K, int n_int8_blocks);
 size_t comet_wq_fp6_bytes(int N, int K, int n_int8_blocks);
@@ -237,7 +241,8 @@ int comet_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t
  * partials P (4-bit blocks on the FP6 matrix instruction, whose FP32 result
  * is exact for these integer products; 8-bit blocks on the INT8 one), then
  * y = sum over blocks of (x_scale * w_scale) * P in FP32 and Y = fp16(y).
- * Needs no workspace and no weight sums.
+ * Needs no workspace and no weight sums. UNSUPPORTED also covers
+ * Mp * K > 2^31 - 1 (the kernel's 32-bit offsets into Xq_fp6).
  *
  *   Xq_fp6, x_scale   in   from comet_quant_act_fp6
  *   Wq_fp6            in   from comet_repack_weights_fp6, on device

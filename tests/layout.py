@@ -69,18 +69,26 @@ def _fp6_ints(codes: np.ndarray) -> np.ndarray:
 
 
 def decode_xq_fp6(Xq: np.ndarray, M: int, K: int, nb8: int) -> np.ndarray:
-    """Xq_fp6 bytes -> q_a int8 [M, K] in permuted channel order."""
+    """Xq_fp6 bytes (16-row tiles, rows padded to Mp) -> q_a int8 [M, K] in
+    permuted channel order."""
     nb = K // 128
     nb4 = nb - nb8
+    Mp = (M + 15) // 16 * 16
+    T = Mp // 16
     Xq = np.asarray(Xq, dtype=np.uint8)
+    assert Xq.size == Mp * (96 * nb4 + 128 * nb8)
     q = np.empty((M, K), np.int8)
-    rows = Xq[: nb4 * M * 96].reshape(nb4, M, 96)
-    groups = np.concatenate([rows[:, :, :64].reshape(nb4, M, 4, 16),
-                             rows[:, :, 64:].reshape(nb4, M, 4, 8)], axis=-1)      # [b, m, g, 24]
-    vals = _fp6_ints(_codes_from_groups(groups)).reshape(nb4, M, 128)
+    tiles = Xq[: nb4 * Mp * 96].reshape(nb4, T, 1536)
+    heads = tiles[:, :, :1024].reshape(nb4, T, 4, 16, 16)                          # [b, t, g, r, 16]
+    tails = tiles[:, :, 1024:].reshape(nb4, T, 4, 16, 8)                           # [b, t, g, r, 8]
+    groups = np.concatenate([heads, tails], axis=-1)                               # [b, t, g, r, 24]
+    codes = _codes_from_groups(groups).transpose(0, 1, 3, 2, 4)                    # [b, t, r, g, 32]
+    codes = codes.reshape(nb4, Mp, 128)[:, :M]                                     # padding rows dropped
+    vals = _fp6_ints(codes)                                                        # [b, m, 32g + j]
     q[:, : nb4 * 128] = vals.transpose(1, 0, 2).reshape(M, nb4 * 128)
-    s8 = Xq[nb4 * M * 96:].view(np.int8).reshape(nb8, M, 128)
-    q[:, nb4 * 128:] = s8.transpose(1, 0, 2).reshape(M, nb8 * 128)
+    t8 = Xq[nb4 * Mp * 96:].view(np.int8).reshape(nb8, T, 2, 4, 16, 16)            # [b, t, h, g, r, j]
+    v8 = t8.transpose(0, 1, 4, 3, 2, 5).reshape(nb8, Mp, 128)[:, :M]               # [b, m, 32g + 16h + j]
+    q[:, nb4 * 128:] = v8.transpose(1, 0, 2).reshape(M, nb8 * 128)
     return q
 
 

@@ -105,7 +105,8 @@ def xq_bytes(M: int, K: int, nb8: int) -> int:
 
 def xq_fp6_bytes(M: int, K: int, nb8: int) -> int:
     nb = K // 128
-    return M * (96 * (nb - nb8) + 128 * nb8)
+    mp = (M + 15) // 16 * 16          # rows padded to whole 16-row tiles
+    return mp * (96 * (nb - nb8) + 128 * nb8)
 
 
 def wq_fp6_bytes(N: int, K: int, nb8: int) -> int:

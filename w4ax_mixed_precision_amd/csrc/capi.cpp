@@ -28,6 +28,13 @@ int check_online_shape(int M, int N, int K, int nb8) {
 
 int hip_status(int e) { return e == 0 ? COMET_OK : COMET_ERR_HIP; }
 
+// The FP6 GEMM addresses its activation buffer (rows padded to 16) with
+// 32-bit byte offsets: at most 128 bytes per (padded row, block).
+bool fp6_offsets_fit(int M, int K) {
+    const int64_t mp = (static_cast<int64_t>(M) + 15) & ~static_cast<int64_t>(15);
+    return mp * K <= std::numeric_limits<int32_t>::max();
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +177,7 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
     if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !Y_fp16) return COMET_ERR_NULL;
     int st = check_online_shape(M, N, K, n_int8_blocks);
     if (st != COMET_OK) return st;
+    if (!fp6_offsets_fit(M, K)) return COMET_ERR_UNSUPPORTED;
     if (ldy < N) return COMET_ERR_SHAPE;
     if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
         return COMET_ERR_UNSUPPORTED;
@@ -201,6 +209,7 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
     if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !P) return COMET_ERR_NULL;
     int st = check_online_shape(M, N, K, n_int8_blocks);
     if (st != COMET_OK) return st;
+    if (!fp6_offsets_fit(M, K)) return COMET_ERR_UNSUPPORTED;
     if (m_begin < 0 || m_count < 1 || m_begin > M - m_count) return COMET_ERR_SHAPE;
     if (static_cast<int64_t>(m_count) * N * (K / kBlock) > std::numeric_limits<int32_t>::max())
         return COMET_ERR_UNSUPPORTED;

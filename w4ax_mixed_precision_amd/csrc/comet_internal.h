@@ -17,8 +17,9 @@ inline size_t xq_bytes(int M, int nb4, int nb8) {
 }
 
 // Bytes of the FP6-layout activation and weight buffers.
-inline size_t xq_fp6_bytes(int M, int nb4, int nb8) {
-    return static_cast<size_t>(M) * (96u * static_cast<size_t>(nb4) + 128u * static_cast<size_t>(nb8));
+inline size_t xq_fp6_bytes(int M, int nb4, int nb8) {     // rows padded to 16-row tiles
+    const size_t mp = (static_cast<size_t>(M) + 15u) & ~static_cast<size_t>(15);
+    return mp * (96u * static_cast<size_t>(nb4) + 128u * static_cast<size_t>(nb8));
 }
 inline size_t wq_fp6_bytes(int N, int nb4, int nb8) {
     return static_cast<size_t>(N) * (96u * static_cast<size_t>(nb4) + 64u * static_cast<size_t>(nb8));

@@ -19,10 +19,12 @@
 //
 // The FP6 variant writes the codes of the 4-bit blocks as FP6 E2M3 values
 // (every integer in [-7, 7] is exact in that format), the operand format of
-// the gfx950 FP6 matrix instruction; 8-bit blocks are the same in both. There a
-// lane codes block positions 32g + 8s .. 32g + 8s + 7 (g = group, s = quarter
-// of the group), i.e. 48 bits of the group's 192-bit code string, and
-// neighbouring lanes trade 16 bits so that every store is a whole dword.
+// the gfx950 FP6 matrix instruction, in 16-row tiles laid out exactly as the
+// GEMM reads them from LDS (each 16-lane k-group of a wave reads one
+// contiguous 256-byte run). A lane codes block positions 32g + 8s .. 32g + 8s
+// + 7 (g = group, s = quarter of the group), i.e. 48 bits of the group's
+// 192-bit code string, and neighbouring lanes trade 16 bits so that every
+// store is a whole dword.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int Mp = (M + 15) & ~15;     // FP6 layout: rows padded to whole 16-row tiles
     const int quarter = lane >> 4;    // which of the wave's four blocks
     const int i = lane & 15;          // lane within the block's 16-lane group
     const int stride = gridDim.y * 16;
@@ -138,12 +141,13 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 
         if (valid) {
             if (!is8 && kFp6) {
-                // group string: head = bits 0..127 at row byte 16g, tail = bits
-                // 128..191 at row byte 64 + 8g; quarter s holds bits 48s..48s+47
+                // group string: head = bits 0..127 at tile byte 256g + 16r, tail
+                // = bits 128..191 at tile byte 1024 + 128g + 8r (r = row in the
+                // 16-row tile); quarter s holds bits 48s..48s+47
                 const int g = i >> 2, sq = i & 3;
-                uint8_t* row = Xq + static_cast<size_t>(bc) * M * 96 + static_cast<size_t>(m) * 96;
-                uint8_t* head = row + 16 * g;
-                uint8_t* tail = row + 64 + 8 * g;
+                uint8_t* tile = Xq + static_cast<size_t>(bc) * Mp * 96 + static_cast<size_t>(m >> 4) * 1536;
+                uint8_t* head = tile + 256 * g + 16 * (m & 15);
+                uint8_t* tail = tile + 1024 + 128 * g + 8 * (m & 15);
                 const uint32_t joined = (f_hi & 0xFFFFu) | (f_nlo << 16);   // bits 32..47 + next 0..15
                 const uint32_t upper = (f_lo >> 16) | (f_hi << 16);         // bits 16..47
                 if (sq == 0) {
@@ -173,10 +177,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
                     w0 |= (static_cast<uint32_t>(q[e]) & 0xFF) << (8 * e);
                     w1 |= (static_cast<uint32_t>(q[4 + e]) & 0xFF) << (8 * e);
                 }
-                const size_t slab4 = kFp6 ? 96 : 64;
-                uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * slab4 +
-                               static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128;
-                *reinterpret_cast<uint2*>(dst + 8 * i) = make_uint2(w0, w1);
+                if constexpr (kFp6) {
+                    // 16-row tiles of 2048 bytes: positions 32g + 16h + j of
+                    // row r at tile byte 1024h + 256g + 16r + j
+                    uint8_t* tile = Xq + static_cast<size_t>(nb4) * Mp * 96 +
+                                    static_cast<size_t>(bc - nb4) * Mp * 128 + static_cast<size_t>(m >> 4) * 2048;
+                    const int g = i >> 2, h = (i >> 1) & 1;
+                    *reinterpret_cast<uint2*>(tile + 1024 * h + 256 * g + 16 * (m & 15) + 8 * (i & 1)) =
+                        make_uint2(w0, w1);
+                } else {
+                    uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * 64 +
+                                   static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128;
+                    *reinterpret_cast<uint2*>(dst + 8 * i) = make_uint2(w0, w1);
+                }
             }
             if (i == 0) x_scale[static_cast<size_t>(bc) * M + m] = s;
         }
