@@ -9,191 +9,279 @@
 // (mmssai.com/?p=43269), section "1.离群点分布规律的重定义": 8 bits for the
 // outlier-dense blocks, 4 bits for the rest.
 //
-// Mapping on gfx950. One workgroup (4 wave64s) per token row. The row is first
-// staged into LDS with coalesced 16-byte loads (HBM sees one contiguous read
-// of 2K bytes), then the channel gather by perm happens in LDS. A wave handles
-// four blocks at a time, 16 lanes per block; the absmax reduction is a 4-step
-// butterfly inside the 16-lane group. Each lane quantizes 8 channels and
-// writes one packed dword (4-bit block) or 8 bytes (8-bit block), so the
-// stores of a block row are one coalesced 64- or 128-byte segment.
-//
-// The FP6 variant writes the codes of the 4-bit blocks as FP6 E2M3 values
-// (every integer in [-7, 7] is exact in that format), the operand format of
-// the gfx950 FP6 matrix instruction, in 16-row tiles laid out exactly as the
-// GEMM reads them from LDS (each 16-lane k-group of a wave reads one
-// contiguous 256-byte run). A lane codes block positions 32g + 8s .. 32g + 8s
-// + 7 (g = group, s = quarter of the group), i.e. 48 bits of the group's
-// 192-bit code string, and neighbouring lanes trade 16 bits so that every
-// store is a whole dword.
+// Mapping on gfx950. One workgroup (4 wave64s) per token row (or per part of
+// a row's blocks when there are few rows). The row is first staged into LDS
+// with direct loads (buffer_load ... lds, 1 KB per wave instruction, all in
+// flight at once; HBM sees one contiguous read of 2K bytes); the channel
+// gather by perm then happens in LDS. A lane owns one 32-channel group of a
+// block (positions 32g .. 32g+31), four lanes (one DPP quad) a block, so a
+// wave covers 16 blocks per pass; the absmax is two DPP steps inside the quad.
+// The perm entries of the next pass are fetched while this one computes. Codes
+// leave as whole 16-byte stores:
+//   * FP6 layout, 4-bit block: one v_cvt_scalef32_2xpk16_fp6_f32 (scale 1)
+//     turns the lane's 32 integer values into its 192-bit FP6 E2M3 string
+//     (every integer in [-7, 7] is exact in E2M3); the instruction takes its
+//     two 16-value sources interleaved (code 2i from the first, 2i + 1 from
+//     the second). Rows are written in the GEMM's 16-row tiles.
+//   * INT4 layout, 4-bit block: zero-extended nibbles u = q + 8, byte j of the
+//     group holding positions j (low) and 16 + j (high).
+//   * 8-bit blocks: int8 codes in position order (FP6 layout: 16-row tiles).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <mutex>
+
 #include "comet_internal.h"
+#include "device_util.h"
 
 namespace comet {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxLdsRowChannels = 32768;     // 64 KB of fp16 per staged row
+constexpr int kWaves = kThreads / 64;
+constexpr int kBlocksPerPass = kWaves * 16;      // 4 lanes per block
+constexpr int kMaxLdsRowChannels = 32768;        // 64 KB of fp16 per staged row
 
-// Integer minimum by value (a reference-returning min leaves stack slots behind).
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 
-__device__ inline float h2f(uint16_t h) {
-    return __half2float(__ushort_as_half(h));
+// Lane exchange inside a DPP quad (no LDS round trip): quad_perm [1,0,3,2]
+// (xor 1) and [2,3,0,1] (xor 2).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
 
-// q = clamp(rint(x * inv), -qmax, qmax); the product is a single rounded
-// multiply (nothing to contract it with) and rint is round-half-even.
-__device__ inline int quantize(float x, float inv, float qmax) {
-    float r = __builtin_rintf(x * inv);
-    r = fminf(qmax, fmaxf(-qmax, r));
-    return static_cast<int>(r);
+// The 32 channels (perm entries) of group g of block b.
+__device__ __forceinline__ void load_positions(const int32_t* __restrict__ perm, int b, int g, int4 (&p)[8]) {
+    const int4* src = reinterpret_cast<const int4*>(perm + b * kBlock + 32 * g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = src[k];
 }
 
-// FP6 E2M3 (sign, 2 exponent bits with bias 1, 3 mantissa bits) of an
-// integer q in [-7, 7]: |q| = 0..7 encode as 0, 8, 16, 20, 24, 26, 28, 30.
-__device__ inline uint32_t fp6_code(int q) {
-    const uint32_t a = static_cast<uint32_t>(q < 0 ? -q : q);
-    const uint32_t mag = static_cast<uint32_t>((0x1E1C1A1814100800ull >> (8u * a)) & 0xFFu);
-    return mag | (q < 0 ? 32u : 0u);
+// Codes and scale of block b of row m for this lane's group g, from the row
+// (LDS or global) and the lane's 32 channels `pos`.
+template <bool kFp6>
+__device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, const int4 (&pos)[8], int b, int nb,
+                                           int nb4, int M, int Mp, int m, int g, uint8_t* __restrict__ Xq,
+                                           float* __restrict__ x_scale) {
+    const bool valid = b < nb;
+    const int bc = valid ? b : nb - 1;
+    const bool is8 = bc >= nb4;
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int idx[4] = {pos[k].x, pos[k].y, pos[k].z, pos[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * k + e] = h2f(row[idx[e]]);
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) a = fmaxf(a, fabsf(v[e]));
+    a = fmaxf(a, dpp_f<0xB1>(a));      // absmax over the block's quad
+    a = fmaxf(a, dpp_f<0x4E>(a));
+
+    const float qmax = is8 ? 127.0f : 7.0f;
+    float inv = 0.0f, sc = 0.0f;
+    if (a > 0.0f) {
+        inv = qmax / a;     // correctly rounded IEEE division
+        sc = a / qmax;
+    }
+    // q = clamp(rint(x * inv), -qmax, qmax). The clamp never acts: |x| <= a
+    // and inv <= (qmax / a)(1 + 2^-24) bound |fl(x * inv)| by
+    // qmax (1 + 2^-24)^2 < qmax + 1/2. Adding +0 turns a -0 into +0.
+    float r[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) r[e] = __builtin_rintf(v[e] * inv) + 0.0f;
+
+    if (valid) {
+        if (!is8 && kFp6) {
+            v16f even, odd;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                even[e] = r[2 * e];
+                odd[e] = r[2 * e + 1];
+            }
+            const v6i c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
+            uint8_t* tile = Xq + static_cast<size_t>(bc) * Mp * 96 + static_cast<size_t>(m >> 4) * 1536;
+            *reinterpret_cast<uint4*>(tile + 256 * g + 16 * (m & 15)) = make_uint4(c[0], c[1], c[2], c[3]);
+            *reinterpret_cast<uint2*>(tile + 1024 + 128 * g + 8 * (m & 15)) = make_uint2(c[4], c[5]);
+        } else if (!is8) {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = static_cast<uint32_t>(static_cast<int>(r[4 * d + k]) + 8);
+                    const uint32_t hi = static_cast<uint32_t>(static_cast<int>(r[16 + 4 * d + k]) + 8);
+                    x |= (lo | (hi << 4)) << (8 * k);
+                }
+                w[d] = x;
+            }
+            uint8_t* dst = Xq + static_cast<size_t>(bc) * M * 64 + static_cast<size_t>(m) * 64 + 16 * g;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    x |= (static_cast<uint32_t>(static_cast<int>(r[4 * d + k])) & 0xFFu) << (8 * k);
+                w[d] = x;
+            }
+            if constexpr (kFp6) {
+                // 16-row tiles of 2048 bytes: positions 32g + 16h + j of
+                // row r at tile byte 1024h + 256g + 16r + j
+                uint8_t* tile = Xq + static_cast<size_t>(nb4) * Mp * 96 +
+                                static_cast<size_t>(bc - nb4) * Mp * 128 + static_cast<size_t>(m >> 4) * 2048;
+                *reinterpret_cast<uint4*>(tile + 256 * g + 16 * (m & 15)) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4*>(tile + 1024 + 256 * g + 16 * (m & 15)) =
+                    make_uint4(w[4], w[5], w[6], w[7]);
+            } else {
+                uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * 64 +
+                               static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128 + 32 * g;
+                *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+        }
+        if (g == 0) x_scale[static_cast<size_t>(bc) * M + m] = sc;
+    }
 }
 
 template <bool kRowInLds, bool kFp6>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
-    int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
+    int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd) {
     extern __shared__ uint16_t row_lds[];
-    const int m = blockIdx.x;
+    // Row of this workgroup. Workgroup w runs on XCD w mod 8 and each XCD has
+    // its own L2; with `rows_per_xcd` > 0 every XCD takes a contiguous range
+    // of rows (whole 16-row tiles), so the partial cache lines that the rows
+    // of one tile write meet in one L2 instead of leaving as partial writes.
+    int m = blockIdx.x;
+    if (rows_per_xcd > 0) {
+        m = (blockIdx.x & 7) * rows_per_xcd + (blockIdx.x >> 3);
+        if (m >= M) return;
+    }
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
-
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if constexpr (kRowInLds) {
         if ((ldx & 7) == 0) {
-            for (int c = threadIdx.x * 8; c < K; c += kThreads * 8)
-                *reinterpret_cast<uint4*>(row_lds + c) = *reinterpret_cast<const uint4*>(xr + c);
+            // direct loads of the row: 1 KB per wave instruction, all in flight
+            // at once; the LDS row buffer is rounded up to whole KB and the
+            // bytes past the row read as 0
+            const Rsrc r = make_rsrc(xr, 2u * static_cast<uint32_t>(K));
+            const int chunks = (K + 511) / 512;
+            uint8_t* lds = reinterpret_cast<uint8_t*>(row_lds);
+            for (int c = wave; c < chunks; c += kWaves) lds_buf16(r, 16u * lane, 1024u * c, lds + 1024 * c);
+            COMET_VMCNT(0);
         } else {
             for (int c = threadIdx.x; c < K; c += kThreads) row_lds[c] = xr[c];
         }
         __syncthreads();
     }
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int Mp = (M + 15) & ~15;     // FP6 layout: rows padded to whole 16-row tiles
-    const int quarter = lane >> 4;    // which of the wave's four blocks
-    const int i = lane & 15;          // lane within the block's 16-lane group
-    const int stride = gridDim.y * 16;
+    const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
+    const int g = lane & 3;               // the lane's 32-channel group
+    const int bl = lane >> 2;             // its block among the wave's 16
+    const int stride = gridDim.y * kBlocksPerPass;
 
-    for (int b0 = (blockIdx.y * 4 + wave) * 4; b0 < nb; b0 += stride) {
-        const int b = b0 + quarter;
-        const bool valid = b < nb;
-        const int bc = valid ? b : nb - 1;
-        const bool is8 = bc >= nb4;
-        const int32_t* pb = perm + bc * kBlock;
-
-        // The 8 block positions this lane codes (see the Xq layout).
-        int4 p0, p1;
-        if (!is8 && kFp6) {
-            const int g = i >> 2, s8 = (i & 3) * 8;
-            p0 = *reinterpret_cast<const int4*>(pb + 32 * g + s8);
-            p1 = *reinterpret_cast<const int4*>(pb + 32 * g + s8 + 4);
-        } else if (!is8) {
-            const int g = i >> 2, j0 = (i & 3) * 4;
-            p0 = *reinterpret_cast<const int4*>(pb + 32 * g + j0);
-            p1 = *reinterpret_cast<const int4*>(pb + 32 * g + 16 + j0);
-        } else {
-            p0 = *reinterpret_cast<const int4*>(pb + 8 * i);
-            p1 = *reinterpret_cast<const int4*>(pb + 8 * i + 4);
-        }
-        const int idx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        float v[8];
-        float a = 0.0f;
+    int b0 = (blockIdx.y * kWaves + wave) * 16;
+    int4 nxt[8];
+    if (b0 < nb) load_positions(perm, imin(b0 + bl, nb - 1), g, nxt);
+    for (; b0 < nb; b0 += stride) {
+        int4 pos[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            v[e] = h2f(kRowInLds ? row_lds[idx[e]] : xr[idx[e]]);
-            a = fmaxf(a, fabsf(v[e]));
-        }
-        // absmax over the block's 16 lanes (xor offsets stay inside the group)
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-
-        const float qmax = is8 ? 127.0f : 7.0f;
-        float inv = 0.0f, s = 0.0f;
-        if (a > 0.0f) {
-            inv = qmax / a;     // correctly rounded IEEE division
-            s = a / qmax;
-        }
-        int q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = a > 0.0f ? quantize(v[e], inv, qmax) : 0;
-
-        // FP6: this lane's 48 code bits (element e at bits 6e), and the low
-        // dword of the neighbouring quarter, taken with every lane active
-        uint32_t f_lo = 0, f_hi = 0, f_nlo = 0;
-        if constexpr (kFp6) {
-            uint64_t f = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f |= static_cast<uint64_t>(fp6_code(q[e])) << (6 * e);
-            f_lo = static_cast<uint32_t>(f);
-            f_hi = static_cast<uint32_t>(f >> 32);
-            f_nlo = __shfl_xor(f_lo, 1);
-        }
-
-        if (valid) {
-            if (!is8 && kFp6) {
-                // group string: head = bits 0..127 at tile byte 256g + 16r, tail
-                // = bits 128..191 at tile byte 1024 + 128g + 8r (r = row in the
-                // 16-row tile); quarter s holds bits 48s..48s+47
-                const int g = i >> 2, sq = i & 3;
-                uint8_t* tile = Xq + static_cast<size_t>(bc) * Mp * 96 + static_cast<size_t>(m >> 4) * 1536;
-                uint8_t* head = tile + 256 * g + 16 * (m & 15);
-                uint8_t* tail = tile + 1024 + 128 * g + 8 * (m & 15);
-                const uint32_t joined = (f_hi & 0xFFFFu) | (f_nlo << 16);   // bits 32..47 + next 0..15
-                const uint32_t upper = (f_lo >> 16) | (f_hi << 16);         // bits 16..47
-                if (sq == 0) {
-                    *reinterpret_cast<uint2*>(head) = make_uint2(f_lo, joined);
-                } else if (sq == 1) {
-                    *reinterpret_cast<uint32_t*>(head + 8) = upper;
-                } else if (sq == 2) {
-                    *reinterpret_cast<uint32_t*>(head + 12) = f_lo;
-                    *reinterpret_cast<uint32_t*>(tail) = joined;
-                } else {
-                    *reinterpret_cast<uint32_t*>(tail + 4) = upper;
-                }
-            } else if (!is8) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = static_cast<uint32_t>(q[e] + 8) & 0xF;
-                    const uint32_t hi = static_cast<uint32_t>(q[4 + e] + 8) & 0xF;
-                    w |= (lo | (hi << 4)) << (8 * e);
-                }
-                uint8_t* dst = Xq + static_cast<size_t>(bc) * M * 64 + static_cast<size_t>(m) * 64;
-                *reinterpret_cast<uint32_t*>(dst + 4 * i) = w;
-            } else {
-                uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w0 |= (static_cast<uint32_t>(q[e]) & 0xFF) << (8 * e);
-                    w1 |= (static_cast<uint32_t>(q[4 + e]) & 0xFF) << (8 * e);
-                }
-                if constexpr (kFp6) {
-                    // 16-row tiles of 2048 bytes: positions 32g + 16h + j of
-                    // row r at tile byte 1024h + 256g + 16r + j
-                    uint8_t* tile = Xq + static_cast<size_t>(nb4) * Mp * 96 +
-                                    static_cast<size_t>(bc - nb4) * Mp * 128 + static_cast<size_t>(m >> 4) * 2048;
-                    const int g = i >> 2, h = (i >> 1) & 1;
-                    *reinterpret_cast<uint2*>(tile + 1024 * h + 256 * g + 16 * (m & 15) + 8 * (i & 1)) =
-                        make_uint2(w0, w1);
-                } else {
-                    uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * 64 +
-                                   static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128;
-                    *reinterpret_cast<uint2*>(dst + 8 * i) = make_uint2(w0, w1);
-                }
-            }
-            if (i == 0) x_scale[static_cast<size_t>(bc) * M + m] = s;
-        }
+        for (int k = 0; k < 8; ++k) pos[k] = nxt[k];
+        if (b0 + stride < nb) load_positions(perm, imin(b0 + stride + bl, nb - 1), g, nxt);
+        code_block<kFp6>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Many rows (M >= 256, K <= 32768): one persistent workgroup of 8 waves per CU
+// walks its rows with two LDS row buffers, so the direct loads of row k+1 run
+// while row k is coded. The 8 x 16 x 2 = 256 blocks a workgroup covers per row
+// (K <= 32768) are the same for every row, so each lane loads its perm entries
+// once, into registers. The rows of an XCD are a contiguous range of whole
+// 16-row tiles, and its workgroups take consecutive rows of it, so the partial
+// cache lines of one output tile meet in that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowPasses = 2;                   // kRowWaves * 16 * kRowPasses = 256 blocks
+
+__device__ __forceinline__ void stage_row(const uint16_t* xr, int K, int wave, int lane, uint8_t* __restrict__ buf) {
+    const Rsrc r = make_rsrc(xr, 2u * static_cast<uint32_t>(K));
+    const int chunks = (K + 511) / 512;
+    for (int c = wave; c < chunks; c += kRowWaves) lds_buf16(r, 16u * lane, 1024u * c, buf + 1024 * c);
+}
+
+// One row: start the direct loads of the next row into `nxt_buf`, then code
+// this row from `cur` (distinct buffers, restrict-qualified so that the LDS
+// gathers do not wait for the loads just issued).
+template <bool kFp6>
+__device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __restrict__ nxt_buf,
+                                         const uint16_t* __restrict__ cur, const int4 (&pos)[kRowPasses][8],
+                                         int K, int nb, int nb4, int M, int Mp, int m, int wave, int lane,
+                                         uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
+    if (next_row) stage_row(next_row, K, wave, lane, nxt_buf);
+    const int g = lane & 3, bl = lane >> 2;
+#pragma unroll
+    for (int p = 0; p < kRowPasses; ++p) {
+        const int b0 = (p * kRowWaves + wave) * 16;
+        if (b0 < nb) code_block<kFp6>(cur, pos[p], b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale);
+    }
+}
+
+template <bool kFp6>
+__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
+    const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm, int nb, int nb4,
+    uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd, int wgs_per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t bufs[];
+    const int row_bytes = ((K + 511) / 512) * 1024;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int first = (blockIdx.x & 7) * rows_per_xcd + (blockIdx.x >> 3);
+    const int end = imin(M, ((blockIdx.x & 7) + 1) * rows_per_xcd);
+    if (first >= end) return;
+    const int n = (end - first + wgs_per_xcd - 1) / wgs_per_xcd;
+    const int Mp = (M + 15) & ~15;
+
+    int4 pos[kRowPasses][8];
+#pragma unroll
+    for (int p = 0; p < kRowPasses; ++p) {
+        const int b = (p * kRowWaves + wave) * 16 + (lane >> 2);
+        load_positions(perm, imin(b, nb - 1), lane & 3, pos[p]);
+    }
+    stage_row(X + static_cast<size_t>(first) * ldx, K, wave, lane, bufs);
+    for (int k = 0; k < n; ++k) {
+        const int m = first + k * wgs_per_xcd;
+        // row k has landed (and this wave's earlier stores are done); after
+        // the barrier every wave is also done with row k-1's buffer
+        COMET_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        const uint16_t* next = k + 1 < n ? X + static_cast<size_t>(m + wgs_per_xcd) * ldx : nullptr;
+        if (k & 1)
+            row_step<kFp6>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4, M, Mp,
+                           m, wave, lane, Xq, x_scale);
+        else
+            row_step<kFp6>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4, M, Mp,
+                           m, wave, lane, Xq, x_scale);
+    }
+}
+
+int cu_count() {
+    static int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 8)
+            v = 256;
+        return v;
+    }();
+    return n;
 }
 
 template <bool kFp6>
@@ -203,19 +291,38 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
     // blocks of a row over gridDim.y workgroups (each stages the whole row).
-    const int per_wg = 16;                                  // blocks per workgroup pass
+    const int per_wg = kBlocksPerPass;                      // blocks per workgroup pass
     int groups = 1;
     const int want = 1024;
     while (groups * per_wg < nb && static_cast<long>(M) * groups < want) ++groups;
-    dim3 grid(M, groups);
+    // XCD-aware row order once there are enough rows for every XCD to get
+    // whole 16-row tiles
+    const int rows_per_xcd = M >= 128 ? ((M + 127) / 128) * 16 : 0;
+    dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M >= 256 && K <= kMaxLdsRowChannels && (ldx & 7) == 0) {
+        // the two row buffers may exceed the 64 KB default of dynamic LDS
+        static std::once_flag once;
+        static hipError_t attr = hipSuccess;
+        std::call_once(once, [] {
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quant_rows_kernel<kFp6>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        });
+        if (attr != hipSuccess) return static_cast<int>(attr);
+        const size_t lds = 2 * static_cast<size_t>((K + 511) / 512) * 1024;
+        const int wgs_per_xcd = cu_count() / 8;
+        const int rows_per_xcd = ((M + 127) / 128) * 16;
+        quant_rows_kernel<kFp6><<<8 * wgs_per_xcd, kRowThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq, x_scale,
+                                                                         rows_per_xcd, wgs_per_xcd);
+        return static_cast<int>(hipGetLastError());
+    }
     if (K <= kMaxLdsRowChannels) {
-        const size_t lds = static_cast<size_t>(K) * sizeof(uint16_t);
+        const size_t lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
         quant_act_kernel<true, kFp6><<<grid, kThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                                 x_scale);
+                                                                 x_scale, rows_per_xcd);
     } else {
         quant_act_kernel<false, kFp6><<<grid, kThreads, 0, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                                x_scale);
+                                                                x_scale, rows_per_xcd);
     }
     return static_cast<int>(hipGetLastError());
 }
