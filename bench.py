@@ -48,6 +48,8 @@ WORKLOADS = {
 
 # Sources whose change invalidates counter data taken on the GEMM kernel.
 KERNEL_SOURCES = ["w4ax_mixed_precision_amd/csrc/w4ax_gemm.hip",
+                  "w4ax_mixed_precision_amd/csrc/w4ax_gemm_fp6.hip",
+                  "w4ax_mixed_precision_amd/csrc/device_util.h",
                   "w4ax_mixed_precision_amd/csrc/comet_internal.h",
                   "w4ax_mixed_precision_amd/build.py"]
 COPY_CAL_BYTES = 1 << 30
