@@ -93,6 +93,8 @@ def _custom_layer(M, K, N, nb8, seed, zero_rows=(), zero_block_rows=(), ldx=None
 @pytest.mark.parametrize("M,K,N,nb8", [
     (1, 128, 128, 0), (1, 128, 128, 1), (3, 256, 256, 2), (17, 512, 384, 0),
     (33, 384, 640, 3), (100, 1024, 512, 1), (5, 33024, 128, 4),   # K > 32768: global gather path
+    # decode kernels with the LDS weight ring (8, 4 and 16 blocks per wave)
+    (2, 4096, 384, 3), (16, 8192, 1152, 7), (9, 16384, 128, 20),
 ])
 def test_edge_shapes(torch, M, K, N, nb8):
     import w4ax_mixed_precision_amd as comet

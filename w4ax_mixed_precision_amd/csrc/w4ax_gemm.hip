@@ -29,6 +29,8 @@
 // products t of four 16x16 tiles come from one v_mfma_f32_16x16x1_4b_f32
 // (outer products of s_x and s_w on the matrix unit), accumulators stay in
 // VGPRs, and 64x64 wave tiles amortize the widening.
+#include <utility>
+
 #include "comet_internal.h"
 #include "device_util.h"
 
@@ -347,13 +349,15 @@ struct StreamSlot {
     int32_t ws;       // weight sum of column `ncol`
 };
 
+// Everything block b needs except the weight word: activation words of the
+// lane's rows, activation scale of row `srow`, weight scale and sum of its
+// column. MR == 1 issues exactly five loads.
 template <int MR>
-__device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b, int grp, int lane, int srow,
-                                             const int (&arow)[MR], StreamSlot<MR>& sl) {
+__device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, int b, int grp, int lane, int srow,
+                                                 const int (&arow)[MR], StreamSlot<MR>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
-    const int M = p.M, N = p.N, nb = p.nb, nb4 = p.nb4;
+    const int M = p.M, N = p.N, nb4 = p.nb4;
     const int ncol = grp * 16 + l16;
-    sl.w = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * nb + b) * kFragBytes + 16 * lane);
     sl.sa = p.x_scale[static_cast<size_t>(b) * M + srow];
     sl.hs = p.w_scale[static_cast<size_t>(b) * N + ncol];
     sl.ws = p.w_sum[static_cast<size_t>(b) * N + ncol];
@@ -371,6 +375,13 @@ __device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b, int gr
         sl.a0[r] = *reinterpret_cast<const uint4*>(src);
         sl.a1[r] = *reinterpret_cast<const uint4*>(src + second);
     }
+}
+
+template <int MR>
+__device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b, int grp, int lane, int srow,
+                                             const int (&arow)[MR], StreamSlot<MR>& sl) {
+    sl.w = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * p.nb + b) * kFragBytes + 16 * lane);
+    stream_fetch_aux<MR>(p, b, grp, lane, srow, arow, sl);
 }
 
 // One block from a slot. `valid` is false for the clamped refetches past the
@@ -409,7 +420,12 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int grp = blockIdx.x;                    // 16-channel group
+    // 16-channel group: workgroup w runs on XCD w mod 8, and each XCD takes a
+    // contiguous range of groups, so neighbouring groups (whose weight scales
+    // and sums share cache lines) are read through one L2
+    const int per = (p.N / 16 + 7) / 8;
+    const int grp = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (grp >= p.N / 16) return;    // whole workgroup, before any barrier
     const int nb = p.nb, nb4 = p.nb4, M = p.M;
     const int bps = (nb + kSplit - 1) / kSplit;
     const int b_begin = imin(nb, wave * bps);
@@ -457,6 +473,97 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel with the weight fragments staged in LDS (decode, M <= 16,
+// nb == NBW * kSplit). The register kernel above holds every in-flight block
+// in VGPRs, which caps a CU at about 64 KB of weights in flight. Here each
+// wave keeps the fragments of its next kR blocks in flight as direct loads
+// into its own 8 KB LDS ring (no VGPRs held) and only the activation words
+// and scales of its next kA blocks in registers, so a CU keeps twice the
+// weight bytes in flight at the same occupancy. Block order, per-wave sums
+// and their reduction are those of the register kernel, so Y is identical.
+// The loop is unrolled at compile time: loads complete in issue order and
+// the wait before block i is a constant of the issue pattern.
+// ---------------------------------------------------------------------------
+
+constexpr int kRingA = 4;   // blocks of activation words and scales in registers
+constexpr int kRingR = 8;   // fragments in flight into the LDS ring
+constexpr int kAuxLoads = 5;     // stream_fetch_aux<1>: two activation words, three scalars
+
+// Loads issued after block i's aux loads: fragment i+kR-kA, then for each
+// block j in (i, i+kA) its aux loads and fragment j+kR-kA (none past nbw).
+constexpr int lds_loads_after(int i, int nbw) {
+    int after = (i + kRingR - kRingA < nbw) ? 1 : 0;
+    for (int j = i + 1; j < i + kRingA; ++j) {
+        if (j < nbw) after += kAuxLoads;
+        if (j + kRingR - kRingA < nbw) after += 1;
+    }
+    return after;
+}
+
+template <class F, int... Is>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+
+template <int NBW, int kSplit>
+__global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProblem p) {
+    constexpr int MR = 1;
+    __shared__ float red[kSplit][4][64];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kSplit][kRingR][kFragBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    const int per = (p.N / 16 + 7) / 8;
+    const int grp = (blockIdx.x & 7) * per + (blockIdx.x >> 3);   // as in the register kernel
+    if (grp >= p.N / 16) return;
+    const int nb4 = p.nb4, M = p.M;
+    const int b_begin = wave * NBW;
+    int arow[MR];
+    arow[0] = imin(l16, M - 1);
+    const int srow = imin(lane, M - 1);
+    const Rsrc wq = make_rsrc(p.Wq, static_cast<uint32_t>(p.N / 16) * p.nb * kFragBytes);
+    const uint32_t wbase = (static_cast<uint32_t>(grp) * p.nb + b_begin) * kFragBytes;
+    uint8_t* my = &ring[wave][0][0];
+    auto fragment = [&](int i) {
+        lds_buf16(wq, 16u * lane, wbase + i * kFragBytes, my + (i % kRingR) * kFragBytes);
+    };
+
+    float y[MR][4] = {};
+    StreamSlot<MR> slot[kRingA];
+    // prologue in the steady-state order: fragments 0 .. kR-kA-1, then for
+    // k < kA the aux loads of block k followed by fragment k + kR - kA
+#pragma unroll
+    for (int i = 0; i < kRingR - kRingA; ++i)
+        if (i < NBW) fragment(i);
+#pragma unroll
+    for (int k = 0; k < kRingA; ++k) {
+        if (k < NBW) stream_fetch_aux<MR>(p, b_begin + k, grp, lane, srow, arow, slot[k]);
+        if (k + kRingR - kRingA < NBW) fragment(k + kRingR - kRingA);
+    }
+    unroll_seq([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        COMET_VMCNT(lds_loads_after(i, NBW));
+        StreamSlot<MR>& sl = slot[i % kRingA];
+        sl.w = *reinterpret_cast<const uint4*>(my + (i % kRingR) * kFragBytes + 16 * lane);
+        stream_compute<MR>(true, b_begin + i < nb4, sl, y);
+        // the ring slot just read is refilled only after its word is used
+        if (i + kRingA < NBW) stream_fetch_aux<MR>(p, b_begin + i + kRingA, grp, lane, srow, arow, sl);
+        if (i + kRingR < NBW) fragment(i + kRingR);
+    }, std::make_integer_sequence<int, NBW>{});
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i][lane] = y[0][i];
+    __syncthreads();
+    for (int q = wave; q < 4; q += kSplit) {
+        float v = red[0][q][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < kSplit; ++w2) v += red[w2][q][lane];
+        const int row = 4 * g + q;
+        if (row < M) p.Y[static_cast<size_t>(row) * p.ldy + grp * 16 + l16] = __half_as_ushort(__float2half_rn(v));
+    }
+}
+
 bool use_stream(int M) { return M <= 64; }
 
 #ifndef COMET_STREAM_TARGET_WAVES
@@ -479,12 +586,32 @@ int launch_stream(const GemmProblem& p, hipStream_t st) {
     // split the blocks of a channel group over enough waves to keep many
     // weight fragments in flight across the chip
     const int groups = p.N / 16;
+    const int grid = 8 * ((groups + 7) / 8);     // XCD-aware order; surplus workgroups exit
+    if constexpr (MR == 1) {
+        // block counts the LDS kernel is built for: one wave per NBW blocks
+        if (p.nb == 32) {
+            gemm_stream_lds_kernel<8, 4><<<grid, 256, 0, st>>>(p);
+            return static_cast<int>(hipGetLastError());
+        }
+        if (p.nb == 64 && groups * 8 < 2 * COMET_STREAM_TARGET_WAVES) {
+            gemm_stream_lds_kernel<8, 8><<<grid, 512, 0, st>>>(p);
+            return static_cast<int>(hipGetLastError());
+        }
+        if (p.nb == 64) {
+            gemm_stream_lds_kernel<16, 4><<<grid, 256, 0, st>>>(p);
+            return static_cast<int>(hipGetLastError());
+        }
+        if (p.nb == 128) {
+            gemm_stream_lds_kernel<16, 8><<<grid, 512, 0, st>>>(p);
+            return static_cast<int>(hipGetLastError());
+        }
+    }
     if (kMax == 4 || groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD)
-        gemm_stream_kernel<MR, kD, 4><<<groups, 256, 0, st>>>(p);
+        gemm_stream_kernel<MR, kD, 4><<<grid, 256, 0, st>>>(p);
     else if (kMax == 8 || groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD)
-        gemm_stream_kernel<MR, kD, (kMax >= 8 ? 8 : 4)><<<groups, 64 * (kMax >= 8 ? 8 : 4), 0, st>>>(p);
+        gemm_stream_kernel<MR, kD, (kMax >= 8 ? 8 : 4)><<<grid, 64 * (kMax >= 8 ? 8 : 4), 0, st>>>(p);
     else
-        gemm_stream_kernel<MR, kD, (kMax >= 16 ? 16 : 4)><<<groups, 64 * (kMax >= 16 ? 16 : 4), 0, st>>>(p);
+        gemm_stream_kernel<MR, kD, (kMax >= 16 ? 16 : 4)><<<grid, 64 * (kMax >= 16 ? 16 : 4), 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
