@@ -138,3 +138,22 @@ def test_determinism_fp6(torch):
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
+
+
+def test_wide_tile_fp6(torch):
+    """A grid large enough for the 128 x 256 workgroup tile, with a ragged last
+    row tile: sampled rows (the tail included) against the oracle, and every Y
+    bit-identical to the INT4-layout kernel (same per-output summation order)."""
+    import w4ax_mixed_precision_amd as comet
+    M, K, N, nb8 = 4000, 1024, 8192, 2
+    G.log(f"[fp6 wide] M={M} K={K} N={N} nb8={nb8}")
+    d = _custom_layer(M, K, N, nb8, seed=4242)
+    pk = comet.comet_pack_weights(d["W"], d["score"], nb8)
+    w = comet.upload_weights(comet.comet_repack_weights_fp6(pk))
+    X = torch.from_numpy(d["X"].view(np.float16)).cuda()
+    rows = np.unique(np.concatenate([G.sample_rows(M), np.arange(M - 40, M)]))
+    _, _, Y6, _ = check(torch, d, w, X, M, K, N, nb8, rows)
+    Xq4, xs4 = comet.comet_quant_act(X, w["perm"], nb8)
+    Y4 = comet.comet_w4ax_gemm(Xq4, xs4, w, M)
+    torch.cuda.synchronize()
+    assert torch.equal(Y4, Y6)

@@ -52,6 +52,9 @@ size_t gemm_workspace_bytes(int M, int N, int K, int nb8);
 int launch_w4ax_gemm(const GemmProblem& p, void* stream);
 int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream);   // FP6 layout; w_sum unused
 
+// Compute units of the current device (quant_act.hip; read once per process).
+int cu_count();
+
 // Host packer (pack_weights.cpp).
 int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
                  uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum);

@@ -273,17 +273,6 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     }
 }
 
-int cu_count() {
-    static int n = [] {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 8)
-            v = 256;
-        return v;
-    }();
-    return n;
-}
-
 template <bool kFp6>
 int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8, uint8_t* Xq,
            float* x_scale, void* stream) {
@@ -328,6 +317,17 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
 }
 
 }  // namespace
+
+int cu_count() {
+    static int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 8)
+            v = 256;
+        return v;
+    }();
+    return n;
+}
 
 int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                      uint8_t* Xq, float* x_scale, void* stream) {

@@ -20,16 +20,21 @@
 // keep the v_mfma_i32_16x16x64_i8 path: weights widened to 16 q_w in
 // registers, accumulator 16 P, scale product divided by 16.
 //
-// Tiling: 128 x 128 output tile per workgroup of four waves (2 x 2, 64 x 64
-// per wave), two workgroups per CU. Operands travel HBM -> LDS by direct loads
-// (buffer_load ... lds: each lane's 16 or 4 bytes land at LDS base + lane *
-// size) into a ring of three stages, two blocks ahead of the compute. Both
-// operand layouts are 16-row (16-channel) tiles in the order a wave reads
-// them, so every direct load is a contiguous copy and every LDS read of a
-// 16-lane k-group is one contiguous 256-byte run (no bank conflicts). Each
-// wave issues 7 direct loads per block of either kind (one scale word, then A
-// and B: 3 + 3 for a 4-bit block, 4 + 2 for an 8-bit one), so at the end of
-// block b a partial wait (vmcnt <= 7) and a barrier publish block b+1.
+// Tiling: four waves per workgroup (2 x 2), two workgroups per CU; a wave
+// computes 64 rows x 16 kWC columns. kWC = 8 (128 x 256 per workgroup) reads
+// a quarter fewer LDS and HBM bytes per output than kWC = 4 (128 x 128), at
+// the register limit (255 VGPRs), and is used when the grid is large. Operands
+// travel HBM -> LDS by direct loads (buffer_load ... lds: each lane's 16 or 4
+// bytes land at LDS base + lane * size) into a ring of stages ahead of the
+// compute: three stages two blocks ahead for kWC = 4, two stages one block
+// ahead for kWC = 8 (whose stage is half again as large and whose block takes
+// twice as long). Both operand layouts are 16-row (16-channel) tiles in the
+// order a wave reads them, so every direct load is a contiguous copy and
+// every LDS read of a 16-lane k-group is one contiguous 256-byte run (no bank
+// conflicts). Each wave issues the same number of direct loads per block of
+// either kind (one scale word, then A and B, plus a balancing load where the
+// kinds differ), so a single partial wait at the end of a block publishes the
+// next one.
 //
 // Epilogue. Per block every output needs y += (s_x s_w) P. On gfx950 the
 // matrix unit and the VALU barely overlap, so the epilogue is kept to one FMA
@@ -39,12 +44,13 @@
 // lane). The epilogue of column tile c is issued after the matrix
 // instructions of tile c+1, so it never waits on a result just produced.
 //
-// LDS stage (25.6 KB):
+// LDS stage (kWC = 4: 25.6 KB, kWC = 8: 38 KB):
 //   4-bit block: A at 0, eight 16-row tiles of 1536 bytes (heads: 256g + 16r,
-//     tails: 1024 + 128g + 8r); B at 12288, the tile's 8 FP6 weight fragments.
+//     tails: 1024 + 128g + 8r); B at 12288, the tile's 2 kWC FP6 fragments.
 //   8-bit block: A at 0, eight 16-row tiles of 2048 bytes (1024h + 256g + 16r
-//     for positions 32g + 16h ..); B at 16384, the tile's 8 INT4 fragments.
-//   then the block's 128 activation scales (f32) and 128 weight scales (fp16).
+//     for positions 32g + 16h ..); B at 16384, the tile's 2 kWC INT4 fragments.
+//   then the block's 128 activation scales (f32) and 32 kWC weight scales
+//   (fp16), and a pad that receives the balancing loads.
 #include "comet_internal.h"
 #include "device_util.h"
 
@@ -53,16 +59,24 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTM = 128;
-constexpr int kTN = 128;
 constexpr int kTileF6 = 1536;                // 16 rows / channels x 128 positions of FP6 codes
 constexpr int kTileI8 = 2048;                // 16 rows x 128 positions of INT8 codes
 constexpr int kOffB6 = 12288;                // B of a 4-bit block
 constexpr int kOffB8 = 16384;                // B of an 8-bit block
-constexpr int kOffSa = 24576;
-constexpr int kOffSw = kOffSa + kTM * 4;
-constexpr int kOffPad = kOffSw + kTN * 2;    // target of wave 3's balancing load
-constexpr int kStage = kOffPad + 256;
-constexpr int kLoadsPerBlock = 7;
+
+// Shape of the workgroup tile for kWC column tiles per wave.
+template <int kWC>
+struct Cfg {
+    static constexpr int kTN = 32 * kWC;                                   // columns per workgroup
+    static constexpr int kOffSa = kOffB6 + 3072 * kWC > kOffB8 + 2048 * kWC ? kOffB6 + 3072 * kWC
+                                                                            : kOffB8 + 2048 * kWC;
+    static constexpr int kOffSw = kOffSa + kTM * 4;
+    static constexpr int kOffPad = kOffSw + kTN * 2;
+    static constexpr int kStage = kOffPad + (kWC == 4 ? 256 : 1024);
+    static constexpr int kStages = kWC == 4 ? 3 : 2;
+    static constexpr int kAhead = kStages - 1;                             // blocks in flight ahead
+    static constexpr int kLoads = kWC == 4 ? 7 : 10;                       // direct loads per wave and block
+};
 
 // Buffer resources of the four inputs, built once per workgroup (SGPRs).
 struct Inputs {
@@ -83,67 +97,89 @@ __device__ __forceinline__ Inputs make_inputs(const GemmProblem& p) {
 
 // Direct loads of block b into stage `st` for the tile at rows m0 (a multiple
 // of 16) and columns n0. `sc` is this lane's scale-word offset: waves 0 and 1
-// load the activation scales of rows 64w + lane (clamped into [0, M)), waves 2
-// and 3 two weight scales per lane.
+// load the activation scales of rows 64w + lane (clamped into [0, M)), the
+// other waves two weight scales per lane (kWC = 4: wave 2; kWC = 8: waves 2
+// and 3, 128 columns each).
+template <int kWC>
 __device__ __forceinline__ void issue(const GemmProblem& p, const Inputs& in, int b, int m0, int n0, int wave,
                                       int lane, uint32_t sc, uint8_t* st) {
+    using C = Cfg<kWC>;
     const uint32_t M = p.M, N = p.N, nb4 = p.nb4, mp = in.mp;
     const uint32_t ub = static_cast<uint32_t>(b);
     if (wave < 2)
-        lds_buf4(in.xs, sc, ub * M * 4u, st + kOffSa + 256 * wave);
+        lds_buf4(in.xs, sc, ub * M * 4u, st + C::kOffSa + 256 * wave);
+    else if (kWC == 8)
+        lds_buf4(in.ws, sc, (ub * N + n0) * 2u + 256u * (wave - 2), st + C::kOffSw + 256 * (wave - 2));
     else
-        lds_buf4(in.ws, sc, (ub * N + n0) * 2u, st + (wave == 2 ? kOffSw : kOffPad));
+        lds_buf4(in.ws, sc, (ub * N + n0) * 2u, st + (wave == 2 ? C::kOffSw : C::kOffPad));
     const uint32_t groups = N / 16;
     const uint32_t lane16 = 16u * static_cast<uint32_t>(lane);
     const uint32_t tile = static_cast<uint32_t>(m0) / 16;
+    // 1 KB pieces of B per wave: 2 kWC tiles of 1536 (4-bit) or 1024 (8-bit)
+    // bytes shared by four waves
+    constexpr int kB6 = 3 * kWC / 4;
+    constexpr int kB8 = kWC / 2;
+    static_assert(1 + 3 + kB6 == C::kLoads && 1 + 4 + kB8 + (kWC == 8 ? 1 : 0) == C::kLoads,
+                  "one partial wait needs equal load counts for both block kinds");
+    static_assert(kOffB6 + 4 * 1024 * kB6 <= C::kOffSa && kOffB8 + 4 * 1024 * kB8 <= C::kOffSa &&
+                      4 * 3072 <= kOffB6 && 4 * 4096 <= kOffB8,
+                  "operands overlap in the stage");
+    static_assert(C::kOffSw == C::kOffSa + 2 * 256 && C::kOffPad + (kWC == 8 ? 4 : 1) * 256 <= C::kStage,
+                  "scale words or balancing loads outside the stage");
     if (b < p.nb4) {
         const uint32_t a = ub * mp * 96u + tile * kTileF6 + 3072u * wave;
-        lds_buf16(in.xq, lane16, a, st + 3072 * wave);
-        lds_buf16(in.xq, lane16, a + 1024, st + 3072 * wave + 1024);
-        lds_buf16(in.xq, lane16, a + 2048, st + 3072 * wave + 2048);
-        const uint32_t w = (ub * groups + n0 / 16) * kTileF6 + 3072u * wave;
-        lds_buf16(in.wq, lane16, w, st + kOffB6 + 3072 * wave);
-        lds_buf16(in.wq, lane16, w + 1024, st + kOffB6 + 3072 * wave + 1024);
-        lds_buf16(in.wq, lane16, w + 2048, st + kOffB6 + 3072 * wave + 2048);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) lds_buf16(in.xq, lane16, a + 1024 * k, st + 3072 * wave + 1024 * k);
+        const uint32_t w = (ub * groups + n0 / 16) * kTileF6 + 1024u * kB6 * wave;
+#pragma unroll
+        for (int k = 0; k < kB6; ++k)
+            lds_buf16(in.wq, lane16, w + 1024 * k, st + kOffB6 + 1024 * kB6 * wave + 1024 * k);
     } else {
         const uint32_t a = nb4 * mp * 96u + (ub - nb4) * mp * 128u + tile * kTileI8 + 4096u * wave;
-        lds_buf16(in.xq, lane16, a, st + 4096 * wave);
-        lds_buf16(in.xq, lane16, a + 1024, st + 4096 * wave + 1024);
-        lds_buf16(in.xq, lane16, a + 2048, st + 4096 * wave + 2048);
-        lds_buf16(in.xq, lane16, a + 3072, st + 4096 * wave + 3072);
-        const uint32_t w = groups * (kTileF6 * nb4 + kFragBytes * (ub - nb4)) + (n0 / 16) * kFragBytes + 2048u * wave;
-        lds_buf16(in.wq, lane16, w, st + kOffB8 + 2048 * wave);
-        lds_buf16(in.wq, lane16, w + 1024, st + kOffB8 + 2048 * wave + 1024);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds_buf16(in.xq, lane16, a + 1024 * k, st + 4096 * wave + 1024 * k);
+        const uint32_t w = groups * (kTileF6 * nb4 + kFragBytes * (ub - nb4)) + (n0 / 16) * kFragBytes +
+                           1024u * kB8 * wave;
+#pragma unroll
+        for (int k = 0; k < kB8; ++k)
+            lds_buf16(in.wq, lane16, w + 1024 * k, st + kOffB8 + 1024 * kB8 * wave + 1024 * k);
+        if (kWC == 8) lds_buf4(in.xs, sc, ub * M * 4u, st + C::kOffPad + 256 * wave);   // balancing load
     }
 }
 
-// End of block b: block b+1 has landed once only block b+2's loads may still
-// be in flight; the barrier publishes it and frees block b's stage.
+// End of block b: block b+1 has landed once only the loads of the blocks
+// issued after it may still be in flight; the barrier publishes it and frees
+// block b's stage.
+template <int kWC>
 __device__ __forceinline__ void end_block(int b, int nb) {
-    if (b + 2 < nb) COMET_VMCNT(kLoadsPerBlock);
+    using C = Cfg<kWC>;
+    if (C::kAhead == 2 && b + 2 < nb) COMET_VMCNT(C::kLoads);
     else COMET_VMCNT(0);
     __builtin_amdgcn_s_barrier();
 }
 
 // Scales of a block for this lane: s_x of its row in the wave's 64 (the A
 // input of the outer products, divided by 16 on the INT8 path) and s_w of its
-// column in each of the 4 column tiles.
+// column in each of the kWC column tiles.
+template <int kWC>
 struct Scales {
     float sa;
-    float sw[4];
+    float sw[kWC];
 };
 
+template <int kWC>
 __device__ __forceinline__ void read_scales(const uint8_t* __restrict__ st, int wr, int wc, int lane, float mul,
-                                            Scales& s) {
-    const float* sa_l = reinterpret_cast<const float*>(st + kOffSa);
-    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(st + kOffSw);
+                                            Scales<kWC>& s) {
+    const float* sa_l = reinterpret_cast<const float*>(st + Cfg<kWC>::kOffSa);
+    const uint16_t* sw_l = reinterpret_cast<const uint16_t*>(st + Cfg<kWC>::kOffSw);
     s.sa = sa_l[64 * wr + lane] * mul;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s.sw[c] = h2f(sw_l[64 * wc + 16 * c + (lane & 15)]);
+    for (int c = 0; c < kWC; ++c) s.sw[c] = h2f(sw_l[16 * kWC * wc + 16 * c + (lane & 15)]);
 }
 
 // t of column tile c: element 4r + i is s_x(row 16r + 4g + i) * s_w(column).
-__device__ __forceinline__ v16f scale_products(const Scales& s, int c) {
+template <int kWC>
+__device__ __forceinline__ v16f scale_products(const Scales<kWC>& s, int c) {
     v16f t = {};
     return __builtin_amdgcn_mfma_f32_16x16x1f32(s.sa, s.sw[c], t, 0, 0, 0);
 }
@@ -155,9 +191,9 @@ __device__ __forceinline__ v8i fp6_operand(const uint8_t* tile, int lane) {
 }
 
 // Epilogue of column tile c: y += t P, or the partials themselves.
-template <bool kDump>
+template <bool kDump, int kWC>
 __device__ __forceinline__ void epilogue(const GemmProblem& p, const v16f& t, const v4f (&D)[4], int c, int b,
-                                         int row0, int col0, int row_lo, int row_hi, float (&y)[4][4][4]) {
+                                         int row0, int col0, int row_lo, int row_hi, float (&y)[4][kWC][4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -173,58 +209,61 @@ __device__ __forceinline__ void epilogue(const GemmProblem& p, const v16f& t, co
         }
 }
 
-// One 4-bit block from stage `st`: issue block b+2 into `nxt`, then the matrix
-// work of column tile c followed by the epilogue of tile c-1.
-template <bool kDump>
+// One 4-bit block from stage `st`: issue the block kAhead further on into
+// `nxt`, then the matrix work of column tile c followed by the epilogue of
+// tile c-1.
+template <bool kDump, int kWC>
 __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in, int b, int m0, int n0,
                                           int row_lo, int row_hi, int wave, int lane, uint32_t sc,
                                           const uint8_t* __restrict__ st, uint8_t* __restrict__ nxt,
-                                          float (&y)[4][4][4]) {
+                                          float (&y)[4][kWC][4]) {
+    constexpr int kAhead = Cfg<kWC>::kAhead;
     const int wr = wave >> 1, wc = wave & 1;
-    if (b + 2 < p.nb) issue(p, in, b + 2, m0, n0, wave, lane, sc, nxt);
+    if (b + kAhead < p.nb) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
     const int row0 = m0 + 64 * wr + 4 * (lane >> 4);
-    const int col0 = n0 + 64 * wc + (lane & 15);
-    Scales s;
-    read_scales(st, wr, wc, lane, 1.0f, s);
+    const int col0 = n0 + 16 * kWC * wc + (lane & 15);
+    Scales<kWC> s;
+    read_scales<kWC>(st, wr, wc, lane, 1.0f, s);
     v8i A[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) A[r] = fp6_operand(st + (4 * wr + r) * kTileF6, lane);
     v4f Dp[4], Dc[4];
     v16f tp = {}, tc = {};
-    if constexpr (!kDump) tp = scale_products(s, 0);
+    if constexpr (!kDump) tp = scale_products<kWC>(s, 0);
     {
-        const v8i B = fp6_operand(st + kOffB6 + (4 * wc) * kTileF6, lane);
+        const v8i B = fp6_operand(st + kOffB6 + (kWC * wc) * kTileF6, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = mfma_fp6(A[r], B);
     }
 #pragma unroll
-    for (int c = 1; c < 4; ++c) {
-        if constexpr (!kDump) tc = scale_products(s, c);
-        const v8i B = fp6_operand(st + kOffB6 + (4 * wc + c) * kTileF6, lane);
+    for (int c = 1; c < kWC; ++c) {
+        if constexpr (!kDump) tc = scale_products<kWC>(s, c);
+        const v8i B = fp6_operand(st + kOffB6 + (kWC * wc + c) * kTileF6, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dc[r] = mfma_fp6(A[r], B);
-        epilogue<kDump>(p, tp, Dp, c - 1, b, row0, col0, row_lo, row_hi, y);
+        epilogue<kDump, kWC>(p, tp, Dp, c - 1, b, row0, col0, row_lo, row_hi, y);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = Dc[r];
         tp = tc;
     }
-    epilogue<kDump>(p, tp, Dp, 3, b, row0, col0, row_lo, row_hi, y);
-    end_block(b, p.nb);
+    epilogue<kDump, kWC>(p, tp, Dp, kWC - 1, b, row0, col0, row_lo, row_hi, y);
+    end_block<kWC>(b, p.nb);
 }
 
 // One 8-bit block: INT8 matrix instruction, weights widened to 16 q_w, so the
 // accumulator holds 16 P; the row scales are divided by 16 (exactly).
-template <bool kDump>
+template <bool kDump, int kWC>
 __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& in, int b, int m0, int n0,
                                            int row_lo, int row_hi, int wave, int lane, uint32_t sc,
                                            const uint8_t* __restrict__ st, uint8_t* __restrict__ nxt,
-                                           float (&y)[4][4][4]) {
+                                           float (&y)[4][kWC][4]) {
+    constexpr int kAhead = Cfg<kWC>::kAhead;
     const int wr = wave >> 1, wc = wave & 1;
-    if (b + 2 < p.nb) issue(p, in, b + 2, m0, n0, wave, lane, sc, nxt);
+    if (b + kAhead < p.nb) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
     const int row0 = m0 + 64 * wr + 4 * (lane >> 4);
-    const int col0 = n0 + 64 * wc + (lane & 15);
-    Scales s;
-    read_scales(st, wr, wc, lane, kDump ? 1.0f : 0.0625f, s);
+    const int col0 = n0 + 16 * kWC * wc + (lane & 15);
+    Scales<kWC> s;
+    read_scales<kWC>(st, wr, wc, lane, kDump ? 1.0f : 0.0625f, s);
     v4i A0[4], A1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -236,9 +275,9 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
     v4f Dp[4], Dc[4];
     v16f tp = {}, tc = {};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        if constexpr (!kDump) tc = scale_products(s, c);
-        const uint4 pk = *reinterpret_cast<const uint4*>(st + kOffB8 + (4 * wc + c) * kFragBytes + 16 * lane);
+    for (int c = 0; c < kWC; ++c) {
+        if constexpr (!kDump) tc = scale_products<kWC>(s, c);
+        const uint4 pk = *reinterpret_cast<const uint4*>(st + kOffB8 + (kWC * wc + c) * kFragBytes + 16 * lane);
         const v4i B0 = widen_weights_lo(pk);
         const v4i B1 = widen_weights_hi(pk);
 #pragma unroll
@@ -249,18 +288,19 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
             for (int i = 0; i < 4; ++i)
                 Dc[r][i] = kDump ? static_cast<float>(acc[i] >> 4) : static_cast<float>(acc[i]);
         }
-        if (c > 0) epilogue<kDump>(p, tp, Dp, c - 1, b, row0, col0, row_lo, row_hi, y);
+        if (c > 0) epilogue<kDump, kWC>(p, tp, Dp, c - 1, b, row0, col0, row_lo, row_hi, y);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = Dc[r];
         tp = tc;
     }
-    epilogue<kDump>(p, tp, Dp, 3, b, row0, col0, row_lo, row_hi, y);
-    end_block(b, p.nb);
+    epilogue<kDump, kWC>(p, tp, Dp, kWC - 1, b, row0, col0, row_lo, row_hi, y);
+    end_block<kWC>(b, p.nb);
 }
 
-template <bool kDump>
+template <bool kDump, int kWC>
 __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * kStage];
+    using C = Cfg<kWC>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStage];
 
     // the partials variant covers rows [m_begin, m_begin + m_count) with tiles
     // that start on a 16-row boundary
@@ -268,11 +308,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
     const int row_hi = kDump ? p.m_begin + p.m_count : p.M;
     const int base = row_lo & ~15;
     const int tiles_m = (row_hi - base + kTM - 1) / kTM;
-    const int tiles_n = p.N / kTN;
+    const int tiles_n = p.N / C::kTN;
     int tm, tn;
     if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
     const int m0 = base + tm * kTM;
-    const int n0 = tn * kTN;
+    const int n0 = tn * C::kTN;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -282,41 +322,41 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
     const Inputs in = make_inputs(p);
     const uint32_t sc = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
 
-    float y[4][4][4];
+    float y[4][kWC][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kWC; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[r][c][i] = 0.0f;
 
-    // prologue: blocks 0 and 1 in flight; wait for block 0
-    issue(p, in, 0, m0, n0, wave, lane, sc, smem);
-    if (1 < nb) {
-        issue(p, in, 1, m0, n0, wave, lane, sc, smem + kStage);
-        COMET_VMCNT(kLoadsPerBlock);
+    // prologue: blocks 0 .. kAhead-1 in flight; wait for block 0
+    issue<kWC>(p, in, 0, m0, n0, wave, lane, sc, smem);
+    if (C::kAhead == 2 && 1 < nb) {
+        issue<kWC>(p, in, 1, m0, n0, wave, lane, sc, smem + C::kStage);
+        COMET_VMCNT(C::kLoads);
     } else {
         COMET_VMCNT(0);
     }
     __builtin_amdgcn_s_barrier();
 
-    // Block b lives in stage b mod 3 and block b+2 is loaded into stage
-    // (b + 2) mod 3. The stage pointers are restrict-qualified in the block
-    // functions: an LDS read of one stage does not wait for the direct loads
-    // in flight into another. The 4-bit blocks come first in the permuted
-    // order, the 8-bit ones last.
+    // Block b lives in stage b mod kStages and block b+kAhead is loaded into
+    // stage (b + kAhead) mod kStages. The stage pointers are restrict-qualified
+    // in the block functions: an LDS read of one stage does not wait for the
+    // direct loads in flight into another. The 4-bit blocks come first in the
+    // permuted order, the 8-bit ones last.
     int cur = 0;
     for (int b = 0; b < nb4; ++b) {
-        const int nxt = cur == 0 ? 2 : cur - 1;
-        block_fp6<kDump>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * kStage,
-                         smem + nxt * kStage, y);
-        cur = cur == 2 ? 0 : cur + 1;
+        const int nxt = cur == 0 ? C::kStages - 1 : cur - 1;
+        block_fp6<kDump, kWC>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
+                              smem + nxt * C::kStage, y);
+        cur = cur == C::kStages - 1 ? 0 : cur + 1;
     }
     for (int b = nb4; b < nb; ++b) {
-        const int nxt = cur == 0 ? 2 : cur - 1;
-        block_int8<kDump>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * kStage,
-                          smem + nxt * kStage, y);
-        cur = cur == 2 ? 0 : cur + 1;
+        const int nxt = cur == 0 ? C::kStages - 1 : cur - 1;
+        block_int8<kDump, kWC>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
+                               smem + nxt * C::kStage, y);
+        cur = cur == C::kStages - 1 ? 0 : cur + 1;
     }
 
     if constexpr (!kDump) {
@@ -326,9 +366,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
             for (int i = 0; i < 4; ++i) {
                 const int row = m0 + 64 * wr + 16 * r + 4 * g + i;
                 if (row < row_hi) {
-                    uint16_t* yrow = p.Y + static_cast<size_t>(row) * p.ldy + n0 + 64 * wc + l16;
+                    uint16_t* yrow = p.Y + static_cast<size_t>(row) * p.ldy + n0 + 16 * kWC * wc + l16;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) yrow[16 * c] = __half_as_ushort(__float2half_rn(y[r][c][i]));
+                    for (int c = 0; c < kWC; ++c) yrow[16 * c] = __half_as_ushort(__float2half_rn(y[r][c][i]));
                 }
             }
     }
@@ -338,14 +378,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
 
 int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool dump = p.P != nullptr;
-    const int rows = dump ? p.m_begin + p.m_count - (p.m_begin & ~15) : p.M;
-    const int tiles = ((rows + kTM - 1) / kTM) * (p.N / kTN);
-    const int grid = 8 * ((tiles + 7) / 8);
-    if (dump)
-        gemm_fp6_kernel<true><<<grid, kThreads, 0, s>>>(p);
-    else
-        gemm_fp6_kernel<false><<<grid, kThreads, 0, s>>>(p);
+    if (p.P != nullptr) {
+        const int rows = p.m_begin + p.m_count - (p.m_begin & ~15);
+        const int tiles = ((rows + kTM - 1) / kTM) * (p.N / Cfg<4>::kTN);
+        gemm_fp6_kernel<true, 4><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
+        return static_cast<int>(hipGetLastError());
+    }
+    // the wide tile when N allows it and the grid still covers every CU's two
+    // workgroup slots about twice
+    const int tiles_m = (p.M + kTM - 1) / kTM;
+    const int wide = p.N % Cfg<8>::kTN == 0 ? tiles_m * (p.N / Cfg<8>::kTN) : 0;
+    if (wide >= 4 * cu_count()) {
+        gemm_fp6_kernel<false, 8><<<8 * ((wide + 7) / 8), kThreads, 0, s>>>(p);
+    } else {
+        const int tiles = tiles_m * (p.N / Cfg<4>::kTN);
+        gemm_fp6_kernel<false, 4><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
+    }
     return static_cast<int>(hipGetLastError());
 }
 
