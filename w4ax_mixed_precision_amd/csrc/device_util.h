@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_buf4(Rsrc r, uint32_t voff, uint32_t soff, u
         voff, soff, 0, 0);
 }
 
+// 16-byte load through a raw buffer resource. An offset at or past the
+// buffer's size (the range check covers the per-lane offset) returns zeros
+// and touches no memory: kOutOfRange, with buffers below 2 GB, is such an
+// offset.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t voff) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 #define COMET_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))

@@ -353,7 +353,7 @@ struct StreamSlot {
 // lane's rows, activation scale of row `srow`, weight scale and sum of its
 // column. MR == 1 issues exactly five loads.
 template <int MR>
-__device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, int b, int grp, int lane, int srow,
+__device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, Rsrc xq, int b, int grp, int lane, int srow,
                                                  const int (&arow)[MR], StreamSlot<MR>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
     const int M = p.M, N = p.N, nb4 = p.nb4;
@@ -362,26 +362,34 @@ __device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, int b, in
     sl.hs = p.w_scale[static_cast<size_t>(b) * N + ncol];
     sl.ws = p.w_sum[static_cast<size_t>(b) * N + ncol];
     // branch-free: 4-bit rows are 64 bytes at 16g, 8-bit rows 128 bytes at
-    // 32g (+16 for the second word); a 4-bit block reloads its one word
+    // 32g (+16 for the second word). A 4-bit block has no second word: its
+    // load takes an offset past the buffer, which returns zeros without a
+    // memory access, so the load count stays fixed at no cache traffic.
     const bool is4 = b < nb4;
-    const uint8_t* slab = is4 ? p.Xq + static_cast<size_t>(b) * M * 64
-                              : p.Xq + static_cast<size_t>(nb4) * M * 64 + static_cast<size_t>(b - nb4) * M * 128;
+    const uint32_t M32 = static_cast<uint32_t>(M), ub = static_cast<uint32_t>(b), nb4u = static_cast<uint32_t>(nb4);
+    const uint32_t slab = is4 ? ub * M32 * 64u : nb4u * M32 * 64u + (ub - nb4u) * M32 * 128u;
     const uint32_t rstride = is4 ? 64u : 128u;
     const uint32_t cofs = is4 ? 16u * g : 32u * g;
-    const uint32_t second = is4 ? 0u : 16u;
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-        const uint8_t* src = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
-        sl.a0[r] = *reinterpret_cast<const uint4*>(src);
-        sl.a1[r] = *reinterpret_cast<const uint4*>(src + second);
+        const uint32_t off = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
+        sl.a0[r] = buf_load16(xq, off);
+        sl.a1[r] = buf_load16(xq, is4 ? kOutOfRange : off + 16u);
     }
 }
 
 template <int MR>
-__device__ __forceinline__ void stream_fetch(const GemmProblem& p, int b, int grp, int lane, int srow,
+__device__ __forceinline__ void stream_fetch(const GemmProblem& p, Rsrc xq, int b, int grp, int lane, int srow,
                                              const int (&arow)[MR], StreamSlot<MR>& sl) {
     sl.w = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * p.nb + b) * kFragBytes + 16 * lane);
-    stream_fetch_aux<MR>(p, b, grp, lane, srow, arow, sl);
+    stream_fetch_aux<MR>(p, xq, b, grp, lane, srow, arow, sl);
+}
+
+// Buffer resource over the INT4-layout activation codes (M rows; M <= 64 here).
+__device__ __forceinline__ Rsrc stream_xq_rsrc(const GemmProblem& p) {
+    const uint32_t M = static_cast<uint32_t>(p.M), nb4 = static_cast<uint32_t>(p.nb4);
+    const uint32_t nb8 = static_cast<uint32_t>(p.nb) - nb4;
+    return make_rsrc(p.Xq, M * (64u * nb4 + 128u * nb8));
 }
 
 // One block from a slot. `valid` is false for the clamped refetches past the
@@ -435,6 +443,7 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
 #pragma unroll
     for (int r = 0; r < MR; ++r) arow[r] = imin(16 * r + l16, M - 1);
     const int srow = imin(lane, M - 1);    // row whose scale this lane feeds the outer product
+    const Rsrc xq = stream_xq_rsrc(p);
     float y[MR][4];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -445,14 +454,14 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
         const int last = b_end - 1;
         StreamSlot<MR> slot[kD];
 #pragma unroll
-        for (int u = 0; u < kD; ++u) stream_fetch<MR>(p, imin(b_begin + u, last), grp, lane, srow, arow, slot[u]);
+        for (int u = 0; u < kD; ++u) stream_fetch<MR>(p, xq, imin(b_begin + u, last), grp, lane, srow, arow, slot[u]);
         for (int b0 = b_begin; b0 < b_end; b0 += kD) {
 #pragma unroll
             for (int u = 0; u < kD; ++u) {
                 const int b = b0 + u;
                 stream_compute<MR>(b < b_end, imin(b, last) < nb4, slot[u], y);
                 if (b0 + kD < b_end)
-                    stream_fetch<MR>(p, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
+                    stream_fetch<MR>(p, xq, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
             }
         }
     }
@@ -523,6 +532,7 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
     arow[0] = imin(l16, M - 1);
     const int srow = imin(lane, M - 1);
     const Rsrc wq = make_rsrc(p.Wq, static_cast<uint32_t>(p.N / 16) * p.nb * kFragBytes);
+    const Rsrc xq = stream_xq_rsrc(p);
     const uint32_t wbase = (static_cast<uint32_t>(grp) * p.nb + b_begin) * kFragBytes;
     uint8_t* my = &ring[wave][0][0];
     auto fragment = [&](int i) {
@@ -538,7 +548,7 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
         if (i < NBW) fragment(i);
 #pragma unroll
     for (int k = 0; k < kRingA; ++k) {
-        if (k < NBW) stream_fetch_aux<MR>(p, b_begin + k, grp, lane, srow, arow, slot[k]);
+        if (k < NBW) stream_fetch_aux<MR>(p, xq, b_begin + k, grp, lane, srow, arow, slot[k]);
         if (k + kRingR - kRingA < NBW) fragment(k + kRingR - kRingA);
     }
     unroll_seq([&](auto ic) {
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
         sl.w = *reinterpret_cast<const uint4*>(my + (i % kRingR) * kFragBytes + 16 * lane);
         stream_compute<MR>(true, b_begin + i < nb4, sl, y);
         // the ring slot just read is refilled only after its word is used
-        if (i + kRingA < NBW) stream_fetch_aux<MR>(p, b_begin + i + kRingA, grp, lane, srow, arow, sl);
+        if (i + kRingA < NBW) stream_fetch_aux<MR>(p, xq, b_begin + i + kRingA, grp, lane, srow, arow, sl);
         if (i + kRingR < NBW) fragment(i + kRingR);
     }, std::make_integer_sequence<int, NBW>{});
 
@@ -574,14 +584,16 @@ bool use_stream(int M) { return M <= 64; }
 #endif
 
 // Widest in-workgroup split whose register budget (512 / waves per SIMD) holds
-// the kernel without spills at the default depth: 120, 187, 249 and 306 VGPRs
-// for 1..4 row tiles.
+// the kernel without spills: 120, 187, 146 and 179 VGPRs for 1..4 row tiles
+// (four blocks in flight for one or two row tiles, two for three or four).
 template <int MR>
 constexpr int max_stream_split() { return MR == 1 ? 16 : (MR <= 3 ? 8 : 4); }
 
 template <int MR>
 int launch_stream(const GemmProblem& p, hipStream_t st) {
-    constexpr int kD = COMET_STREAM_DEPTH;
+    // three or four row tiles hold 24-32 activation registers per block: two
+    // blocks in flight keep them at two waves per SIMD (four blocks: one)
+    constexpr int kD = MR >= 3 ? 2 : COMET_STREAM_DEPTH;
     constexpr int kMax = max_stream_split<MR>();
     // split the blocks of a channel group over enough waves to keep many
     // weight fragments in flight across the chip
