@@ -33,6 +33,15 @@
  *     block order (QUIK blog, section "核融合": the integer result is
  *     dequantized to fp16 while still in registers).
  *
+ *  6. RMS normalization before the quantizer (the next step the quantization
+ *     fuses into). QoQ/QServe article, section "运行时设计": the activation
+ *     quantization of the QKV projection and of the first FFN layer is fused
+ *     into the layer norm that precedes it; QUIK blog, section "核融合": one
+ *     kernel reads the input, takes its statistics and quantizes. The LLaMA
+ *     models the pages evaluate normalize with RMSNorm. The normalized row is
+ *     the block's FP16 activation (QoQ/QServe, same section: FP16 block inputs
+ *     and outputs), which step 3 then quantizes.
+ *
  * Readings of points the pages leave open (INT4 range, rounding mode, scale
  * form, all-zero blocks, tie-breaking of the channel sort) are listed with the
  * design notes at the repository root; each is stated where it is used below.
@@ -394,6 +403,65 @@ int orc_epilogue(const int32_t *P, const float *sa, const uint16_t *sw16, int ro
             if (y32) y32[o] = y;
             if (Y16) Y16[o] = orc_float_to_half(y);
             if (yexact) yexact[o] = ye;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 6. RMS normalization (the step before the quantizer)                      */
+/* ------------------------------------------------------------------------ */
+
+/* Row statistic, in the order this library defines it (the pages fix none):
+ * 512 partial sums in binary64, partial p holding x_k^2 for k = p, p + 512,
+ * p + 1024, ... added in increasing k; then halving steps with strides 256,
+ * 128, ..., 1, each replacing partial p (p < stride) by partial p + partial
+ * p + stride. Every square of a binary16 value is exact in binary64. */
+double orc_rms_sumsq(const uint16_t *x, int K)
+{
+    double part[512];
+    for (int p = 0; p < 512; ++p) {
+        double s = 0.0;
+        for (int k = p; k < K; k += 512) {
+            double v = (double)orc_half_to_float(x[k]);
+            s = s + v * v;
+        }
+        part[p] = s;
+    }
+    for (int stride = 256; stride >= 1; stride /= 2)
+        for (int p = 0; p < stride; ++p)
+            part[p] = part[p] + part[p + stride];
+    return part[0];
+}
+
+/* Xn[m][k] = fp16( (x * r) * gamma_k ) with r = binary32( 1 / sqrt(S / K +
+ * eps) ), S the row statistic above, the reciprocal square root taken in
+ * binary64 and rounded once to binary32, the two products in binary32, and
+ * the result rounded to binary16 (nearest, ties to even). Channels stay in
+ * their original order; gamma is fp16 [K]. Non-finite inputs are rejected. */
+int orc_rmsnorm_rows(const uint16_t *X, int M, int K, int ldx, const uint16_t *gamma, float eps,
+                     uint16_t *Xn, int ldn)
+{
+    if (M <= 0 || K <= 0 || ldx < K || ldn < K || !(eps > 0.0f) || !isfinite(eps))
+        return ORC_ERR_ARG;
+    for (int k = 0; k < K; ++k)
+        if (!isfinite(orc_half_to_float(gamma[k])))
+            return ORC_ERR_NONFINITE;
+    int rc = ORC_OK;
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *x = X + (size_t)m * ldx;
+        for (int k = 0; k < K; ++k)
+            if (!isfinite(orc_half_to_float(x[k])))
+                rc = ORC_ERR_NONFINITE;
+        if (rc != ORC_OK)
+            return rc;
+        double S = orc_rms_sumsq(x, K);
+        double r64 = 1.0 / sqrt(S / (double)K + (double)eps);
+        float r = (float)r64;
+        for (int k = 0; k < K; ++k) {
+            float t = orc_half_to_float(x[k]) * r;
+            float u = t * orc_half_to_float(gamma[k]);
+            Xn[(size_t)m * ldn + k] = orc_float_to_half(u);
         }
     }
     return ORC_OK;

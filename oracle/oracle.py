@@ -12,6 +12,7 @@ Logical arrays (no GPU layout here):
   qa     int8  [M, K]     activation codes in permuted order
   sa     f32   [M, nb]    activation scales
   P      int32 [rows, N, nb] exact block partials
+  Xn     uint16 [M, K]    RMS-normalized activations (fp16 bits, original order)
 """
 from __future__ import annotations
 
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.orc_block_partials_zero_extend.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.orc_epilogue.argtypes = [P, P, P, I, I, I, P, P, P]
         L.orc_forward_rows.argtypes = [P, I, I, I, P, P, P, P, I, I, I, P, P]
+        L.orc_rms_sumsq.restype = ctypes.c_double
+        L.orc_rms_sumsq.argtypes = [P, I]
+        L.orc_rmsnorm_rows.argtypes = [P, I, I, I, P, ctypes.c_float, P, I]
         L.orc_threads.restype = I
         L.orc_half_to_float_array.restype = None
         L.orc_half_to_float_array.argtypes = [P, P, ctypes.c_int64]
@@ -72,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.orc_float_to_half_array.argtypes = [P, P, ctypes.c_int64]
         for f in ("orc_channel_order", "orc_quantize_weights", "orc_quantize_activations",
                   "orc_block_partials", "orc_block_partials_zero_extend", "orc_epilogue",
-                  "orc_forward_rows"):
+                  "orc_forward_rows", "orc_rmsnorm_rows"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -212,6 +216,23 @@ def forward_rows(X16, perm, flags, qw, sw16, rows):
                                   _p(np.ascontiguousarray(sw16, np.uint16)), N, m0, m1,
                                   _p(Y16), _p(ye)), "forward_rows")
     return Y16, ye
+
+
+def rms_sumsq(x16: np.ndarray) -> float:
+    """The row statistic sum of x^2 in the order comet_oracle.c defines."""
+    x = np.ascontiguousarray(x16, dtype=np.uint16)
+    return float(lib().orc_rms_sumsq(_p(x), x.size))
+
+
+def rmsnorm(X16: np.ndarray, gamma16: np.ndarray, eps: float) -> np.ndarray:
+    """fp16 bits of the RMS-normalized rows (step 6 of comet_oracle.c)."""
+    X = np.ascontiguousarray(X16, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma16, dtype=np.uint16)
+    M, K = X.shape
+    assert g.shape == (K,)
+    out = np.empty((M, K), np.uint16)
+    _check(lib().orc_rmsnorm_rows(_p(X), M, K, K, _p(g), ctypes.c_float(eps), _p(out), K), "orc_rmsnorm_rows")
+    return out
 
 
 def threads() -> int:

@@ -541,3 +541,134 @@ def test_golden_worked_examples(orc):
         if "P_zero_extend_raw" in exp:
             Pz = orc.block_partials_zero_extend(qa, qw, wsum, flags)
             assert Pz[0, 0, 0] + 8 * wsum[0, 0] == exp["P_zero_extend_raw"][0]
+
+
+# --------------------------------------------------------------------------
+# RMS normalization feeding the quantizer
+# --------------------------------------------------------------------------
+
+def _exact_sumsq(x16):
+    return sum((Fraction(float(v)) ** 2 for v in x16.view(np.float16).astype(np.float64)), Fraction(0))
+
+
+def test_rms_sumsq_exact_on_dyadic_rows(orc):
+    """Rows of multiples of 2^-8 in [-4, 4]: every partial sum is exact in
+    binary64, so the statistic equals the exact rational sum of squares
+    whatever the order."""
+    rng = np.random.default_rng(11)
+    for K in (128, 1000, 8192, 28672):
+        x = (rng.integers(-1024, 1025, K) / 256.0).astype(np.float16).view(np.uint16)
+        assert Fraction(orc.rms_sumsq(x)) == _exact_sumsq(x), K
+
+
+def test_rms_sumsq_close_to_exact_on_wide_rows(orc):
+    """Heavy-tailed rows spanning many binades: within binary64 rounding of the
+    exact sum (no term dropped, none counted twice)."""
+    rng = np.random.default_rng(12)
+    for K in (512, 4096, 11008):
+        x = (rng.standard_t(3, K) * 10.0 ** rng.uniform(-3, 2, K)).astype(np.float16).view(np.uint16)
+        exact = _exact_sumsq(x)
+        got = Fraction(orc.rms_sumsq(x))
+        assert abs(got - exact) <= exact * Fraction(K, 2 ** 52), K
+
+
+def test_rmsnorm_against_float64_formula(orc):
+    """Against x / sqrt(mean(x^2) + eps) * gamma in float64 with one final
+    rounding: the oracle rounds r to binary32 and forms two binary32
+    products, so results agree to one fp16 step, rarely differing."""
+    rng = np.random.default_rng(13)
+    cfg = synth.LayerConfig("t", 64, 4096, 128, 5)
+    X = synth.make_x(cfg)
+    g = (1.0 + 0.2 * rng.standard_normal(4096)).astype(np.float16)
+    Xn = f16(orc.rmsnorm(X, g.view(np.uint16), 1e-5))
+    x = f16(X)
+    ref = x / np.sqrt((x * x).mean(1, keepdims=True) + 1e-5) * g.astype(np.float64)
+    ref16 = ref.astype(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(ref16).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(Xn - ref16) <= ulp)
+    assert np.mean(Xn != ref16) < 2e-3
+
+
+def test_rmsnorm_power_of_two_equivariance(orc):
+    """Scaling a row by 2^j scales S by 4^j and r by 2^-j exactly (eps far
+    below the rounding of S/K), so the normalized row is unchanged."""
+    rng = np.random.default_rng(14)
+    # magnitudes in [0.25, ~5]: every scaled copy stays a normal fp16 number
+    z = rng.standard_normal((4, 2048))
+    x = (np.sign(z) * (0.25 + np.abs(z))).astype(np.float16)
+    g = (0.5 + rng.random(2048)).astype(np.float16).view(np.uint16)
+    base = orc.rmsnorm(x.view(np.uint16), g, 1e-30)
+    for j in (-3, 2, 5):
+        xs = (x.astype(np.float64) * 2.0 ** j).astype(np.float16)
+        assert np.array_equal(orc.rmsnorm(xs.view(np.uint16), g, 1e-30), base), j
+
+
+def test_rmsnorm_uses_gamma_per_channel(orc):
+    """gamma applies per channel in the original order: swapping two gamma
+    entries swaps exactly those two outputs."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((2, 512)).astype(np.float16).view(np.uint16)
+    g = (0.5 + rng.random(512)).astype(np.float16)
+    g2 = g.copy()
+    g2[[3, 400]] = g[[400, 3]]
+    a = f16(orc.rmsnorm(x, g.view(np.uint16), 1e-5))
+    b = f16(orc.rmsnorm(x, g2.view(np.uint16), 1e-5))
+    same = np.ones(512, bool)
+    same[[3, 400]] = False
+    assert np.array_equal(a[:, same], b[:, same])
+    # the swapped channels follow their new weight: recomputing with the
+    # swapped gamma applied by hand to the unnormalized rows moves them
+    assert not np.array_equal(a[:, [3, 400]], b[:, [3, 400]])
+
+
+def test_rmsnorm_rejects(orc):
+    x = np.zeros((1, 128), np.uint16)
+    g = np.full(128, 0x3C00, np.uint16)
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            orc.rmsnorm(x, g, eps)
+    xbad = x.copy()
+    xbad[0, 5] = 0x7C00
+    with pytest.raises(ValueError):
+        orc.rmsnorm(xbad, g, 1e-5)
+
+
+def test_golden_rmsnorm_examples(orc):
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rmsnorm_examples.json")))["examples"]
+    for e in ex:
+        K, M = e["K"], e["M"]
+        X = synth.to_fp16(np.full((M, K), e["X"]["all"]))
+        g = np.full(K, e["gamma"]["all"])
+        if "k0" in e["gamma"]:
+            g[0] = e["gamma"]["k0"]
+        Xn = orc.rmsnorm(X, synth.to_fp16(g), e["eps"])
+        exp = e["expect"]
+        assert f16(Xn)[0, 0] == exp["xn_k0"] and np.all(f16(Xn)[0, 1:] == exp["xn_rest"]), e["name"]
+        perm, flags = orc.channel_order(np.zeros(K, np.float32), e["nb8"])
+        qa, sa = orc.quantize_activations(Xn, perm, flags)
+        assert qa[0, 0] == exp["qa_k0"] and np.all(qa[0, 1:] == exp["qa_rest"]), e["name"]
+        sa_exp = np.float32(1.5) / np.float32(7) if exp["sa"] == "fp32(1.5/7)" else np.float32(exp["sa"])
+        assert np.all(sa[0] == sa_exp), e["name"]
+
+
+def test_rmsnorm_rounding_structure(orc):
+    """The documented rounding: r = binary32 of the exactly rounded binary64
+    reciprocal square root, then two binary32 products and one fp16 rounding.
+    The statistic here is the exact rational sum of squares (dyadic rows, so
+    the binary64 statistic is exact too); r is taken from it with 60-digit
+    decimal arithmetic; the products use numpy float32."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    rng = np.random.default_rng(16)
+    K = 1024
+    for trial in range(6):
+        x = (rng.integers(-2048, 2049, K) / 512.0).astype(np.float16)
+        g = (0.5 + rng.random(K)).astype(np.float16)
+        eps = 1e-5
+        S = _exact_sumsq(x.view(np.uint16))
+        v = Decimal(S.numerator) / Decimal(S.denominator) / Decimal(K) + Decimal(float(np.float32(eps)))
+        r64 = float(Decimal(1) / v.sqrt())
+        r32 = np.float32(r64)
+        want = ((x.astype(np.float32) * r32) * g.astype(np.float32)).astype(np.float16)
+        got = orc.rmsnorm(x.view(np.uint16)[None], g.view(np.uint16), eps)[0]
+        assert np.array_equal(got, want.view(np.uint16)), trial
