@@ -263,6 +263,67 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N,
                                  int K, int m_begin, int m_count, int32_t* P, void* stream);
 
+/* ------------------------------------------------------------------------
+ * RMS normalization fused into the activation quantizer. QoQ/QServe article
+ * (youleyou.com/wenzhang/3078652.html), section "运行时设计": the activation
+ * quantization of the QKV projection and of the first FFN layer is fused into
+ * the layer norm before it; QUIK blog (deep-paper.org/paper/2310.09259),
+ * section "核融合": one kernel reads the input, takes its statistics and
+ * quantizes. The normalization (RMSNorm, as in the LLaMA models the pages
+ * evaluate) of row m:
+ *   S  = sum over k of x_k^2 in binary64, formed as 512 partials (partial p
+ *        holds x_k^2 for k = p, p + 512, ... added in increasing k) that are
+ *        then halved with strides 256, 128, ..., 1 (partial p += partial
+ *        p + stride for p < stride);
+ *   r  = binary32( 1 / sqrt(S / K + eps) ), the root and quotient in binary64;
+ *   xn_k = fp16( (x_k * r) * gamma_k ), two binary32 products, nearest-even.
+ * Every kernel of the library forms S the same way, so the fused calls give
+ * exactly the codes and scales of comet_rmsnorm followed by comet_quant_act.
+ * Normalized values must stay finite (|gamma| sqrt(K) < 65504); eps must be a
+ * positive finite float.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * comet_quant_act of the RMS-normalized rows: the normalized row is formed in
+ * the quantizer and never stored.
+ *
+ *   X_fp16           in   [M, ldx] fp16, device, 16-byte aligned, rows NOT normalized
+ *   gamma_perm_fp16  in   [K] fp16, device, 16-byte aligned: the RMSNorm weight in the
+ *                         permuted channel order, gamma_perm[k] = gamma[perm[k]]
+ *                         (comet_permute_channels)
+ *   eps              in   > 0, finite
+ *   perm, n_int8_blocks, Xq, x_scale, stream: as comet_quant_act
+ * Errors: as comet_quant_act, plus NULL (gamma_perm), ARG (eps), ALIGN (gamma_perm).
+ */
+int comet_rmsnorm_quant_act(const void* X_fp16, int M, int K, int ldx, const void* gamma_perm_fp16, float eps,
+                            const int32_t* perm, int n_int8_blocks, void* Xq, float* x_scale, void* stream);
+
+/* The same on the FP6 layout (comet_quant_act_fp6's output). */
+int comet_rmsnorm_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const void* gamma_perm_fp16, float eps,
+                                const int32_t* perm, int n_int8_blocks, void* Xq_fp6, float* x_scale,
+                                void* stream);
+
+/*
+ * The normalization on its own (the unfused step, for comparison):
+ * Xn[m][k] = xn_k of row m, original channel order.
+ *
+ *   X_fp16      in   [M, ldx] fp16, device (2-byte aligned), ldx >= K
+ *   gamma_fp16  in   [K] fp16, device, original channel order
+ *   eps         in   > 0, finite
+ *   Xn_fp16     out  [M, ldn] fp16, device, ldn >= K (columns past K untouched)
+ * Errors: NULL, SHAPE (M < 1, K < 1, ldx < K, ldn < K), ARG (eps), ALIGN (odd
+ * addresses), HIP.
+ */
+int comet_rmsnorm(const void* X_fp16, int M, int K, int ldx, const void* gamma_fp16, float eps, void* Xn_fp16,
+                  int ldn, void* stream);
+
+/*
+ * Offline, host memory: out[k] = v[perm[k]] for k < K (for example the
+ * RMSNorm weight into the permuted order the fused calls take).
+ * Errors: NULL, SHAPE (K < 1), ARG (a perm entry outside [0, K)).
+ */
+int comet_permute_channels(const uint16_t* v, const int32_t* perm, int K, uint16_t* out);
+
 /* Static description of a status code. */
 const char* comet_status_string(int status);
 

@@ -151,3 +151,53 @@ def test_pack_rejections():
     L = comet.lib()
     p = ctypes.c_void_p(A)
     assert L.comet_pack_weights(None, 128, 256, p, 0, p, p, p, p, p) == NULL
+
+
+def test_rmsnorm_quant_rejections():
+    """Fused normalization + quantization: every check before any HIP call."""
+    L = comet.lib()
+    a = 4096          # 16-byte aligned fake device addresses; never dereferenced
+    for f in (L.comet_rmsnorm_quant_act, L.comet_rmsnorm_quant_act_fp6):
+        ok = (a, 4, 256, 256, a, 1e-5, a, 1, a, a, None)
+        def call(**kw):
+            args = list(ok)
+            for i, v in kw.items():
+                args[int(i[1:])] = v
+            return f(*args)
+        assert call(a4=None) == NULL and call(a0=None) == NULL and call(a6=None) == NULL
+        assert call(a8=None) == NULL and call(a9=None) == NULL
+        assert call(a1=0) == SHAPE and call(a2=200) == SHAPE and call(a3=128) == SHAPE
+        assert call(a7=3) == ARG and call(a7=-1) == ARG
+        for eps in (0.0, -1e-5, float("inf"), float("nan")):
+            assert call(a5=eps) == ARG, eps
+        assert call(a4=a + 2) == ALIGN and call(a0=a + 8) == ALIGN
+
+
+def test_rmsnorm_rejections():
+    L = comet.lib()
+    a = 4096
+    f = L.comet_rmsnorm
+    assert f(None, 2, 64, 64, a, 1e-5, a, 64, None) == NULL
+    assert f(a, 2, 64, 64, None, 1e-5, a, 64, None) == NULL
+    assert f(a, 2, 64, 64, a, 1e-5, None, 64, None) == NULL
+    assert f(a, 0, 64, 64, a, 1e-5, a, 64, None) == SHAPE
+    assert f(a, 2, 0, 64, a, 1e-5, a, 64, None) == SHAPE
+    assert f(a, 2, 64, 63, a, 1e-5, a, 64, None) == SHAPE
+    assert f(a, 2, 64, 64, a, 1e-5, a, 63, None) == SHAPE
+    assert f(a, 2, 64, 64, a, 0.0, a, 64, None) == ARG
+    assert f(a, 2, 64, 64, a, float("nan"), a, 64, None) == ARG
+    assert f(a + 1, 2, 64, 64, a, 1e-5, a, 64, None) == ALIGN
+
+
+def test_permute_channels():
+    v = (np.arange(300, dtype=np.uint16) * 7) % 65000
+    perm = np.random.default_rng(3).permutation(300).astype(np.int32)
+    assert np.array_equal(comet.comet_permute_channels(v, perm), v[perm])
+    L = comet.lib()
+    bad = perm.copy()
+    bad[5] = 300
+    out = np.empty(300, np.uint16)
+    P = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    assert L.comet_permute_channels(P(v), P(bad), 300, P(out)) == ARG
+    assert L.comet_permute_channels(P(v), P(perm), 0, P(out)) == SHAPE
+    assert L.comet_permute_channels(None, P(perm), 300, P(out)) == NULL

@@ -57,12 +57,18 @@ def lib() -> ctypes.CDLL:
     L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
     L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P]
+    F = ctypes.c_float
+    L.comet_rmsnorm_quant_act.argtypes = [P, I, I, I, P, F, P, I, P, P, P]
+    L.comet_rmsnorm_quant_act_fp6.argtypes = [P, I, I, I, P, F, P, I, P, P, P]
+    L.comet_rmsnorm.argtypes = [P, I, I, I, P, F, P, I, P]
+    L.comet_permute_channels.argtypes = [P, P, I, P]
     L.comet_status_string.argtypes = [I]
     L.comet_status_string.restype = ctypes.c_char_p
     L.comet_version.restype = ctypes.c_char_p
     for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
               "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
-              "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials"):
+              "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_rmsnorm_quant_act",
+              "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -72,7 +78,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_w4ax_gemm_workspace_bytes", "comet_w4ax_gemm_partials",
            "comet_xq_fp6_bytes", "comet_wq_fp6_bytes", "comet_repack_weights_fp6",
            "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
-           "comet_status_string", "comet_version")
+           "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
+           "comet_permute_channels", "comet_status_string", "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -182,6 +189,49 @@ def comet_quant_act(X, perm, nb8: int, Xq=None, x_scale=None, stream=None):
                                _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
     _check("comet_quant_act", rc)
     return Xq, x_scale
+
+
+def comet_permute_channels(v: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """Host: out[k] = v[perm[k]] (fp16 bits), e.g. the RMSNorm weight into the permuted order."""
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    out = np.empty(perm.shape[0], np.uint16)
+    _check("comet_permute_channels", lib().comet_permute_channels(
+        v.ctypes.data_as(ctypes.c_void_p), perm.ctypes.data_as(ctypes.c_void_p), perm.shape[0],
+        out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def comet_rmsnorm_quant_act(X, gamma_perm, eps: float, perm, nb8: int, Xq=None, x_scale=None, fp6=False,
+                            stream=None):
+    """RMS normalization fused into the quantizer (either layout). X: fp16 cuda tensor [M, ldx] of
+    un-normalized rows; gamma_perm: fp16 cuda tensor [K] in permuted order."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    if Xq is None:
+        n = xq_fp6_bytes(M, K, nb8) if fp6 else xq_bytes(M, K, nb8)
+        Xq = torch.empty(n, dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty((K // 128, M), dtype=torch.float32, device=X.device)
+    call = "comet_rmsnorm_quant_act_fp6" if fp6 else "comet_rmsnorm_quant_act"
+    rc = getattr(lib(), call)(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(gamma_perm), float(eps), _dev_ptr(perm),
+                              int(nb8), _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
+    _check(call, rc)
+    return Xq, x_scale
+
+
+def comet_rmsnorm(X, gamma, eps: float, K: int | None = None, Xn=None, stream=None):
+    """The normalization on its own: fp16 [M, K] in the original channel order."""
+    import torch
+    M, ldx = X.shape
+    K = ldx if K is None else K
+    if Xn is None:
+        Xn = torch.empty((M, K), dtype=torch.float16, device=X.device)
+    rc = lib().comet_rmsnorm(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(gamma), float(eps), _dev_ptr(Xn),
+                             Xn.stride(0), _stream(stream))
+    _check("comet_rmsnorm", rc)
+    return Xn
 
 
 def workspace_bytes(M: int, N: int, K: int, nb8: int) -> int:

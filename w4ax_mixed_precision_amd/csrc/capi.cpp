@@ -35,6 +35,18 @@ bool fp6_offsets_fit(int M, int K) {
     return mp * K <= std::numeric_limits<int32_t>::max();
 }
 
+// Shared checks of the two fused normalization + quantization calls.
+int check_rmsnorm_quant(const void* X, int M, int K, int ldx, const void* gamma_perm, float eps,
+                        const int32_t* perm, int nb8, const void* Xq, const float* x_scale) {
+    if (!X || !gamma_perm || !perm || !Xq || !x_scale) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (nb8 < 0 || nb8 > K / kBlock) return COMET_ERR_ARG;
+    if (!(eps > 0.0f) || !(eps <= std::numeric_limits<float>::max())) return COMET_ERR_ARG;
+    if (!aligned16(X) || !aligned16(gamma_perm) || !aligned16(perm) || !aligned16(Xq) || !aligned16(x_scale))
+        return COMET_ERR_ALIGN;
+    return COMET_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +181,50 @@ int comet_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t
     return hip_status(comet::launch_quant_act_fp6(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
                                                   n_int8_blocks, static_cast<uint8_t*>(Xq_fp6), x_scale,
                                                   stream));
+}
+
+int comet_rmsnorm_quant_act(const void* X_fp16, int M, int K, int ldx, const void* gamma_perm_fp16, float eps,
+                            const int32_t* perm, int n_int8_blocks, void* Xq, float* x_scale, void* stream) {
+    const int st = check_rmsnorm_quant(X_fp16, M, K, ldx, gamma_perm_fp16, eps, perm, n_int8_blocks, Xq, x_scale);
+    if (st != COMET_OK) return st;
+    return hip_status(comet::launch_rmsnorm_quant_act(static_cast<const uint16_t*>(X_fp16), M, K, ldx,
+                                                      static_cast<const uint16_t*>(gamma_perm_fp16), eps, perm,
+                                                      n_int8_blocks, static_cast<uint8_t*>(Xq), x_scale, false,
+                                                      stream));
+}
+
+int comet_rmsnorm_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const void* gamma_perm_fp16, float eps,
+                                const int32_t* perm, int n_int8_blocks, void* Xq_fp6, float* x_scale,
+                                void* stream) {
+    const int st =
+        check_rmsnorm_quant(X_fp16, M, K, ldx, gamma_perm_fp16, eps, perm, n_int8_blocks, Xq_fp6, x_scale);
+    if (st != COMET_OK) return st;
+    return hip_status(comet::launch_rmsnorm_quant_act(static_cast<const uint16_t*>(X_fp16), M, K, ldx,
+                                                      static_cast<const uint16_t*>(gamma_perm_fp16), eps, perm,
+                                                      n_int8_blocks, static_cast<uint8_t*>(Xq_fp6), x_scale, true,
+                                                      stream));
+}
+
+int comet_rmsnorm(const void* X_fp16, int M, int K, int ldx, const void* gamma_fp16, float eps, void* Xn_fp16,
+                  int ldn, void* stream) {
+    if (!X_fp16 || !gamma_fp16 || !Xn_fp16) return COMET_ERR_NULL;
+    if (M < 1 || K < 1 || ldx < K || ldn < K) return COMET_ERR_SHAPE;
+    if (!(eps > 0.0f) || !(eps <= std::numeric_limits<float>::max())) return COMET_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(X_fp16) | reinterpret_cast<uintptr_t>(gamma_fp16) |
+         reinterpret_cast<uintptr_t>(Xn_fp16)) & 1u)
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_rmsnorm(static_cast<const uint16_t*>(X_fp16), M, K, ldx,
+                                            static_cast<const uint16_t*>(gamma_fp16), eps,
+                                            static_cast<uint16_t*>(Xn_fp16), ldn, stream));
+}
+
+int comet_permute_channels(const uint16_t* v, const int32_t* perm, int K, uint16_t* out) {
+    if (!v || !perm || !out) return COMET_ERR_NULL;
+    if (K < 1) return COMET_ERR_SHAPE;
+    for (int k = 0; k < K; ++k)
+        if (perm[k] < 0 || perm[k] >= K) return COMET_ERR_ARG;
+    for (int k = 0; k < K; ++k) out[k] = v[perm[k]];
+    return COMET_OK;
 }
 
 int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,

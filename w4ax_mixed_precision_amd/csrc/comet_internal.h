@@ -33,6 +33,12 @@ int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* pe
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                          uint8_t* Xq, float* x_scale, void* stream);
 
+// RMS normalization fused into the quantizer (either layout), and on its own.
+int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma_perm, float eps,
+                             const int32_t* perm, int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream);
+int launch_rmsnorm(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma, float eps, uint16_t* Xn,
+                   int ldn, void* stream);
+
 struct GemmProblem {
     const uint8_t* Xq;
     const float* x_scale;

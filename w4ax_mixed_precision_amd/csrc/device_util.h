@@ -20,6 +20,16 @@ __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
+// The value unchanged but opaque to the optimizer. A binary32 product that is
+// then rounded to fp16 must stay a product: otherwise the compiler folds the
+// two into one mixed-precision FMA (v_fma_mixlo_f16) that rounds once,
+// directly to fp16, instead of to binary32 and then to fp16, and a value on
+// an fp16 tie after the first rounding comes out one step away.
+__device__ __forceinline__ float opaque(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // 4-bit two's-complement weight nibbles to bytes holding 16 q_w (sign kept).
 __device__ __forceinline__ v4i widen_weights_lo(uint4 p) {   // block positions 32g + j
     return v4i{static_cast<int>((p.x << 4) & 0xF0F0F0F0u), static_cast<int>((p.y << 4) & 0xF0F0F0F0u),

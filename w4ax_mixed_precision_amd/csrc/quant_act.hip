@@ -26,6 +26,17 @@
 //   * INT4 layout, 4-bit block: zero-extended nibbles u = q + 8, byte j of the
 //     group holding positions j (low) and 16 + j (high).
 //   * 8-bit blocks: int8 codes in position order (FP6 layout: 16-row tiles).
+//
+// The same kernels optionally fuse the RMS normalization that precedes the
+// quantizer in a transformer block (QoQ/QServe article,
+// youleyou.com/wenzhang/3078652.html, section "运行时设计": the activation
+// quantization of the QKV projection and of the first FFN layer is fused into
+// the layer norm before it). The row is already staged once for the gather,
+// so the statistic costs one more pass over LDS, and the normalized row never
+// goes to memory: xn = fp16((x r) gamma), r = binary32(1 / sqrt(S / K + eps)),
+// S a binary64 sum of squares in a fixed order (512 strided partials, then
+// halving steps with strides 256 .. 1), the same in every kernel here, so the
+// fused codes equal those of normalizing first and quantizing after.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -59,12 +70,48 @@ __device__ __forceinline__ void load_positions(const int32_t* __restrict__ perm,
     for (int k = 0; k < 8; ++k) p[k] = src[k];
 }
 
+// Normalization of a row: r = binary32(1 / sqrt(S / K + eps)) with S the
+// binary64 sum of squares taken as 512 partials (partial p: x_k^2 for k = p,
+// p + 512, ... in increasing k) halved with strides 256, 128, ..., 1. The T
+// threads of the workgroup form the partials into `red` (512 doubles of LDS);
+// after the barrier every wave halves them on its own (strides 256 .. 64
+// inside a lane, 32 .. 1 by an xor butterfly, whose every addition has the
+// operands of the halving step), so all waves hold the same r without a
+// second barrier. The caller must not overwrite `red` before every wave has
+// read it.
+template <int T>
+__device__ __forceinline__ float rms_scale(const uint16_t* __restrict__ row, int K, float eps,
+                                           double* __restrict__ red) {
+    for (int p = threadIdx.x; p < 512; p += T) {
+        double s = 0.0;
+        for (int k = p; k < K; k += 512) {
+            const double v = h2f(row[k]);
+            s = s + v * v;                      // v * v is exact in binary64
+        }
+        red[p] = s;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    double a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = red[lane + 64 * i];
+    const double b0 = a[0] + a[4], b1 = a[1] + a[5], b2 = a[2] + a[6], b3 = a[3] + a[7];   // stride 256
+    const double c0 = b0 + b2, c1 = b1 + b3;                                               // stride 128
+    double d = c0 + c1;                                                                    // stride 64
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) d = d + __shfl_xor(d, st);
+    const double r = 1.0 / __builtin_sqrt(d / static_cast<double>(K) + static_cast<double>(eps));
+    return static_cast<float>(r);
+}
+
 // Codes and scale of block b of row m for this lane's group g, from the row
-// (LDS or global) and the lane's 32 channels `pos`.
-template <bool kFp6>
+// (LDS or global) and the lane's 32 channels `pos`. With kNorm each gathered
+// value first becomes fp16((x rs) gamma), gamma in permuted order (`gperm`).
+template <bool kFp6, bool kNorm = false>
 __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, const int4 (&pos)[8], int b, int nb,
                                            int nb4, int M, int Mp, int m, int g, uint8_t* __restrict__ Xq,
-                                           float* __restrict__ x_scale) {
+                                           float* __restrict__ x_scale, float rs = 0.0f,
+                                           const uint16_t* __restrict__ gperm = nullptr) {
     const bool valid = b < nb;
     const int bc = valid ? b : nb - 1;
     const bool is8 = bc >= nb4;
@@ -74,6 +121,21 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
         const int idx[4] = {pos[k].x, pos[k].y, pos[k].z, pos[k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * k + e] = h2f(row[idx[e]]);
+    }
+    if constexpr (kNorm) {
+        // the lane's 32 gamma values are contiguous in permuted order
+        const uint4* gp = reinterpret_cast<const uint4*>(gperm + bc * kBlock + 32 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 w = gp[q];
+            const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gm = h2f(static_cast<uint16_t>(h[e >> 1] >> (16 * (e & 1))));
+                const float t = v[8 * q + e] * rs;
+                v[8 * q + e] = __half2float(__float2half_rn(opaque(t * gm)));
+            }
+        }
     }
     float a = 0.0f;
 #pragma unroll
@@ -150,10 +212,11 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
     }
 }
 
-template <bool kRowInLds, bool kFp6>
+template <bool kRowInLds, bool kFp6, bool kNorm>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
-    int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd) {
+    int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd,
+    const uint16_t* __restrict__ gperm, float eps) {
     extern __shared__ uint16_t row_lds[];
     // Row of this workgroup. Workgroup w runs on XCD w mod 8 and each XCD has
     // its own L2; with `rows_per_xcd` > 0 every XCD takes a contiguous range
@@ -187,6 +250,13 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const int g = lane & 3;               // the lane's 32-channel group
     const int bl = lane >> 2;             // its block among the wave's 16
     const int stride = gridDim.y * kBlocksPerPass;
+    float rs = 0.0f;
+    if constexpr (kNorm) {
+        // after the staged row (LDS, whole KB chunks) or in place of it
+        double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) +
+                                                (kRowInLds ? static_cast<size_t>((K + 511) / 512) * 1024 : 0));
+        rs = rms_scale<kThreads>(kRowInLds ? row_lds : xr, K, eps, red);
+    }
 
     int b0 = (blockIdx.y * kWaves + wave) * 16;
     int4 nxt[8];
@@ -196,7 +266,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) pos[k] = nxt[k];
         if (b0 + stride < nb) load_positions(perm, imin(b0 + stride + bl, nb - 1), g, nxt);
-        code_block<kFp6>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale);
+        code_block<kFp6, kNorm>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale, rs,
+                                gperm);
     }
 }
 
@@ -222,26 +293,34 @@ __device__ __forceinline__ void stage_row(const uint16_t* xr, int K, int wave, i
 // One row: start the direct loads of the next row into `nxt_buf`, then code
 // this row from `cur` (distinct buffers, restrict-qualified so that the LDS
 // gathers do not wait for the loads just issued).
-template <bool kFp6>
+template <bool kFp6, bool kNorm>
 __device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __restrict__ nxt_buf,
                                          const uint16_t* __restrict__ cur, const int4 (&pos)[kRowPasses][8],
                                          int K, int nb, int nb4, int M, int Mp, int m, int wave, int lane,
-                                         uint8_t* __restrict__ Xq, float* __restrict__ x_scale) {
+                                         uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
+                                         const uint16_t* __restrict__ gperm, float eps, double* __restrict__ red) {
     if (next_row) stage_row(next_row, K, wave, lane, nxt_buf);
+    float rs = 0.0f;
+    if constexpr (kNorm) rs = rms_scale<kRowThreads>(cur, K, eps, red);
     const int g = lane & 3, bl = lane >> 2;
 #pragma unroll
     for (int p = 0; p < kRowPasses; ++p) {
         const int b0 = (p * kRowWaves + wave) * 16;
-        if (b0 < nb) code_block<kFp6>(cur, pos[p], b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale);
+        if (b0 < nb) code_block<kFp6, kNorm>(cur, pos[p], b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale, rs, gperm);
     }
 }
 
-template <bool kFp6>
+template <bool kFp6, bool kNorm>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm, int nb, int nb4,
-    uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd, int wgs_per_xcd) {
+    uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd, int wgs_per_xcd,
+    const uint16_t* __restrict__ gperm, float eps) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t bufs[];
     const int row_bytes = ((K + 511) / 512) * 1024;
+    // the statistic's partials (kNorm) follow the two row buffers; they are
+    // written after the barrier that opens a row, when every wave has read
+    // those of the previous row
+    double* red = reinterpret_cast<double*>(bufs + 2 * static_cast<size_t>(row_bytes));
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int first = (blockIdx.x & 7) * rows_per_xcd + (blockIdx.x >> 3);
@@ -265,17 +344,30 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
         __builtin_amdgcn_s_barrier();
         const uint16_t* next = k + 1 < n ? X + static_cast<size_t>(m + wgs_per_xcd) * ldx : nullptr;
         if (k & 1)
-            row_step<kFp6>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4, M, Mp,
-                           m, wave, lane, Xq, x_scale);
+            row_step<kFp6, kNorm>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4,
+                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red);
         else
-            row_step<kFp6>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4, M, Mp,
-                           m, wave, lane, Xq, x_scale);
+            row_step<kFp6, kNorm>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4,
+                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red);
     }
 }
 
-template <bool kFp6>
+// Dynamic LDS above the 64 KB default for the kernels that need it, set once
+// per kernel (one flag per kernel address).
+template <auto Kern>
+hipError_t allow_lds(int bytes) {
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [bytes] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   bytes);
+    });
+    return attr;
+}
+
+template <bool kFp6, bool kNorm>
 int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8, uint8_t* Xq,
-           float* x_scale, void* stream) {
+           float* x_scale, const uint16_t* gperm, float eps, void* stream) {
     const int nb = K / kBlock;
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
@@ -289,31 +381,47 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     const int rows_per_xcd = M >= 128 ? ((M + 127) / 128) * 16 : 0;
     dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t red = kNorm ? 512 * sizeof(double) : 0;   // partials of the row statistic
+    const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
     if (M >= 256 && K <= kMaxLdsRowChannels && (ldx & 7) == 0) {
-        // the two row buffers may exceed the 64 KB default of dynamic LDS
-        static std::once_flag once;
-        static hipError_t attr = hipSuccess;
-        std::call_once(once, [] {
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&quant_rows_kernel<kFp6>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-        });
+        // the two row buffers (and the partials) may exceed the 64 KB default
+        const hipError_t attr = allow_lds<&quant_rows_kernel<kFp6, kNorm>>(160 * 1024);
         if (attr != hipSuccess) return static_cast<int>(attr);
-        const size_t lds = 2 * static_cast<size_t>((K + 511) / 512) * 1024;
         const int wgs_per_xcd = cu_count() / 8;
         const int rows_per_xcd = ((M + 127) / 128) * 16;
-        quant_rows_kernel<kFp6><<<8 * wgs_per_xcd, kRowThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq, x_scale,
-                                                                         rows_per_xcd, wgs_per_xcd);
+        quant_rows_kernel<kFp6, kNorm><<<8 * wgs_per_xcd, kRowThreads, 2 * row_lds + red, s>>>(
+            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, wgs_per_xcd, gperm, eps);
         return static_cast<int>(hipGetLastError());
     }
     if (K <= kMaxLdsRowChannels) {
-        const size_t lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
-        quant_act_kernel<true, kFp6><<<grid, kThreads, lds, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                                 x_scale, rows_per_xcd);
+        const hipError_t attr = allow_lds<&quant_act_kernel<true, kFp6, kNorm>>(160 * 1024);
+        if (attr != hipSuccess) return static_cast<int>(attr);
+        quant_act_kernel<true, kFp6, kNorm><<<grid, kThreads, row_lds + red, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
+                                                                                x_scale, rows_per_xcd, gperm, eps);
     } else {
-        quant_act_kernel<false, kFp6><<<grid, kThreads, 0, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                                x_scale, rows_per_xcd);
+        quant_act_kernel<false, kFp6, kNorm><<<grid, kThreads, red, s>>>(X, M, K, ldx, perm, nb, nb4, Xq, x_scale,
+                                                                       rows_per_xcd, gperm, eps);
     }
     return static_cast<int>(hipGetLastError());
+}
+
+// Standalone RMS normalization (the unfused step): one workgroup of 512
+// threads per row, the same statistic as the fused kernels, fp16 out in the
+// original channel order.
+constexpr int kNormThreads = 512;
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* __restrict__ X, int K, int ldx,
+                                                               const uint16_t* __restrict__ gamma, float eps,
+                                                               uint16_t* __restrict__ Xn, int ldn) {
+    __shared__ double red[512];
+    const int m = blockIdx.x;
+    const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
+    const float rs = rms_scale<kNormThreads>(xr, K, eps, red);
+    uint16_t* out = Xn + static_cast<size_t>(m) * ldn;
+    for (int k = threadIdx.x; k < K; k += kNormThreads) {
+        const float t = h2f(xr[k]) * rs;
+        out[k] = __half_as_ushort(__float2half_rn(opaque(t * h2f(gamma[k]))));
+    }
 }
 
 }  // namespace
@@ -331,12 +439,24 @@ int cu_count() {
 
 int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                      uint8_t* Xq, float* x_scale, void* stream) {
-    return launch<false>(X, M, K, ldx, perm, nb8, Xq, x_scale, stream);
+    return launch<false, false>(X, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream);
 }
 
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                          uint8_t* Xq, float* x_scale, void* stream) {
-    return launch<true>(X, M, K, ldx, perm, nb8, Xq, x_scale, stream);
+    return launch<true, false>(X, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream);
+}
+
+int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma_perm, float eps,
+                             const int32_t* perm, int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream) {
+    return fp6 ? launch<true, true>(X, M, K, ldx, perm, nb8, Xq, x_scale, gamma_perm, eps, stream)
+               : launch<false, true>(X, M, K, ldx, perm, nb8, Xq, x_scale, gamma_perm, eps, stream);
+}
+
+int launch_rmsnorm(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma, float eps, uint16_t* Xn,
+                   int ldn, void* stream) {
+    rmsnorm_kernel<<<M, kNormThreads, 0, static_cast<hipStream_t>(stream)>>>(X, K, ldx, gamma, eps, Xn, ldn);
+    return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace comet
