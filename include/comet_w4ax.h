@@ -271,10 +271,13 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
  * section "核融合": one kernel reads the input, takes its statistics and
  * quantizes. The normalization (RMSNorm, as in the LLaMA models the pages
  * evaluate) of row m:
- *   S  = sum over k of x_k^2 in binary64, formed as 512 partials (partial p
- *        holds x_k^2 for k = p, p + 512, ... added in increasing k) that are
- *        then halved with strides 256, 128, ..., 1 (partial p += partial
- *        p + stride for p < stride);
+ *   S  = sum over k of x_k^2 in binary64, in this order: the channels fall
+ *        in chunks of 512 (chunk c = channels 512c .. 512c + 511); partial
+ *        (w, j), w = 0..7, j = 0..63, adds x_k^2 for k = 512c + 8j + e over
+ *        the chunks c = w, w + 8, w + 16, ... and e = 0..7 (increasing c,
+ *        then e); for each w the 64 partials are halved with strides 32, 16,
+ *        ..., 1 (partial j += partial j + stride for j < stride), and the 8
+ *        results with strides 4, 2, 1;
  *   r  = binary32( 1 / sqrt(S / K + eps) ), the root and quotient in binary64;
  *   xn_k = fp16( (x_k * r) * gamma_k ), two binary32 products, nearest-even.
  * Every kernel of the library forms S the same way, so the fused calls give

@@ -412,26 +412,42 @@ int orc_epilogue(const int32_t *P, const float *sa, const uint16_t *sw16, int ro
 /* 6. RMS normalization (the step before the quantizer)                      */
 /* ------------------------------------------------------------------------ */
 
-/* Row statistic, in the order this library defines it (the pages fix none):
- * 512 partial sums in binary64, partial p holding x_k^2 for k = p, p + 512,
- * p + 1024, ... added in increasing k; then halving steps with strides 256,
- * 128, ..., 1, each replacing partial p (p < stride) by partial p + partial
- * p + stride. Every square of a binary16 value is exact in binary64. */
+/* Row statistic, in the order this library defines it (the pages fix none).
+ * The row is cut into chunks of 512 channels, c = 0, 1, ...; lane j (0..63)
+ * of virtual wave w (0..7) owns channels 512c + 8j + e (e = 0..7) of the
+ * chunks c = w, w + 8, w + 16, ...; its partial adds x_k^2 over those chunks
+ * in increasing c and, inside a chunk, increasing e (channels k >= K add
+ * nothing). The 64 lane partials of a wave are then halved with strides 32,
+ * 16, ..., 1 (partial j += partial j + stride for j < stride), and the 8 wave
+ * results with strides 4, 2, 1. All in binary64, where every square of a
+ * binary16 value is exact. */
 double orc_rms_sumsq(const uint16_t *x, int K)
 {
-    double part[512];
-    for (int p = 0; p < 512; ++p) {
-        double s = 0.0;
-        for (int k = p; k < K; k += 512) {
-            double v = (double)orc_half_to_float(x[k]);
-            s = s + v * v;
+    double wave[8];
+    int chunks = (K + 511) / 512;
+    for (int w = 0; w < 8; ++w) {
+        double lane[64];
+        for (int j = 0; j < 64; ++j) {
+            double s = 0.0;
+            for (int c = w; c < chunks; c += 8)
+                for (int e = 0; e < 8; ++e) {
+                    int k = 512 * c + 8 * j + e;
+                    if (k < K) {
+                        double v = (double)orc_half_to_float(x[k]);
+                        s = s + v * v;
+                    }
+                }
+            lane[j] = s;
         }
-        part[p] = s;
+        for (int stride = 32; stride >= 1; stride /= 2)
+            for (int j = 0; j < stride; ++j)
+                lane[j] = lane[j] + lane[j + stride];
+        wave[w] = lane[0];
     }
-    for (int stride = 256; stride >= 1; stride /= 2)
-        for (int p = 0; p < stride; ++p)
-            part[p] = part[p] + part[p + stride];
-    return part[0];
+    for (int stride = 4; stride >= 1; stride /= 2)
+        for (int w = 0; w < stride; ++w)
+            wave[w] = wave[w] + wave[w + stride];
+    return wave[0];
 }
 
 /* Xn[m][k] = fp16( (x * r) * gamma_k ) with r = binary32( 1 / sqrt(S / K +

@@ -34,9 +34,12 @@
 // the layer norm before it). The row is already staged once for the gather,
 // so the statistic costs one more pass over LDS, and the normalized row never
 // goes to memory: xn = fp16((x r) gamma), r = binary32(1 / sqrt(S / K + eps)),
-// S a binary64 sum of squares in a fixed order (512 strided partials, then
-// halving steps with strides 256 .. 1), the same in every kernel here, so the
-// fused codes equal those of normalizing first and quantizing after.
+// S a binary64 sum of squares in a fixed order that follows the staging: the
+// wave that loads a 512-channel chunk also sums its squares (8 consecutive
+// channels per lane), so each wave's part needs no barrier, and the parts of
+// the 8 (virtual) waves meet at the barrier the row needs anyway. Every kernel
+// here forms S the same way, so the fused codes equal those of normalizing
+// first and quantizing after.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -70,38 +73,58 @@ __device__ __forceinline__ void load_positions(const int32_t* __restrict__ perm,
     for (int k = 0; k < 8; ++k) p[k] = src[k];
 }
 
-// Normalization of a row: r = binary32(1 / sqrt(S / K + eps)) with S the
-// binary64 sum of squares taken as 512 partials (partial p: x_k^2 for k = p,
-// p + 512, ... in increasing k) halved with strides 256, 128, ..., 1. The T
-// threads of the workgroup form the partials into `red` (512 doubles of LDS);
-// after the barrier every wave halves them on its own (strides 256 .. 64
-// inside a lane, 32 .. 1 by an xor butterfly, whose every addition has the
-// operands of the halving step), so all waves hold the same r without a
-// second barrier. The caller must not overwrite `red` before every wave has
-// read it.
-template <int T>
-__device__ __forceinline__ float rms_scale(const uint16_t* __restrict__ row, int K, float eps,
-                                           double* __restrict__ red) {
-    for (int p = threadIdx.x; p < 512; p += T) {
-        double s = 0.0;
-        for (int k = p; k < K; k += 512) {
-            const double v = h2f(row[k]);
-            s = s + v * v;                      // v * v is exact in binary64
+// Row statistic S = sum of x_k^2 in binary64, in this fixed order: chunk c
+// holds channels 512c .. 512c + 511; lane j of virtual wave w (0..7) adds the
+// squares of channels 512c + 8j + e (e = 0..7) over the chunks c = w, w + 8,
+// ... in increasing c, then e; the 64 lane sums are halved with strides 32 ..
+// 1 and the 8 wave sums with strides 4, 2, 1. A workgroup's wave w stages the
+// chunks c = w mod (waves) itself, so it can form its part as soon as its own
+// direct loads have landed. The xor butterfly gives every lane the halving
+// result (each of its additions has the operands of a halving step).
+__device__ __forceinline__ double wave_sumsq(const uint16_t* row, int K, int w, int lane) {
+    double s = 0.0;
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    const int chunks = (K + 511) / 512;
+    for (int c = w; c < chunks; c += 8) {
+        const int k0 = 512 * c + 8 * lane;
+        if (vec && k0 + 8 <= K) {
+            const uint4 q = *reinterpret_cast<const uint4*>(row + k0);
+            const uint32_t h[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double v = h2f(static_cast<uint16_t>(h[e >> 1] >> (16 * (e & 1))));
+                s = s + v * v;                  // v * v is exact in binary64
+            }
+        } else {
+            for (int e = 0; e < 8 && k0 + e < K; ++e) {
+                const double v = h2f(row[k0 + e]);
+                s = s + v * v;
+            }
         }
-        red[p] = s;
     }
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    double a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = red[lane + 64 * i];
-    const double b0 = a[0] + a[4], b1 = a[1] + a[5], b2 = a[2] + a[6], b3 = a[3] + a[7];   // stride 256
-    const double c0 = b0 + b2, c1 = b1 + b3;                                               // stride 128
-    double d = c0 + c1;                                                                    // stride 64
-#pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) d = d + __shfl_xor(d, st);
-    const double r = 1.0 / __builtin_sqrt(d / static_cast<double>(K) + static_cast<double>(eps));
-    return static_cast<float>(r);
+    for (int st = 32; st >= 1; st >>= 1) s = s + __shfl_xor(s, st);
+    return s;
+}
+
+// r = binary32(1 / sqrt(S / K + eps)) from the 8 wave sums (LDS, published).
+__device__ __forceinline__ float rms_from_waves(const double* red, int K, float eps) {
+    const double b0 = red[0] + red[4], b1 = red[1] + red[5], b2 = red[2] + red[6], b3 = red[3] + red[7];
+    const double c0 = b0 + b2, c1 = b1 + b3;
+    const double S = c0 + c1;
+    return static_cast<float>(1.0 / __builtin_sqrt(S / static_cast<double>(K) + static_cast<double>(eps)));
+}
+
+// The 8 wave sums of a row by the T / 64 waves of a workgroup (wave i forms
+// virtual waves i, i + T / 64, ...), written to `red`; the caller publishes
+// them with a barrier.
+template <int T>
+__device__ __forceinline__ void wave_sums(const uint16_t* row, int K, double* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int v = wave; v < 8; v += T / 64) {
+        const double W = wave_sumsq(row, K, v, lane);
+        if (lane == 0) red[v] = W;
+    }
 }
 
 // Codes and scale of block b of row m for this lane's group g, from the row
@@ -230,6 +253,10 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the row statistic's 8 wave sums (kNorm) follow the staged row
+    double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) +
+                                            (kRowInLds ? static_cast<size_t>((K + 511) / 512) * 1024 : 0));
+    bool sums_done = false;
     if constexpr (kRowInLds) {
         if ((ldx & 7) == 0) {
             // direct loads of the row: 1 KB per wave instruction, all in flight
@@ -240,23 +267,27 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
             uint8_t* lds = reinterpret_cast<uint8_t*>(row_lds);
             for (int c = wave; c < chunks; c += kWaves) lds_buf16(r, 16u * lane, 1024u * c, lds + 1024 * c);
             COMET_VMCNT(0);
+            // this wave's chunks have landed: its wave sums need no barrier
+            if constexpr (kNorm) wave_sums<kThreads>(row_lds, K, red);
+            sums_done = true;
         } else {
             for (int c = threadIdx.x; c < K; c += kThreads) row_lds[c] = xr[c];
         }
         __syncthreads();
+    }
+    float rs = 0.0f;
+    if constexpr (kNorm) {
+        if (!sums_done) {
+            wave_sums<kThreads>(kRowInLds ? row_lds : xr, K, red);
+            __syncthreads();
+        }
+        rs = rms_from_waves(red, K, eps);
     }
 
     const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
     const int g = lane & 3;               // the lane's 32-channel group
     const int bl = lane >> 2;             // its block among the wave's 16
     const int stride = gridDim.y * kBlocksPerPass;
-    float rs = 0.0f;
-    if constexpr (kNorm) {
-        // after the staged row (LDS, whole KB chunks) or in place of it
-        double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) +
-                                                (kRowInLds ? static_cast<size_t>((K + 511) / 512) * 1024 : 0));
-        rs = rms_scale<kThreads>(kRowInLds ? row_lds : xr, K, eps, red);
-    }
 
     int b0 = (blockIdx.y * kWaves + wave) * 16;
     int4 nxt[8];
@@ -298,15 +329,25 @@ __device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __re
                                          const uint16_t* __restrict__ cur, const int4 (&pos)[kRowPasses][8],
                                          int K, int nb, int nb4, int M, int Mp, int m, int wave, int lane,
                                          uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
-                                         const uint16_t* __restrict__ gperm, float eps, double* __restrict__ red) {
+                                         const uint16_t* __restrict__ gperm, float eps, const double* red_cur,
+                                         double* red_nxt) {
     if (next_row) stage_row(next_row, K, wave, lane, nxt_buf);
     float rs = 0.0f;
-    if constexpr (kNorm) rs = rms_scale<kRowThreads>(cur, K, eps, red);
+    if constexpr (kNorm) rs = rms_from_waves(red_cur, K, eps);
     const int g = lane & 3, bl = lane >> 2;
 #pragma unroll
     for (int p = 0; p < kRowPasses; ++p) {
         const int b0 = (p * kRowWaves + wave) * 16;
         if (b0 < nb) code_block<kFp6, kNorm>(cur, pos[p], b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale, rs, gperm);
+    }
+    if constexpr (kNorm) {
+        // the next row's chunks of this wave have landed once its loads are
+        // done: its wave sum, published by the barrier that opens that row
+        if (next_row) {
+            COMET_VMCNT(0);
+            const double W = wave_sumsq(reinterpret_cast<const uint16_t*>(nxt_buf), K, wave, lane);
+            if (lane == 0) red_nxt[wave] = W;
+        }
     }
 }
 
@@ -317,10 +358,9 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ gperm, float eps) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t bufs[];
     const int row_bytes = ((K + 511) / 512) * 1024;
-    // the statistic's partials (kNorm) follow the two row buffers; they are
-    // written after the barrier that opens a row, when every wave has read
-    // those of the previous row
-    double* red = reinterpret_cast<double*>(bufs + 2 * static_cast<size_t>(row_bytes));
+    // the 8 wave sums of the row statistic (kNorm) follow the two row
+    // buffers, alternating between two sets: row k+1's are written during row
+    // k, while the waves read row k's from the other set
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int first = (blockIdx.x & 7) * rows_per_xcd + (blockIdx.x >> 3);
@@ -335,7 +375,13 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
         const int b = (p * kRowWaves + wave) * 16 + (lane >> 2);
         load_positions(perm, imin(b, nb - 1), lane & 3, pos[p]);
     }
+    double* red = reinterpret_cast<double*>(bufs + 2 * static_cast<size_t>(row_bytes));
     stage_row(X + static_cast<size_t>(first) * ldx, K, wave, lane, bufs);
+    if constexpr (kNorm) {
+        COMET_VMCNT(0);
+        const double W = wave_sumsq(reinterpret_cast<const uint16_t*>(bufs), K, wave, lane);
+        if (lane == 0) red[wave] = W;
+    }
     for (int k = 0; k < n; ++k) {
         const int m = first + k * wgs_per_xcd;
         // row k has landed (and this wave's earlier stores are done); after
@@ -345,10 +391,12 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
         const uint16_t* next = k + 1 < n ? X + static_cast<size_t>(m + wgs_per_xcd) * ldx : nullptr;
         if (k & 1)
             row_step<kFp6, kNorm>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4,
-                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red);
+                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red + 8 * (k & 1),
+                                  red + 8 * ((k + 1) & 1));
         else
             row_step<kFp6, kNorm>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4,
-                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red);
+                                  M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red + 8 * (k & 1),
+                                  red + 8 * ((k + 1) & 1));
     }
 }
 
@@ -381,7 +429,7 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     const int rows_per_xcd = M >= 128 ? ((M + 127) / 128) * 16 : 0;
     dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t red = kNorm ? 512 * sizeof(double) : 0;   // partials of the row statistic
+    const size_t red = kNorm ? 16 * sizeof(double) : 0;    // wave sums of the row statistic
     const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
     if (M >= 256 && K <= kMaxLdsRowChannels && (ldx & 7) == 0) {
         // the two row buffers (and the partials) may exceed the 64 KB default
@@ -413,10 +461,12 @@ constexpr int kNormThreads = 512;
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* __restrict__ X, int K, int ldx,
                                                                const uint16_t* __restrict__ gamma, float eps,
                                                                uint16_t* __restrict__ Xn, int ldn) {
-    __shared__ double red[512];
+    __shared__ double red[8];
     const int m = blockIdx.x;
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
-    const float rs = rms_scale<kNormThreads>(xr, K, eps, red);
+    wave_sums<kNormThreads>(xr, K, red);
+    __syncthreads();
+    const float rs = rms_from_waves(red, K, eps);
     uint16_t* out = Xn + static_cast<size_t>(m) * ldn;
     for (int k = threadIdx.x; k < K; k += kNormThreads) {
         const float t = h2f(xr[k]) * rs;
