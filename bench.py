@@ -220,6 +220,53 @@ def run_gpu(layers, steps, warmup, torch, comet):
     return step_ms, per
 
 
+def fusion_ablation(torch, comet, synth, M=4096, K=8192, nb8=7, iters=20):
+    """The quantizer fused into the RMS normalization before it, against the two
+    steps apart (comet_rmsnorm, then comet_quant_act_fp6), at the 70B up/gate
+    input (4096 tokens x 8192 channels). HIP events on the launch stream around
+    `iters` back-to-back iterations of each variant."""
+    cfg = synth.LayerConfig("norm_quant_70b", M, K, 128, 17)
+    X = torch.from_numpy(synth.make_x(cfg).view(np.float16)).cuda()
+    rng = np.random.default_rng(17)
+    gamma16 = synth.to_fp16(1.0 + 0.25 * rng.standard_normal(K))
+    score = synth.make_scores(cfg)
+    perm = np.argsort(score, kind="stable").astype(np.int32)     # any permutation serves for timing
+    gamma = torch.from_numpy(gamma16.view(np.float16)).cuda()
+    gperm = torch.from_numpy(comet.comet_permute_channels(gamma16, perm).view(np.float16)).cuda()
+    pd = torch.from_numpy(perm).cuda()
+    Xn = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    Xq = torch.empty(comet.xq_fp6_bytes(M, K, nb8), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+
+    def unfused():
+        comet.comet_rmsnorm(X, gamma, 1e-5, Xn=Xn)
+        comet.comet_quant_act_fp6(Xn, pd, nb8, Xq=Xq, x_scale=xs)
+
+    def fused():
+        comet.comet_rmsnorm_quant_act(X, gperm, 1e-5, pd, nb8, Xq=Xq, x_scale=xs, fp6=True)
+
+    res = {}
+    for name, fn in (("unfused", unfused), ("fused", fused)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / iters
+    codes = M * (96 * (K // 128 - nb8) + 128 * nb8) + 4 * M * (K // 128)
+    xbytes = 2 * M * K
+    return {"shape": {"M": M, "K": K, "int8_blocks": nb8, "layout": "fp6"},
+            "unfused_us": res["unfused"], "fused_us": res["fused"],
+            "speedup": res["unfused"] / res["fused"],
+            "hbm_bytes_unfused": 3 * xbytes + codes, "hbm_bytes_fused": xbytes + codes,
+            "fused_gbs": (xbytes + codes) / (res["fused"] * 1e-6) / 1e9,
+            "timing": f"HIP events around {iters} back-to-back iterations of each variant"}
+
+
 def cpu_baseline(layers, budget_s):
     """The oracle as it stands, on a bounded sample of rows of every layer: host
     time of steps 3-5 (activation quantization, block partials, epilogue) with
@@ -321,6 +368,8 @@ def main():
             "layout": l.layout, "gemm_peak_tops": l.peak,
             "weight_copies": len(l.w)}
 
+    fusion = fusion_ablation(torch, comet, synth) if args.workload == "prefill_70b" else None
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(layers, args.cpu_seconds)
@@ -340,6 +389,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "norm_quant_fusion": fusion,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
