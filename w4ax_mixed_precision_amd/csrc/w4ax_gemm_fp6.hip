@@ -235,6 +235,10 @@ __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = mfma_fp6(A[r], B);
     }
+    // Each column tile is one scheduling region: without the fences the
+    // scheduler pulls a tile's epilogue up behind its own matrix instructions,
+    // so the multiply-adds wait on results still in flight.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 1; c < kWC; ++c) {
         if constexpr (!kDump) tc = scale_products<kWC>(s, c);
@@ -245,6 +249,7 @@ __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = Dc[r];
         tp = tc;
+        __builtin_amdgcn_sched_barrier(0);
     }
     epilogue<kDump, kWC>(p, tp, Dp, kWC - 1, b, row0, col0, row_lo, row_hi, y);
     end_block<kWC>(b, p.nb);
