@@ -45,6 +45,8 @@ STREAM_MULT = 4
 STREAM_CALIB = 5
 STREAM_CHI = 6          # chi-square draws of the Student-t activations
 STREAM_CALIB_CHI = 7    # chi-square draws of the Student-t calibration batch
+STREAM_GATE = 8         # gate projection outputs (SwiGLU input)
+STREAM_UP = 9           # up projection outputs (SwiGLU input)
 
 _CHUNK = 1 << 22        # values per generation chunk (bounds peak host memory)
 
@@ -236,6 +238,28 @@ def make_scores(cfg: LayerConfig) -> np.ndarray:
     cal = _activations(cfg, cfg.calib_tokens, STREAM_CALIB, STREAM_CALIB_CHI)
     cal16 = to_fp16(cal).view(np.float16).astype(np.float32)
     return np.abs(cal16).max(axis=0).astype(np.float32)
+
+
+def make_gate_up(cfg: LayerConfig, rows: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """The gate and up projection outputs that feed the down projection's
+    SwiGLU, fp16 bit patterns [M, K] each (K = the down projection's input
+    width). Gate: normal with standard deviation 2 and the configuration's
+    outlier channels multiplied by its 20..100 factors, so a few channels
+    carry the large values the down projection's input is known for (QUIK
+    blog, Figure 10 of its down-projection case study); up: standard normal.
+    The up value is clipped to |u| <= 16384 / max(|g|, 1), which keeps every
+    product |g u| inside the fp16 range."""
+    M = cfg.M if rows is None else rows
+    K = cfg.K
+    g = normal(cfg.seed, STREAM_GATE, M * K, scale=2.0, dtype=np.float32).reshape(M, K)
+    ch, mu = outlier_plan(cfg)
+    if len(ch):
+        g[:, ch] *= mu.astype(np.float32)[None, :]
+    g16 = to_fp16(g)
+    gv = np.abs(g16.view(np.float16).astype(np.float32))
+    u = normal(cfg.seed, STREAM_UP, M * K, dtype=np.float32).reshape(M, K)
+    cap = 16384.0 / np.maximum(gv, 1.0)
+    return g16, to_fp16(np.clip(u, -cap, cap))
 
 
 def make_layer(cfg: LayerConfig) -> dict:

@@ -42,6 +42,15 @@
  *     the block's FP16 activation (QoQ/QServe, same section: FP16 block inputs
  *     and outputs), which step 3 then quantizes.
  *
+ *  7. SwiGLU before the quantizer of the second FFN layer. QoQ/QServe
+ *     article, section "运行时设计": the activation quantization of the second
+ *     FFN layer is fused into the activation kernel before it; QUIK blog,
+ *     section "案例研究: 敏感的 LLaMA-2 Down-Projection 层": LLaMA's MLP uses
+ *     SwiGLU, and the down projection takes the element-wise product of the
+ *     gate and up projections' outputs. With the standard SiLU, the down
+ *     projection's fp16 input is h = fp16( silu(g) u ), silu(g) = g / (1 +
+ *     e^-g), and step 3 quantizes it.
+ *
  * Readings of points the pages leave open (INT4 range, rounding mode, scale
  * form, all-zero blocks, tie-breaking of the channel sort) are listed with the
  * design notes at the repository root; each is stated where it is used below.
@@ -481,6 +490,86 @@ int orc_rmsnorm_rows(const uint16_t *X, int M, int K, int ldx, const uint16_t *g
         }
     }
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 7. SwiGLU (the step before the down projection's quantizer)               */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 nearest to a binary64 value, ties to even; overflow gives an
+ * infinity. The value is scaled by a power of two so that its binary16
+ * quantum becomes 1, rounded there with rint(), and scaled back; every step
+ * but the rint() is exact. */
+uint16_t orc_double_to_half(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7e00u;
+    if (a >= 65520.0) /* at or past the midpoint between 65504 and 2^16 */
+        return (uint16_t)(sign | 0x7c00u);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    int q = e - 11; /* binary16 quantum of that binade */
+    if (q < -24)
+        q = -24; /* subnormal quantum */
+    double r = ldexp(rint(ldexp(a, -q)), q);
+    return (uint16_t)(sign | orc_float_to_half((float)r)); /* r is a binary16 value */
+}
+
+/* h = silu(g) u = g u / (1 + e^-g), the exact real value rounded once to
+ * binary16 (ties to even); this library's reading of a step whose precision
+ * the pages do not state. Evaluated in binary64: sigma = 1 / (1 + e^-g) for
+ * g >= 0 and e^g / (1 + e^g) below (no overflow), g u exact (two binary16
+ * significands fit in 22 bits). When sigma rounds to exactly 1 (g > 36) the
+ * true product lies strictly between g u and the next binary64 value toward
+ * zero, so that value stands in for it: a tie of g u on the binary16 grid
+ * then resolves toward zero, as it must. */
+uint16_t orc_silu_mul(uint16_t g16, uint16_t u16)
+{
+    double g = (double)orc_half_to_float(g16);
+    double u = (double)orc_half_to_float(u16);
+    double sigma;
+    if (g >= 0.0) {
+        sigma = 1.0 / (1.0 + exp(-g));
+    } else {
+        double e = exp(g);
+        sigma = e / (1.0 + e);
+    }
+    double gu = g * u;
+    double v = gu * sigma;
+    if (sigma == 1.0 && gu != 0.0)
+        v = nextafter(gu, 0.0);
+    return orc_double_to_half(v);
+}
+
+/* H[m][k] = orc_silu_mul(G[m][k], U[m][k]) for the gate and up rows (row
+ * stride ldx, both) into H (row stride ldh). Non-finite inputs are rejected,
+ * and so is a product that overflows binary16. */
+int orc_swiglu_rows(const uint16_t *G, const uint16_t *U, int M, int K, int ldx, uint16_t *H, int ldh)
+{
+    if (M <= 0 || K <= 0 || ldx < K || ldh < K)
+        return ORC_ERR_ARG;
+    for (int m = 0; m < M; ++m)
+        for (int k = 0; k < K; ++k) {
+            uint16_t g = G[(size_t)m * ldx + k], u = U[(size_t)m * ldx + k];
+            if (!isfinite(orc_half_to_float(g)) || !isfinite(orc_half_to_float(u)))
+                return ORC_ERR_NONFINITE;
+            uint16_t h = orc_silu_mul(g, u);
+            if (!isfinite(orc_half_to_float(h)))
+                return ORC_ERR_NONFINITE;
+            H[(size_t)m * ldh + k] = h;
+        }
+    return ORC_OK;
+}
+
+/* Element-wise form for the pins: h[i] = orc_silu_mul(g[i], u[i]). */
+void orc_silu_mul_array(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = orc_silu_mul(g[i], u[i]);
 }
 
 /* ------------------------------------------------------------------------ */

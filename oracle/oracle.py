@@ -69,6 +69,13 @@ def lib() -> ctypes.CDLL:
         L.orc_rms_sumsq.restype = ctypes.c_double
         L.orc_rms_sumsq.argtypes = [P, I]
         L.orc_rmsnorm_rows.argtypes = [P, I, I, I, P, ctypes.c_float, P, I]
+        L.orc_double_to_half.argtypes = [ctypes.c_double]
+        L.orc_double_to_half.restype = ctypes.c_uint16
+        L.orc_silu_mul.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        L.orc_silu_mul.restype = ctypes.c_uint16
+        L.orc_silu_mul_array.argtypes = [P, P, P, ctypes.c_int64]
+        L.orc_silu_mul_array.restype = None
+        L.orc_swiglu_rows.argtypes = [P, P, I, I, I, P, I]
         L.orc_threads.restype = I
         L.orc_half_to_float_array.restype = None
         L.orc_half_to_float_array.argtypes = [P, P, ctypes.c_int64]
@@ -233,6 +240,31 @@ def rmsnorm(X16: np.ndarray, gamma16: np.ndarray, eps: float) -> np.ndarray:
     out = np.empty((M, K), np.uint16)
     _check(lib().orc_rmsnorm_rows(_p(X), M, K, K, _p(g), ctypes.c_float(eps), _p(out), K), "orc_rmsnorm_rows")
     return out
+
+
+def double_to_half(v: float) -> int:
+    return int(lib().orc_double_to_half(ctypes.c_double(v)))
+
+
+def silu_mul(g16: np.ndarray, u16: np.ndarray) -> np.ndarray:
+    """fp16 bits of fp16(silu(g) u), element-wise (step 7 of comet_oracle.c)."""
+    g = np.ascontiguousarray(g16, dtype=np.uint16)
+    u = np.ascontiguousarray(u16, dtype=np.uint16)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    lib().orc_silu_mul_array(_p(g), _p(u), _p(h), g.size)
+    return h
+
+
+def swiglu(G16: np.ndarray, U16: np.ndarray) -> np.ndarray:
+    """fp16 bits of the down projection's input rows from the gate and up rows."""
+    G = np.ascontiguousarray(G16, dtype=np.uint16)
+    U = np.ascontiguousarray(U16, dtype=np.uint16)
+    assert G.shape == U.shape and G.ndim == 2
+    M, K = G.shape
+    H = np.empty((M, K), np.uint16)
+    _check(lib().orc_swiglu_rows(_p(G), _p(U), M, K, K, _p(H), K), "orc_swiglu_rows")
+    return H
 
 
 def threads() -> int:

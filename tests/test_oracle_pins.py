@@ -672,3 +672,155 @@ def test_rmsnorm_rounding_structure(orc):
         want = ((x.astype(np.float32) * r32) * g.astype(np.float32)).astype(np.float16)
         got = orc.rmsnorm(x.view(np.uint16)[None], g.view(np.uint16), eps)[0]
         assert np.array_equal(got, want.view(np.uint16)), trial
+
+
+# --------------------------------------------------------------------------
+# SwiGLU feeding the down projection's quantizer
+# --------------------------------------------------------------------------
+
+def _fp16_nearest(x: Fraction, negative: bool, tie_toward_zero: bool) -> int:
+    """binary16 bits of the rational x rounded to nearest; ties go to the even
+    significand, or toward zero when the caller knows the true value lies
+    strictly inside the interval below |x|. Computed with exact rationals."""
+    sign = 0x8000 if negative else 0
+    a = abs(x)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    q = max(e - 10, -24)
+    m = a / Fraction(2) ** q
+    r = m.numerator // m.denominator
+    frac = m - r
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and not tie_toward_zero and r % 2 == 1):
+        r += 1
+    val = Fraction(r) * Fraction(2) ** q
+    if val > 65504:
+        return sign | 0x7C00
+    return sign | int(np.float16(float(val)).view(np.uint16))
+
+
+def _silu_mul_exact_bits(g: float, u: float) -> int:
+    """fp16(silu(g) u) from 60-digit decimal arithmetic: silu(g) = g / (1 +
+    e^-g) exactly as the definition reads; the product g u is exact."""
+    from decimal import Decimal, localcontext
+    neg = (np.signbit(g) != np.signbit(u))
+    if g == 0 or u == 0:
+        return 0x8000 if neg else 0
+    with localcontext() as ctx:
+        ctx.prec = 60
+        G, U = Decimal(g), Decimal(u)
+        s = 1 / (1 + (-G).exp())
+        x = Fraction(G * U * s)
+        # s rounds to 1 only when e^-g < 1e-60: the true |value| is then just
+        # below |g u|, so a tie of g u on the fp16 grid resolves toward zero
+        return _fp16_nearest(x, neg, tie_toward_zero=(s == 1))
+
+
+def test_silu_mul_every_gate_value(orc):
+    """Every finite fp16 gate value g with u = 1, and every 7th with u = -3:
+    the oracle's binary64 evaluation equals the exact rounding of the
+    definition computed with decimal arithmetic."""
+    g = np.concatenate([np.arange(0, 0x7C00, dtype=np.uint16), np.arange(0x8000, 0xFC00, dtype=np.uint16)])
+    got1 = orc.silu_mul(g, np.full(g.shape, 0x3C00, np.uint16))       # u = 1
+    gs = g[::7]
+    got3 = orc.silu_mul(gs, np.full(gs.shape, 0xC200, np.uint16))     # u = -3
+    gv = g.view(np.float16).astype(np.float64)
+    for i in range(g.size):
+        assert got1[i] == _silu_mul_exact_bits(gv[i], 1.0), hex(int(g[i]))
+    for i in range(gs.size):
+        assert got3[i] == _silu_mul_exact_bits(float(gs.view(np.float16)[i]), -3.0), hex(int(gs[i]))
+
+
+def test_silu_mul_random_pairs(orc):
+    """Gate and up values of both signs over many binades, including fp16
+    subnormal products and products near the fp16 maximum."""
+    rng = np.random.default_rng(21)
+    n = 20000
+    g = (rng.choice([-1, 1], n) * 2.0 ** rng.uniform(-14, 7, n)).astype(np.float16)
+    u = (rng.choice([-1, 1], n) * 2.0 ** rng.uniform(-14, 8, n)).astype(np.float16)
+    got = orc.silu_mul(g.view(np.uint16), u.view(np.uint16))
+    gv, uv = g.astype(np.float64), u.astype(np.float64)
+    for i in range(n):
+        want = _silu_mul_exact_bits(gv[i], uv[i])
+        if (want & 0x7C00) == 0x7C00:
+            continue                      # overflow: outside what a caller may pass
+        assert got[i] == want, (float(gv[i]), float(uv[i]))
+
+
+def test_silu_mul_ties_on_large_gates(orc):
+    """Large gates, where sigma(g) rounds to 1 in binary64 and g u often lies
+    exactly on an fp16 midpoint: the true value is below |g u|, so the result
+    rounds toward zero, not to even. Cases are checked against the exact
+    rounding, and enough of them are true ties to exercise the rule."""
+    rng = np.random.default_rng(22)
+    g = rng.integers(37, 2048, 3000).astype(np.float16)
+    u = (rng.integers(-255, 256, 3000) / 64.0).astype(np.float16)
+    got = orc.silu_mul(g.view(np.uint16), u.view(np.uint16))
+    ties = 0
+    for i in range(g.size):
+        gu = Fraction(float(g[i])) * Fraction(float(u[i]))
+        want = _silu_mul_exact_bits(float(g[i]), float(u[i]))
+        if (want & 0x7C00) == 0x7C00:
+            continue
+        even = _fp16_nearest(gu, gu < 0, tie_toward_zero=False)
+        ties += int(want != even)
+        assert got[i] == want, (float(g[i]), float(u[i]))
+    assert ties >= 50
+    # a hand-checkable case: 1025 * 3 = 3075 sits halfway between 3074 and 3076
+    assert orc.silu_mul(np.float16([1025]).view(np.uint16), np.float16([3]).view(np.uint16))[0] == \
+        np.float16(3074).view(np.uint16)
+
+
+def test_silu_mul_closed_forms_and_symmetry(orc):
+    """silu(0) = 0 with the product's sign; sigma(g) -> 0 far below zero;
+    negating u negates h exactly; for a fixed g, h is monotone in u with the
+    direction of the sign of silu(g), which is that of g."""
+    z = np.array([0x0000, 0x8000, 0x0000, 0x8000], np.uint16)
+    u = np.float16([2.0, 2.0, -2.0, -2.0]).view(np.uint16)
+    assert orc.silu_mul(z, u).tolist() == [0x0000, 0x8000, 0x8000, 0x0000]
+    far = np.float16([-65504.0, -1000.0, -120.0]).view(np.uint16)
+    assert orc.silu_mul(far, np.full(3, np.float16(65504.0).view(np.uint16))).tolist() == [0x8000] * 3
+    rng = np.random.default_rng(23)
+    g = rng.standard_normal(4000).astype(np.float16)
+    uu = (rng.standard_normal(4000) * 4).astype(np.float16)
+    h = orc.silu_mul(g.view(np.uint16), uu.view(np.uint16))
+    hn = orc.silu_mul(g.view(np.uint16), (-uu).view(np.uint16))
+    assert np.array_equal(h ^ 0x8000, hn)
+    us = np.sort(uu)
+    for gi in g[:20]:
+        hv = f16(orc.silu_mul(np.full(us.shape, gi).view(np.uint16), us.view(np.uint16)))
+        d = np.diff(hv)
+        assert np.all(d >= 0) if gi >= 0 else np.all(d <= 0), float(gi)   # sign of silu(g) is that of g
+
+
+def test_double_to_half_against_numpy(orc):
+    """The binary64 -> binary16 rounding against numpy's direct conversion,
+    on random values and on values a hair either side of fp16 midpoints
+    (where a detour through binary32 would round twice)."""
+    rng = np.random.default_rng(24)
+    vals = list(rng.standard_normal(3000) * 2.0 ** rng.integers(-26, 17, 3000))
+    mids = (np.arange(1, 0x7BFF, 37, dtype=np.uint16).view(np.float16).astype(np.float64) +
+            np.arange(2, 0x7C00, 37, dtype=np.uint16).view(np.float16).astype(np.float64)) / 2
+    for m in mids:
+        vals += [m, np.nextafter(m, 0.0), np.nextafter(m, np.inf), m * (1 + 2.0 ** -40), m * (1 - 2.0 ** -40)]
+    vals += [65519.99, 65520.0, 2.0 ** -25, 2.0 ** -25 * (1 + 2.0 ** -30), 3 * 2.0 ** -26]
+    for v in vals:
+        for s in (1.0, -1.0):
+            assert orc.double_to_half(s * v) == int(np.float16(s * v).view(np.uint16)), s * v
+
+
+def test_swiglu_rows_and_rejects(orc):
+    """Row form equals the element form; non-finite inputs and overflowing
+    products are rejected."""
+    rng = np.random.default_rng(25)
+    G = rng.standard_normal((3, 300)).astype(np.float16).view(np.uint16)
+    U = rng.standard_normal((3, 300)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.swiglu(G, U), orc.silu_mul(G, U))
+    bad = G.copy(); bad[1, 7] = 0x7C00
+    with pytest.raises(ValueError):
+        orc.swiglu(bad, U)
+    big = np.full((1, 128), np.float16(300.0).view(np.uint16), np.uint16)
+    with pytest.raises(ValueError):
+        orc.swiglu(big, big)              # 300 * 300 overflows fp16
