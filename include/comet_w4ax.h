@@ -320,6 +320,51 @@ int comet_rmsnorm_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const
 int comet_rmsnorm(const void* X_fp16, int M, int K, int ldx, const void* gamma_fp16, float eps, void* Xn_fp16,
                   int ldn, void* stream);
 
+/* ------------------------------------------------------------------------
+ * SwiGLU fused into the activation quantizer of the down projection.
+ * QoQ/QServe article (youleyou.com/wenzhang/3078652.html), section
+ * "运行时设计": the second FFN layer's activation quantization is fused into
+ * the activation kernel before it; QUIK blog (deep-paper.org/paper/2310.09259),
+ * section "案例研究: 敏感的 LLaMA-2 Down-Projection 层": LLaMA's MLP uses
+ * SwiGLU, and the down projection takes the element-wise product of the gate
+ * and up projections' outputs. With the standard SiLU, element k of row m is
+ *   h = fp16( silu(g) u ),  silu(g) = g / (1 + e^-g),
+ * the exact real value rounded once to binary16 (nearest, ties to even): the
+ * pages give no precision for this step, and the exact rounding is what makes
+ * the fused codes reproducible. g and u must be finite and the product must
+ * not overflow binary16 (|h| <= 65504); otherwise the result is unspecified.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * comet_quant_act of the SwiGLU rows: h is formed in the quantizer and never
+ * stored.
+ *
+ *   gate_fp16, up_fp16  in  [M, ldx] fp16 each, device, 16-byte aligned: the gate and
+ *                           up projections' outputs in the original channel order
+ *                           (e.g. the two halves of one [M, 2K] output: up = gate + K,
+ *                           ldx = 2K)
+ *   perm, n_int8_blocks, Xq, x_scale, stream: as comet_quant_act
+ * Errors: as comet_quant_act (NULL and ALIGN also for up_fp16).
+ */
+int comet_swiglu_quant_act(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx, const int32_t* perm,
+                           int n_int8_blocks, void* Xq, float* x_scale, void* stream);
+
+/* The same for the FP6 layout (Xq_fp6 and x_scale as comet_quant_act_fp6). */
+int comet_swiglu_quant_act_fp6(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx,
+                               const int32_t* perm, int n_int8_blocks, void* Xq_fp6, float* x_scale,
+                               void* stream);
+
+/*
+ * The unfused step: H[m][k] = fp16(silu(gate[m][k]) up[m][k]) as defined above,
+ * original channel order.
+ *
+ *   gate_fp16, up_fp16  in   [M, ldx] fp16, device, 2-byte aligned
+ *   H_fp16              out  [M, ldh] fp16, device, 2-byte aligned (columns >= K untouched)
+ * Errors: NULL, SHAPE (M < 1, K < 1, ldx < K, ldh < K), ALIGN, HIP.
+ */
+int comet_swiglu(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx, void* H_fp16, int ldh,
+                 void* stream);
+
 /*
  * Offline, host memory: out[k] = v[perm[k]] for k < K (for example the
  * RMSNorm weight into the permuted order the fused calls take).

@@ -189,6 +189,40 @@ def test_rmsnorm_rejections():
     assert f(a + 1, 2, 64, 64, a, 1e-5, a, 64, None) == ALIGN
 
 
+def test_swiglu_quant_rejections():
+    """Fused SwiGLU + quantization: every check before any HIP call."""
+    L = comet.lib()
+    a = 4096
+    for f in (L.comet_swiglu_quant_act, L.comet_swiglu_quant_act_fp6):
+        ok = (a, a, 4, 256, 512, a, 1, a, a, None)
+        def call(**kw):
+            args = list(ok)
+            for i, v in kw.items():
+                args[int(i[1:])] = v
+            return f(*args)
+        for i in (0, 1, 5, 7, 8):
+            assert call(**{f"a{i}": None}) == NULL, i
+        assert call(a2=0) == SHAPE and call(a3=200) == SHAPE and call(a3=0) == SHAPE and call(a4=255) == SHAPE
+        assert call(a6=3) == ARG and call(a6=-1) == ARG
+        assert call(a0=a + 2) == ALIGN and call(a1=a + 8) == ALIGN and call(a7=a + 4) == ALIGN
+
+
+def test_swiglu_rejections():
+    L = comet.lib()
+    a = 4096
+    f = L.comet_swiglu
+    assert f(None, a, 2, 64, 64, a, 64, None) == NULL
+    assert f(a, None, 2, 64, 64, a, 64, None) == NULL
+    assert f(a, a, 2, 64, 64, None, 64, None) == NULL
+    assert f(a, a, 0, 64, 64, a, 64, None) == SHAPE
+    assert f(a, a, 2, 0, 64, a, 64, None) == SHAPE
+    assert f(a, a, 2, 64, 63, a, 64, None) == SHAPE
+    assert f(a, a, 2, 64, 64, a, 63, None) == SHAPE
+    assert f(a + 1, a, 2, 64, 64, a, 64, None) == ALIGN
+    assert f(a, a + 1, 2, 64, 64, a, 64, None) == ALIGN
+    assert f(a, a, 2, 64, 64, a + 1, 64, None) == ALIGN
+
+
 def test_permute_channels():
     v = (np.arange(300, dtype=np.uint16) * 7) % 65000
     perm = np.random.default_rng(3).permutation(300).astype(np.int32)

@@ -62,13 +62,17 @@ def lib() -> ctypes.CDLL:
     L.comet_rmsnorm_quant_act_fp6.argtypes = [P, I, I, I, P, F, P, I, P, P, P]
     L.comet_rmsnorm.argtypes = [P, I, I, I, P, F, P, I, P]
     L.comet_permute_channels.argtypes = [P, P, I, P]
+    L.comet_swiglu_quant_act.argtypes = [P, P, I, I, I, P, I, P, P, P]
+    L.comet_swiglu_quant_act_fp6.argtypes = [P, P, I, I, I, P, I, P, P, P]
+    L.comet_swiglu.argtypes = [P, P, I, I, I, P, I, P]
     L.comet_status_string.argtypes = [I]
     L.comet_status_string.restype = ctypes.c_char_p
     L.comet_version.restype = ctypes.c_char_p
     for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
               "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
               "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_rmsnorm_quant_act",
-              "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels"):
+              "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels",
+              "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -79,7 +83,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_xq_fp6_bytes", "comet_wq_fp6_bytes", "comet_repack_weights_fp6",
            "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
            "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
-           "comet_permute_channels", "comet_status_string", "comet_version")
+           "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
+           "comet_status_string", "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -232,6 +237,41 @@ def comet_rmsnorm(X, gamma, eps: float, K: int | None = None, Xn=None, stream=No
                              Xn.stride(0), _stream(stream))
     _check("comet_rmsnorm", rc)
     return Xn
+
+
+def comet_swiglu_quant_act(gate, up, perm, nb8: int, Xq=None, x_scale=None, fp6=False, stream=None):
+    """SwiGLU fused into the quantizer (either layout). gate, up: fp16 cuda tensors [M, K] (views
+    with one common row stride, e.g. the two halves of a [M, 2K] projection output)."""
+    import torch
+    M = gate.shape[0]
+    K = perm.shape[0]
+    if tuple(up.shape) != tuple(gate.shape) or up.stride(0) != gate.stride(0):
+        raise ValueError("gate and up must have the same shape and row stride")
+    if Xq is None:
+        n = xq_fp6_bytes(M, K, nb8) if fp6 else xq_bytes(M, K, nb8)
+        Xq = torch.empty(n, dtype=torch.uint8, device=gate.device)
+    if x_scale is None:
+        x_scale = torch.empty((K // 128, M), dtype=torch.float32, device=gate.device)
+    call = "comet_swiglu_quant_act_fp6" if fp6 else "comet_swiglu_quant_act"
+    rc = getattr(lib(), call)(_dev_ptr(gate), _dev_ptr(up), M, K, gate.stride(0), _dev_ptr(perm), int(nb8),
+                              _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
+    _check(call, rc)
+    return Xq, x_scale
+
+
+def comet_swiglu(gate, up, K: int | None = None, H=None, stream=None):
+    """The SwiGLU on its own: fp16 [M, K] = fp16(silu(gate) up), original channel order."""
+    import torch
+    M, ld = gate.shape
+    K = ld if K is None else K
+    if up.stride(0) != gate.stride(0):
+        raise ValueError("gate and up must share their row stride")
+    if H is None:
+        H = torch.empty((M, K), dtype=torch.float16, device=gate.device)
+    rc = lib().comet_swiglu(_dev_ptr(gate), _dev_ptr(up), M, K, gate.stride(0), _dev_ptr(H), H.stride(0),
+                            _stream(stream))
+    _check("comet_swiglu", rc)
+    return H
 
 
 def workspace_bytes(M: int, N: int, K: int, nb8: int) -> int:

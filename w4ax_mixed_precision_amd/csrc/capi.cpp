@@ -47,6 +47,16 @@ int check_rmsnorm_quant(const void* X, int M, int K, int ldx, const void* gamma_
     return COMET_OK;
 }
 
+int check_swiglu_quant(const void* G, const void* U, int M, int K, int ldx, const int32_t* perm, int nb8,
+                       const void* Xq, const float* x_scale) {
+    if (!G || !U || !perm || !Xq || !x_scale) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (nb8 < 0 || nb8 > K / kBlock) return COMET_ERR_ARG;
+    if (!aligned16(G) || !aligned16(U) || !aligned16(perm) || !aligned16(Xq) || !aligned16(x_scale))
+        return COMET_ERR_ALIGN;
+    return COMET_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +226,39 @@ int comet_rmsnorm(const void* X_fp16, int M, int K, int ldx, const void* gamma_f
     return hip_status(comet::launch_rmsnorm(static_cast<const uint16_t*>(X_fp16), M, K, ldx,
                                             static_cast<const uint16_t*>(gamma_fp16), eps,
                                             static_cast<uint16_t*>(Xn_fp16), ldn, stream));
+}
+
+int comet_swiglu_quant_act(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx, const int32_t* perm,
+                           int n_int8_blocks, void* Xq, float* x_scale, void* stream) {
+    const int st = check_swiglu_quant(gate_fp16, up_fp16, M, K, ldx, perm, n_int8_blocks, Xq, x_scale);
+    if (st != COMET_OK) return st;
+    return hip_status(comet::launch_swiglu_quant_act(static_cast<const uint16_t*>(gate_fp16),
+                                                     static_cast<const uint16_t*>(up_fp16), M, K, ldx, perm,
+                                                     n_int8_blocks, static_cast<uint8_t*>(Xq), x_scale, false,
+                                                     stream));
+}
+
+int comet_swiglu_quant_act_fp6(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx,
+                               const int32_t* perm, int n_int8_blocks, void* Xq_fp6, float* x_scale,
+                               void* stream) {
+    const int st = check_swiglu_quant(gate_fp16, up_fp16, M, K, ldx, perm, n_int8_blocks, Xq_fp6, x_scale);
+    if (st != COMET_OK) return st;
+    return hip_status(comet::launch_swiglu_quant_act(static_cast<const uint16_t*>(gate_fp16),
+                                                     static_cast<const uint16_t*>(up_fp16), M, K, ldx, perm,
+                                                     n_int8_blocks, static_cast<uint8_t*>(Xq_fp6), x_scale, true,
+                                                     stream));
+}
+
+int comet_swiglu(const void* gate_fp16, const void* up_fp16, int M, int K, int ldx, void* H_fp16, int ldh,
+                 void* stream) {
+    if (!gate_fp16 || !up_fp16 || !H_fp16) return COMET_ERR_NULL;
+    if (M < 1 || K < 1 || ldx < K || ldh < K) return COMET_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(gate_fp16) | reinterpret_cast<uintptr_t>(up_fp16) |
+         reinterpret_cast<uintptr_t>(H_fp16)) & 1u)
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_swiglu(static_cast<const uint16_t*>(gate_fp16),
+                                           static_cast<const uint16_t*>(up_fp16), M, K, ldx,
+                                           static_cast<uint16_t*>(H_fp16), ldh, stream));
 }
 
 int comet_permute_channels(const uint16_t* v, const int32_t* perm, int K, uint16_t* out) {

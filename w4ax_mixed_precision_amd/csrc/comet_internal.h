@@ -36,6 +36,11 @@ int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t
 // RMS normalization fused into the quantizer (either layout), and on its own.
 int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma_perm, float eps,
                              const int32_t* perm, int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream);
+// SwiGLU before the quantizer (fused) and on its own: H = fp16(silu(G) U).
+int launch_swiglu_quant_act(const uint16_t* G, const uint16_t* U, int M, int K, int ldx, const int32_t* perm,
+                            int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream);
+int launch_swiglu(const uint16_t* G, const uint16_t* U, int M, int K, int ldx, uint16_t* H, int ldh,
+                  void* stream);
 int launch_rmsnorm(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma, float eps, uint16_t* Xn,
                    int ldn, void* stream);
 

@@ -40,6 +40,15 @@
 // the 8 (virtual) waves meet at the barrier the row needs anyway. Every kernel
 // here forms S the same way, so the fused codes equal those of normalizing
 // first and quantizing after.
+//
+// The same kernels also fuse the SwiGLU before the down projection (QoQ/QServe
+// article, section "运行时设计": the quantization of the second FFN layer's
+// input is fused into the activation kernel before it; QUIK blog, section
+// "案例研究: 敏感的 LLaMA-2 Down-Projection 层": the down projection takes the
+// element-wise product of the gate and up projections). The gate and up rows
+// are both staged, and each gathered channel becomes h = fp16(silu(g) u), the
+// exact value rounded once (evaluated in binary64, see silu_mul_bits), so the
+// fused codes equal those of comet_swiglu followed by the quantizer.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -127,14 +136,49 @@ __device__ __forceinline__ void wave_sums(const uint16_t* row, int K, double* re
     }
 }
 
+// binary16 nearest to a binary64 value (ties to even). The binary64 value is
+// first rounded to binary32 with round-to-odd (nearest, then the odd
+// neighbour if that was inexact and even): binary32 keeps 13 more significand
+// bits than binary16 and the odd last bit records whether anything was cut, so
+// the second rounding decides ties and near-ties as a direct one would.
+__device__ __forceinline__ uint16_t half_of_double(double v) {
+    float f = static_cast<float>(v);
+    if (static_cast<double>(f) != v) {
+        uint32_t b = __float_as_uint(f);
+        if ((b & 1u) == 0u) b = __builtin_fabs(static_cast<double>(f)) < __builtin_fabs(v) ? b + 1u : b - 1u;
+        f = __uint_as_float(b);
+    }
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+// h = fp16(silu(g) u) with silu(g) = g / (1 + e^-g): sigma(g) = n / (1 + e)
+// with e = e^-|g| and n = 1 (g >= 0) or e (g < 0), which never overflows; g u
+// is exact in binary64 (22 significand bits). The binary64 value is within a
+// few units in its last place of the exact one, far inside the binary16
+// rounding margin except at an exact tie. Ties arise only when sigma rounds to
+// 1 (g > 36) and g u sits on a binary16 midpoint; the true value is then just
+// below |g u|, so the next binary64 value toward zero stands in for it.
+__device__ __forceinline__ uint16_t silu_mul_bits(uint16_t gb, uint16_t ub) {
+    const double g = h2f(gb), u = h2f(ub);
+    const double e = exp(-__builtin_fabs(g));
+    const double sigma = (g >= 0.0 ? 1.0 : e) / (1.0 + e);
+    const double gu = g * u;
+    double v = gu * sigma;
+    if (sigma == 1.0 && gu != 0.0) v = __longlong_as_double(__double_as_longlong(gu) - 1);
+    return half_of_double(v);
+}
+
 // Codes and scale of block b of row m for this lane's group g, from the row
 // (LDS or global) and the lane's 32 channels `pos`. With kNorm each gathered
-// value first becomes fp16((x rs) gamma), gamma in permuted order (`gperm`).
-template <bool kFp6, bool kNorm = false>
+// value first becomes fp16((x rs) gamma), gamma in permuted order (`gperm`);
+// with kSwi `row` is the gate row and each value is fp16(silu(g) u) with u
+// from the up row `row_u`.
+template <bool kFp6, bool kNorm = false, bool kSwi = false>
 __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, const int4 (&pos)[8], int b, int nb,
                                            int nb4, int M, int Mp, int m, int g, uint8_t* __restrict__ Xq,
                                            float* __restrict__ x_scale, float rs = 0.0f,
-                                           const uint16_t* __restrict__ gperm = nullptr) {
+                                           const uint16_t* __restrict__ gperm = nullptr,
+                                           const uint16_t* __restrict__ row_u = nullptr) {
     const bool valid = b < nb;
     const int bc = valid ? b : nb - 1;
     const bool is8 = bc >= nb4;
@@ -143,7 +187,15 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
     for (int k = 0; k < 8; ++k) {
         const int idx[4] = {pos[k].x, pos[k].y, pos[k].z, pos[k].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * k + e] = h2f(row[idx[e]]);
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (kSwi) {
+                v[4 * k + e] = h2f(silu_mul_bits(row[idx[e]], row_u[idx[e]]));   // gate row, up row
+                // one value at a time: interleaving 32 binary64 evaluations
+                // runs out of registers
+                __builtin_amdgcn_sched_barrier(0);
+            } else
+                v[4 * k + e] = h2f(row[idx[e]]);
+        }
     }
     if constexpr (kNorm) {
         // the lane's 32 gamma values are contiguous in permuted order
@@ -235,11 +287,11 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
     }
 }
 
-template <bool kRowInLds, bool kFp6, bool kNorm>
+template <bool kRowInLds, bool kFp6, bool kNorm, bool kSwi = false>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
     int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd,
-    const uint16_t* __restrict__ gperm, float eps) {
+    const uint16_t* __restrict__ gperm, float eps, const uint16_t* __restrict__ U = nullptr) {
     extern __shared__ uint16_t row_lds[];
     // Row of this workgroup. Workgroup w runs on XCD w mod 8 and each XCD has
     // its own L2; with `rows_per_xcd` > 0 every XCD takes a contiguous range
@@ -251,11 +303,15 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
         if (m >= M) return;
     }
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
+    const uint16_t* ur = kSwi ? U + static_cast<size_t>(m) * ldx : nullptr;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // whole 1 KB direct-load chunks of one staged row; with kSwi the up row
+    // follows the gate row
+    const size_t row_bytes = static_cast<size_t>((K + 511) / 512) * 1024;
+    uint16_t* up_lds = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(row_lds) + row_bytes);
     // the row statistic's 8 wave sums (kNorm) follow the staged row
-    double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) +
-                                            (kRowInLds ? static_cast<size_t>((K + 511) / 512) * 1024 : 0));
+    double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) + (kRowInLds ? row_bytes : 0));
     bool sums_done = false;
     if constexpr (kRowInLds) {
         if ((ldx & 7) == 0) {
@@ -266,12 +322,20 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
             const int chunks = (K + 511) / 512;
             uint8_t* lds = reinterpret_cast<uint8_t*>(row_lds);
             for (int c = wave; c < chunks; c += kWaves) lds_buf16(r, 16u * lane, 1024u * c, lds + 1024 * c);
+            if constexpr (kSwi) {
+                const Rsrc ru = make_rsrc(ur, 2u * static_cast<uint32_t>(K));
+                uint8_t* ul = reinterpret_cast<uint8_t*>(up_lds);
+                for (int c = wave; c < chunks; c += kWaves) lds_buf16(ru, 16u * lane, 1024u * c, ul + 1024 * c);
+            }
             COMET_VMCNT(0);
             // this wave's chunks have landed: its wave sums need no barrier
             if constexpr (kNorm) wave_sums<kThreads>(row_lds, K, red);
             sums_done = true;
         } else {
-            for (int c = threadIdx.x; c < K; c += kThreads) row_lds[c] = xr[c];
+            for (int c = threadIdx.x; c < K; c += kThreads) {
+                row_lds[c] = xr[c];
+                if constexpr (kSwi) up_lds[c] = ur[c];
+            }
         }
         __syncthreads();
     }
@@ -297,8 +361,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) pos[k] = nxt[k];
         if (b0 + stride < nb) load_positions(perm, imin(b0 + stride + bl, nb - 1), g, nxt);
-        code_block<kFp6, kNorm>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale, rs,
-                                gperm);
+        code_block<kFp6, kNorm, kSwi>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale,
+                                      rs, gperm, kRowInLds ? up_lds : ur);
     }
 }
 
@@ -413,9 +477,9 @@ hipError_t allow_lds(int bytes) {
     return attr;
 }
 
-template <bool kFp6, bool kNorm>
+template <bool kFp6, bool kNorm, bool kSwi = false>
 int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8, uint8_t* Xq,
-           float* x_scale, const uint16_t* gperm, float eps, void* stream) {
+           float* x_scale, const uint16_t* gperm, float eps, void* stream, const uint16_t* U = nullptr) {
     const int nb = K / kBlock;
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
@@ -431,24 +495,32 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t red = kNorm ? 16 * sizeof(double) : 0;    // wave sums of the row statistic
     const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
-    if (M >= 256 && K <= kMaxLdsRowChannels && (ldx & 7) == 0) {
-        // the two row buffers (and the partials) may exceed the 64 KB default
-        const hipError_t attr = allow_lds<&quant_rows_kernel<kFp6, kNorm>>(160 * 1024);
-        if (attr != hipSuccess) return static_cast<int>(attr);
-        const int wgs_per_xcd = cu_count() / 8;
-        const int rows_per_xcd = ((M + 127) / 128) * 16;
-        quant_rows_kernel<kFp6, kNorm><<<8 * wgs_per_xcd, kRowThreads, 2 * row_lds + red, s>>>(
-            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, wgs_per_xcd, gperm, eps);
-        return static_cast<int>(hipGetLastError());
+    const size_t buf = (kSwi ? 2 : 1) * row_lds;                          // one row, or gate and up rows
+    constexpr size_t kLds = 160 * 1024;
+    // (the SwiGLU form stays on the per-row kernel: with its binary64
+    // evaluation on top of the perm entries held in registers, the persistent
+    // kernel runs out of registers)
+    if constexpr (!kSwi) {
+        if (M >= 256 && K <= kMaxLdsRowChannels && 2 * buf + red <= kLds && (ldx & 7) == 0) {
+            // the two row buffers (and the wave sums) may exceed the 64 KB
+            // default; the kernel's 256 blocks per row cover K <= 32768
+            const hipError_t attr = allow_lds<&quant_rows_kernel<kFp6, kNorm>>(kLds);
+            if (attr != hipSuccess) return static_cast<int>(attr);
+            const int wgs_per_xcd = cu_count() / 8;
+            const int rows_per_xcd = ((M + 127) / 128) * 16;
+            quant_rows_kernel<kFp6, kNorm><<<8 * wgs_per_xcd, kRowThreads, 2 * buf + red, s>>>(
+                X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, wgs_per_xcd, gperm, eps);
+            return static_cast<int>(hipGetLastError());
+        }
     }
     if (K <= kMaxLdsRowChannels) {
-        const hipError_t attr = allow_lds<&quant_act_kernel<true, kFp6, kNorm>>(160 * 1024);
+        const hipError_t attr = allow_lds<&quant_act_kernel<true, kFp6, kNorm, kSwi>>(kLds);
         if (attr != hipSuccess) return static_cast<int>(attr);
-        quant_act_kernel<true, kFp6, kNorm><<<grid, kThreads, row_lds + red, s>>>(X, M, K, ldx, perm, nb, nb4, Xq,
-                                                                                x_scale, rows_per_xcd, gperm, eps);
+        quant_act_kernel<true, kFp6, kNorm, kSwi><<<grid, kThreads, buf + red, s>>>(
+            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, gperm, eps, U);
     } else {
-        quant_act_kernel<false, kFp6, kNorm><<<grid, kThreads, red, s>>>(X, M, K, ldx, perm, nb, nb4, Xq, x_scale,
-                                                                       rows_per_xcd, gperm, eps);
+        quant_act_kernel<false, kFp6, kNorm, kSwi><<<grid, kThreads, red, s>>>(
+            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, gperm, eps, U);
     }
     return static_cast<int>(hipGetLastError());
 }
@@ -472,6 +544,38 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* _
         const float t = h2f(xr[k]) * rs;
         out[k] = __half_as_ushort(__float2half_rn(opaque(t * h2f(gamma[k]))));
     }
+}
+
+// Standalone SwiGLU (the unfused step): H = fp16(silu(G) U) element-wise, one
+// workgroup of 256 threads per row, 8 consecutive channels per thread when
+// every row start is 16-byte aligned.
+constexpr int kSwiThreads = 256;
+
+__global__ __launch_bounds__(kSwiThreads) void swiglu_kernel(const uint16_t* __restrict__ G,
+                                                             const uint16_t* __restrict__ U, int K, int ldx,
+                                                             uint16_t* __restrict__ H, int ldh, int vec) {
+    const size_t m = blockIdx.x;
+    const uint16_t* gr = G + m * ldx;
+    const uint16_t* ur = U + m * ldx;
+    uint16_t* hr = H + m * ldh;
+    int k0 = 0;
+    if (vec) {
+        for (int k = 8 * threadIdx.x; k + 8 <= K; k += 8 * kSwiThreads) {
+            const uint4 gq = *reinterpret_cast<const uint4*>(gr + k);
+            const uint4 uq = *reinterpret_cast<const uint4*>(ur + k);
+            const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
+            uint32_t hw[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = silu_mul_bits(static_cast<uint16_t>(gw[d]), static_cast<uint16_t>(uw[d]));
+                const uint32_t hi = silu_mul_bits(static_cast<uint16_t>(gw[d] >> 16), static_cast<uint16_t>(uw[d] >> 16));
+                hw[d] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4*>(hr + k) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+        k0 = K & ~7;
+    }
+    for (int k = k0 + threadIdx.x; k < K; k += kSwiThreads) hr[k] = silu_mul_bits(gr[k], ur[k]);
 }
 
 }  // namespace
@@ -501,6 +605,20 @@ int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uin
                              const int32_t* perm, int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream) {
     return fp6 ? launch<true, true>(X, M, K, ldx, perm, nb8, Xq, x_scale, gamma_perm, eps, stream)
                : launch<false, true>(X, M, K, ldx, perm, nb8, Xq, x_scale, gamma_perm, eps, stream);
+}
+
+int launch_swiglu_quant_act(const uint16_t* G, const uint16_t* U, int M, int K, int ldx, const int32_t* perm,
+                            int nb8, uint8_t* Xq, float* x_scale, bool fp6, void* stream) {
+    return fp6 ? launch<true, false, true>(G, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream, U)
+               : launch<false, false, true>(G, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream, U);
+}
+
+int launch_swiglu(const uint16_t* G, const uint16_t* U, int M, int K, int ldx, uint16_t* H, int ldh,
+                  void* stream) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(G) | reinterpret_cast<uintptr_t>(U) |
+                       reinterpret_cast<uintptr_t>(H)) & 15u) == 0 && (ldx & 7) == 0 && (ldh & 7) == 0;
+    swiglu_kernel<<<M, kSwiThreads, 0, static_cast<hipStream_t>(stream)>>>(G, U, K, ldx, H, ldh, vec ? 1 : 0);
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_rmsnorm(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma, float eps, uint16_t* Xn,
