@@ -220,6 +220,60 @@ def run_gpu(layers, steps, warmup, torch, comet):
     return step_ms, per
 
 
+def _time_variants(torch, variants, iters):
+    """Mean microseconds per call of each (name, fn): HIP events on the launch
+    stream around `iters` back-to-back calls, after 3 untimed ones."""
+    res = {}
+    for name, fn in variants:
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / iters
+    return res
+
+
+def swiglu_ablation(torch, comet, synth, M=4096, K=28672, nb8=67, iters=10):
+    """The quantizer fused into the SwiGLU before it, against the two steps
+    apart (comet_swiglu, then comet_quant_act_fp6), at the 70B down-projection
+    input (4096 tokens x 28672 channels; gate and up as the two halves of one
+    [M, 2K] projection output)."""
+    cfg = synth.LayerConfig("swiglu_quant_70b", M, K, 128, 29)
+    g16, u16 = synth.make_gate_up(cfg)
+    gu = torch.empty((M, 2 * K), dtype=torch.float16, device="cuda")
+    gu[:, :K] = torch.from_numpy(g16.view(np.float16)).cuda()
+    gu[:, K:] = torch.from_numpy(u16.view(np.float16)).cuda()
+    del g16, u16
+    gate, up = gu[:, :K], gu[:, K:]
+    perm = np.random.default_rng(29).permutation(K).astype(np.int32)   # any permutation serves for timing
+    pd = torch.from_numpy(perm).cuda()
+    H = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    Xq = torch.empty(comet.xq_fp6_bytes(M, K, nb8), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+
+    def unfused():
+        comet.comet_swiglu(gate, up, K=K, H=H)
+        comet.comet_quant_act_fp6(H, pd, nb8, Xq=Xq, x_scale=xs)
+
+    def fused():
+        comet.comet_swiglu_quant_act(gate, up, pd, nb8, Xq=Xq, x_scale=xs, fp6=True)
+
+    res = _time_variants(torch, (("unfused", unfused), ("fused", fused)), iters)
+    codes = M * (96 * (K // 128 - nb8) + 128 * nb8) + 4 * M * (K // 128)
+    hbytes = 2 * M * K
+    return {"shape": {"M": M, "K": K, "int8_blocks": nb8, "layout": "fp6"},
+            "unfused_us": res["unfused"], "fused_us": res["fused"],
+            "speedup": res["unfused"] / res["fused"],
+            "hbm_bytes_unfused": 4 * hbytes + codes, "hbm_bytes_fused": 2 * hbytes + codes,
+            "fused_gbs": (2 * hbytes + codes) / (res["fused"] * 1e-6) / 1e9,
+            "timing": f"HIP events around {iters} back-to-back iterations of each variant"}
+
+
 def fusion_ablation(torch, comet, synth, M=4096, K=8192, nb8=7, iters=20):
     """The quantizer fused into the RMS normalization before it, against the two
     steps apart (comet_rmsnorm, then comet_quant_act_fp6), at the 70B up/gate
@@ -245,18 +299,7 @@ def fusion_ablation(torch, comet, synth, M=4096, K=8192, nb8=7, iters=20):
     def fused():
         comet.comet_rmsnorm_quant_act(X, gperm, 1e-5, pd, nb8, Xq=Xq, x_scale=xs, fp6=True)
 
-    res = {}
-    for name, fn in (("unfused", unfused), ("fused", fused)):
-        for _ in range(3):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        res[name] = a.elapsed_time(b) * 1e3 / iters
+    res = _time_variants(torch, (("unfused", unfused), ("fused", fused)), iters)
     codes = M * (96 * (K // 128 - nb8) + 128 * nb8) + 4 * M * (K // 128)
     xbytes = 2 * M * K
     return {"shape": {"M": M, "K": K, "int8_blocks": nb8, "layout": "fp6"},
@@ -369,6 +412,7 @@ def main():
             "weight_copies": len(l.w)}
 
     fusion = fusion_ablation(torch, comet, synth) if args.workload == "prefill_70b" else None
+    swi = swiglu_ablation(torch, comet, synth) if args.workload == "prefill_70b" else None
 
     cpu = None
     if not args.no_cpu:
@@ -390,6 +434,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "norm_quant_fusion": fusion,
+        "swiglu_quant_fusion": swi,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

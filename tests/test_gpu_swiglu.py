@@ -90,11 +90,39 @@ def test_swiglu_large_gates_and_ties(torch):
     assert np.array_equal(H.cpu().numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("uval", [1.0, -3.0, 0.7109375, 61.0])
+def test_swiglu_every_gate_value(torch, uval):
+    """Every finite fp16 gate value against one up value: the binary32 test
+    and the binary64 fix-up together give the oracle's bits for the whole gate
+    domain (the binary32 error bound depends on g only)."""
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    g = np.concatenate([np.arange(0, 0x7C00, dtype=np.uint16), np.arange(0x8000, 0xFC00, dtype=np.uint16)])
+    gv = g.view(np.float16).astype(np.float64)
+    keep = np.abs(gv * uval) < 60000.0                      # products inside the fp16 range
+    g = g[keep][: (keep.sum() // 1024) * 1024].reshape(-1, 1024)
+    u = np.full(g.shape, np.float16(uval).view(np.uint16), np.uint16)
+    want = O.swiglu(g, u)
+    H = comet.comet_swiglu(torch.from_numpy(g.view(np.float16)).cuda(), torch.from_numpy(u.view(np.float16)).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(H.cpu().numpy().view(np.uint16), want)
+    # the fused form on the same rows (identity permutation, all 4-bit blocks):
+    # its codes equal the oracle's quantization of the oracle's rows
+    perm = np.arange(1024, dtype=np.int32)
+    qa, sa = O.quantize_activations(want, perm, np.zeros(8, np.uint8))
+    Xq, xs = comet.comet_swiglu_quant_act(torch.from_numpy(g.view(np.float16)).cuda(),
+                                          torch.from_numpy(u.view(np.float16)).cuda(),
+                                          torch.from_numpy(perm).cuda(), 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_xq(Xq.cpu().numpy(), g.shape[0], 1024, 0), qa)
+    assert np.array_equal(xs.cpu().numpy().T.view(np.uint32), sa.view(np.uint32))
+
+
 # (M, K, ldx, nb8): per-row kernel with the rows in LDS, element-wise staging
 # (ldx not a multiple of 8), rows in global memory (K > 32768), the 70B
 # down-projection width, and many rows
-CASES = [(1, 128, 256, 0), (1, 128, 256, 1), (17, 1024, 2048, 2), (9, 4096, 4100, 3), (5, 33024, 66048, 4),
-         (40, 28672, 57344, 9), (300, 2048, 4096, 1)]
+CASES = [(1, 128, 256, 0), (1, 128, 256, 1), (3, 640, 1280, 1), (17, 1024, 2048, 2), (9, 4096, 4100, 3),
+         (5, 33024, 66048, 4), (40, 28672, 57344, 9), (300, 2048, 4096, 1)]
 
 
 @pytest.mark.parametrize("fp6", [False, True])
@@ -139,3 +167,30 @@ def test_fused_swiglu_equals_unfused(torch, fp6):
         assert np.array_equal(a, b)
     else:
         assert torch.equal(Xq_u, Xq_f)
+
+
+@pytest.mark.parametrize("fp6", [False, True])
+def test_swiglu_rows_of_undecided_values(torch, fp6):
+    """A row where every value is an exact fp16 tie of g u with sigma = 1 in
+    binary32 (g = 1025, u = 3: the true value 3075 (1 - e^-1025) rounds down
+    to 3074), so the binary32 test decides none of them: more than a wave's
+    queue holds, and the rest take the binary64 form directly. A second row
+    is ordinary."""
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    M, K, nb8 = 2, 28672, 9
+    g, u, score = _inputs(M, K, seed=44)
+    g[0] = np.float16(1025.0).view(np.uint16)
+    u[0] = np.float16(3.0).view(np.uint16)
+    H = O.swiglu(g, u)
+    assert np.all(H[0] == np.float16(3074.0).view(np.uint16))
+    perm, flags = O.channel_order(score, nb8)
+    qa, sa = O.quantize_activations(H, perm, flags)
+    gd, ud = _halves(torch, g, u, 2 * K)
+    Hd = comet.comet_swiglu(gd, ud, K=K)
+    Xq, xs = comet.comet_swiglu_quant_act(gd, ud, torch.from_numpy(perm).cuda(), nb8, fp6=fp6)
+    torch.cuda.synchronize()
+    assert np.array_equal(Hd.cpu().numpy().view(np.uint16), H)
+    dec = decode_xq_fp6 if fp6 else decode_xq
+    assert np.array_equal(dec(Xq.cpu().numpy(), M, K, nb8), qa)
+    assert np.array_equal(xs.cpu().numpy().T.view(np.uint32), sa.view(np.uint32))

@@ -60,10 +60,9 @@
 namespace comet {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBlocksPerPass = kWaves * 16;      // 4 lanes per block
+constexpr int kThreads = 256;                    // per-row kernel: 4 waves, 16 blocks each per pass
 constexpr int kMaxLdsRowChannels = 32768;        // 64 KB of fp16 per staged row
+constexpr int kSwiWaveQueue = 512;               // SwiGLU fix-up queue entries per wave
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v6i __attribute__((ext_vector_type(6)));
@@ -168,6 +167,44 @@ __device__ __forceinline__ uint16_t silu_mul_bits(uint16_t gb, uint16_t ub) {
     return half_of_double(v);
 }
 
+// The same value from binary32 arithmetic when that decides it.
+//   e = e^-|g| = 2^-(n + f): n = rint(|g| log2 e), and f = |g| log2 e - n
+//       from two fused multiply-adds with log2 e split into two binary32
+//       parts (absolute error below 2^-25); 2^-f from v_exp_f32 (|f| <= 1/2,
+//       so its result is normal), then scaled by 2^-n exactly (to 0 far out,
+//       where either sigma is 1 or the product is far below the smallest
+//       fp16 value);
+//   sigma = (g >= 0 ? 1 : e) * rcp(1 + e), v = (g u) sigma, g u exact.
+// With at most 1.2 units in the last place from e, 1 from the reciprocal and
+// half a unit per rounding, v is within a relative 2^-20.4 of silu(g) u. The
+// true value then lies inside [|v| (1 - 2^-19), |v| (1 + 2^-19)] with room
+// for the rounding of those two bounds; if both round to the same fp16 value,
+// so does the true value (rounding is monotone), and the function returns
+// true with it. Otherwise (about 0.6% of inputs) the caller takes
+// silu_mul_bits.
+__device__ __forceinline__ bool silu_mul_fast(uint16_t gb, uint16_t ub, uint16_t& h) {
+    constexpr float kLog2eHi = 1.44269502162933349609375f;       // binary32 log2(e)
+    constexpr float kLog2eLo = 1.925963033500011e-08f;          // log2(e) - kLog2eHi
+    const float g = h2f(gb), u = h2f(ub);
+    const float a = __builtin_fabsf(g);
+    const float n = __builtin_rintf(a * kLog2eHi);
+    const float f = __builtin_fmaf(a, kLog2eLo, __builtin_fmaf(a, kLog2eHi, -n));
+    const float e = __builtin_ldexpf(__builtin_amdgcn_exp2f(-f), -static_cast<int>(n));
+    const float sigma = (g >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(1.0f + e);
+    const float v = (g * u) * sigma;
+    const float m = __builtin_fabsf(v);
+    const float w = m * 0x1p-19f;
+    const uint16_t lo = __half_as_ushort(__float2half_rn(m - w));
+    const uint16_t hi = __half_as_ushort(__float2half_rn(m + w));
+    h = static_cast<uint16_t>(lo | (__builtin_signbit(v) ? 0x8000u : 0u));
+    return lo == hi;
+}
+
+__device__ __forceinline__ uint16_t silu_mul_any(uint16_t gb, uint16_t ub) {
+    uint16_t h;
+    return silu_mul_fast(gb, ub, h) ? h : silu_mul_bits(gb, ub);
+}
+
 // Codes and scale of block b of row m for this lane's group g, from the row
 // (LDS or global) and the lane's 32 channels `pos`. With kNorm each gathered
 // value first becomes fp16((x rs) gamma), gamma in permuted order (`gperm`);
@@ -189,7 +226,7 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if constexpr (kSwi) {
-                v[4 * k + e] = h2f(silu_mul_bits(row[idx[e]], row_u[idx[e]]));   // gate row, up row
+                v[4 * k + e] = h2f(silu_mul_any(row[idx[e]], row_u[idx[e]]));   // gate row, up row
                 // one value at a time: interleaving 32 binary64 evaluations
                 // runs out of registers
                 __builtin_amdgcn_sched_barrier(0);
@@ -287,8 +324,8 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
     }
 }
 
-template <bool kRowInLds, bool kFp6, bool kNorm, bool kSwi = false>
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(
+template <bool kRowInLds, bool kFp6, bool kNorm, bool kSwi = false, int T = kThreads>
+__global__ __launch_bounds__(T) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
     int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd,
     const uint16_t* __restrict__ gperm, float eps, const uint16_t* __restrict__ U = nullptr) {
@@ -306,14 +343,83 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* ur = kSwi ? U + static_cast<size_t>(m) * ldx : nullptr;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // whole 1 KB direct-load chunks of one staged row; with kSwi the up row
-    // follows the gate row
+    // whole 1 KB direct-load chunks of one staged row
     const size_t row_bytes = static_cast<size_t>((K + 511) / 512) * 1024;
-    uint16_t* up_lds = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(row_lds) + row_bytes);
-    // the row statistic's 8 wave sums (kNorm) follow the staged row
+    // the row statistic's 8 wave sums (kNorm), or the SwiGLU fix-up queue
+    // (kSwi), follow the staged row
     double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) + (kRowInLds ? row_bytes : 0));
     bool sums_done = false;
-    if constexpr (kRowInLds) {
+    if constexpr (kRowInLds && kSwi) {
+        // The staged row is h itself: every thread forms 8 consecutive values
+        // per step from coalesced gate and up loads with the binary32 test.
+        // The channels it cannot decide go to its wave's queue (a ballot
+        // gives each flagged lane its slot; once the queue is full, straight
+        // to the binary64 form), which the wave then clears itself.
+        int* queue = reinterpret_cast<int*>(red) + wave * kSwiWaveQueue;
+        int qcount = 0;                                   // wave-uniform
+        const bool vec = ((reinterpret_cast<uintptr_t>(xr) | reinterpret_cast<uintptr_t>(ur)) & 15u) == 0;
+        // Every lane of a wave calls put for each step (the ballot and the
+        // queue count stay wave-uniform); lanes past the row end pass
+        // valid = false.
+        auto put = [&](int k, uint16_t gb, uint16_t ub, bool valid) {
+            uint16_t h = 0;
+            const bool bad = valid && !silu_mul_fast(gb, ub, h);
+            const uint64_t mask = __ballot(bad);
+            if (mask) {
+                const int slot = qcount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                              static_cast<uint32_t>(mask >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+                if (bad) {
+                    if (slot < kSwiWaveQueue) queue[slot] = k;
+                    else h = silu_mul_bits(gb, ub);
+                }
+                qcount += __popcll(mask);
+            }
+            if (valid) row_lds[k] = h;
+        };
+        auto put8 = [&](int k0, const uint4& gq, const uint4& uq, bool valid) {
+            const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                put(k0 + e, static_cast<uint16_t>(gw[e >> 1] >> (16 * (e & 1))),
+                    static_cast<uint16_t>(uw[e >> 1] >> (16 * (e & 1))), valid);
+        };
+        constexpr int kStep = 8 * T;
+        if (vec) {
+            // K is a multiple of 128, so every 8-channel step is whole. Two
+            // register sets take turns: one step is coded while the loads of
+            // the next are in flight (past the row end the loads repeat the
+            // last step, in bounds, and are not used).
+            auto ld = [&](int k, uint4& gq, uint4& uq) {
+                const int kk = imin(k, K - 8);
+                gq = *reinterpret_cast<const uint4*>(xr + kk);
+                uq = *reinterpret_cast<const uint4*>(ur + kk);
+            };
+            const int t8 = 8 * static_cast<int>(threadIdx.x);
+            uint4 ga, ua, gb, ub;
+            ld(t8, ga, ua);
+            for (int base = 0; base < K; base += 2 * kStep) {          // uniform trip count
+                ld(base + kStep + t8, gb, ub);
+                put8(base + t8, ga, ua, base + t8 < K);
+                ld(base + 2 * kStep + t8, ga, ua);
+                put8(base + kStep + t8, gb, ub, base + kStep + t8 < K);
+            }
+        } else {
+            for (int base = 0; base < K; base += T) {
+                const int k = base + static_cast<int>(threadIdx.x);
+                const bool valid = k < K;
+                put(k, valid ? xr[k] : uint16_t(0), valid ? ur[k] : uint16_t(0), valid);
+            }
+        }
+        // this wave's undecided channels (LDS operations of one wave complete
+        // in order, so these writes land after its binary32 ones)
+        const int n = imin(qcount, kSwiWaveQueue);
+        for (int i = lane; i < n; i += 64) {
+            const int k = queue[i];
+            row_lds[k] = silu_mul_bits(xr[k], ur[k]);
+        }
+        __syncthreads();
+    } else if constexpr (kRowInLds) {
         if ((ldx & 7) == 0) {
             // direct loads of the row: 1 KB per wave instruction, all in flight
             // at once; the LDS row buffer is rounded up to whole KB and the
@@ -321,28 +427,20 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
             const Rsrc r = make_rsrc(xr, 2u * static_cast<uint32_t>(K));
             const int chunks = (K + 511) / 512;
             uint8_t* lds = reinterpret_cast<uint8_t*>(row_lds);
-            for (int c = wave; c < chunks; c += kWaves) lds_buf16(r, 16u * lane, 1024u * c, lds + 1024 * c);
-            if constexpr (kSwi) {
-                const Rsrc ru = make_rsrc(ur, 2u * static_cast<uint32_t>(K));
-                uint8_t* ul = reinterpret_cast<uint8_t*>(up_lds);
-                for (int c = wave; c < chunks; c += kWaves) lds_buf16(ru, 16u * lane, 1024u * c, ul + 1024 * c);
-            }
+            for (int c = wave; c < chunks; c += T / 64) lds_buf16(r, 16u * lane, 1024u * c, lds + 1024 * c);
             COMET_VMCNT(0);
             // this wave's chunks have landed: its wave sums need no barrier
-            if constexpr (kNorm) wave_sums<kThreads>(row_lds, K, red);
+            if constexpr (kNorm) wave_sums<T>(row_lds, K, red);
             sums_done = true;
         } else {
-            for (int c = threadIdx.x; c < K; c += kThreads) {
-                row_lds[c] = xr[c];
-                if constexpr (kSwi) up_lds[c] = ur[c];
-            }
+            for (int c = threadIdx.x; c < K; c += T) row_lds[c] = xr[c];
         }
         __syncthreads();
     }
     float rs = 0.0f;
     if constexpr (kNorm) {
         if (!sums_done) {
-            wave_sums<kThreads>(kRowInLds ? row_lds : xr, K, red);
+            wave_sums<T>(kRowInLds ? row_lds : xr, K, red);
             __syncthreads();
         }
         rs = rms_from_waves(red, K, eps);
@@ -351,9 +449,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
     const int g = lane & 3;               // the lane's 32-channel group
     const int bl = lane >> 2;             // its block among the wave's 16
-    const int stride = gridDim.y * kBlocksPerPass;
+    const int stride = gridDim.y * (T / 64) * 16;
 
-    int b0 = (blockIdx.y * kWaves + wave) * 16;
+    int b0 = (blockIdx.y * (T / 64) + wave) * 16;
     int4 nxt[8];
     if (b0 < nb) load_positions(perm, imin(b0 + bl, nb - 1), g, nxt);
     for (; b0 < nb; b0 += stride) {
@@ -361,8 +459,10 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) pos[k] = nxt[k];
         if (b0 + stride < nb) load_positions(perm, imin(b0 + stride + bl, nb - 1), g, nxt);
-        code_block<kFp6, kNorm, kSwi>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale,
-                                      rs, gperm, kRowInLds ? up_lds : ur);
+        // from the staged h row, or (rows in global memory) from the gate and
+        // up rows with h formed per gathered channel
+        code_block<kFp6, kNorm, kSwi && !kRowInLds>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g,
+                                                    Xq, x_scale, rs, gperm, ur);
     }
 }
 
@@ -484,7 +584,10 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
     // blocks of a row over gridDim.y workgroups (each stages the whole row).
-    const int per_wg = kBlocksPerPass;                      // blocks per workgroup pass
+    // the SwiGLU form stages h with 8 waves per workgroup (its evaluation
+    // wants the latency cover); the others with 4
+    constexpr int T = kSwi ? 512 : kThreads;
+    const int per_wg = (T / 64) * 16;                       // blocks per workgroup pass
     int groups = 1;
     const int want = 1024;
     while (groups * per_wg < nb && static_cast<long>(M) * groups < want) ++groups;
@@ -493,9 +596,10 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     const int rows_per_xcd = M >= 128 ? ((M + 127) / 128) * 16 : 0;
     dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t red = kNorm ? 16 * sizeof(double) : 0;    // wave sums of the row statistic
+    // wave sums of the row statistic, or the SwiGLU fix-up queue and its count
+    const size_t red = kNorm ? 16 * sizeof(double) : kSwi ? (T / 64) * kSwiWaveQueue * sizeof(int) : 0;
     const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
-    const size_t buf = (kSwi ? 2 : 1) * row_lds;                          // one row, or gate and up rows
+    const size_t buf = row_lds;
     constexpr size_t kLds = 160 * 1024;
     // (the SwiGLU form stays on the per-row kernel: with its binary64
     // evaluation on top of the perm entries held in registers, the persistent
@@ -514,12 +618,12 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
         }
     }
     if (K <= kMaxLdsRowChannels) {
-        const hipError_t attr = allow_lds<&quant_act_kernel<true, kFp6, kNorm, kSwi>>(kLds);
+        const hipError_t attr = allow_lds<&quant_act_kernel<true, kFp6, kNorm, kSwi, T>>(kLds);
         if (attr != hipSuccess) return static_cast<int>(attr);
-        quant_act_kernel<true, kFp6, kNorm, kSwi><<<grid, kThreads, buf + red, s>>>(
+        quant_act_kernel<true, kFp6, kNorm, kSwi, T><<<grid, T, buf + red, s>>>(
             X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, gperm, eps, U);
     } else {
-        quant_act_kernel<false, kFp6, kNorm, kSwi><<<grid, kThreads, red, s>>>(
+        quant_act_kernel<false, kFp6, kNorm, kSwi, T><<<grid, T, kNorm ? red : 0, s>>>(
             X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, gperm, eps, U);
     }
     return static_cast<int>(hipGetLastError());
@@ -567,15 +671,15 @@ __global__ __launch_bounds__(kSwiThreads) void swiglu_kernel(const uint16_t* __r
             uint32_t hw[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint32_t lo = silu_mul_bits(static_cast<uint16_t>(gw[d]), static_cast<uint16_t>(uw[d]));
-                const uint32_t hi = silu_mul_bits(static_cast<uint16_t>(gw[d] >> 16), static_cast<uint16_t>(uw[d] >> 16));
+                const uint32_t lo = silu_mul_any(static_cast<uint16_t>(gw[d]), static_cast<uint16_t>(uw[d]));
+                const uint32_t hi = silu_mul_any(static_cast<uint16_t>(gw[d] >> 16), static_cast<uint16_t>(uw[d] >> 16));
                 hw[d] = lo | (hi << 16);
             }
             *reinterpret_cast<uint4*>(hr + k) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         }
         k0 = K & ~7;
     }
-    for (int k = k0 + threadIdx.x; k < K; k += kSwiThreads) hr[k] = silu_mul_bits(gr[k], ur[k]);
+    for (int k = k0 + threadIdx.x; k < K; k += kSwiThreads) hr[k] = silu_mul_any(gr[k], ur[k]);
 }
 
 }  // namespace
