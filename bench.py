@@ -350,6 +350,8 @@ def main():
     ap.add_argument("--workload", default="prefill_70b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fusion", action="store_true",
+                    help="skip the fused-quantizer ablations (outside the timed step)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -411,8 +413,9 @@ def main():
             "layout": l.layout, "gemm_peak_tops": l.peak,
             "weight_copies": len(l.w)}
 
-    fusion = fusion_ablation(torch, comet, synth) if args.workload == "prefill_70b" else None
-    swi = swiglu_ablation(torch, comet, synth) if args.workload == "prefill_70b" else None
+    ablate = args.workload == "prefill_70b" and not args.no_fusion
+    fusion = fusion_ablation(torch, comet, synth) if ablate else None
+    swi = swiglu_ablation(torch, comet, synth) if ablate else None
 
     cpu = None
     if not args.no_cpu:
