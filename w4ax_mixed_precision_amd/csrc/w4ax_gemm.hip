@@ -483,6 +483,160 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
 }
 
 // ---------------------------------------------------------------------------
+// Streaming kernel for two to four row tiles (17 <= M <= 64): a wave's
+// activation words of a block feed G channel groups. In the one-group kernel
+// above every group's waves load all M rows of every block, so at M = 64 the
+// activation stream out of L2 is four times the weight stream out of HBM and
+// binds the kernel. Here a workgroup owns G neighbouring groups (16 G output
+// channels) and its kSplit waves split the blocks as above; a wave loads the
+// activation words of a block once, widens them in place, and runs them
+// against the G weight fragments of the block. Per wave and block: G weight
+// words, MR activation words (two for an 8-bit block), one activation scale,
+// G weight scales and sums; the G partial tiles are summed through LDS one
+// group after another, in wave order.
+// ---------------------------------------------------------------------------
+
+template <int MR, int G>
+struct StreamSlotG {
+    uint4 w[G];
+    uint4 a0[MR];
+    uint4 a1[MR];
+    float sa;
+    uint32_t hs[G];
+    int32_t ws[G];
+};
+
+template <int MR, int G>
+__device__ __forceinline__ void stream_fetch_g(const GemmProblem& p, Rsrc xq, int b, int grp0, int lane, int srow,
+                                               const int (&arow)[MR], StreamSlotG<MR, G>& sl) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const int M = p.M, N = p.N, nb4 = p.nb4;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        sl.w[j] = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp0 + j) * p.nb + b) * kFragBytes +
+                                                  16 * lane);
+    sl.sa = p.x_scale[static_cast<size_t>(b) * M + srow];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int ncol = (grp0 + j) * 16 + l16;
+        sl.hs[j] = p.w_scale[static_cast<size_t>(b) * N + ncol];
+        sl.ws[j] = p.w_sum[static_cast<size_t>(b) * N + ncol];
+    }
+    const bool is4 = b < nb4;
+    const uint32_t M32 = static_cast<uint32_t>(M), ub = static_cast<uint32_t>(b), nb4u = static_cast<uint32_t>(nb4);
+    const uint32_t slab = is4 ? ub * M32 * 64u : nb4u * M32 * 64u + (ub - nb4u) * M32 * 128u;
+    const uint32_t rstride = is4 ? 64u : 128u;
+    const uint32_t cofs = is4 ? 16u * g : 32u * g;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        const uint32_t off = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
+        sl.a0[r] = buf_load16(xq, off);
+        sl.a1[r] = buf_load16(xq, is4 ? kOutOfRange : off + 16u);
+    }
+}
+
+template <int MR, int G>
+__device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlotG<MR, G>& sl,
+                                                 float (&y)[G][MR][4]) {
+    // 4-bit rows: the one word holds both halves of the lane's 32 positions;
+    // widen it in place into the two operand words an 8-bit row loads
+    if (is4) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const v4i lo = widen_act_lo(sl.a0[r]);
+            const v4i hi = widen_act_hi(sl.a0[r]);
+            sl.a0[r] = uint4{static_cast<uint32_t>(lo[0]), static_cast<uint32_t>(lo[1]),
+                             static_cast<uint32_t>(lo[2]), static_cast<uint32_t>(lo[3])};
+            sl.a1[r] = uint4{static_cast<uint32_t>(hi[0]), static_cast<uint32_t>(hi[1]),
+                             static_cast<uint32_t>(hi[2]), static_cast<uint32_t>(hi[3])};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const v4i B0 = widen_weights_lo(sl.w[j]);
+        const v4i B1 = widen_weights_hi(sl.w[j]);
+        const float sw = valid ? h2f(static_cast<uint16_t>(sl.hs[j])) * 0.0625f : 0.0f;
+        const int corr = is4 ? -128 * sl.ws[j] : 0;
+        const v4i cinit = {corr, corr, corr, corr};
+        v16f t = {};
+        t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            v4i acc = mfma_i8(as_v4i(sl.a0[r]), B0, cinit);
+            acc = mfma_i8(as_v4i(sl.a1[r]), B1, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+        }
+    }
+}
+
+template <int MR, int G, int kD, int kSplit>
+__global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem p) {
+    __shared__ float red[kSplit][MR * 4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    // unit of G groups, XCD-aware as in the one-group kernel
+    const int units = p.N / (16 * G);
+    const int per = (units + 7) / 8;
+    const int unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (unit >= units) return;      // whole workgroup, before any barrier
+    const int grp0 = unit * G;
+    const int nb = p.nb, nb4 = p.nb4, M = p.M;
+    const int bps = (nb + kSplit - 1) / kSplit;
+    const int b_begin = imin(nb, wave * bps);
+    const int b_end = imin(nb, b_begin + bps);
+
+    int arow[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) arow[r] = imin(16 * r + l16, M - 1);
+    const int srow = imin(lane, M - 1);
+    const Rsrc xq = stream_xq_rsrc(p);
+    float y[G][MR][4];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[j][r][i] = 0.0f;
+
+    if (b_begin < b_end) {
+        const int last = b_end - 1;
+        StreamSlotG<MR, G> slot[kD];
+#pragma unroll
+        for (int u = 0; u < kD; ++u) stream_fetch_g<MR, G>(p, xq, imin(b_begin + u, last), grp0, lane, srow, arow, slot[u]);
+        for (int b0 = b_begin; b0 < b_end; b0 += kD) {
+#pragma unroll
+            for (int u = 0; u < kD; ++u) {
+                const int b = b0 + u;
+                stream_compute_g<MR, G>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                if (b0 + kD < b_end)
+                    stream_fetch_g<MR, G>(p, xq, imin(b + kD, last), grp0, lane, srow, arow, slot[u]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        if (j > 0) __syncthreads();     // the previous group's sums are read
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][4 * r + i][lane] = y[j][r][i];
+        __syncthreads();
+        for (int q = wave; q < MR * 4; q += kSplit) {
+            float v = red[0][q][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < kSplit; ++w2) v += red[w2][q][lane];
+            const int row = 16 * (q >> 2) + 4 * g + (q & 3);
+            if (row < M)
+                p.Y[static_cast<size_t>(row) * p.ldy + (grp0 + j) * 16 + l16] = __half_as_ushort(__float2half_rn(v));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming kernel with the weight fragments staged in LDS (decode, M <= 16,
 // nb == NBW * kSplit). The register kernel above holds every in-flight block
 // in VGPRs, which caps a CU at about 64 KB of weights in flight. Here each
@@ -574,6 +728,194 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel for two to four row tiles with the weight fragments in an
+// LDS ring (nb == NBW * kSplit). At M = 64 a block's activation words take 32
+// registers per wave, which leaves room for only two blocks in flight in the
+// register kernels: about 4 MB of weights in flight across the chip, far too
+// little to cover HBM latency. Here each wave owns G neighbouring channel
+// groups (as in gemm_stream_g_kernel: its activation words feed G weight
+// fragments) and keeps the fragments of its next kRR blocks in flight as
+// direct loads into its own LDS ring (G KB per block, no registers held);
+// activation words and scales run kRA blocks ahead in registers. Loads
+// complete in issue order, so the wait before block i is a constant of the
+// issue pattern, as in gemm_stream_lds_kernel.
+// ---------------------------------------------------------------------------
+
+template <int MR, int G>
+struct AuxSlotG {
+    uint4 a0[MR];
+    uint4 a1[MR];
+    float sa;
+    uint32_t hs[G];
+    int32_t ws[G];
+};
+
+// Loads of one block's aux fetch: two activation words per row tile, the
+// activation scale, G weight scales and G weight sums.
+template <int MR, int G>
+constexpr int aux_loads_g() { return 2 * MR + 1 + 2 * G; }
+
+// Loads issued after block i's aux loads (see the issue order in the kernel).
+template <int MR, int G, int kRA, int kRR>
+constexpr int lds_g_loads_after(int i, int nbw) {
+    int after = (i + kRR - kRA < nbw) ? G : 0;
+    for (int j = i + 1; j < i + kRA; ++j) {
+        if (j < nbw) after += aux_loads_g<MR, G>();
+        if (j + kRR - kRA < nbw) after += G;
+    }
+    return after;
+}
+
+template <int MR, int G>
+__device__ __forceinline__ void stream_fetch_aux_g(const GemmProblem& p, Rsrc xq, int b, int grp0, int lane,
+                                                   int srow, const int (&arow)[MR], AuxSlotG<MR, G>& sl) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const int M = p.M, N = p.N, nb4 = p.nb4;
+    const bool is4 = b < nb4;
+    const uint32_t M32 = static_cast<uint32_t>(M), ub = static_cast<uint32_t>(b), nb4u = static_cast<uint32_t>(nb4);
+    const uint32_t slab = is4 ? ub * M32 * 64u : nb4u * M32 * 64u + (ub - nb4u) * M32 * 128u;
+    const uint32_t rstride = is4 ? 64u : 128u;
+    const uint32_t cofs = is4 ? 16u * g : 32u * g;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        const uint32_t off = slab + static_cast<uint32_t>(arow[r]) * rstride + cofs;
+        sl.a0[r] = buf_load16(xq, off);
+        sl.a1[r] = buf_load16(xq, is4 ? kOutOfRange : off + 16u);
+    }
+    sl.sa = p.x_scale[static_cast<size_t>(b) * M + srow];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int ncol = (grp0 + j) * 16 + l16;
+        sl.hs[j] = p.w_scale[static_cast<size_t>(b) * N + ncol];
+        sl.ws[j] = p.w_sum[static_cast<size_t>(b) * N + ncol];
+    }
+}
+
+template <int MR, int G>
+__device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G>& sl, const uint8_t* frags, int lane,
+                                                     float (&y)[G][MR][4]) {
+    // branch-free operand words (a branch on the block kind splits the
+    // straight-line block sequence, and the compiler then waits for every
+    // outstanding load before the next LDS read): a 4-bit row's second word
+    // was loaded as zero, so (a1 | (a0 & m4)) >> sh is the high half of a0
+    // for a 4-bit block and a1 for an 8-bit one
+    const uint32_t mask = is4 ? 0x0F0F0F0Fu : 0xFFFFFFFFu;
+    const uint32_t m4 = is4 ? 0xFFFFFFFFu : 0u;
+    const uint32_t sh = is4 ? 4u : 0u;
+    v4i A0[MR], A1[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        const uint4 a = sl.a0[r], c = sl.a1[r];
+        A0[r] = v4i{static_cast<int>(a.x & mask), static_cast<int>(a.y & mask), static_cast<int>(a.z & mask),
+                    static_cast<int>(a.w & mask)};
+        A1[r] = v4i{static_cast<int>(((c.x | (a.x & m4)) >> sh) & mask),
+                    static_cast<int>(((c.y | (a.y & m4)) >> sh) & mask),
+                    static_cast<int>(((c.z | (a.z & m4)) >> sh) & mask),
+                    static_cast<int>(((c.w | (a.w & m4)) >> sh) & mask)};
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(frags + j * kFragBytes + 16 * lane);
+        const v4i B0 = widen_weights_lo(w);
+        const v4i B1 = widen_weights_hi(w);
+        const float sw = h2f(static_cast<uint16_t>(sl.hs[j])) * 0.0625f;
+        const int corr = is4 ? -128 * sl.ws[j] : 0;
+        const v4i cinit = {corr, corr, corr, corr};
+        v16f t = {};
+        t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            v4i acc = mfma_i8(A0[r], B0, cinit);
+            acc = mfma_i8(A1[r], B1, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+        }
+    }
+}
+
+template <int MR, int G, int NBW, int kSplit, int kRA, int kRR>
+__global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_lds_g_kernel(GemmProblem p) {
+    // two LDS objects: the compiler can then tell ring reads from other LDS
+    // accesses and waits only for the direct loads a read depends on (with
+    // one object it waits for every outstanding load before each read)
+    __shared__ float red[kSplit][MR * 4][64];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kSplit][kRR * G][kFragBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    const int units = p.N / (16 * G);
+    const int per = (units + 7) / 8;
+    const int unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (unit >= units) return;      // whole workgroup, before any barrier
+    const int grp0 = unit * G;
+    const int nb4 = p.nb4, M = p.M;
+    const int b_begin = wave * NBW;
+    int arow[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) arow[r] = imin(16 * r + l16, M - 1);
+    const int srow = imin(lane, M - 1);
+    const Rsrc wq = make_rsrc(p.Wq, static_cast<uint32_t>(p.N / 16) * p.nb * kFragBytes);
+    const Rsrc xq = stream_xq_rsrc(p);
+    uint8_t* my = &ring[wave][0][0];
+    // the G fragments of block i (channel groups grp0 .. grp0 + G - 1) into
+    // ring slot i mod kRR
+    auto fragments = [&](int i) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            lds_buf16(wq, 16u * lane, (static_cast<uint32_t>(grp0 + j) * p.nb + b_begin + i) * kFragBytes,
+                      my + ((i % kRR) * G + j) * kFragBytes);
+    };
+
+    float y[G][MR][4];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[j][r][i] = 0.0f;
+    AuxSlotG<MR, G> slot[kRA];
+    // issue order: fragments of blocks 0 .. kRR-kRA-1; then for k < kRA the
+    // aux loads of block k followed by the fragments of block k + kRR - kRA;
+    // in the loop, after block i: aux of i + kRA, fragments of i + kRR
+#pragma unroll
+    for (int i = 0; i < kRR - kRA; ++i)
+        if (i < NBW) fragments(i);
+#pragma unroll
+    for (int k = 0; k < kRA; ++k) {
+        if (k < NBW) stream_fetch_aux_g<MR, G>(p, xq, b_begin + k, grp0, lane, srow, arow, slot[k]);
+        if (k + kRR - kRA < NBW) fragments(k + kRR - kRA);
+    }
+    unroll_seq([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR>(i, NBW)));
+        AuxSlotG<MR, G>& sl = slot[i % kRA];
+        stream_compute_lds_g<MR, G>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y);
+        if (i + kRA < NBW) stream_fetch_aux_g<MR, G>(p, xq, b_begin + i + kRA, grp0, lane, srow, arow, sl);
+        // the ring slot just read is refilled only after its words are used
+        if (i + kRR < NBW) fragments(i + kRR);
+    }, std::make_integer_sequence<int, NBW>{});
+
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        if (j > 0) __syncthreads();     // the previous group's sums are read
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][4 * r + i][lane] = y[j][r][i];
+        __syncthreads();
+        for (int q = wave; q < MR * 4; q += kSplit) {
+            float v = red[0][q][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < kSplit; ++w2) v += red[w2][q][lane];
+            const int row = 16 * (q >> 2) + 4 * g + (q & 3);
+            if (row < M)
+                p.Y[static_cast<size_t>(row) * p.ldy + (grp0 + j) * 16 + l16] = __half_as_ushort(__float2half_rn(v));
+        }
+    }
+}
+
 bool use_stream(int M) { return M <= 64; }
 
 #ifndef COMET_STREAM_TARGET_WAVES
@@ -583,48 +925,87 @@ bool use_stream(int M) { return M <= 64; }
 #define COMET_STREAM_DEPTH 4
 #endif
 
-// Widest in-workgroup split whose register budget (512 / waves per SIMD) holds
-// the kernel without spills: 120, 187, 146 and 179 VGPRs for 1..4 row tiles
-// (four blocks in flight for one or two row tiles, two for three or four).
-template <int MR>
-constexpr int max_stream_split() { return MR == 1 ? 16 : (MR <= 3 ? 8 : 4); }
-
-template <int MR>
-int launch_stream(const GemmProblem& p, hipStream_t st) {
-    // three or four row tiles hold 24-32 activation registers per block: two
-    // blocks in flight keep them at two waves per SIMD (four blocks: one)
-    constexpr int kD = MR >= 3 ? 2 : COMET_STREAM_DEPTH;
-    constexpr int kMax = max_stream_split<MR>();
-    // split the blocks of a channel group over enough waves to keep many
-    // weight fragments in flight across the chip
+// One row tile (M <= 16): one channel group per workgroup, its blocks split
+// over the waves; the LDS-ring kernel for 32, 64 and 128 blocks, the register
+// kernel (four blocks in flight, 120 VGPRs) otherwise.
+int launch_stream1(const GemmProblem& p, hipStream_t st) {
+    constexpr int kD = COMET_STREAM_DEPTH;
     const int groups = p.N / 16;
     const int grid = 8 * ((groups + 7) / 8);     // XCD-aware order; surplus workgroups exit
-    if constexpr (MR == 1) {
-        // block counts the LDS kernel is built for: one wave per NBW blocks
-        if (p.nb == 32) {
-            gemm_stream_lds_kernel<8, 4><<<grid, 256, 0, st>>>(p);
-            return static_cast<int>(hipGetLastError());
-        }
-        if (p.nb == 64 && groups * 8 < 2 * COMET_STREAM_TARGET_WAVES) {
-            gemm_stream_lds_kernel<8, 8><<<grid, 512, 0, st>>>(p);
-            return static_cast<int>(hipGetLastError());
-        }
-        if (p.nb == 64) {
-            gemm_stream_lds_kernel<16, 4><<<grid, 256, 0, st>>>(p);
-            return static_cast<int>(hipGetLastError());
-        }
-        if (p.nb == 128) {
-            gemm_stream_lds_kernel<16, 8><<<grid, 512, 0, st>>>(p);
-            return static_cast<int>(hipGetLastError());
-        }
+    if (p.nb == 32) {
+        gemm_stream_lds_kernel<8, 4><<<grid, 256, 0, st>>>(p);
+    } else if (p.nb == 64 && groups * 8 < 2 * COMET_STREAM_TARGET_WAVES) {
+        gemm_stream_lds_kernel<8, 8><<<grid, 512, 0, st>>>(p);
+    } else if (p.nb == 64) {
+        gemm_stream_lds_kernel<16, 4><<<grid, 256, 0, st>>>(p);
+    } else if (p.nb == 128) {
+        gemm_stream_lds_kernel<16, 8><<<grid, 512, 0, st>>>(p);
+    } else if (groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD) {
+        // split the blocks of a channel group over enough waves to keep
+        // many weight fragments in flight across the chip
+        gemm_stream_kernel<1, kD, 4><<<grid, 256, 0, st>>>(p);
+    } else if (groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD) {
+        gemm_stream_kernel<1, kD, 8><<<grid, 512, 0, st>>>(p);
+    } else {
+        gemm_stream_kernel<1, kD, 16><<<grid, 1024, 0, st>>>(p);
     }
-    if (kMax == 4 || groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD)
-        gemm_stream_kernel<MR, kD, 4><<<grid, 256, 0, st>>>(p);
-    else if (kMax == 8 || groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD)
-        gemm_stream_kernel<MR, kD, (kMax >= 8 ? 8 : 4)><<<grid, 64 * (kMax >= 8 ? 8 : 4), 0, st>>>(p);
-    else
-        gemm_stream_kernel<MR, kD, (kMax >= 16 ? 16 : 4)><<<grid, 64 * (kMax >= 16 ? 16 : 4), 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
+}
+
+// Register multi-group kernel, any block count. Measured against the
+// one-group kernel on the K = 8192 decode shapes it is faster in 11 of 12
+// (N = 10240, M = 64: 34 against 32 us).
+template <int MR, int G, int kSplit>
+int launch_stream_g_cfg(const GemmProblem& p, hipStream_t st) {
+    constexpr int kD = 2;
+    const int units = p.N / (16 * G);
+    const int grid = 8 * ((units + 7) / 8);
+    gemm_stream_g_kernel<MR, G, kD, kSplit><<<grid, 64 * kSplit, 0, st>>>(p);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int MR>
+int launch_stream_g(const GemmProblem& p, hipStream_t st) {
+    const int groups = p.N / 16;
+    // four groups per workgroup while that still leaves about two four-wave
+    // workgroups per CU; else two groups, with eight waves per workgroup when
+    // four-wave workgroups alone would not cover the CUs
+    if (groups / 4 >= 384) return launch_stream_g_cfg<MR, 4, 4>(p, st);
+    if (groups / 2 >= 384) return launch_stream_g_cfg<MR, 2, 4>(p, st);
+    return launch_stream_g_cfg<MR, 2, 8>(p, st);
+}
+
+// LDS-ring multi-group kernel, 64 blocks. Two configurations, chosen by
+// measurement on the LLaMA-70B decode shapes (K = 8192; N = 8192, 10240,
+// 28672; M = 17 .. 64):
+//   wide:   G = 4, four waves of 16 blocks, 4-block ring (64 KB, plus 16 KB
+//           for the reduction: two workgroups per CU);
+//   narrow: G = 2, eight waves of 8 blocks, 4-block ring (64 KB + 32 KB).
+// The wide form reads each activation word for twice the channels and is
+// faster when it still yields about 1.5 workgroups per CU (N >= 24576), and
+// at M > 32 from 160 workgroups on (N = 10240, M = 64: 23 against 26 us); the
+// narrow one has twice the waves and wins on the smaller grids.
+template <int MR, int G, int kSplit, int kRR, int kRA>
+int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st) {
+    const int units = p.N / (16 * G);
+    const int grid = 8 * ((units + 7) / 8);
+    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR><<<grid, 64 * kSplit, 0, st>>>(p);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int MR>
+int launch_stream_lds_g(const GemmProblem& p, hipStream_t st) {
+    const int wide_units = p.N / 64;
+    const bool wide = wide_units >= 384 || (p.M > 32 && wide_units >= 160);
+    if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2>(p, st);
+    return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2>(p, st);
+}
+
+// Two to four row tiles (16 < M <= 64): several channel groups per wave.
+template <int MR>
+int launch_stream(const GemmProblem& p, hipStream_t st) {
+    if (p.nb == 64) return launch_stream_lds_g<MR>(p, st);
+    return launch_stream_g<MR>(p, st);
 }
 
 }  // namespace
@@ -640,7 +1021,7 @@ int launch_w4ax_gemm(const GemmProblem& p, void* stream) {
     }
     if (use_stream(p.M)) {
         const int mr = (p.M + 15) / 16;
-        if (mr == 1) return launch_stream<1>(p, s);
+        if (mr == 1) return launch_stream1(p, s);
         if (mr == 2) return launch_stream<2>(p, s);
         if (mr == 3) return launch_stream<3>(p, s);
         return launch_stream<4>(p, s);
