@@ -46,18 +46,29 @@ WORKLOADS = {
 }
 
 
-# Sources whose change invalidates counter data taken on the GEMM kernel.
-KERNEL_SOURCES = ["w4ax_mixed_precision_amd/csrc/w4ax_gemm.hip",
-                  "w4ax_mixed_precision_amd/csrc/w4ax_gemm_fp6.hip",
-                  "w4ax_mixed_precision_amd/csrc/device_util.h",
-                  "w4ax_mixed_precision_amd/csrc/comet_internal.h",
-                  "w4ax_mixed_precision_amd/build.py"]
+# Sources whose change invalidates counter data taken on the GEMM kernels of
+# a workload: the GEMM source of the layout the workload runs, plus what every
+# kernel includes and the build flags.
+_COMMON_SOURCES = ["w4ax_mixed_precision_amd/csrc/device_util.h",
+                   "w4ax_mixed_precision_amd/csrc/comet_internal.h",
+                   "w4ax_mixed_precision_amd/build.py"]
+KERNEL_SOURCES = {"int4": ["w4ax_mixed_precision_amd/csrc/w4ax_gemm.hip"] + _COMMON_SOURCES,
+                  "fp6": ["w4ax_mixed_precision_amd/csrc/w4ax_gemm_fp6.hip"] + _COMMON_SOURCES}
 COPY_CAL_BYTES = 1 << 30
 
 
-def kernel_sources_digest():
+def workload_layouts(workload):
+    return sorted({layout_of(synth_cfg(n).M) for n in WORKLOADS[workload]})
+
+
+def synth_cfg(name):
+    from gen import synth
+    return synth.CONFIGS[name]
+
+
+def kernel_sources_digest(workload):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in [r for lay in workload_layouts(workload) for r in KERNEL_SOURCES[lay]]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -71,7 +82,7 @@ def measured_traffic(workload):
         return None, "no counter summary"
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sources_sha256") != kernel_sources_digest():
+    if rec.get("kernel_sources_sha256") != kernel_sources_digest(workload):
         return None, "kernel changed since the counters were taken"
     return float(rec["hbm_bytes_per_step"]), path
 

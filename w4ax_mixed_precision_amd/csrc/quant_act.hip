@@ -349,6 +349,18 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
     // (kSwi), follow the staged row
     double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) + (kRowInLds ? row_bytes : 0));
     bool sums_done = false;
+
+    const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
+    const int g = lane & 3;               // the lane's 32-channel group
+    const int bl = lane >> 2;             // its block among the wave's 16
+    const int stride = gridDim.y * (T / 64) * 16;
+    int b0 = (blockIdx.y * (T / 64) + wave) * 16;
+    int4 nxt[8];
+    // the perm entries of the first pass do not depend on the row: their
+    // loads go out before the row's, so the two latencies overlap (the
+    // SwiGLU form, whose staging is long and register-heavy, loads them
+    // after it)
+    if (!kSwi && b0 < nb) load_positions(perm, imin(b0 + bl, nb - 1), g, nxt);
     if constexpr (kRowInLds && kSwi) {
         // The staged row is h itself: every thread forms 8 consecutive values
         // per step from coalesced gate and up loads with the binary32 test.
@@ -446,14 +458,7 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
         rs = rms_from_waves(red, K, eps);
     }
 
-    const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
-    const int g = lane & 3;               // the lane's 32-channel group
-    const int bl = lane >> 2;             // its block among the wave's 16
-    const int stride = gridDim.y * (T / 64) * 16;
-
-    int b0 = (blockIdx.y * (T / 64) + wave) * 16;
-    int4 nxt[8];
-    if (b0 < nb) load_positions(perm, imin(b0 + bl, nb - 1), g, nxt);
+    if (kSwi && b0 < nb) load_positions(perm, imin(b0 + bl, nb - 1), g, nxt);
     for (; b0 < nb; b0 += stride) {
         int4 pos[8];
 #pragma unroll
