@@ -24,6 +24,16 @@
  *  3. Activation quantization (online). Per token and per block, absmax
  *     scaling to INT4 ([-7, 7]) or INT8 ([-127, 127]); QoQ/QServe article,
  *     section "保护量化范围", names the symmetric 8-bit range [-127, 127].
+ *  3b. Asymmetric 4-bit activations (a variant of step 3, the outlier-handling
+ *     scheme of the QUIK blog, section "反量化背后的数学": activations carry a
+ *     scale and a zero point, weights a scale only, and the zero point enters
+ *     the result through a term that needs only the zero point and the
+ *     offline sum of the weights). On a 4-bit block the range [lo, hi] is the
+ *     block's minimum and maximum widened to include 0, the step is
+ *     s = (hi - lo) / 15, the zero point z = round(-lo / s) in [0, 15] and the
+ *     stored code u = round(x / s) + z in [0, 15]; the value represented is
+ *     s (u - z). 8-bit blocks stay symmetric (step 3). The signed code q =
+ *     u - z then enters steps 4 and 5 unchanged.
  *  4. Block partials. The exact INT32 dot product of each 128-channel block.
  *     A second form uses the zero-extended 4-bit code u = q + 8 and removes
  *     the offset with the precomputed weight sum (COMET article, section
@@ -314,6 +324,144 @@ int orc_quantize_activations(const uint16_t *X, int M, int K, int ldx, const int
         }
     }
     return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3b. Activation quantization, asymmetric 4-bit blocks                      */
+/* ------------------------------------------------------------------------ */
+
+/* Step, reciprocal and zero point of one 4-bit (token, block) with range
+ * [lo, hi], lo <= 0 <= hi, lo < hi:
+ *   d = hi - lo (one binary32 subtraction), inv = 15 / d, s = d / 15 (each one
+ *   correctly rounded division), z = round(-lo * inv) clamped to [0, 15]. */
+void orc_act_asym_params(float lo, float hi, float *inv, float *s, int *z)
+{
+    float d = hi - lo;
+    *inv = 15.0f / d;
+    *s = d / 15.0f;
+    float t = -lo * *inv;
+    int zz = (int)rintf(t);
+    *z = zz < 0 ? 0 : (zz > 15 ? 15 : zz);
+}
+
+/* One element's stored code: u = round(x * inv) + z clamped to [0, 15] (the
+ * product is a single rounded multiply). */
+int orc_act_asym_code(float x, float inv, int z)
+{
+    float p = x * inv;
+    int u = (int)rintf(p) + z;
+    return u < 0 ? 0 : (u > 15 ? 15 : u);
+}
+
+/* qa: [M][K] signed codes in permuted channel order (4-bit blocks: u - z in
+ * [-15, 15]; 8-bit blocks: step 3's symmetric codes). u4: [M][K] the stored
+ * 4-bit codes u (0 on 8-bit blocks). sa: [M][nb] steps. za: [M][nb] zero
+ * points (0 on 8-bit blocks). A 4-bit block whose range is [0, 0] (all zero)
+ * gets step 0, zero point 0 and codes 0. */
+int orc_quantize_activations_asym(const uint16_t *X, int M, int K, int ldx, const int32_t *perm,
+                                  const uint8_t *is_int8, int8_t *qa, uint8_t *u4, float *sa,
+                                  uint8_t *za)
+{
+    if (M <= 0 || K <= 0 || K % ORC_BLOCK != 0 || ldx < K)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xrow = X + (size_t)m * ldx;
+        for (int b = 0; b < nb; ++b) {
+            int8_t *q = qa + (size_t)m * K + (size_t)b * ORC_BLOCK;
+            uint8_t *u = u4 + (size_t)m * K + (size_t)b * ORC_BLOCK;
+            if (is_int8[b]) {
+                /* step 3, unchanged */
+                float a = 0.0f;
+                for (int k = 0; k < ORC_BLOCK; ++k) {
+                    float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                    if (!isfinite(v))
+                        bad = 1;
+                    if (fabsf(v) > a)
+                        a = fabsf(v);
+                }
+                float inv = 0.0f, s = 0.0f;
+                if (a > 0.0f)
+                    orc_act_scale(a, 127, &inv, &s);
+                sa[(size_t)m * nb + b] = s;
+                za[(size_t)m * nb + b] = 0;
+                for (int k = 0; k < ORC_BLOCK; ++k) {
+                    float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                    q[k] = a > 0.0f ? (int8_t)orc_act_quantize_value(v, inv, 127) : 0;
+                    u[k] = 0;
+                }
+                continue;
+            }
+            float lo = 0.0f, hi = 0.0f;     /* the range always holds 0 */
+            for (int k = 0; k < ORC_BLOCK; ++k) {
+                float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                if (!isfinite(v))
+                    bad = 1;
+                if (v < lo)
+                    lo = v;
+                if (v > hi)
+                    hi = v;
+            }
+            if (lo == hi) {                 /* all zero */
+                sa[(size_t)m * nb + b] = 0.0f;
+                za[(size_t)m * nb + b] = 0;
+                for (int k = 0; k < ORC_BLOCK; ++k) {
+                    q[k] = 0;
+                    u[k] = 0;
+                }
+                continue;
+            }
+            float inv, s;
+            int z;
+            orc_act_asym_params(lo, hi, &inv, &s, &z);
+            sa[(size_t)m * nb + b] = s;
+            za[(size_t)m * nb + b] = (uint8_t)z;
+            for (int k = 0; k < ORC_BLOCK; ++k) {
+                float v = orc_half_to_float(xrow[perm[b * ORC_BLOCK + k]]);
+                int uu = orc_act_asym_code(v, inv, z);
+                u[k] = (uint8_t)uu;
+                q[k] = (int8_t)(uu - z);
+            }
+        }
+    }
+    return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* The asymmetric partials through the stored code and the zero point: on a
+ * 4-bit block P = sum(u * qw) - z * wsum (QUIK blog, section "反量化背后的数学":
+ * the zero-point term needs only z and the offline weight sum); 8-bit blocks
+ * take the signed codes. */
+int orc_block_partials_zero_point(const int8_t *qa, const uint8_t *u4, const uint8_t *za,
+                                  const int8_t *qw, const int32_t *wsum, const uint8_t *is_int8,
+                                  int M, int N, int K, int m0, int m1, int32_t *P)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0 || m0 < 0 || m1 > M || m0 >= m1)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int m = m0; m < m1; ++m) {
+        for (int n = 0; n < N; ++n) {
+            const int8_t *w = qw + (size_t)n * K;
+            int32_t *out = P + ((size_t)(m - m0) * N + n) * nb;
+            for (int b = 0; b < nb; ++b) {
+                int32_t acc = 0;
+                if (is_int8[b]) {
+                    const int8_t *a = qa + (size_t)m * K;
+                    for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k)
+                        acc += (int32_t)a[k] * (int32_t)w[k];
+                } else {
+                    const uint8_t *u = u4 + (size_t)m * K;
+                    for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k)
+                        acc += (int32_t)u[k] * (int32_t)w[k];
+                    acc -= (int32_t)za[(size_t)m * nb + b] * wsum[(size_t)n * nb + b];
+                }
+                out[b] = acc;
+            }
+        }
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.orc_quantize_weights.argtypes = [P, I, I, P, P, P, P]
         L.orc_quantize_activations.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_block_partials.argtypes = [P, P, I, I, I, I, I, P]
+        L.orc_act_asym_params.argtypes = [ctypes.c_float, ctypes.c_float, P, P, P]
+        L.orc_act_asym_code.argtypes = [ctypes.c_float, ctypes.c_float, I]
+        L.orc_quantize_activations_asym.argtypes = [P, I, I, I, P, P, P, P, P, P]
+        L.orc_block_partials_zero_point.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         L.orc_block_partials_zero_extend.argtypes = [P, P, P, P, I, I, I, I, I, P]
         L.orc_epilogue.argtypes = [P, P, P, I, I, I, P, P, P]
         L.orc_forward_rows.argtypes = [P, I, I, I, P, P, P, P, I, I, I, P, P]
@@ -168,6 +172,50 @@ def quantize_activations(X16: np.ndarray, perm: np.ndarray, flags: np.ndarray):
     _check(lib().orc_quantize_activations(_p(X16), M, K, K, _p(perm), _p(flags), _p(qa), _p(sa)),
            "quantize_activations")
     return qa, sa
+
+
+def act_asym_params(lo: float, hi: float) -> tuple[float, float, int]:
+    """(inv, s, z) of a 4-bit block with range [lo, hi], lo <= 0 <= hi, lo < hi."""
+    inv, s, z = ctypes.c_float(), ctypes.c_float(), ctypes.c_int()
+    lib().orc_act_asym_params(lo, hi, ctypes.byref(inv), ctypes.byref(s), ctypes.byref(z))
+    return inv.value, s.value, z.value
+
+
+def act_asym_code(x: float, inv: float, z: int) -> int:
+    return lib().orc_act_asym_code(x, inv, z)
+
+
+def quantize_activations_asym(X16: np.ndarray, perm: np.ndarray, flags: np.ndarray):
+    """Asymmetric 4-bit blocks (step 3b): (qa signed codes u - z, u4 stored codes,
+    sa steps [M, nb], za zero points [M, nb])."""
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    M, K = X16.shape
+    nb = K // 128
+    qa = np.zeros((M, K), np.int8)
+    u4 = np.zeros((M, K), np.uint8)
+    sa = np.zeros((M, nb), np.float32)
+    za = np.zeros((M, nb), np.uint8)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    _check(lib().orc_quantize_activations_asym(_p(X16), M, K, K, _p(perm), _p(flags), _p(qa), _p(u4),
+                                               _p(sa), _p(za)), "quantize_activations_asym")
+    return qa, u4, sa, za
+
+
+def block_partials_zero_point(qa, u4, za, qw, wsum, flags, rows=None):
+    qa = np.ascontiguousarray(qa, dtype=np.int8)
+    u4 = np.ascontiguousarray(u4, dtype=np.uint8)
+    za = np.ascontiguousarray(za, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    wsum = np.ascontiguousarray(wsum, dtype=np.int32)
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    P = np.zeros((m1 - m0, N, K // 128), np.int32)
+    _check(lib().orc_block_partials_zero_point(_p(qa), _p(u4), _p(za), _p(qw), _p(wsum), _p(flags),
+                                               M, N, K, m0, m1, _p(P)), "block_partials_zero_point")
+    return P
 
 
 def block_partials(qa: np.ndarray, qw: np.ndarray, rows: tuple[int, int] | None = None):
@@ -278,6 +326,15 @@ def quantize_layer(X16, W16, score, nb8):
     qa, sa = quantize_activations(X16, perm, flags)
     return {"perm": perm, "flags": flags, "qw": qw, "sw16": sw16, "wsum": wsum,
             "qa": qa, "sa": sa}
+
+
+def quantize_layer_asym(X16, W16, score, nb8):
+    """quantize_layer with asymmetric 4-bit activation blocks (step 3b)."""
+    perm, flags = channel_order(score, nb8)
+    qw, sw16, wsum = quantize_weights(W16, perm)
+    qa, u4, sa, za = quantize_activations_asym(X16, perm, flags)
+    return {"perm": perm, "flags": flags, "qw": qw, "sw16": sw16, "wsum": wsum,
+            "qa": qa, "u4": u4, "sa": sa, "za": za}
 
 
 def reference(X16, W16, score, nb8, rows=None):
