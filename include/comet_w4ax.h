@@ -205,6 +205,49 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
                              int32_t* P, void* stream);
 
 /*
+ * Asymmetric 4-bit activation blocks (the QUIK blog's scheme, section
+ * "反量化背后的数学": activations with a scale and a zero point, weights with
+ * a scale only; the zero-point term z * sum(w) needs only the zero point and
+ * the offline weight sum). On the INT4 layout only: the FP6 format cannot hold
+ * the codes 8..15.
+ *
+ * comet_quant_act_asym: as comet_quant_act, but every 4-bit (token, block)
+ * takes its range [lo, hi] = [min(0, min x), max(0, max x)] and, if hi > lo,
+ *   d = hi - lo, inv = 15 / d, s = d / 15 (IEEE float operations),
+ *   z = clamp(round_half_even(-lo * inv), 0, 15),
+ *   u = clamp(round_half_even(x * inv) + z, 0, 15);
+ * an all-zero block gets s = 0, z = 0, u = 0. The nibble stores u (same
+ * positions as comet_quant_act's u = q + 8); the value represented is
+ * s (u - z). 8-bit blocks are coded exactly as by comet_quant_act, z = 0.
+ *   x_zero  out  device, uint8 [nb][Mp], Mp = M rounded up to a multiple of
+ *                16 (comet_x_zero_bytes); rows M .. Mp-1 are not written
+ * Errors: as comet_quant_act (NULL and ALIGN also for x_zero).
+ */
+int comet_quant_act_asym(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                         int n_int8_blocks, void* Xq, float* x_scale, uint8_t* x_zero, void* stream);
+
+/* Bytes of x_zero for M rows and K channels (0 for an invalid shape). */
+size_t comet_x_zero_bytes(int M, int K);
+
+/*
+ * comet_w4ax_gemm on asymmetric codes: on a 4-bit block the exact partial is
+ *   P = sum over the block of u q_w - z w_sum = sum of (u - z) q_w,
+ * formed on the matrix cores from the stored u with the accumulator starting
+ * at the zero-point term; then Y as comet_w4ax_gemm. Arguments and errors as
+ * comet_w4ax_gemm, plus x_zero (in, from comet_quant_act_asym; NULL, ALIGN).
+ */
+int comet_w4ax_gemm_asym(const void* Xq, const float* x_scale, const uint8_t* x_zero, const void* Wq_packed,
+                         const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks, int M, int N,
+                         int K, void* Y_fp16, int ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug variant: the partials P above of rows [m_begin, m_begin + m_count), as
+ * comet_w4ax_gemm_partials. */
+int comet_w4ax_gemm_asym_partials(const void* Xq, const float* x_scale, const uint8_t* x_zero,
+                                  const void* Wq_packed, const uint16_t* w_scale_fp16, const int16_t* w_sum,
+                                  int n_int8_blocks, int M, int N, int K, int m_begin, int m_count, int32_t* P,
+                                  void* stream);
+
+/*
  * FP6 layout, sizes: bytes of Xq_fp6 for M rows (padded to a multiple of 16)
  * and of Wq_fp6 for N output channels (0 for an invalid shape).
  */

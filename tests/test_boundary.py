@@ -235,3 +235,37 @@ def test_permute_channels():
     assert L.comet_permute_channels(P(v), P(bad), 300, P(out)) == ARG
     assert L.comet_permute_channels(P(v), P(perm), 0, P(out)) == SHAPE
     assert L.comet_permute_channels(None, P(perm), 300, P(out)) == NULL
+
+
+def qaa(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, Xq=A, xs=A, xz=A):
+    return comet.lib().comet_quant_act_asym(X, M, K, ldx, perm, nb8, Xq, xs, xz, None)
+
+
+def gma(Xq=A, xs=A, xz=A, Wq=A, ws=A, wsum=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512):
+    return comet.lib().comet_w4ax_gemm_asym(Xq, xs, xz, Wq, ws, wsum, nb8, M, N, K, Y, ldy, None, 0, None)
+
+
+def gpa(Xq=A, xs=A, xz=A, Wq=A, ws=A, wsum=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A):
+    return comet.lib().comet_w4ax_gemm_asym_partials(Xq, xs, xz, Wq, ws, wsum, nb8, M, N, K, m0, mc, P, None)
+
+
+def test_asym_rejections():
+    """The asymmetric-code calls: the checks of their symmetric forms plus the zero points."""
+    assert qaa(xz=None) == NULL and qaa(X=None) == NULL and qaa(xs=None) == NULL
+    assert qaa(M=0) == SHAPE and qaa(K=100) == SHAPE and qaa(ldx=511) == SHAPE
+    assert qaa(nb8=5) == ARG and qaa(nb8=-1) == ARG
+    assert qaa(xz=MIS) == ALIGN and qaa(Xq=MIS) == ALIGN
+    assert gma(xz=None) == NULL and gma(Y=None) == NULL and gma(wsum=None) == NULL
+    assert gma(xz=MIS) == ALIGN and gma(Wq=MIS) == ALIGN
+    assert gma(M=0) == SHAPE and gma(ldy=500) == SHAPE and gma(nb8=5) == ARG
+    assert gma(N=200, ldy=200) == UNSUP
+    assert gpa(xz=None) == NULL and gpa(P=None) == NULL and gpa(xz=MIS) == ALIGN
+    assert gpa(m0=-1) == SHAPE and gpa(m0=10, mc=7) == SHAPE
+
+
+def test_x_zero_bytes():
+    L = comet.lib()
+    assert L.comet_x_zero_bytes(1, 512) == 4 * 16
+    assert L.comet_x_zero_bytes(17, 8192) == 64 * 32
+    assert L.comet_x_zero_bytes(4096, 28672) == 224 * 4096
+    assert L.comet_x_zero_bytes(0, 512) == 0 and L.comet_x_zero_bytes(16, 100) == 0

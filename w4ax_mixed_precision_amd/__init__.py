@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
     L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
     L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P]
+    L.comet_quant_act_asym.argtypes = [P, I, I, I, P, I, P, P, P, P]
+    L.comet_x_zero_bytes.argtypes = [I, I]
+    L.comet_x_zero_bytes.restype = Z
+    L.comet_w4ax_gemm_asym.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, Z, P]
+    L.comet_w4ax_gemm_asym_partials.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P]
     F = ctypes.c_float
     L.comet_rmsnorm_quant_act.argtypes = [P, I, I, I, P, F, P, I, P, P, P]
     L.comet_rmsnorm_quant_act_fp6.argtypes = [P, I, I, I, P, F, P, I, P, P, P]
@@ -72,7 +77,8 @@ def lib() -> ctypes.CDLL:
               "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
               "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_rmsnorm_quant_act",
               "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels",
-              "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu"):
+              "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
+              "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -84,7 +90,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
            "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
            "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
-           "comet_status_string", "comet_version")
+           "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
+           "comet_w4ax_gemm_asym_partials", "comet_status_string", "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -194,6 +201,56 @@ def comet_quant_act(X, perm, nb8: int, Xq=None, x_scale=None, stream=None):
                                _dev_ptr(Xq), _dev_ptr(x_scale), _stream(stream))
     _check("comet_quant_act", rc)
     return Xq, x_scale
+
+
+def x_zero_bytes(M: int, K: int) -> int:
+    return int(lib().comet_x_zero_bytes(M, K))
+
+
+def comet_quant_act_asym(X, perm, nb8: int, Xq=None, x_scale=None, x_zero=None, stream=None):
+    """Asymmetric 4-bit blocks: returns (Xq uint8 [xq_bytes], x_scale float32 [nb, M],
+    x_zero uint8 [nb, Mp], Mp = M rounded up to 16)."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    if Xq is None:
+        Xq = torch.empty(xq_bytes(M, K, nb8), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty((K // 128, M), dtype=torch.float32, device=X.device)
+    if x_zero is None:
+        x_zero = torch.zeros((K // 128, (M + 15) // 16 * 16), dtype=torch.uint8, device=X.device)
+    rc = lib().comet_quant_act_asym(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(perm), int(nb8),
+                                    _dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(x_zero), _stream(stream))
+    _check("comet_quant_act_asym", rc)
+    return Xq, x_scale, x_zero
+
+
+def comet_w4ax_gemm_asym(Xq, x_scale, x_zero, w: dict, M: int, Y=None, stream=None):
+    """Y fp16 [M, N] from asymmetric activation codes (comet_quant_act_asym)."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_asym(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(x_zero), _dev_ptr(w["Wq"]),
+                                    _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]), int(nb8), M, N, K,
+                                    _dev_ptr(Y), Y.stride(0), None, 0, _stream(stream))
+    _check("comet_w4ax_gemm_asym", rc)
+    return Y
+
+
+def comet_w4ax_gemm_asym_partials(Xq, x_scale, x_zero, w: dict, M: int, m_begin: int = 0,
+                                  m_count: int | None = None, P=None, stream=None):
+    """Exact INT32 block partials (asymmetric codes) of rows [m_begin, m_begin + m_count)."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    m_count = M - m_begin if m_count is None else m_count
+    if P is None:
+        P = torch.empty((m_count, N, K // 128), dtype=torch.int32, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_asym_partials(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(x_zero),
+                                             _dev_ptr(w["Wq"]), _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]),
+                                             int(nb8), M, N, K, m_begin, m_count, _dev_ptr(P), _stream(stream))
+    _check("comet_w4ax_gemm_asym_partials", rc)
+    return P
 
 
 def comet_permute_channels(v: np.ndarray, perm: np.ndarray) -> np.ndarray:

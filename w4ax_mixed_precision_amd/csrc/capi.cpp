@@ -90,10 +90,28 @@ size_t comet_w4ax_gemm_workspace_bytes(int M, int N, int K, int n_int8_blocks) {
     return comet::gemm_workspace_bytes(M, N, K, n_int8_blocks);
 }
 
-int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
-                     const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks,
-                     int M, int N, int K, void* Y_fp16, int ldy, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int comet_quant_act_asym(const void* X_fp16, int M, int K, int ldx, const int32_t* perm,
+                         int n_int8_blocks, void* Xq, float* x_scale, uint8_t* x_zero, void* stream) {
+    if (!X_fp16 || !perm || !Xq || !x_scale || !x_zero) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (n_int8_blocks < 0 || n_int8_blocks > K / kBlock) return COMET_ERR_ARG;
+    if (!aligned16(X_fp16) || !aligned16(perm) || !aligned16(Xq) || !aligned16(x_scale) || !aligned16(x_zero))
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_quant_act_asym(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
+                                                   n_int8_blocks, static_cast<uint8_t*>(Xq), x_scale, x_zero,
+                                                   stream));
+}
+
+size_t comet_x_zero_bytes(int M, int K) {
+    if (M < 1 || K < kBlock || K % kBlock != 0) return 0;
+    return static_cast<size_t>(K / kBlock) * ((static_cast<size_t>(M) + 15u) & ~static_cast<size_t>(15));
+}
+
+namespace {
+
+int gemm_impl(const void* Xq, const float* x_scale, const uint8_t* x_zero, const void* Wq_packed,
+              const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks, int M, int N, int K,
+              void* Y_fp16, int ldy, void* workspace, size_t workspace_bytes, void* stream) {
     if (!Xq || !x_scale || !Wq_packed || !w_scale_fp16 || !w_sum || !Y_fp16) return COMET_ERR_NULL;
     int st = check_online_shape(M, N, K, n_int8_blocks);
     if (st != COMET_OK) return st;
@@ -112,6 +130,7 @@ int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
     comet::GemmProblem p{};
     p.Xq = static_cast<const uint8_t*>(Xq);
     p.x_scale = x_scale;
+    p.x_zero = x_zero;
     p.Wq = static_cast<const uint8_t*>(Wq_packed);
     p.w_scale = w_scale_fp16;
     p.w_sum = w_sum;
@@ -130,10 +149,9 @@ int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
     return hip_status(comet::launch_w4ax_gemm(p, stream));
 }
 
-int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* Wq_packed,
-                             const uint16_t* w_scale_fp16, const int16_t* w_sum,
-                             int n_int8_blocks, int M, int N, int K, int m_begin, int m_count,
-                             int32_t* P, void* stream) {
+int partials_impl(const void* Xq, const float* x_scale, const uint8_t* x_zero, const void* Wq_packed,
+                  const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks, int M, int N, int K,
+                  int m_begin, int m_count, int32_t* P, void* stream) {
     if (!Xq || !x_scale || !Wq_packed || !w_scale_fp16 || !w_sum || !P) return COMET_ERR_NULL;
     int st = check_online_shape(M, N, K, n_int8_blocks);
     if (st != COMET_OK) return st;
@@ -146,6 +164,7 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
     comet::GemmProblem p{};
     p.Xq = static_cast<const uint8_t*>(Xq);
     p.x_scale = x_scale;
+    p.x_zero = x_zero;
     p.Wq = static_cast<const uint8_t*>(Wq_packed);
     p.w_scale = w_scale_fp16;
     p.w_sum = w_sum;
@@ -160,6 +179,43 @@ int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* W
     p.m_begin = m_begin;
     p.m_count = m_count;
     return hip_status(comet::launch_w4ax_gemm(p, stream));
+}
+
+}  // namespace
+
+int comet_w4ax_gemm(const void* Xq, const float* x_scale, const void* Wq_packed,
+                     const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks,
+                     int M, int N, int K, void* Y_fp16, int ldy, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    return gemm_impl(Xq, x_scale, nullptr, Wq_packed, w_scale_fp16, w_sum, n_int8_blocks, M, N, K, Y_fp16, ldy,
+                     workspace, workspace_bytes, stream);
+}
+
+int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* Wq_packed,
+                             const uint16_t* w_scale_fp16, const int16_t* w_sum,
+                             int n_int8_blocks, int M, int N, int K, int m_begin, int m_count,
+                             int32_t* P, void* stream) {
+    return partials_impl(Xq, x_scale, nullptr, Wq_packed, w_scale_fp16, w_sum, n_int8_blocks, M, N, K, m_begin,
+                         m_count, P, stream);
+}
+
+int comet_w4ax_gemm_asym(const void* Xq, const float* x_scale, const uint8_t* x_zero, const void* Wq_packed,
+                         const uint16_t* w_scale_fp16, const int16_t* w_sum, int n_int8_blocks, int M, int N,
+                         int K, void* Y_fp16, int ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x_zero) return COMET_ERR_NULL;
+    if (!aligned16(x_zero)) return COMET_ERR_ALIGN;
+    return gemm_impl(Xq, x_scale, x_zero, Wq_packed, w_scale_fp16, w_sum, n_int8_blocks, M, N, K, Y_fp16, ldy,
+                     workspace, workspace_bytes, stream);
+}
+
+int comet_w4ax_gemm_asym_partials(const void* Xq, const float* x_scale, const uint8_t* x_zero,
+                                  const void* Wq_packed, const uint16_t* w_scale_fp16, const int16_t* w_sum,
+                                  int n_int8_blocks, int M, int N, int K, int m_begin, int m_count, int32_t* P,
+                                  void* stream) {
+    if (!x_zero) return COMET_ERR_NULL;
+    if (!aligned16(x_zero)) return COMET_ERR_ALIGN;
+    return partials_impl(Xq, x_scale, x_zero, Wq_packed, w_scale_fp16, w_sum, n_int8_blocks, M, N, K, m_begin,
+                         m_count, P, stream);
 }
 
 size_t comet_xq_fp6_bytes(int M, int K, int n_int8_blocks) {

@@ -30,6 +30,10 @@ inline size_t wq_fp6_bytes(int N, int nb4, int nb8) {
 int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                      uint8_t* Xq, float* x_scale, void* stream);
 
+// Asymmetric 4-bit blocks (INT4 layout); x_zero [nb][Mp], Mp = M rounded up to 16.
+int launch_quant_act_asym(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                          uint8_t* Xq, float* x_scale, uint8_t* x_zero, void* stream);
+
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                          uint8_t* Xq, float* x_scale, void* stream);
 
@@ -53,6 +57,8 @@ struct GemmProblem {
     int M, N, K, nb, nb4;
     uint16_t* Y;
     int ldy;
+    const uint8_t* x_zero;   // zero points of asymmetric 4-bit blocks [nb][Mp] (Mp = M rounded
+                             // up to 16), or nullptr for symmetric codes
     int32_t* P;              // debug partials output, or nullptr
     int m_begin, m_count;    // row range of the partials output
     void* workspace;

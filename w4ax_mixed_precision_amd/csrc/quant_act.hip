@@ -210,12 +210,13 @@ __device__ __forceinline__ uint16_t silu_mul_any(uint16_t gb, uint16_t ub) {
 // value first becomes fp16((x rs) gamma), gamma in permuted order (`gperm`);
 // with kSwi `row` is the gate row and each value is fp16(silu(g) u) with u
 // from the up row `row_u`.
-template <bool kFp6, bool kNorm = false, bool kSwi = false>
+template <bool kFp6, bool kNorm = false, bool kSwi = false, bool kAsym = false>
 __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, const int4 (&pos)[8], int b, int nb,
                                            int nb4, int M, int Mp, int m, int g, uint8_t* __restrict__ Xq,
                                            float* __restrict__ x_scale, float rs = 0.0f,
                                            const uint16_t* __restrict__ gperm = nullptr,
-                                           const uint16_t* __restrict__ row_u = nullptr) {
+                                           const uint16_t* __restrict__ row_u = nullptr,
+                                           uint8_t* __restrict__ x_zero = nullptr) {
     const bool valid = b < nb;
     const int bc = valid ? b : nb - 1;
     const bool is8 = bc >= nb4;
@@ -248,6 +249,55 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
                 v[8 * q + e] = __half2float(__float2half_rn(opaque(t * gm)));
             }
         }
+    }
+    if constexpr (kAsym) {
+        // 4-bit blocks with a scale and a zero point (the QUIK blog's
+        // activation scheme, section "反量化背后的数学"): the range is the
+        // block's minimum and maximum widened to include 0, step d / 15 with
+        // d = hi - lo, zero point z = round(-lo * inv), code u = round(x *
+        // inv) + z, both clamped to [0, 15]; inv = 15 / d and the step are
+        // correctly rounded divisions. 8-bit blocks take the symmetric path.
+        if (!is8) {
+            float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                lo = fminf(lo, v[e]);
+                hi = fmaxf(hi, v[e]);
+            }
+            lo = fminf(lo, dpp_f<0xB1>(lo));     // over the block's quad
+            lo = fminf(lo, dpp_f<0x4E>(lo));
+            hi = fmaxf(hi, dpp_f<0xB1>(hi));
+            hi = fmaxf(hi, dpp_f<0x4E>(hi));
+            float inv = 0.0f, sc = 0.0f, zf = 0.0f;
+            if (lo != hi) {
+                const float d = hi - lo;
+                inv = 15.0f / d;
+                sc = d / 15.0f;
+                zf = fminf(fmaxf(__builtin_rintf(-lo * inv), 0.0f), 15.0f);
+            }
+            if (valid) {
+                uint32_t w[4];
+#pragma unroll
+                for (int d4 = 0; d4 < 4; ++d4) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float ul = fminf(fmaxf(__builtin_rintf(v[4 * d4 + k] * inv) + zf, 0.0f), 15.0f);
+                        const float uh = fminf(fmaxf(__builtin_rintf(v[16 + 4 * d4 + k] * inv) + zf, 0.0f), 15.0f);
+                        x |= (static_cast<uint32_t>(ul) | (static_cast<uint32_t>(uh) << 4)) << (8 * k);
+                    }
+                    w[d4] = x;
+                }
+                uint8_t* dst = Xq + static_cast<size_t>(bc) * M * 64 + static_cast<size_t>(m) * 64 + 16 * g;
+                *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                if (g == 0) {
+                    x_scale[static_cast<size_t>(bc) * M + m] = sc;
+                    x_zero[static_cast<size_t>(bc) * Mp + m] = static_cast<uint8_t>(zf);
+                }
+            }
+            return;
+        }
+        if (valid && g == 0) x_zero[static_cast<size_t>(bc) * Mp + m] = 0;
     }
     float a = 0.0f;
 #pragma unroll
@@ -324,11 +374,12 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
     }
 }
 
-template <bool kRowInLds, bool kFp6, bool kNorm, bool kSwi = false, int T = kThreads>
+template <bool kRowInLds, bool kFp6, bool kNorm, bool kSwi = false, int T = kThreads, bool kAsym = false>
 __global__ __launch_bounds__(T) void quant_act_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm,
     int nb, int nb4, uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd,
-    const uint16_t* __restrict__ gperm, float eps, const uint16_t* __restrict__ U = nullptr) {
+    const uint16_t* __restrict__ gperm, float eps, const uint16_t* __restrict__ U = nullptr,
+    uint8_t* __restrict__ x_zero = nullptr) {
     extern __shared__ uint16_t row_lds[];
     // Row of this workgroup. Workgroup w runs on XCD w mod 8 and each XCD has
     // its own L2; with `rows_per_xcd` > 0 every XCD takes a contiguous range
@@ -466,8 +517,8 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
         if (b0 + stride < nb) load_positions(perm, imin(b0 + stride + bl, nb - 1), g, nxt);
         // from the staged h row, or (rows in global memory) from the gate and
         // up rows with h formed per gathered channel
-        code_block<kFp6, kNorm, kSwi && !kRowInLds>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp, m, g,
-                                                    Xq, x_scale, rs, gperm, ur);
+        code_block<kFp6, kNorm, kSwi && !kRowInLds, kAsym>(kRowInLds ? row_lds : xr, pos, b0 + bl, nb, nb4, M, Mp,
+                                                           m, g, Xq, x_scale, rs, gperm, ur, x_zero);
     }
 }
 
@@ -703,6 +754,33 @@ int cu_count() {
 int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                      uint8_t* Xq, float* x_scale, void* stream) {
     return launch<false, false>(X, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream);
+}
+
+// Asymmetric 4-bit blocks (INT4 layout): the per-row kernel, every M; the
+// zero points go to x_zero [nb][Mp], Mp = M rounded up to a multiple of 16.
+int launch_quant_act_asym(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
+                          uint8_t* Xq, float* x_scale, uint8_t* x_zero, void* stream) {
+    const int nb = K / kBlock;
+    const int nb4 = nb - nb8;
+    constexpr int T = kThreads;
+    const int per_wg = (T / 64) * 16;
+    int groups = 1;
+    while (groups * per_wg < nb && static_cast<long>(M) * groups < 1024) ++groups;
+    const int rows_per_xcd = M >= 128 ? ((M + 127) / 128) * 16 : 0;
+    dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    constexpr size_t kLds = 160 * 1024;
+    const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;
+    if (K <= kMaxLdsRowChannels) {
+        const hipError_t attr = allow_lds<&quant_act_kernel<true, false, false, false, T, true>>(kLds);
+        if (attr != hipSuccess) return static_cast<int>(attr);
+        quant_act_kernel<true, false, false, false, T, true><<<grid, T, row_lds, s>>>(
+            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, nullptr, 0.0f, nullptr, x_zero);
+    } else {
+        quant_act_kernel<false, false, false, false, T, true><<<grid, T, 0, s>>>(
+            X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, nullptr, 0.0f, nullptr, x_zero);
+    }
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,

@@ -39,6 +39,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Accumulator start of a 4-bit block: -16 z w_sum per output (weights enter
+// as 16 q_w), so the accumulator ends at exactly 16 (sum(u q_w) - z w_sum);
+// symmetric codes have z = 8 for every row, 8-bit blocks start at 0. The
+// kernels form it inline from one scalar select (is4 ? -16 w_sum : 0) times
+// the zero point of each row: the same value returned as a vector from a
+// helper made the compiler schedule the streaming kernels' loads far ahead
+// and spill.
+#define COMET_ACC_START_ASYM(m, zw)                                                           \
+    (v4i{(m) * static_cast<int>((zw) & 0xFFu), (m) * static_cast<int>(((zw) >> 8) & 0xFFu), \
+         (m) * static_cast<int>(((zw) >> 16) & 0xFFu), (m) * static_cast<int>((zw) >> 24)})
+
 // ---------------------------------------------------------------------------
 // Tiled kernel (prefill shapes): 128 x 128 output tile per workgroup of four
 // waves in a 2 x 2 arrangement, 64 x 64 per wave, one workgroup per CU.
@@ -80,6 +91,10 @@ constexpr int kLdsSa = kTM * 4;
 constexpr int kLdsSw = kTN * 2;
 constexpr int kLdsWs = kTN * 2;
 constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSw + kLdsWs;
+// asymmetric codes: each wave's own copy of the zero points of rows m0 ..
+// m0 + 255 (one 4-byte direct load per lane; the tile uses the first 128)
+constexpr int kLdsZ = 4 * 256;
+constexpr int stage_bytes(bool asym) { return kStage + (asym ? kLdsZ : 0); }
 constexpr int kStages = COMET_TILED_STAGES;
 static_assert(kStages == 3 || kStages == 4, "the unrolled ring below is written for three or four stages");
 
@@ -89,6 +104,7 @@ struct IssueOffsets {
     uint32_t a4_0, a4_1;               // 4-bit A pieces 2w, 2w+1
     uint32_t a8_0, a8_1, a8_2, a8_3;   // 8-bit A pieces 4w .. 4w+3
     uint32_t sc;                        // scale words: wave 0/1 activation scales, 2 weight scales, 3 sums
+    uint32_t z;                         // zero-point word of rows m0 + 4 lane .. + 3 (clamped into [0, Mp))
 };
 
 __device__ __forceinline__ IssueOffsets issue_offsets(int M, int m0, int wave, int lane) {
@@ -111,14 +127,19 @@ __device__ __forceinline__ IssueOffsets issue_offsets(int M, int m0, int wave, i
     // waves 0 and 1: activation scales of rows 64w + lane (clamped into [0, M));
     // waves 2 and 3: two weight scales / sums per lane
     o.sc = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, M - 1)) * 4u : 4u * lane;
+    o.z = static_cast<uint32_t>(imin(m0 + 4 * lane, ((M + 15) & ~15) - 4));
     return o;
 }
 
 // Direct loads of block b into stage `st`: every wave issues 1 scale word
-// load, 2 (4-bit) or 4 (8-bit) A pieces and 2 B fragments, in that order.
+// load, 2 (4-bit) or 4 (8-bit) A pieces and 2 B fragments, in that order
+// (asymmetric codes: first one zero-point word into the wave's own copy).
+template <bool kAsym = false>
 __device__ __forceinline__ void tiled_issue(const GemmProblem& p, int b, int n0, int wave, int lane,
                                             const IssueOffsets& o, uint8_t* st) {
     const int M = p.M, N = p.N, nb = p.nb, nb4 = p.nb4;
+    if constexpr (kAsym)
+        lds_load4(p.x_zero + static_cast<size_t>(b) * ((M + 15) & ~15) + o.z, st + kStage + 256 * wave);
     if (wave < 2) {
         lds_load4(reinterpret_cast<const uint8_t*>(p.x_scale + static_cast<size_t>(b) * M) + o.sc,
                   st + kLdsA + kLdsB + 256 * wave);
@@ -147,25 +168,32 @@ __device__ __forceinline__ void tiled_issue(const GemmProblem& p, int b, int n0,
 }
 
 // Loads one wave issues for block b (0 past the last block).
+template <bool kAsym = false>
 __device__ __forceinline__ int issued_loads(int b, int nb, int nb4) {
-    return b >= nb ? 0 : (b < nb4 ? 5 : 7);
+    return b >= nb ? 0 : (b < nb4 ? 5 : 7) + (kAsym ? 1 : 0);
 }
 
-// Wait until at most `younger` of this wave's direct loads are outstanding.
+// Wait until at most `younger` of this wave's direct loads are outstanding
+// (the sums of one or two blocks' counts above; any other value waits for
+// all, which is never too little).
 __device__ __forceinline__ void wait_loads(int younger) {
     switch (younger) {
-        case 0: COMET_VMCNT(0); break;
         case 5: COMET_VMCNT(5); break;
+        case 6: COMET_VMCNT(6); break;
         case 7: COMET_VMCNT(7); break;
+        case 8: COMET_VMCNT(8); break;
         case 10: COMET_VMCNT(10); break;
         case 12: COMET_VMCNT(12); break;
-        default: COMET_VMCNT(14); break;
+        case 13: COMET_VMCNT(13); break;
+        case 14: COMET_VMCNT(14); break;
+        case 16: COMET_VMCNT(16); break;
+        default: COMET_VMCNT(0); break;
     }
 }
 
 // One block of the tiled kernel: issue block b+3 into `nxt`, compute block b
 // from `st`, then make block b+1 visible.
-template <bool kDump>
+template <bool kDump, bool kAsym = false>
 __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0, int n0, int row_lo,
                                             int row_hi, int wave, int lane, const IssueOffsets& ioff,
                                             int a4_base, int a8_base, const uint8_t* st, uint8_t* nxt,
@@ -173,7 +201,7 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
     const int wr = wave >> 1, wc = wave & 1;
     const int g = lane >> 4, l16 = lane & 15;
     const int nb = p.nb, nb4 = p.nb4, N = p.N;
-    if (b + kStages - 1 < nb) tiled_issue(p, b + kStages - 1, n0, wave, lane, ioff, nxt);
+    if (b + kStages - 1 < nb) tiled_issue<kAsym>(p, b + kStages - 1, n0, wave, lane, ioff, nxt);
 
     const bool is4 = b < nb4;
     const float* sa_l = reinterpret_cast<const float*>(st + kLdsA + kLdsB);
@@ -182,6 +210,14 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
     // s_x / 16 of this lane's row: the outer product then gives s_x * s_w / 16
     const float sa_lane = sa_l[64 * wr + lane] * 0.0625f;
     const int corr_factor = is4 ? -128 : 0;
+    // asymmetric codes: zero points of this lane's output rows 64 wr + 16 r +
+    // 4 g + i, from the wave's own copy
+    uint32_t zw[4] = {0u, 0u, 0u, 0u};
+    if constexpr (kAsym) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zw[r] = *reinterpret_cast<const uint32_t*>(st + kStage + 256 * wave + 64 * wr + 16 * r + 4 * g);
+    }
 
     // A operands of the four row tiles: row tile r is 1 KB (4-bit) or 2 KB
     // (8-bit) further into the stage; the second half of an 8-bit row is the
@@ -214,9 +250,10 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
         const v4i B1 = widen_weights_hi(pk);
         const int corr = corr_factor * static_cast<int>(ws_l[col]);
         const v4i cinit = {corr, corr, corr, corr};
+        const int zmul = (corr_factor >> 3) * static_cast<int>(ws_l[col]);     // is4 ? -16 w_sum : 0
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            v4i acc = mfma_i8(A0[r], B0, cinit);
+            v4i acc = mfma_i8(A0[r], B0, kAsym ? COMET_ACC_START_ASYM(zmul, zw[r]) : cinit);
             acc = mfma_i8(A1[r], B1, acc);
             if constexpr (kDump) {
                 const int ncol = n0 + col;
@@ -242,17 +279,18 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
     }
     // block b+1's loads are done (only b+2 and b+3 may still be in flight),
     // and every wave is finished with stage `st` before it is refilled
-    wait_loads(issued_loads(b + 2, nb, nb4) + (kStages == 4 ? issued_loads(b + 3, nb, nb4) : 0));
+    wait_loads(issued_loads<kAsym>(b + 2, nb, nb4) + (kStages == 4 ? issued_loads<kAsym>(b + 3, nb, nb4) : 0));
     __builtin_amdgcn_s_barrier();
 }
 
-template <bool kDump>
+template <bool kDump, bool kAsym = false>
 __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_kernel(GemmProblem p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStage];
+    constexpr int kSt = stage_bytes(kAsym);
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kSt];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kSt];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[kSt];
 #if COMET_TILED_STAGES == 4
-    __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage3[kSt];
 #endif
 
     const int row_lo = kDump ? p.m_begin : 0;
@@ -286,29 +324,29 @@ __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_ke
                         16 * (8 * (l16 & 7) + ((2 * g) ^ ((((l16 & 7) >> 1) & 3) | (((l16 >> 3) & 1) << 2))));
 
     // prologue: blocks 0 .. kStages-2 in flight; wait for block 0
-    tiled_issue(p, 0, n0, wave, lane, ioff, stage0);
-    if (1 < nb) tiled_issue(p, 1, n0, wave, lane, ioff, stage1);
-    if (kStages == 4 && 2 < nb) tiled_issue(p, 2, n0, wave, lane, ioff, stage2);
-    wait_loads(issued_loads(1, nb, nb4) + (kStages == 4 ? issued_loads(2, nb, nb4) : 0));
+    tiled_issue<kAsym>(p, 0, n0, wave, lane, ioff, stage0);
+    if (1 < nb) tiled_issue<kAsym>(p, 1, n0, wave, lane, ioff, stage1);
+    if (kStages == 4 && 2 < nb) tiled_issue<kAsym>(p, 2, n0, wave, lane, ioff, stage2);
+    wait_loads(issued_loads<kAsym>(1, nb, nb4) + (kStages == 4 ? issued_loads<kAsym>(2, nb, nb4) : 0));
     __builtin_amdgcn_s_barrier();
 
 #if COMET_TILED_STAGES == 3
     for (int b = 0; b < nb; b += 3) {
-        tiled_block<kDump>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage2, y);
+        tiled_block<kDump, kAsym>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage2, y);
         if (b + 1 < nb)
-            tiled_block<kDump>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
+            tiled_block<kDump, kAsym>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
         if (b + 2 < nb)
-            tiled_block<kDump>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
+            tiled_block<kDump, kAsym>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
     }
 #else
     for (int b = 0; b < nb; b += 4) {
-        tiled_block<kDump>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage3, y);
+        tiled_block<kDump, kAsym>(p, b, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage0, stage3, y);
         if (b + 1 < nb)
-            tiled_block<kDump>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
+            tiled_block<kDump, kAsym>(p, b + 1, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage1, stage0, y);
         if (b + 2 < nb)
-            tiled_block<kDump>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
+            tiled_block<kDump, kAsym>(p, b + 2, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage2, stage1, y);
         if (b + 3 < nb)
-            tiled_block<kDump>(p, b + 3, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage3, stage2, y);
+            tiled_block<kDump, kAsym>(p, b + 3, m0, n0, row_lo, row_hi, wave, lane, ioff, a4_base, a8_base, stage3, stage2, y);
     }
 #endif
 
@@ -347,12 +385,22 @@ struct StreamSlot {
     float sa;         // activation scale of row `srow`
     uint32_t hs;      // weight scale bits of column `ncol`
     int32_t ws;       // weight sum of column `ncol`
+    uint32_t zw[MR];  // asymmetric codes: zero points of rows 16r + 4g .. 16r + 4g + 3
 };
+
+// Zero points of the four output rows 16r + 4g + i (i = 0..3) of row tile r,
+// one byte each, as one aligned word of x_zero [nb][Mp].
+__device__ __forceinline__ uint32_t zero_word(const GemmProblem& p, int b, int r, int g) {
+    const int Mp = (p.M + 15) & ~15;
+    return *reinterpret_cast<const uint32_t*>(p.x_zero + static_cast<size_t>(b) * Mp + 16 * r + 4 * g);
+}
+
+
 
 // Everything block b needs except the weight word: activation words of the
 // lane's rows, activation scale of row `srow`, weight scale and sum of its
 // column. MR == 1 issues exactly five loads.
-template <int MR>
+template <int MR, bool kAsym = false>
 __device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, Rsrc xq, int b, int grp, int lane, int srow,
                                                  const int (&arow)[MR], StreamSlot<MR>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
@@ -376,13 +424,17 @@ __device__ __forceinline__ void stream_fetch_aux(const GemmProblem& p, Rsrc xq, 
         sl.a0[r] = buf_load16(xq, off);
         sl.a1[r] = buf_load16(xq, is4 ? kOutOfRange : off + 16u);
     }
+    if constexpr (kAsym) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) sl.zw[r] = zero_word(p, b, r, g);
+    }
 }
 
-template <int MR>
+template <int MR, bool kAsym = false>
 __device__ __forceinline__ void stream_fetch(const GemmProblem& p, Rsrc xq, int b, int grp, int lane, int srow,
                                              const int (&arow)[MR], StreamSlot<MR>& sl) {
     sl.w = *reinterpret_cast<const uint4*>(p.Wq + (static_cast<size_t>(grp) * p.nb + b) * kFragBytes + 16 * lane);
-    stream_fetch_aux<MR>(p, xq, b, grp, lane, srow, arow, sl);
+    stream_fetch_aux<MR, kAsym>(p, xq, b, grp, lane, srow, arow, sl);
 }
 
 // Buffer resource over the INT4-layout activation codes (M rows; M <= 64 here).
@@ -394,7 +446,7 @@ __device__ __forceinline__ Rsrc stream_xq_rsrc(const GemmProblem& p) {
 
 // One block from a slot. `valid` is false for the clamped refetches past the
 // wave's last block: they get a zero scale product, which adds exactly zero.
-template <int MR>
+template <int MR, bool kAsym = false>
 __device__ __forceinline__ void stream_compute(bool valid, bool is4, const StreamSlot<MR>& sl,
                                                float (&y)[MR][4]) {
     const v4i B0 = widen_weights_lo(sl.w);
@@ -402,6 +454,7 @@ __device__ __forceinline__ void stream_compute(bool valid, bool is4, const Strea
     const float sw = valid ? h2f(static_cast<uint16_t>(sl.hs)) * 0.0625f : 0.0f;
     const int corr = is4 ? -128 * sl.ws : 0;
     const v4i cinit = {corr, corr, corr, corr};
+    const int zmul = is4 ? -16 * sl.ws : 0;
     // t[4r + i] = s_x[row 16r + 4g + i] * s_w[col] / 16 for the MR row tiles
     v16f t = {};
     t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
@@ -415,14 +468,14 @@ __device__ __forceinline__ void stream_compute(bool valid, bool is4, const Strea
             A0 = as_v4i(sl.a0[r]);
             A1 = as_v4i(sl.a1[r]);
         }
-        v4i acc = mfma_i8(A0, B0, cinit);
+        v4i acc = mfma_i8(A0, B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
         acc = mfma_i8(A1, B1, acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[r][i]);
     }
 }
 
-template <int MR, int kD, int kSplit>
+template <int MR, int kD, int kSplit, bool kAsym = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p) {
     __shared__ float red[kSplit][MR * 4][64];
     const int lane = threadIdx.x & 63;
@@ -454,14 +507,15 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
         const int last = b_end - 1;
         StreamSlot<MR> slot[kD];
 #pragma unroll
-        for (int u = 0; u < kD; ++u) stream_fetch<MR>(p, xq, imin(b_begin + u, last), grp, lane, srow, arow, slot[u]);
+        for (int u = 0; u < kD; ++u)
+            stream_fetch<MR, kAsym>(p, xq, imin(b_begin + u, last), grp, lane, srow, arow, slot[u]);
         for (int b0 = b_begin; b0 < b_end; b0 += kD) {
 #pragma unroll
             for (int u = 0; u < kD; ++u) {
                 const int b = b0 + u;
-                stream_compute<MR>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                stream_compute<MR, kAsym>(b < b_end, imin(b, last) < nb4, slot[u], y);
                 if (b0 + kD < b_end)
-                    stream_fetch<MR>(p, xq, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
+                    stream_fetch<MR, kAsym>(p, xq, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
             }
         }
     }
@@ -504,9 +558,10 @@ struct StreamSlotG {
     float sa;
     uint32_t hs[G];
     int32_t ws[G];
+    uint32_t zw[MR];
 };
 
-template <int MR, int G>
+template <int MR, int G, bool kAsym = false>
 __device__ __forceinline__ void stream_fetch_g(const GemmProblem& p, Rsrc xq, int b, int grp0, int lane, int srow,
                                                const int (&arow)[MR], StreamSlotG<MR, G>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
@@ -533,9 +588,13 @@ __device__ __forceinline__ void stream_fetch_g(const GemmProblem& p, Rsrc xq, in
         sl.a0[r] = buf_load16(xq, off);
         sl.a1[r] = buf_load16(xq, is4 ? kOutOfRange : off + 16u);
     }
+    if constexpr (kAsym) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) sl.zw[r] = zero_word(p, b, r, g);
+    }
 }
 
-template <int MR, int G>
+template <int MR, int G, bool kAsym = false>
 __device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlotG<MR, G>& sl,
                                                  float (&y)[G][MR][4]) {
     // 4-bit rows: the one word holds both halves of the lane's 32 positions;
@@ -558,11 +617,12 @@ __device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlo
         const float sw = valid ? h2f(static_cast<uint16_t>(sl.hs[j])) * 0.0625f : 0.0f;
         const int corr = is4 ? -128 * sl.ws[j] : 0;
         const v4i cinit = {corr, corr, corr, corr};
+        const int zmul = is4 ? -16 * sl.ws[j] : 0;
         v16f t = {};
         t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            v4i acc = mfma_i8(as_v4i(sl.a0[r]), B0, cinit);
+            v4i acc = mfma_i8(as_v4i(sl.a0[r]), B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
             acc = mfma_i8(as_v4i(sl.a1[r]), B1, acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -571,7 +631,7 @@ __device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlo
     }
 }
 
-template <int MR, int G, int kD, int kSplit>
+template <int MR, int G, int kD, int kSplit, bool kAsym = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem p) {
     __shared__ float red[kSplit][MR * 4][64];
     const int lane = threadIdx.x & 63;
@@ -605,14 +665,15 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem 
         const int last = b_end - 1;
         StreamSlotG<MR, G> slot[kD];
 #pragma unroll
-        for (int u = 0; u < kD; ++u) stream_fetch_g<MR, G>(p, xq, imin(b_begin + u, last), grp0, lane, srow, arow, slot[u]);
+        for (int u = 0; u < kD; ++u)
+            stream_fetch_g<MR, G, kAsym>(p, xq, imin(b_begin + u, last), grp0, lane, srow, arow, slot[u]);
         for (int b0 = b_begin; b0 < b_end; b0 += kD) {
 #pragma unroll
             for (int u = 0; u < kD; ++u) {
                 const int b = b0 + u;
-                stream_compute_g<MR, G>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                stream_compute_g<MR, G, kAsym>(b < b_end, imin(b, last) < nb4, slot[u], y);
                 if (b0 + kD < b_end)
-                    stream_fetch_g<MR, G>(p, xq, imin(b + kD, last), grp0, lane, srow, arow, slot[u]);
+                    stream_fetch_g<MR, G, kAsym>(p, xq, imin(b + kD, last), grp0, lane, srow, arow, slot[u]);
             }
         }
     }
@@ -651,14 +712,16 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem 
 
 constexpr int kRingA = 4;   // blocks of activation words and scales in registers
 constexpr int kRingR = 8;   // fragments in flight into the LDS ring
-constexpr int kAuxLoads = 5;     // stream_fetch_aux<1>: two activation words, three scalars
+// stream_fetch_aux<1>: two activation words, three scalars (and the
+// zero-point word with asymmetric codes)
+constexpr int aux_loads(bool asym) { return asym ? 6 : 5; }
 
 // Loads issued after block i's aux loads: fragment i+kR-kA, then for each
 // block j in (i, i+kA) its aux loads and fragment j+kR-kA (none past nbw).
-constexpr int lds_loads_after(int i, int nbw) {
+constexpr int lds_loads_after(int i, int nbw, bool asym) {
     int after = (i + kRingR - kRingA < nbw) ? 1 : 0;
     for (int j = i + 1; j < i + kRingA; ++j) {
-        if (j < nbw) after += kAuxLoads;
+        if (j < nbw) after += aux_loads(asym);
         if (j + kRingR - kRingA < nbw) after += 1;
     }
     return after;
@@ -669,7 +732,7 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
     (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int NBW, int kSplit>
+template <int NBW, int kSplit, bool kAsym = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProblem p) {
     constexpr int MR = 1;
     __shared__ float red[kSplit][4][64];
@@ -702,17 +765,17 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
         if (i < NBW) fragment(i);
 #pragma unroll
     for (int k = 0; k < kRingA; ++k) {
-        if (k < NBW) stream_fetch_aux<MR>(p, xq, b_begin + k, grp, lane, srow, arow, slot[k]);
+        if (k < NBW) stream_fetch_aux<MR, kAsym>(p, xq, b_begin + k, grp, lane, srow, arow, slot[k]);
         if (k + kRingR - kRingA < NBW) fragment(k + kRingR - kRingA);
     }
     unroll_seq([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        COMET_VMCNT(lds_loads_after(i, NBW));
+        COMET_VMCNT(lds_loads_after(i, NBW, kAsym));
         StreamSlot<MR>& sl = slot[i % kRingA];
         sl.w = *reinterpret_cast<const uint4*>(my + (i % kRingR) * kFragBytes + 16 * lane);
-        stream_compute<MR>(true, b_begin + i < nb4, sl, y);
+        stream_compute<MR, kAsym>(true, b_begin + i < nb4, sl, y);
         // the ring slot just read is refilled only after its word is used
-        if (i + kRingA < NBW) stream_fetch_aux<MR>(p, xq, b_begin + i + kRingA, grp, lane, srow, arow, sl);
+        if (i + kRingA < NBW) stream_fetch_aux<MR, kAsym>(p, xq, b_begin + i + kRingA, grp, lane, srow, arow, sl);
         if (i + kRingR < NBW) fragment(i + kRingR);
     }, std::make_integer_sequence<int, NBW>{});
 
@@ -742,34 +805,36 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
 // issue pattern, as in gemm_stream_lds_kernel.
 // ---------------------------------------------------------------------------
 
-template <int MR, int G>
+template <int MR, int G, bool kAsym = false>
 struct AuxSlotG {
     uint4 a0[MR];
     uint4 a1[MR];
     float sa;
     uint32_t hs[G];
     int32_t ws[G];
+    uint32_t zw[kAsym ? MR : 1];
 };
 
 // Loads of one block's aux fetch: two activation words per row tile, the
-// activation scale, G weight scales and G weight sums.
-template <int MR, int G>
-constexpr int aux_loads_g() { return 2 * MR + 1 + 2 * G; }
+// activation scale, G weight scales and G weight sums (and a zero-point word
+// per row tile with asymmetric codes).
+template <int MR, int G, bool kAsym>
+constexpr int aux_loads_g() { return 2 * MR + 1 + 2 * G + (kAsym ? MR : 0); }
 
 // Loads issued after block i's aux loads (see the issue order in the kernel).
-template <int MR, int G, int kRA, int kRR>
+template <int MR, int G, int kRA, int kRR, bool kAsym>
 constexpr int lds_g_loads_after(int i, int nbw) {
     int after = (i + kRR - kRA < nbw) ? G : 0;
     for (int j = i + 1; j < i + kRA; ++j) {
-        if (j < nbw) after += aux_loads_g<MR, G>();
+        if (j < nbw) after += aux_loads_g<MR, G, kAsym>();
         if (j + kRR - kRA < nbw) after += G;
     }
     return after;
 }
 
-template <int MR, int G>
+template <int MR, int G, bool kAsym = false>
 __device__ __forceinline__ void stream_fetch_aux_g(const GemmProblem& p, Rsrc xq, int b, int grp0, int lane,
-                                                   int srow, const int (&arow)[MR], AuxSlotG<MR, G>& sl) {
+                                                   int srow, const int (&arow)[MR], AuxSlotG<MR, G, kAsym>& sl) {
     const int g = lane >> 4, l16 = lane & 15;
     const int M = p.M, N = p.N, nb4 = p.nb4;
     const bool is4 = b < nb4;
@@ -790,10 +855,14 @@ __device__ __forceinline__ void stream_fetch_aux_g(const GemmProblem& p, Rsrc xq
         sl.hs[j] = p.w_scale[static_cast<size_t>(b) * N + ncol];
         sl.ws[j] = p.w_sum[static_cast<size_t>(b) * N + ncol];
     }
+    if constexpr (kAsym) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) sl.zw[r] = zero_word(p, b, r, g);
+    }
 }
 
-template <int MR, int G>
-__device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G>& sl, const uint8_t* frags, int lane,
+template <int MR, int G, bool kAsym = false>
+__device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, kAsym>& sl, const uint8_t* frags, int lane,
                                                      float (&y)[G][MR][4]) {
     // branch-free operand words (a branch on the block kind splits the
     // straight-line block sequence, and the compiler then waits for every
@@ -822,11 +891,12 @@ __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G>& 
         const float sw = h2f(static_cast<uint16_t>(sl.hs[j])) * 0.0625f;
         const int corr = is4 ? -128 * sl.ws[j] : 0;
         const v4i cinit = {corr, corr, corr, corr};
+        const int zmul = is4 ? -16 * sl.ws[j] : 0;
         v16f t = {};
         t = __builtin_amdgcn_mfma_f32_16x16x1f32(sl.sa, sw, t, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            v4i acc = mfma_i8(A0[r], B0, cinit);
+            v4i acc = mfma_i8(A0[r], B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
             acc = mfma_i8(A1[r], B1, acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -835,7 +905,7 @@ __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G>& 
     }
 }
 
-template <int MR, int G, int NBW, int kSplit, int kRA, int kRR>
+template <int MR, int G, int NBW, int kSplit, int kRA, int kRR, bool kAsym = false>
 __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_lds_g_kernel(GemmProblem p) {
     // two LDS objects: the compiler can then tell ring reads from other LDS
     // accesses and waits only for the direct loads a read depends on (with
@@ -875,7 +945,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < MR; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[j][r][i] = 0.0f;
-    AuxSlotG<MR, G> slot[kRA];
+    AuxSlotG<MR, G, kAsym> slot[kRA];
     // issue order: fragments of blocks 0 .. kRR-kRA-1; then for k < kRA the
     // aux loads of block k followed by the fragments of block k + kRR - kRA;
     // in the loop, after block i: aux of i + kRA, fragments of i + kRR
@@ -884,15 +954,15 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
         if (i < NBW) fragments(i);
 #pragma unroll
     for (int k = 0; k < kRA; ++k) {
-        if (k < NBW) stream_fetch_aux_g<MR, G>(p, xq, b_begin + k, grp0, lane, srow, arow, slot[k]);
+        if (k < NBW) stream_fetch_aux_g<MR, G, kAsym>(p, xq, b_begin + k, grp0, lane, srow, arow, slot[k]);
         if (k + kRR - kRA < NBW) fragments(k + kRR - kRA);
     }
     unroll_seq([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR>(i, NBW)));
-        AuxSlotG<MR, G>& sl = slot[i % kRA];
-        stream_compute_lds_g<MR, G>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y);
-        if (i + kRA < NBW) stream_fetch_aux_g<MR, G>(p, xq, b_begin + i + kRA, grp0, lane, srow, arow, sl);
+        COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR, kAsym>(i, NBW)));
+        AuxSlotG<MR, G, kAsym>& sl = slot[i % kRA];
+        stream_compute_lds_g<MR, G, kAsym>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y);
+        if (i + kRA < NBW) stream_fetch_aux_g<MR, G, kAsym>(p, xq, b_begin + i + kRA, grp0, lane, srow, arow, sl);
         // the ring slot just read is refilled only after its words are used
         if (i + kRR < NBW) fragments(i + kRR);
     }, std::make_integer_sequence<int, NBW>{});
@@ -928,26 +998,27 @@ bool use_stream(int M) { return M <= 64; }
 // One row tile (M <= 16): one channel group per workgroup, its blocks split
 // over the waves; the LDS-ring kernel for 32, 64 and 128 blocks, the register
 // kernel (four blocks in flight, 120 VGPRs) otherwise.
+template <bool kAsym>
 int launch_stream1(const GemmProblem& p, hipStream_t st) {
     constexpr int kD = COMET_STREAM_DEPTH;
     const int groups = p.N / 16;
     const int grid = 8 * ((groups + 7) / 8);     // XCD-aware order; surplus workgroups exit
     if (p.nb == 32) {
-        gemm_stream_lds_kernel<8, 4><<<grid, 256, 0, st>>>(p);
+        gemm_stream_lds_kernel<8, 4, kAsym><<<grid, 256, 0, st>>>(p);
     } else if (p.nb == 64 && groups * 8 < 2 * COMET_STREAM_TARGET_WAVES) {
-        gemm_stream_lds_kernel<8, 8><<<grid, 512, 0, st>>>(p);
+        gemm_stream_lds_kernel<8, 8, kAsym><<<grid, 512, 0, st>>>(p);
     } else if (p.nb == 64) {
-        gemm_stream_lds_kernel<16, 4><<<grid, 256, 0, st>>>(p);
+        gemm_stream_lds_kernel<16, 4, kAsym><<<grid, 256, 0, st>>>(p);
     } else if (p.nb == 128) {
-        gemm_stream_lds_kernel<16, 8><<<grid, 512, 0, st>>>(p);
+        gemm_stream_lds_kernel<16, 8, kAsym><<<grid, 512, 0, st>>>(p);
     } else if (groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD) {
         // split the blocks of a channel group over enough waves to keep
         // many weight fragments in flight across the chip
-        gemm_stream_kernel<1, kD, 4><<<grid, 256, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 4, kAsym><<<grid, 256, 0, st>>>(p);
     } else if (groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD) {
-        gemm_stream_kernel<1, kD, 8><<<grid, 512, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 8, kAsym><<<grid, 512, 0, st>>>(p);
     } else {
-        gemm_stream_kernel<1, kD, 16><<<grid, 1024, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 16, kAsym><<<grid, 1024, 0, st>>>(p);
     }
     return static_cast<int>(hipGetLastError());
 }
@@ -955,24 +1026,24 @@ int launch_stream1(const GemmProblem& p, hipStream_t st) {
 // Register multi-group kernel, any block count. Measured against the
 // one-group kernel on the K = 8192 decode shapes it is faster in 11 of 12
 // (N = 10240, M = 64: 34 against 32 us).
-template <int MR, int G, int kSplit>
+template <int MR, int G, int kSplit, bool kAsym>
 int launch_stream_g_cfg(const GemmProblem& p, hipStream_t st) {
     constexpr int kD = 2;
     const int units = p.N / (16 * G);
     const int grid = 8 * ((units + 7) / 8);
-    gemm_stream_g_kernel<MR, G, kD, kSplit><<<grid, 64 * kSplit, 0, st>>>(p);
+    gemm_stream_g_kernel<MR, G, kD, kSplit, kAsym><<<grid, 64 * kSplit, 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int MR>
+template <int MR, bool kAsym>
 int launch_stream_g(const GemmProblem& p, hipStream_t st) {
     const int groups = p.N / 16;
     // four groups per workgroup while that still leaves about two four-wave
     // workgroups per CU; else two groups, with eight waves per workgroup when
     // four-wave workgroups alone would not cover the CUs
-    if (groups / 4 >= 384) return launch_stream_g_cfg<MR, 4, 4>(p, st);
-    if (groups / 2 >= 384) return launch_stream_g_cfg<MR, 2, 4>(p, st);
-    return launch_stream_g_cfg<MR, 2, 8>(p, st);
+    if (groups / 4 >= 384) return launch_stream_g_cfg<MR, 4, 4, kAsym>(p, st);
+    if (groups / 2 >= 384) return launch_stream_g_cfg<MR, 2, 4, kAsym>(p, st);
+    return launch_stream_g_cfg<MR, 2, 8, kAsym>(p, st);
 }
 
 // LDS-ring multi-group kernel, 64 blocks. Two configurations, chosen by
@@ -985,27 +1056,46 @@ int launch_stream_g(const GemmProblem& p, hipStream_t st) {
 // faster when it still yields about 1.5 workgroups per CU (N >= 24576), and
 // at M > 32 from 160 workgroups on (N = 10240, M = 64: 23 against 26 us); the
 // narrow one has twice the waves and wins on the smaller grids.
-template <int MR, int G, int kSplit, int kRR, int kRA>
+template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st) {
     const int units = p.N / (16 * G);
     const int grid = 8 * ((units + 7) / 8);
-    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR><<<grid, 64 * kSplit, 0, st>>>(p);
+    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR, kAsym><<<grid, 64 * kSplit, 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int MR>
+template <int MR, bool kAsym>
 int launch_stream_lds_g(const GemmProblem& p, hipStream_t st) {
     const int wide_units = p.N / 64;
     const bool wide = wide_units >= 384 || (p.M > 32 && wide_units >= 160);
-    if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2>(p, st);
-    return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2>(p, st);
+    if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2, kAsym>(p, st);
+    return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2, kAsym>(p, st);
 }
 
 // Two to four row tiles (16 < M <= 64): several channel groups per wave.
-template <int MR>
+template <int MR, bool kAsym>
 int launch_stream(const GemmProblem& p, hipStream_t st) {
-    if (p.nb == 64) return launch_stream_lds_g<MR>(p, st);
-    return launch_stream_g<MR>(p, st);
+    if (p.nb == 64) return launch_stream_lds_g<MR, kAsym>(p, st);
+    return launch_stream_g<MR, kAsym>(p, st);
+}
+
+template <bool kAsym>
+int launch_gemm(const GemmProblem& p, hipStream_t s) {
+    if (p.P) {
+        const int tiles = ((p.m_count + kTM - 1) / kTM) * (p.N / kTN);
+        gemm_tiled_kernel<true, kAsym><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
+        return static_cast<int>(hipGetLastError());
+    }
+    if (use_stream(p.M)) {
+        const int mr = (p.M + 15) / 16;
+        if (mr == 1) return launch_stream1<kAsym>(p, s);
+        if (mr == 2) return launch_stream<2, kAsym>(p, s);
+        if (mr == 3) return launch_stream<3, kAsym>(p, s);
+        return launch_stream<4, kAsym>(p, s);
+    }
+    const int tiles = ((p.M + kTM - 1) / kTM) * (p.N / kTN);
+    gemm_tiled_kernel<false, kAsym><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
+    return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
@@ -1014,21 +1104,7 @@ size_t gemm_workspace_bytes(int, int, int, int) { return 0; }
 
 int launch_w4ax_gemm(const GemmProblem& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.P) {
-        const int tiles = ((p.m_count + kTM - 1) / kTM) * (p.N / kTN);
-        gemm_tiled_kernel<true><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
-        return static_cast<int>(hipGetLastError());
-    }
-    if (use_stream(p.M)) {
-        const int mr = (p.M + 15) / 16;
-        if (mr == 1) return launch_stream1(p, s);
-        if (mr == 2) return launch_stream<2>(p, s);
-        if (mr == 3) return launch_stream<3>(p, s);
-        return launch_stream<4>(p, s);
-    }
-    const int tiles = ((p.M + kTM - 1) / kTM) * (p.N / kTN);
-    gemm_tiled_kernel<false><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
-    return static_cast<int>(hipGetLastError());
+    return p.x_zero ? launch_gemm<true>(p, s) : launch_gemm<false>(p, s);
 }
 
 }  // namespace comet
