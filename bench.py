@@ -321,6 +321,66 @@ def fusion_ablation(torch, comet, synth, M=4096, K=8192, nb8=7, iters=20):
             "timing": f"HIP events around {iters} back-to-back iterations of each variant"}
 
 
+def asym_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
+    """Asymmetric 4-bit activation blocks (scale and zero point) against the
+    symmetric ones, both on the INT4 layout, at the LLaMA-70B up_proj shape
+    (K = 8192, N = 28672, 7 of 64 blocks 8-bit): quantizer + GEMM per M (the
+    streaming kernels for M <= 64, the tiled INT8 kernel above), HIP events
+    around `iters` back-to-back iterations over weight copies of >= 1 GB; and
+    the error of each against the unquantized product X W^T on 16 rows."""
+    cfg0 = synth.CONFIGS["prefill_up_70b"]
+    K, N, nb8 = cfg0.K, cfg0.N, cfg0.nb8
+    W, score = synth.make_w(cfg0), synth.make_scores(cfg0)
+    pk = comet.comet_pack_weights(W, score, nb8)
+    w0 = comet.upload_weights(pk)
+    copies = copies_for(synth.LayerConfig("asym", 1, K, N, 0, int8_frac=None))
+    ws = [w0] + [{k: (v.clone() if hasattr(v, "clone") else v) for k, v in w0.items()} for _ in range(copies - 1)]
+    Xall = synth.make_x(cfg0)
+    out = {"shape": {"K": K, "N": N, "int8_blocks": nb8, "layout": "int4"}, "per_M": {},
+           "timing": f"HIP events around {iters} back-to-back quantizer + GEMM pairs, {copies} weight copies"}
+    for M in Ms:
+        X = torch.from_numpy(Xall[:M].view(np.float16)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        Xq = torch.empty(comet.xq_bytes(M, K, nb8), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+        xz = torch.zeros((K // 128, (M + 15) // 16 * 16), dtype=torch.uint8, device="cuda")
+        it = {"i": 0}
+
+        def sym():
+            w = ws[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_quant_act(X, w["perm"], nb8, Xq=Xq, x_scale=xs)
+            comet.comet_w4ax_gemm(Xq, xs, w, M, Y=Y)
+
+        def asym():
+            w = ws[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_quant_act_asym(X, w["perm"], nb8, Xq=Xq, x_scale=xs, x_zero=xz)
+            comet.comet_w4ax_gemm_asym(Xq, xs, xz, w, M, Y=Y)
+
+        res = _time_variants(torch, (("sym", sym), ("asym", asym)), iters if M <= 64 else 5)
+        out["per_M"][str(M)] = {"sym_us": res["sym"], "asym_us": res["asym"],
+                                "asym_over_sym": res["asym"] / res["sym"]}
+    # error against the unquantized product on 16 planted-outlier rows
+    rows = 16
+    X = torch.from_numpy(Xall[:rows].view(np.float16)).cuda()
+    ref = Xall[:rows].view(np.float16).astype(np.float64) @ W.view(np.float16).astype(np.float64).T
+    err = {}
+    for name in ("sym", "asym"):
+        if name == "sym":
+            Xq, xs = comet.comet_quant_act(X, w0["perm"], nb8)
+            Y = comet.comet_w4ax_gemm(Xq, xs, w0, rows)
+        else:
+            Xq, xs, xz = comet.comet_quant_act_asym(X, w0["perm"], nb8)
+            Y = comet.comet_w4ax_gemm_asym(Xq, xs, xz, w0, rows)
+        y = Y.float().cpu().numpy().astype(np.float64)
+        err[name] = float(np.sqrt(np.mean((y - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+    out["rel_rms_err_vs_unquantized"] = err
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layers, budget_s):
     """The oracle as it stands, on a bounded sample of rows of every layer: host
     time of steps 3-5 (activation quantization, block partials, epilogue) with
@@ -362,7 +422,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fusion", action="store_true",
-                    help="skip the fused-quantizer ablations (outside the timed step)")
+                    help="skip the fused-quantizer and asymmetric-variant ablations (outside the timed step)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -427,6 +487,7 @@ def main():
     ablate = args.workload == "prefill_70b" and not args.no_fusion
     fusion = fusion_ablation(torch, comet, synth) if ablate else None
     swi = swiglu_ablation(torch, comet, synth) if ablate else None
+    asym = asym_ablation(torch, comet, synth) if ablate else None
 
     cpu = None
     if not args.no_cpu:
@@ -449,6 +510,7 @@ def main():
         "kernels": kernels,
         "norm_quant_fusion": fusion,
         "swiglu_quant_fusion": swi,
+        "asym_activation_variant": asym,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
