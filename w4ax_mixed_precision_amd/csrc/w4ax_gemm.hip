@@ -995,11 +995,25 @@ bool use_stream(int M) { return M <= 64; }
 #define COMET_STREAM_DEPTH 4
 #endif
 
-// One row tile (M <= 16): one channel group per workgroup, its blocks split
-// over the waves; the LDS-ring kernel for 32, 64 and 128 blocks, the register
+// One row tile (M <= 16): at 64 blocks mostly the multi-group LDS-ring
+// kernel (below); otherwise one channel group per workgroup, its blocks split
+// over the waves: the LDS-ring kernel for 32, 64 and 128 blocks, the register
 // kernel (four blocks in flight, 120 VGPRs) otherwise.
+template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym>
+int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st);
+
 template <bool kAsym>
 int launch_stream1(const GemmProblem& p, hipStream_t st) {
+    // 64 blocks: the multi-group LDS-ring kernel in its narrow form (two
+    // groups per wave, eight waves of 8 blocks), except where its grid of
+    // N / 32 workgroups falls between one and two per CU and leaves the CUs
+    // unevenly loaded. Measured at K = 8192, M = 1..16 against the one-group
+    // kernels below: N = 8192 9.3-9.5 against 10.8-11.2 us, N = 28672
+    // 24.7-26.5 against 29.1-31.8 us; N = 10240 (320 workgroups) 13.1-13.5
+    // against 12.8-13.4 us, which stays on the one-group kernel.
+    const int narrow_units = p.N / 32;
+    if (p.nb == 64 && !(narrow_units > 256 && narrow_units < 512))
+        return launch_stream_lds_g_cfg<1, 2, 8, 4, 2, kAsym>(p, st);
     constexpr int kD = COMET_STREAM_DEPTH;
     const int groups = p.N / 16;
     const int grid = 8 * ((groups + 7) / 8);     // XCD-aware order; surplus workgroups exit
