@@ -531,33 +531,38 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
 // 16-row tiles, and its workgroups take consecutive rows of it, so the partial
 // cache lines of one output tile meet in that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = 512;
-constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kRowPasses = 2;                   // kRowWaves * 16 * kRowPasses = 256 blocks
+// Two shapes: 8 waves with 2 passes (8 x 16 x 2 = 256 blocks, K <= 32768, one
+// workgroup per CU), and for K <= 8192 4 waves with 1 pass (64 blocks): half
+// the perm registers and a quarter of the LDS, so two workgroups share a CU
+// and one's row loads and code stores overlap the other's coding.
+template <int kWaves>
+constexpr int row_passes() { return kWaves == 8 ? 2 : 1; }
 
+template <int kWaves>
 __device__ __forceinline__ void stage_row(const uint16_t* xr, int K, int wave, int lane, uint8_t* __restrict__ buf) {
     const Rsrc r = make_rsrc(xr, 2u * static_cast<uint32_t>(K));
     const int chunks = (K + 511) / 512;
-    for (int c = wave; c < chunks; c += kRowWaves) lds_buf16(r, 16u * lane, 1024u * c, buf + 1024 * c);
+    for (int c = wave; c < chunks; c += kWaves) lds_buf16(r, 16u * lane, 1024u * c, buf + 1024 * c);
 }
 
 // One row: start the direct loads of the next row into `nxt_buf`, then code
 // this row from `cur` (distinct buffers, restrict-qualified so that the LDS
 // gathers do not wait for the loads just issued).
-template <bool kFp6, bool kNorm>
+template <bool kFp6, bool kNorm, int kWaves>
 __device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __restrict__ nxt_buf,
-                                         const uint16_t* __restrict__ cur, const int4 (&pos)[kRowPasses][8],
+                                         const uint16_t* __restrict__ cur,
+                                         const int4 (&pos)[row_passes<kWaves>()][8],
                                          int K, int nb, int nb4, int M, int Mp, int m, int wave, int lane,
                                          uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
                                          const uint16_t* __restrict__ gperm, float eps, const double* red_cur,
                                          double* red_nxt) {
-    if (next_row) stage_row(next_row, K, wave, lane, nxt_buf);
+    if (next_row) stage_row<kWaves>(next_row, K, wave, lane, nxt_buf);
     float rs = 0.0f;
     if constexpr (kNorm) rs = rms_from_waves(red_cur, K, eps);
     const int g = lane & 3, bl = lane >> 2;
 #pragma unroll
-    for (int p = 0; p < kRowPasses; ++p) {
-        const int b0 = (p * kRowWaves + wave) * 16;
+    for (int p = 0; p < row_passes<kWaves>(); ++p) {
+        const int b0 = (p * kWaves + wave) * 16;
         if (b0 < nb) code_block<kFp6, kNorm>(cur, pos[p], b0 + bl, nb, nb4, M, Mp, m, g, Xq, x_scale, rs, gperm);
     }
     if constexpr (kNorm) {
@@ -565,14 +570,13 @@ __device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __re
         // done: its wave sum, published by the barrier that opens that row
         if (next_row) {
             COMET_VMCNT(0);
-            const double W = wave_sumsq(reinterpret_cast<const uint16_t*>(nxt_buf), K, wave, lane);
-            if (lane == 0) red_nxt[wave] = W;
+            wave_sums<64 * kWaves>(reinterpret_cast<const uint16_t*>(nxt_buf), K, red_nxt);
         }
     }
 }
 
-template <bool kFp6, bool kNorm>
-__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
+template <bool kFp6, bool kNorm, int kWaves = 8>
+__global__ __launch_bounds__(64 * kWaves) void quant_rows_kernel(
     const uint16_t* __restrict__ X, int M, int K, int ldx, const int32_t* __restrict__ perm, int nb, int nb4,
     uint8_t* __restrict__ Xq, float* __restrict__ x_scale, int rows_per_xcd, int wgs_per_xcd,
     const uint16_t* __restrict__ gperm, float eps) {
@@ -589,18 +593,17 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     const int n = (end - first + wgs_per_xcd - 1) / wgs_per_xcd;
     const int Mp = (M + 15) & ~15;
 
-    int4 pos[kRowPasses][8];
+    int4 pos[row_passes<kWaves>()][8];
 #pragma unroll
-    for (int p = 0; p < kRowPasses; ++p) {
-        const int b = (p * kRowWaves + wave) * 16 + (lane >> 2);
+    for (int p = 0; p < row_passes<kWaves>(); ++p) {
+        const int b = (p * kWaves + wave) * 16 + (lane >> 2);
         load_positions(perm, imin(b, nb - 1), lane & 3, pos[p]);
     }
     double* red = reinterpret_cast<double*>(bufs + 2 * static_cast<size_t>(row_bytes));
-    stage_row(X + static_cast<size_t>(first) * ldx, K, wave, lane, bufs);
+    stage_row<kWaves>(X + static_cast<size_t>(first) * ldx, K, wave, lane, bufs);
     if constexpr (kNorm) {
         COMET_VMCNT(0);
-        const double W = wave_sumsq(reinterpret_cast<const uint16_t*>(bufs), K, wave, lane);
-        if (lane == 0) red[wave] = W;
+        wave_sums<64 * kWaves>(reinterpret_cast<const uint16_t*>(bufs), K, red);
     }
     for (int k = 0; k < n; ++k) {
         const int m = first + k * wgs_per_xcd;
@@ -610,11 +613,11 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
         __builtin_amdgcn_s_barrier();
         const uint16_t* next = k + 1 < n ? X + static_cast<size_t>(m + wgs_per_xcd) * ldx : nullptr;
         if (k & 1)
-            row_step<kFp6, kNorm>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4,
+            row_step<kFp6, kNorm, kWaves>(next, bufs, reinterpret_cast<const uint16_t*>(bufs + row_bytes), pos, K, nb, nb4,
                                   M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red + 8 * (k & 1),
                                   red + 8 * ((k + 1) & 1));
         else
-            row_step<kFp6, kNorm>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4,
+            row_step<kFp6, kNorm, kWaves>(next, bufs + row_bytes, reinterpret_cast<const uint16_t*>(bufs), pos, K, nb, nb4,
                                   M, Mp, m, wave, lane, Xq, x_scale, gperm, eps, red + 8 * (k & 1),
                                   red + 8 * ((k + 1) & 1));
     }
@@ -664,11 +667,18 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
         if (M >= 256 && K <= kMaxLdsRowChannels && 2 * buf + red <= kLds && (ldx & 7) == 0) {
             // the two row buffers (and the wave sums) may exceed the 64 KB
             // default; the kernel's 256 blocks per row cover K <= 32768
-            const hipError_t attr = allow_lds<&quant_rows_kernel<kFp6, kNorm>>(kLds);
+            const int rows_per_xcd = ((M + 127) / 128) * 16;
+            if (nb <= 64) {
+                // 4 waves, 2 workgroups per CU (2 x 2 x 16 KB of LDS at most)
+                const int wgs_per_xcd = 2 * (cu_count() / 8);
+                quant_rows_kernel<kFp6, kNorm, 4><<<8 * wgs_per_xcd, 256, 2 * buf + red, s>>>(
+                    X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, wgs_per_xcd, gperm, eps);
+                return static_cast<int>(hipGetLastError());
+            }
+            const hipError_t attr = allow_lds<&quant_rows_kernel<kFp6, kNorm, 8>>(kLds);
             if (attr != hipSuccess) return static_cast<int>(attr);
             const int wgs_per_xcd = cu_count() / 8;
-            const int rows_per_xcd = ((M + 127) / 128) * 16;
-            quant_rows_kernel<kFp6, kNorm><<<8 * wgs_per_xcd, kRowThreads, 2 * buf + red, s>>>(
+            quant_rows_kernel<kFp6, kNorm, 8><<<8 * wgs_per_xcd, 512, 2 * buf + red, s>>>(
                 X, M, K, ldx, perm, nb, nb4, Xq, x_scale, rows_per_xcd, wgs_per_xcd, gperm, eps);
             return static_cast<int>(hipGetLastError());
         }
