@@ -43,6 +43,17 @@
  *     block order (QUIK blog, section "核融合": the integer result is
  *     dequantized to fp16 while still in registers).
  *
+ *  8. QoQ's progressive group quantization (W4A8; QoQ/QServe article, section
+ *     "渐进式分组量化" and "W4A8 GEMM的核心设计"), a variant of steps 2-5 kept
+ *     apart from them: weights first to per-channel symmetric INT8 in the
+ *     protected range [-119, 119] with an fp16 scale s1, then each
+ *     128-channel group of those INT8 values to asymmetric UINT4 with an
+ *     integer step s2 and zero point z, so that s2 (u - z) is again an 8-bit
+ *     integer; activations per token symmetric INT8; the product is one exact
+ *     integer accumulation over all of K (the dequantization to 8 bits happens
+ *     before the multiply), and only a per-(token, channel) scale remains:
+ *     Y = fp16( (s_x s1) * P ).
+ *
  *  6. RMS normalization before the quantizer (the next step the quantization
  *     fuses into). QoQ/QServe article, section "运行时设计": the activation
  *     quantization of the QKV projection and of the first FFN layer is fused
@@ -760,4 +771,174 @@ int orc_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8. QoQ progressive group quantization (W4A8)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest integer of the rational num / den (den > 0), ties to even. */
+static int orc_div_round_even(int num, int den)
+{
+    int q = num / den, r = num % den;          /* C division truncates toward 0 */
+    if (r < 0) {                                /* make the remainder non-negative */
+        q -= 1;
+        r += den;
+    }
+    /* num / den = q + r / den with 0 <= r < den */
+    if (2 * r > den || (2 * r == den && (q & 1)))
+        q += 1;
+    return q;
+}
+
+/* Second level of one group of 8-bit weights w8[0..n): range [lo, hi] =
+ * [min(0, min w8), max(0, max w8)], integer step s2 = max(1, ceil((hi - lo)
+ * / 15)), zero point z = round(-lo / s2), code u = clamp(round(w8 / s2) + z,
+ * 0, 15), all in exact integer arithmetic, ties to even. Returns s2; z and u
+ * through the pointers. */
+int orc_qoq_group(const int8_t *w8, int n, int *z, uint8_t *u)
+{
+    int lo = 0, hi = 0;
+    for (int k = 0; k < n; ++k) {
+        if (w8[k] < lo) lo = w8[k];
+        if (w8[k] > hi) hi = w8[k];
+    }
+    int s2 = (hi - lo + 14) / 15;
+    if (s2 < 1)
+        s2 = 1;
+    int zz = orc_div_round_even(-lo, s2);
+    *z = zz;
+    for (int k = 0; k < n; ++k) {
+        int v = orc_div_round_even(w8[k], s2) + zz;
+        u[k] = (uint8_t)(v < 0 ? 0 : (v > 15 ? 15 : v));
+    }
+    return s2;
+}
+
+/* Weights [N][K] (original channel order) with channel order perm:
+ *   s1[n] = fp16(a / 119) with a = max |W[n, :]| (the smallest fp16 subnormal
+ *   if that rounds to 0; 0 for an all-zero row), w8 = clamp(round(W / s1),
+ *   -119, 119) (binary32 division, ties to even);
+ *   per 128-channel group g of permuted positions: s2[n][g], z[n][g] and the
+ *   codes u[n][k'] by orc_qoq_group.
+ * w8 is also returned ([N][K], permuted order). */
+int orc_qoq_quantize_weights(const uint16_t *W, int N, int K, const int32_t *perm, uint16_t *s1,
+                             int8_t *w8, uint8_t *s2, uint8_t *z, uint8_t *u)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int n = 0; n < N; ++n) {
+        const uint16_t *wrow = W + (size_t)n * K;
+        float a = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float v = orc_half_to_float(wrow[k]);
+            if (!isfinite(v))
+                bad = 1;
+            if (fabsf(v) > a)
+                a = fabsf(v);
+        }
+        uint16_t h = 0;
+        if (a > 0.0f) {
+            h = orc_float_to_half(a / 119.0f);
+            if (h == 0)
+                h = 1;
+        }
+        s1[n] = h;
+        float s = orc_half_to_float(h);
+        int8_t *wq = w8 + (size_t)n * K;
+        for (int k = 0; k < K; ++k) {
+            if (h == 0) {
+                wq[k] = 0;
+                continue;
+            }
+            float v = orc_half_to_float(wrow[perm[k]]);
+            int q = (int)rintf(v / s);
+            wq[k] = (int8_t)(q < -119 ? -119 : (q > 119 ? 119 : q));
+        }
+        for (int b = 0; b < nb; ++b) {
+            int zz;
+            s2[(size_t)n * nb + b] = (uint8_t)orc_qoq_group(wq + (size_t)b * ORC_BLOCK, ORC_BLOCK, &zz,
+                                                             u + (size_t)n * K + (size_t)b * ORC_BLOCK);
+            z[(size_t)n * nb + b] = (uint8_t)zz;
+        }
+    }
+    return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* Activations [M][ldx], per token over all K in permuted order: a = max |x|,
+ * inv = 127 / a and s = a / 127 (binary32 divisions), q = clamp(round(x *
+ * inv), -127, 127); an all-zero token gets s = 0 and q = 0. */
+int orc_qoq_quantize_activations(const uint16_t *X, int M, int K, int ldx, const int32_t *perm, int8_t *qa,
+                                 float *sa)
+{
+    if (M <= 0 || K <= 0 || K % ORC_BLOCK != 0 || ldx < K)
+        return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xrow = X + (size_t)m * ldx;
+        float a = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float v = orc_half_to_float(xrow[perm[k]]);
+            if (!isfinite(v))
+                bad = 1;
+            if (fabsf(v) > a)
+                a = fabsf(v);
+        }
+        int8_t *q = qa + (size_t)m * K;
+        if (a == 0.0f) {
+            sa[m] = 0.0f;
+            memset(q, 0, (size_t)K);
+            continue;
+        }
+        float inv, s;
+        orc_act_scale(a, 127, &inv, &s);
+        sa[m] = s;
+        for (int k = 0; k < K; ++k)
+            q[k] = (int8_t)orc_act_quantize_value(orc_half_to_float(xrow[perm[k]]), inv, 127);
+    }
+    return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* Rows [m0, m1): P[m - m0][n] = sum over groups of s2 * (sum_k qa u - z sum_k
+ * qa) (the zero point subtracted after the multiplication, as the page puts
+ * it), exact in 64-bit and returned as int32 (|P| <= 127 * 128 * K < 2^31 for
+ * K <= 131072); then y32 = fl(s_x s1) * (float)P, Y16 = fp16(y32), and
+ * yexact = s_x s1 P in double. Any output pointer may be NULL. */
+int orc_qoq_gemm(const int8_t *qa, const float *sa, const uint8_t *u, const uint8_t *s2, const uint8_t *z,
+                 const uint16_t *s1, int M, int N, int K, int m0, int m1, int32_t *P, float *y32,
+                 uint16_t *Y16, double *yexact)
+{
+    if (N <= 0 || K <= 0 || K % ORC_BLOCK != 0 || K > 131072 || m0 < 0 || m1 > M || m0 >= m1)
+        return ORC_ERR_ARG;
+    int nb = K / ORC_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int m = m0; m < m1; ++m) {
+        const int8_t *a = qa + (size_t)m * K;
+        for (int n = 0; n < N; ++n) {
+            const uint8_t *w = u + (size_t)n * K;
+            int64_t acc = 0;
+            for (int b = 0; b < nb; ++b) {
+                int64_t dot = 0, asum = 0;
+                for (int k = b * ORC_BLOCK; k < (b + 1) * ORC_BLOCK; ++k) {
+                    dot += (int64_t)a[k] * (int64_t)w[k];
+                    asum += a[k];
+                }
+                int64_t st = s2[(size_t)n * nb + b];
+                acc += st * dot - st * (int64_t)z[(size_t)n * nb + b] * asum;
+            }
+            size_t o = (size_t)(m - m0) * N + n;
+            if (P) P[o] = (int32_t)acc;
+            float sw = orc_half_to_float(s1[n]);
+            float t = sa[m] * sw;
+            float y = t * (float)acc;
+            if (y32) y32[o] = y;
+            if (Y16) Y16[o] = orc_float_to_half(y);
+            if (yexact) yexact[o] = (double)sa[m] * (double)sw * (double)acc;
+        }
+    }
+    return ORC_OK;
 }

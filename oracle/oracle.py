@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.orc_quantize_weights.argtypes = [P, I, I, P, P, P, P]
         L.orc_quantize_activations.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_block_partials.argtypes = [P, P, I, I, I, I, I, P]
+        L.orc_qoq_group.argtypes = [P, I, P, P]
+        L.orc_qoq_quantize_weights.argtypes = [P, I, I, P, P, P, P, P, P]
+        L.orc_qoq_quantize_activations.argtypes = [P, I, I, I, P, P, P]
+        L.orc_qoq_gemm.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P]
         L.orc_act_asym_params.argtypes = [ctypes.c_float, ctypes.c_float, P, P, P]
         L.orc_act_asym_code.argtypes = [ctypes.c_float, ctypes.c_float, I]
         L.orc_quantize_activations_asym.argtypes = [P, I, I, I, P, P, P, P, P, P]
@@ -346,3 +350,74 @@ def reference(X16, W16, score, nb8, rows=None):
     y32, Y16, ye = epilogue(P, d["sa"][m0:m1], d["sw16"])
     d.update({"P": P, "y32": y32, "Y16": Y16, "yexact": ye, "rows": (m0, m1)})
     return d
+
+
+# ----------------------------------------------------------------------------
+# Step 8: QoQ progressive group quantization (W4A8)
+# ----------------------------------------------------------------------------
+
+def qoq_group(w8: np.ndarray):
+    """(s2, z, u) of one group of 8-bit weights."""
+    w8 = np.ascontiguousarray(w8, dtype=np.int8)
+    u = np.zeros(len(w8), np.uint8)
+    z = ctypes.c_int()
+    s2 = lib().orc_qoq_group(_p(w8), len(w8), ctypes.byref(z), _p(u))
+    return s2, z.value, u
+
+
+def qoq_quantize_weights(W16: np.ndarray, perm: np.ndarray):
+    """(s1 fp16 bits [N], w8 int8 [N, K], s2 uint8 [N, nb], z uint8 [N, nb], u uint8 [N, K])."""
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    N, K = W16.shape
+    nb = K // 128
+    s1 = np.zeros(N, np.uint16)
+    w8 = np.zeros((N, K), np.int8)
+    s2 = np.zeros((N, nb), np.uint8)
+    z = np.zeros((N, nb), np.uint8)
+    u = np.zeros((N, K), np.uint8)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    _check(lib().orc_qoq_quantize_weights(_p(W16), N, K, _p(perm), _p(s1), _p(w8), _p(s2), _p(z), _p(u)),
+           "qoq_quantize_weights")
+    return s1, w8, s2, z, u
+
+
+def qoq_quantize_activations(X16: np.ndarray, perm: np.ndarray):
+    """(qa int8 [M, K] permuted, sa float32 [M])."""
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    M, K = X16.shape
+    qa = np.zeros((M, K), np.int8)
+    sa = np.zeros(M, np.float32)
+    perm = np.ascontiguousarray(perm, dtype=np.int32)
+    _check(lib().orc_qoq_quantize_activations(_p(X16), M, K, K, _p(perm), _p(qa), _p(sa)),
+           "qoq_quantize_activations")
+    return qa, sa
+
+
+def qoq_gemm(qa, sa, u, s2, z, s1, rows=None):
+    """(P int32 [rows, N], y32, Y16, yexact) for rows (default all)."""
+    qa = np.ascontiguousarray(qa, dtype=np.int8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.uint8)
+    s2 = np.ascontiguousarray(s2, dtype=np.uint8)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    s1 = np.ascontiguousarray(s1, dtype=np.uint16)
+    M, K = qa.shape
+    N = u.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    P = np.zeros((m1 - m0, N), np.int32)
+    y32 = np.zeros((m1 - m0, N), np.float32)
+    Y16 = np.zeros((m1 - m0, N), np.uint16)
+    ye = np.zeros((m1 - m0, N), np.float64)
+    _check(lib().orc_qoq_gemm(_p(qa), _p(sa), _p(u), _p(s2), _p(z), _p(s1), M, N, K, m0, m1, _p(P), _p(y32),
+                              _p(Y16), _p(ye)), "qoq_gemm")
+    return P, y32, Y16, ye
+
+
+def qoq_layer(X16, W16, score, rows=None):
+    """Every logical array of a QoQ W4A8 layer plus its product rows."""
+    perm, _ = channel_order(score, 0)
+    s1, w8, s2, z, u = qoq_quantize_weights(W16, perm)
+    qa, sa = qoq_quantize_activations(X16, perm)
+    P, y32, Y16, ye = qoq_gemm(qa, sa, u, s2, z, s1, rows)
+    return {"perm": perm, "s1": s1, "w8": w8, "s2": s2, "z": z, "u": u, "qa": qa, "sa": sa,
+            "P": P, "y32": y32, "Y16": Y16, "yexact": ye}
