@@ -188,3 +188,20 @@ def test_determinism_and_streams(torch):
     torch.cuda.synchronize()
     assert torch.equal(Y, Y2) and torch.equal(Y, Y3)
     assert torch.equal(Xq, Xq3) and torch.equal(xs, xs3)
+
+
+@pytest.mark.parametrize("name", ["decode_70b_n8192_m1", "decode_70b_n28672_m16", "decode_70b_n10240_m64"])
+def test_decode_determinism_and_streams(torch, name):
+    """The streaming kernels (split-K inside the workgroup, summed in wave order):
+    bit-identical Y across runs and on a side stream."""
+    import w4ax_mixed_precision_amd as comet
+    d, pk, w, Xq, xs, Y = run_layer(torch, name)
+    cfg = d["cfg"]
+    Y2 = comet.comet_w4ax_gemm(Xq, xs, w, cfg.M)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        Y3 = comet.comet_w4ax_gemm(Xq, xs, w, cfg.M)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2) and torch.equal(Y, Y3)
