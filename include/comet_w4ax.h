@@ -248,6 +248,45 @@ int comet_w4ax_gemm_asym_partials(const void* Xq, const float* x_scale, const ui
                                   void* stream);
 
 /*
+ * QoQ W4A8 variant: progressive group quantization (QoQ/QServe article,
+ * sections "渐进式分组量化" and "W4A8 GEMM的核心设计"). Weights: per output
+ * channel symmetric INT8 in the protected range [-119, 119] with an fp16 scale
+ * s1 = fp16(max |W[n, :]| / 119), w8 = clamp(round(W / s1), -119, 119); then per
+ * 128-channel group of the permuted order (perm as comet_pack_weights, ascending
+ * score) over the range [lo, hi] = [min(0, min w8), max(0, max w8)]: integer
+ * step s2 = max(1, ceil((hi - lo) / 15)), zero point z = round(-lo / s2),
+ * code u = clamp(round(w8 / s2) + z, 0, 15) (exact integer rounding, ties to
+ * even), so that s2 (u - z) is an 8-bit integer. Activations: one symmetric
+ * INT8 scale per token over all K. Product: P = sum over K of q_a s2 (u - z),
+ * one exact INT32 sum; Y = fp16( fl(x_scale * s1) * float(P) ).
+ *
+ * comet_pack_weights_qoq (host): perm int32 [K]; Wu_packed N*K/2 bytes in the
+ * Wq fragment order of comet_pack_weights, unsigned codes u; s1_fp16 [N];
+ * s2z uint16 [K/128][N] = s2 | z << 8. Errors: NULL, SHAPE, ARG (non-finite
+ * score or weight), UNSUPPORTED (N % 128).
+ */
+int comet_pack_weights_qoq(const uint16_t* W_fp16, int N, int K, const float* chan_score, int32_t* perm,
+                           uint8_t* Wu_packed, uint16_t* s1_fp16, uint16_t* s2z);
+
+/* Per-token INT8 codes in 8-bit slabs (block b, row m at byte (b M + m) 128,
+ * positions in order; M*K bytes) and x_scale float [M]: a = max |x| over the
+ * row, inv = 127 / a, s = a / 127, q = round(x * inv). Errors: NULL, SHAPE,
+ * ALIGN, UNSUPPORTED (K > 32768), HIP. */
+int comet_quant_act_token_i8(const void* X_fp16, int M, int K, int ldx, const int32_t* perm, void* Xq,
+                             float* x_scale, void* stream);
+
+/* The QoQ GEMM, M <= 64 (weight-streaming decode shapes): the codes are
+ * dequantized to s2 (u - z) in registers before the INT8 matrix instruction.
+ * Y fp16 [M][ldy]. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 64, N % 128,
+ * K > 32768), HIP. */
+int comet_w4a8_qoq_gemm(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
+                        const uint16_t* s1_fp16, int M, int N, int K, void* Y_fp16, int ldy, void* stream);
+
+/* Debug variant: the exact products P int32 [M][N] instead of Y. */
+int comet_w4a8_qoq_gemm_products(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
+                                 const uint16_t* s1_fp16, int M, int N, int K, int32_t* P, void* stream);
+
+/*
  * FP6 layout, sizes: bytes of Xq_fp6 for M rows (padded to a multiple of 16)
  * and of Wq_fp6 for N output channels (0 for an invalid shape).
  */

@@ -21,6 +21,24 @@ def decode_wq(Wq: np.ndarray, N: int, K: int) -> np.ndarray:
     return q.reshape(N, K)
 
 
+def decode_wu(Wu: np.ndarray, N: int, K: int) -> np.ndarray:
+    """QoQ pack: unsigned codes u uint8 [N, K] in permuted channel order (the
+    fragment order of decode_wq, nibbles read without sign)."""
+    nb = K // 128
+    f = np.asarray(Wu, dtype=np.uint8).reshape(N // 16, nb, 4, 16, 16)   # [c, b, g, n16, j]
+    u = np.empty((N // 16, 16, nb, 4, 2, 16), np.uint8)                  # [c, n16, b, g, half, j]
+    u[:, :, :, :, 0, :] = (f & 0xF).transpose(0, 3, 1, 2, 4)
+    u[:, :, :, :, 1, :] = (f >> 4).transpose(0, 3, 1, 2, 4)
+    return u.reshape(N, K)
+
+
+def decode_xq_token_i8(Xq: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Per-token INT8 slabs ([nb][M][128]) -> q int8 [M, K] in permuted order."""
+    nb = K // 128
+    s = np.asarray(Xq, dtype=np.uint8).view(np.int8).reshape(nb, M, 128)
+    return s.transpose(1, 0, 2).reshape(M, K)
+
+
 def decode_xq(Xq: np.ndarray, M: int, K: int, nb8: int) -> np.ndarray:
     """Xq bytes -> q_a int8 [M, K] in permuted channel order."""
     nb = K // 128

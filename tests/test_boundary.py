@@ -269,3 +269,30 @@ def test_x_zero_bytes():
     assert L.comet_x_zero_bytes(17, 8192) == 64 * 32
     assert L.comet_x_zero_bytes(4096, 28672) == 224 * 4096
     assert L.comet_x_zero_bytes(0, 512) == 0 and L.comet_x_zero_bytes(16, 100) == 0
+
+
+def test_qoq_rejections():
+    L = comet.lib()
+
+    def pq(W=A, N=128, K=256, sc=A, perm=A, Wu=A, s1=A, s2z=A):
+        return L.comet_pack_weights_qoq(W, N, K, sc, perm, Wu, s1, s2z)
+
+    def qt(X=A, M=16, K=512, ldx=512, perm=A, Xq=A, xs=A):
+        return L.comet_quant_act_token_i8(X, M, K, ldx, perm, Xq, xs, None)
+
+    def gq(Xq=A, xs=A, Wu=A, s2z=A, s1=A, M=16, N=512, K=512, Y=A, ldy=512):
+        return L.comet_w4a8_qoq_gemm(Xq, xs, Wu, s2z, s1, M, N, K, Y, ldy, None)
+
+    def gqp(Xq=A, xs=A, Wu=A, s2z=A, s1=A, M=16, N=512, K=512, P=A):
+        return L.comet_w4a8_qoq_gemm_products(Xq, xs, Wu, s2z, s1, M, N, K, P, None)
+
+    assert pq(W=None) == NULL and pq(s2z=None) == NULL
+    assert pq(K=100) == SHAPE and pq(N=0) == SHAPE and pq(N=96) == UNSUP
+    assert qt(X=None) == NULL and qt(xs=None) == NULL
+    assert qt(M=0) == SHAPE and qt(K=100) == SHAPE and qt(ldx=500) == SHAPE
+    assert qt(K=33024, ldx=33024) == UNSUP and qt(Xq=MIS) == ALIGN
+    assert gq(Y=None) == NULL and gq(s1=None) == NULL
+    assert gq(M=0) == SHAPE and gq(ldy=500) == SHAPE and gq(K=100) == SHAPE
+    assert gq(M=65) == UNSUP and gq(N=200, ldy=200) == UNSUP and gq(K=33024) == UNSUP
+    assert gq(Wu=MIS) == ALIGN and gq(Y=MIS) == ALIGN and gq(s2z=MIS) == ALIGN
+    assert gqp(P=None) == NULL and gqp(P=MIS) == ALIGN and gqp(M=65) == UNSUP

@@ -74,3 +74,22 @@ def test_repack_fp6_matches_oracle(orc, name, nb8):
     perm, _ = orc.channel_order(score, nb8)
     qw, _, _ = orc.quantize_weights(W, perm)
     assert np.array_equal(decode_wq_fp6(pk["WqF"], N, K, nb8), qw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "q_proj_7b"])
+def test_qoq_pack_matches_oracle(name):
+    """The library's QoQ pack (perm, s1, s2, z, unsigned codes in fragment order)
+    equals the oracle's progressive group quantization bit for bit."""
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    from tests.layout import decode_wu
+    cfg = synth.CONFIGS[name]
+    W, score = synth.make_w(cfg), synth.make_scores(cfg)
+    pk = comet.comet_pack_weights_qoq(W, score)
+    perm, _ = O.channel_order(score, 0)
+    s1, w8, s2, z, u = O.qoq_quantize_weights(W, perm)
+    assert np.array_equal(pk["perm"], perm)
+    assert np.array_equal(pk["s1"], s1)
+    assert np.array_equal((pk["s2z"] & 0xFF).T, s2)
+    assert np.array_equal((pk["s2z"] >> 8).T, z)
+    assert np.array_equal(decode_wu(pk["Wu"], cfg.N, cfg.K), u)

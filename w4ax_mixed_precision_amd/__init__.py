@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P]
     L.comet_quant_act_asym.argtypes = [P, I, I, I, P, I, P, P, P, P]
+    L.comet_pack_weights_qoq.argtypes = [P, I, I, P, P, P, P, P]
+    L.comet_quant_act_token_i8.argtypes = [P, I, I, I, P, P, P, P]
+    L.comet_w4a8_qoq_gemm.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
+    L.comet_w4a8_qoq_gemm_products.argtypes = [P, P, P, P, P, I, I, I, P, P]
     L.comet_x_zero_bytes.argtypes = [I, I]
     L.comet_x_zero_bytes.restype = Z
     L.comet_w4ax_gemm_asym.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, Z, P]
@@ -78,7 +82,9 @@ def lib() -> ctypes.CDLL:
               "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_rmsnorm_quant_act",
               "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels",
               "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
-              "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials"):
+              "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
+              "comet_pack_weights_qoq", "comet_quant_act_token_i8", "comet_w4a8_qoq_gemm",
+              "comet_w4a8_qoq_gemm_products"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -91,7 +97,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
            "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
-           "comet_w4ax_gemm_asym_partials", "comet_status_string", "comet_version")
+           "comet_w4ax_gemm_asym_partials", "comet_pack_weights_qoq", "comet_quant_act_token_i8",
+           "comet_w4a8_qoq_gemm", "comet_w4a8_qoq_gemm_products", "comet_status_string", "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -250,6 +257,68 @@ def comet_w4ax_gemm_asym_partials(Xq, x_scale, x_zero, w: dict, M: int, m_begin:
                                              _dev_ptr(w["Wq"]), _dev_ptr(w["w_scale"]), _dev_ptr(w["w_sum"]),
                                              int(nb8), M, N, K, m_begin, m_count, _dev_ptr(P), _stream(stream))
     _check("comet_w4ax_gemm_asym_partials", rc)
+    return P
+
+
+def comet_pack_weights_qoq(W16: np.ndarray, score: np.ndarray) -> dict:
+    """QoQ progressive group quantization of W (host): perm, Wu (unsigned codes,
+    fragment order), s1 fp16 bits [N], s2z uint16 [nb, N] (s2 | z << 8)."""
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    N, K = W16.shape
+    score = np.ascontiguousarray(score, dtype=np.float32)
+    perm = np.zeros(K, np.int32)
+    Wu = np.zeros(N * K // 2, np.uint8)
+    s1 = np.zeros(N, np.uint16)
+    s2z = np.zeros((K // 128, N), np.uint16)
+    _check("comet_pack_weights_qoq", lib().comet_pack_weights_qoq(_np_ptr(W16), N, K, _np_ptr(score),
+                                                                  _np_ptr(perm), _np_ptr(Wu), _np_ptr(s1),
+                                                                  _np_ptr(s2z)))
+    return {"perm": perm, "Wu": Wu, "s1": s1, "s2z": s2z, "N": N, "K": K}
+
+
+def upload_qoq(pk: dict, device="cuda") -> dict:
+    import torch
+    d = {k: torch.from_numpy(pk[k].view(np.int16) if pk[k].dtype == np.uint16 else pk[k]).to(device)
+         for k in ("perm", "Wu", "s1", "s2z")}
+    d.update({"N": pk["N"], "K": pk["K"]})
+    return d
+
+
+def comet_quant_act_token_i8(X, perm, Xq=None, x_scale=None, stream=None):
+    """Per-token INT8 codes (8-bit slabs, M*K bytes) and x_scale float32 [M]."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    if Xq is None:
+        Xq = torch.empty(M * K, dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    rc = lib().comet_quant_act_token_i8(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(perm), _dev_ptr(Xq),
+                                        _dev_ptr(x_scale), _stream(stream))
+    _check("comet_quant_act_token_i8", rc)
+    return Xq, x_scale
+
+
+def comet_w4a8_qoq_gemm(Xq, x_scale, w: dict, M: int, Y=None, stream=None):
+    import torch
+    N, K = w["N"], w["K"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    rc = lib().comet_w4a8_qoq_gemm(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["Wu"]), _dev_ptr(w["s2z"]),
+                                   _dev_ptr(w["s1"]), M, N, K, _dev_ptr(Y), Y.stride(0), _stream(stream))
+    _check("comet_w4a8_qoq_gemm", rc)
+    return Y
+
+
+def comet_w4a8_qoq_gemm_products(Xq, x_scale, w: dict, M: int, P=None, stream=None):
+    import torch
+    N, K = w["N"], w["K"]
+    if P is None:
+        P = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    rc = lib().comet_w4a8_qoq_gemm_products(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["Wu"]),
+                                            _dev_ptr(w["s2z"]), _dev_ptr(w["s1"]), M, N, K, _dev_ptr(P),
+                                            _stream(stream))
+    _check("comet_w4a8_qoq_gemm_products", rc)
     return P
 
 

@@ -4,6 +4,7 @@
 #include <limits>
 
 #include "comet_internal.h"
+#include "qoq_internal.h"
 
 namespace {
 
@@ -100,6 +101,61 @@ int comet_quant_act_asym(const void* X_fp16, int M, int K, int ldx, const int32_
     return hip_status(comet::launch_quant_act_asym(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
                                                    n_int8_blocks, static_cast<uint8_t*>(Xq), x_scale, x_zero,
                                                    stream));
+}
+
+int comet_pack_weights_qoq(const uint16_t* W_fp16, int N, int K, const float* chan_score, int32_t* perm,
+                           uint8_t* Wu_packed, uint16_t* s1_fp16, uint16_t* s2z) {
+    if (!W_fp16 || !chan_score || !perm || !Wu_packed || !s1_fp16 || !s2z) return COMET_ERR_NULL;
+    if (N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (N % 128 != 0) return COMET_ERR_UNSUPPORTED;
+    return comet::pack_weights_qoq(W_fp16, N, K, chan_score, perm, Wu_packed, s1_fp16, s2z);
+}
+
+int comet_quant_act_token_i8(const void* X_fp16, int M, int K, int ldx, const int32_t* perm, void* Xq,
+                             float* x_scale, void* stream) {
+    if (!X_fp16 || !perm || !Xq || !x_scale) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (K > 32768) return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(X_fp16) || !aligned16(perm) || !aligned16(Xq) || !aligned16(x_scale)) return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_quant_act_token_i8(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm,
+                                                       static_cast<uint8_t*>(Xq), x_scale, stream));
+}
+
+namespace {
+
+int qoq_check(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
+              const uint16_t* s1_fp16, int M, int N, int K) {
+    if (!Xq || !x_scale || !Wu_packed || !s2z || !s1_fp16) return COMET_ERR_NULL;
+    if (M < 1 || N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (N % 128 != 0 || M > 64 || K > 32768) return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(Wu_packed) || !aligned16(s2z) || !aligned16(s1_fp16))
+        return COMET_ERR_ALIGN;
+    return COMET_OK;
+}
+
+}  // namespace
+
+int comet_w4a8_qoq_gemm(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
+                        const uint16_t* s1_fp16, int M, int N, int K, void* Y_fp16, int ldy, void* stream) {
+    if (!Y_fp16) return COMET_ERR_NULL;
+    const int st = qoq_check(Xq, x_scale, Wu_packed, s2z, s1_fp16, M, N, K);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (!aligned16(Y_fp16)) return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_qoq_gemm(static_cast<const uint8_t*>(Xq), x_scale,
+                                             static_cast<const uint8_t*>(Wu_packed), s2z, s1_fp16, M, N, K,
+                                             static_cast<uint16_t*>(Y_fp16), ldy, nullptr, stream));
+}
+
+int comet_w4a8_qoq_gemm_products(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
+                                 const uint16_t* s1_fp16, int M, int N, int K, int32_t* P, void* stream) {
+    if (!P) return COMET_ERR_NULL;
+    const int st = qoq_check(Xq, x_scale, Wu_packed, s2z, s1_fp16, M, N, K);
+    if (st != COMET_OK) return st;
+    if (!aligned16(P)) return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_qoq_gemm(static_cast<const uint8_t*>(Xq), x_scale,
+                                             static_cast<const uint8_t*>(Wu_packed), s2z, s1_fp16, M, N, K,
+                                             nullptr, N, P, stream));
 }
 
 size_t comet_x_zero_bytes(int M, int K) {

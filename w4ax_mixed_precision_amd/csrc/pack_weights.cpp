@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "comet_internal.h"
+#include "qoq_internal.h"
 
 namespace comet {
 namespace {
@@ -169,6 +170,106 @@ int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, i
         pool.emplace_back([=, &ok] {
             for (int n = n0; n < n1; ++n)
                 if (!pack_row(W + static_cast<size_t>(n) * K, N, K, perm, n, Wq, w_scale, w_sum)) {
+                    ok[t] = 0;
+                    return;
+                }
+        });
+    }
+    for (auto& th : pool) th.join();
+    for (char c : ok)
+        if (!c) return COMET_ERR_ARG;
+    return COMET_OK;
+}
+
+// ---------------------------------------------------------------------------
+// QoQ progressive group quantization (QoQ/QServe article, sections
+// "渐进式分组量化" and "W4A8 GEMM的核心设计"): per output channel symmetric
+// INT8 in the protected range [-119, 119] with an fp16 scale s1; then per
+// 128-channel group of the permuted order an integer step s2 and zero point z
+// over the group's range widened to include 0, codes u in [0, 15], so that
+// s2 (u - z) is an 8-bit integer again. The codes go into the same fragment
+// order as the INT4 pack (unsigned nibbles); s2 and z of (channel, group) are
+// one 16-bit word s2 | z << 8.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Nearest integer of num / den (den > 0), ties to even, in integers.
+inline int round_div_even(int num, int den) {
+    int q = num / den, r = num % den;
+    if (r < 0) {
+        q -= 1;
+        r += den;
+    }
+    if (2 * r > den || (2 * r == den && (q & 1))) ++q;
+    return q;
+}
+
+bool pack_row_qoq(const uint16_t* wrow, int N, int K, const int32_t* perm, int n, uint8_t* Wu, uint16_t* s1,
+                  uint16_t* s2z) {
+    const int nb = K / kBlock;
+    float a = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const float v = half_bits_to_float(wrow[k]);
+        if (!std::isfinite(v)) return false;
+        a = std::max(a, std::fabs(v));
+    }
+    uint16_t hs = 0;
+    if (a > 0.0f) {
+        hs = float_to_half_bits(a / 119.0f);
+        if (hs == 0) hs = 1;
+    }
+    s1[n] = hs;
+    const float s = half_bits_to_float(hs);
+    const int frag_col = n / 16, lane_col = n % 16;
+    int w8[kBlock];
+    uint8_t u[kBlock];
+    for (int b = 0; b < nb; ++b) {
+        int lo = 0, hi = 0;
+        for (int p = 0; p < kBlock; ++p) {
+            int q = 0;
+            if (hs != 0) {
+                const float r = std::rint(half_bits_to_float(wrow[perm[b * kBlock + p]]) / s);
+                q = static_cast<int>(std::min(119.0f, std::max(-119.0f, r)));
+            }
+            w8[p] = q;
+            lo = std::min(lo, q);
+            hi = std::max(hi, q);
+        }
+        const int st = std::max(1, (hi - lo + 14) / 15);
+        const int z = round_div_even(-lo, st);
+        for (int p = 0; p < kBlock; ++p)
+            u[p] = static_cast<uint8_t>(std::min(15, std::max(0, round_div_even(w8[p], st) + z)));
+        s2z[static_cast<size_t>(b) * N + n] = static_cast<uint16_t>(st | (z << 8));
+        uint8_t* frag = Wu + (static_cast<size_t>(frag_col) * nb + b) * kFragBytes;
+        for (int g = 0; g < 4; ++g) {
+            uint8_t* dst = frag + 16 * (16 * g + lane_col);
+            for (int j = 0; j < 16; ++j) dst[j] = static_cast<uint8_t>(u[32 * g + j] | (u[32 * g + 16 + j] << 4));
+        }
+    }
+    return true;
+}
+
+}  // namespace
+
+int pack_weights_qoq(const uint16_t* W, int N, int K, const float* score, int32_t* perm, uint8_t* Wu,
+                     uint16_t* s1, uint16_t* s2z) {
+    for (int k = 0; k < K; ++k)
+        if (!std::isfinite(score[k])) return COMET_ERR_ARG;
+    std::vector<int32_t> order(K);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [score](int32_t x, int32_t y) { return score[x] < score[y]; });
+    std::copy(order.begin(), order.end(), perm);
+    unsigned hw = std::thread::hardware_concurrency();
+    const int threads = static_cast<int>(std::max(1u, std::min(hw ? hw : 1u, 32u)));
+    const int per = (N + threads - 1) / threads;
+    std::vector<char> ok(threads, 1);
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t) {
+        const int n0 = t * per, n1 = std::min(N, n0 + per);
+        if (n0 >= n1) break;
+        pool.emplace_back([=, &ok] {
+            for (int n = n0; n < n1; ++n)
+                if (!pack_row_qoq(W + static_cast<size_t>(n) * K, N, K, perm, n, Wu, s1, s2z)) {
                     ok[t] = 0;
                     return;
                 }

@@ -55,6 +55,7 @@
 #include <mutex>
 
 #include "comet_internal.h"
+#include "qoq_internal.h"
 #include "device_util.h"
 
 namespace comet {
@@ -750,6 +751,66 @@ __global__ __launch_bounds__(kSwiThreads) void swiglu_kernel(const uint16_t* __r
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Per-token INT8 activations of the QoQ W4A8 variant (QoQ/QServe article,
+// section "运行时设计": W4A8 GEMMs take 8-bit activations): one scale per
+// token over all K. One workgroup per row stages the row in LDS, takes its
+// absmax (a maximum does not depend on the channel order), then each lane
+// codes one 32-channel group of a block from the perm gather: q = round(x *
+// inv), inv = 127 / a and s = a / 127 correctly rounded (the clamp to 127
+// never acts, as for the per-block quantizer). Codes go to 8-bit slabs:
+// block b, row m at byte (b M + m) 128, positions in order.
+// ---------------------------------------------------------------------------
+constexpr int kTokThreads = 256;
+
+__global__ __launch_bounds__(kTokThreads) void quant_token_i8_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                                    int ldx, const int32_t* __restrict__ perm,
+                                                                    int nb, uint8_t* __restrict__ Xq,
+                                                                    float* __restrict__ x_scale) {
+    extern __shared__ uint16_t row_lds[];
+    __shared__ float wmax[kTokThreads / 64];
+    const int m = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
+    float a = 0.0f;
+    for (int c = threadIdx.x; c < K; c += kTokThreads) {
+        const uint16_t h = xr[c];
+        row_lds[c] = h;
+        a = fmaxf(a, fabsf(h2f(h)));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    if (lane == 0) wmax[wave] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    float inv = 0.0f, sc = 0.0f;
+    if (a > 0.0f) {
+        inv = 127.0f / a;
+        sc = a / 127.0f;
+    }
+    for (int t = threadIdx.x; t < 4 * nb; t += kTokThreads) {
+        const int b = t >> 2, g = t & 3;
+        const int4* pp = reinterpret_cast<const int4*>(perm + b * kBlock + 32 * g);
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int4 pk = pp[k];
+            const int idx[4] = {pk.x, pk.y, pk.z, pk.w};
+            uint32_t x = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = static_cast<int>(__builtin_rintf(h2f(row_lds[idx[e]]) * inv));
+                x |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * e);
+            }
+            w[k] = x;
+        }
+        uint8_t* dst = Xq + (static_cast<size_t>(b) * M + m) * 128 + 32 * g;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    if (threadIdx.x == 0) x_scale[m] = sc;
+}
+
 int cu_count() {
     static int n = [] {
         int dev = 0, v = 0;
@@ -821,6 +882,14 @@ int launch_swiglu(const uint16_t* G, const uint16_t* U, int M, int K, int ldx, u
 int launch_rmsnorm(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma, float eps, uint16_t* Xn,
                    int ldn, void* stream) {
     rmsnorm_kernel<<<M, kNormThreads, 0, static_cast<hipStream_t>(stream)>>>(X, K, ldx, gamma, eps, Xn, ldn);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_quant_act_token_i8(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, uint8_t* Xq,
+                              float* x_scale, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    quant_token_i8_kernel<<<M, kTokThreads, static_cast<size_t>(K) * 2, s>>>(X, M, K, ldx, perm, K / kBlock, Xq,
+                                                                           x_scale);
     return static_cast<int>(hipGetLastError());
 }
 
