@@ -381,6 +381,65 @@ def asym_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
     return out
 
 
+def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64), iters=20):
+    """QoQ's W4A8 variant (per-channel INT8 then per-group UINT4 weights,
+    dequantized to 8 bits in registers; per-token INT8 activations; one
+    integer sum over K) against the W4Ax path on the INT4 layout, at the
+    LLaMA-70B up_proj shape (K = 8192, N = 28672) for decode row counts:
+    quantizer + GEMM, HIP events around `iters` back-to-back pairs over weight
+    copies of >= 1 GB; and each one's error against the unquantized product on
+    16 rows."""
+    cfg0 = synth.CONFIGS["prefill_up_70b"]
+    K, N, nb8 = cfg0.K, cfg0.N, cfg0.nb8
+    W, score = synth.make_w(cfg0), synth.make_scores(cfg0)
+    w4 = comet.upload_weights(comet.comet_pack_weights(W, score, nb8))
+    wq = comet.upload_qoq(comet.comet_pack_weights_qoq(W, score))
+    copies = copies_for(synth.LayerConfig("qoq", 1, K, N, 0, int8_frac=None))
+    clone = lambda w: {k: (v.clone() if hasattr(v, "clone") else v) for k, v in w.items()}
+    w4s = [w4] + [clone(w4) for _ in range(copies - 1)]
+    wqs = [wq] + [clone(wq) for _ in range(copies - 1)]
+    Xall = synth.make_x(cfg0)
+    out = {"shape": {"K": K, "N": N, "int8_blocks_w4ax": nb8}, "per_M": {},
+           "timing": f"HIP events around {iters} back-to-back quantizer + GEMM pairs, {copies} weight copies"}
+    for M in Ms:
+        X = torch.from_numpy(Xall[:M].view(np.float16)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        Xq4 = torch.empty(comet.xq_bytes(M, K, nb8), dtype=torch.uint8, device="cuda")
+        xs4 = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+        Xq8 = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+        xs8 = torch.empty(M, dtype=torch.float32, device="cuda")
+        it = {"i": 0}
+
+        def w4ax():
+            w = w4s[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_quant_act(X, w["perm"], nb8, Xq=Xq4, x_scale=xs4)
+            comet.comet_w4ax_gemm(Xq4, xs4, w, M, Y=Y)
+
+        def qoq():
+            w = wqs[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_quant_act_token_i8(X, w["perm"], Xq=Xq8, x_scale=xs8)
+            comet.comet_w4a8_qoq_gemm(Xq8, xs8, w, M, Y=Y)
+
+        res = _time_variants(torch, (("w4ax", w4ax), ("qoq", qoq)), iters)
+        out["per_M"][str(M)] = {"w4ax_us": res["w4ax"], "qoq_us": res["qoq"],
+                                "qoq_over_w4ax": res["qoq"] / res["w4ax"]}
+    rows = 16
+    X = torch.from_numpy(Xall[:rows].view(np.float16)).cuda()
+    ref = Xall[:rows].view(np.float16).astype(np.float64) @ W.view(np.float16).astype(np.float64).T
+    Xq, xs = comet.comet_quant_act(X, w4["perm"], nb8)
+    y4 = comet.comet_w4ax_gemm(Xq, xs, w4, rows).float().cpu().numpy().astype(np.float64)
+    Xq, xs = comet.comet_quant_act_token_i8(X, wq["perm"])
+    yq = comet.comet_w4a8_qoq_gemm(Xq, xs, wq, rows).float().cpu().numpy().astype(np.float64)
+    nrm = np.sqrt(np.mean(ref ** 2))
+    out["rel_rms_err_vs_unquantized"] = {"w4ax": float(np.sqrt(np.mean((y4 - ref) ** 2)) / nrm),
+                                         "qoq": float(np.sqrt(np.mean((yq - ref) ** 2)) / nrm)}
+    del w4s, wqs
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layers, budget_s):
     """The oracle as it stands, on a bounded sample of rows of every layer: host
     time of steps 3-5 (activation quantization, block partials, epilogue) with
@@ -488,6 +547,7 @@ def main():
     fusion = fusion_ablation(torch, comet, synth) if ablate else None
     swi = swiglu_ablation(torch, comet, synth) if ablate else None
     asym = asym_ablation(torch, comet, synth) if ablate else None
+    qoq = qoq_ablation(torch, comet, synth) if ablate else None
 
     cpu = None
     if not args.no_cpu:
@@ -511,6 +571,7 @@ def main():
         "norm_quant_fusion": fusion,
         "swiglu_quant_fusion": swi,
         "asym_activation_variant": asym,
+        "qoq_w4a8_variant": qoq,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

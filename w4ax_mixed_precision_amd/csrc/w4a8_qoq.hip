@@ -7,17 +7,19 @@
 // gfx950 mapping (decode shapes, M <= 64). Weight-streaming kernel in the
 // structure of the W4Ax register streaming kernel: a workgroup owns G = 2
 // channel groups of 16 outputs, its waves split the 128-channel groups of K,
-// a wave's activation words of a group feed both channel groups, INT8
-// v_mfma_i32_16x16x64_i8 accumulate across all groups, and the wave partials
-// are added through LDS (integer sums: exact in any order). The page's
-// register-level dequantization ("subtraction after multiplication", four
-// 8-bit lanes per 32-bit operation) becomes, per 32-bit word of four codes:
-//   a = s2 u per byte: two 24-bit multiplies of the even and odd bytes (each
-//       product <= 15 * 16 = 240 stays inside its byte);
-//   r = a - s2 z per byte without borrows between bytes:
-//       ((a | 0x80808080) - (c & 0x7F7F7F7F)) ^ ((a ^ ~c) & 0x80808080),
-//       c = s2 z in every byte;
-// the protected INT8 range keeps every r in [-127, 127].
+// a wave's activation words of a group feed both channel groups, and the wave
+// partials are added through LDS (integer sums: exact in any order). The
+// product of a group is s2 sum(q_a (u - z)); the page dequantizes the codes to
+// the 8-bit s2 (u - z) in registers before the multiply. On gfx950 the two
+// halves are split between the vector unit and the matrix core, which gives
+// the same exact integer at a third of the VALU work: the zero point comes off
+// in registers, per 32-bit word of four codes
+//     (u - z) = ((u | 0x80808080) - z 0x01010101) ^ 0x80808080
+// (u + 128 - z lies in [113, 143], so no byte borrows from the next), the
+// INT8 matrix instruction forms sum(q_a (u - z)) (|.| <= 127 15 128), and the
+// step multiplies that group sum into the running INT32 total (one 24-bit
+// multiply-add per output). The multiply-per-byte form of the page would
+// cost two 24-bit multiplies and a borrow-free subtraction per four codes.
 #include "comet_internal.h"
 #include "device_util.h"
 #include "qoq_internal.h"
@@ -27,21 +29,14 @@ namespace {
 
 constexpr int kQG = 2;          // channel groups per workgroup
 
-// Four unsigned codes (one per byte) to four bytes s2 (u - z).
-__device__ __forceinline__ uint32_t dequant4(uint32_t u, uint32_t s2, uint32_t c_lo7, uint32_t c_not_hi) {
-    const uint32_t even = (u & 0x00FF00FFu) * s2;            // bytes 0 and 2, each <= 240
-    const uint32_t odd = ((u >> 8) & 0x00FF00FFu) * s2;      // bytes 1 and 3
-    const uint32_t a = even | (odd << 8);
-    return ((a | 0x80808080u) - c_lo7) ^ ((a & 0x80808080u) ^ c_not_hi);
-}
-
-__device__ __forceinline__ v4i dequant16(uint4 p, bool hi, uint32_t s2, uint32_t c_lo7, uint32_t c_not_hi) {
+// The signed differences u - z of the 16 codes in one half of a lane's word.
+__device__ __forceinline__ v4i minus_zero16(uint4 p, bool hi, uint32_t zrep) {
     const uint32_t w[4] = {p.x, p.y, p.z, p.w};
     v4i r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t u = (hi ? (w[i] >> 4) : w[i]) & 0x0F0F0F0Fu;
-        r[i] = static_cast<int>(dequant4(u, s2, c_lo7, c_not_hi));
+        r[i] = static_cast<int>(((u | 0x80808080u) - zrep) ^ 0x80808080u);
     }
     return r;
 }
@@ -77,15 +72,17 @@ template <int MR>
 __device__ __forceinline__ void qoq_compute(const QoqSlot<MR>& sl, v4i (&acc)[kQG][MR]) {
 #pragma unroll
     for (int j = 0; j < kQG; ++j) {
-        const uint32_t s2 = sl.sz[j] & 0xFFu, z = (sl.sz[j] >> 8) & 0xFFu;
-        const uint32_t c = (s2 * z) * 0x01010101u;        // s2 z <= 240 in every byte
-        const uint32_t c_lo7 = c & 0x7F7F7F7Fu, c_not_hi = ~c & 0x80808080u;
-        const v4i B0 = dequant16(sl.w[j], false, s2, c_lo7, c_not_hi);
-        const v4i B1 = dequant16(sl.w[j], true, s2, c_lo7, c_not_hi);
+        const int s2 = static_cast<int>(sl.sz[j] & 0xFFu);
+        const uint32_t zrep = ((sl.sz[j] >> 8) & 0xFFu) * 0x01010101u;
+        const v4i B0 = minus_zero16(sl.w[j], false, zrep);
+        const v4i B1 = minus_zero16(sl.w[j], true, zrep);
+        const v4i zero = {0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            acc[j][r] = mfma_i8(as_v4i(sl.a0[r]), B0, acc[j][r]);
-            acc[j][r] = mfma_i8(as_v4i(sl.a1[r]), B1, acc[j][r]);
+            v4i g = mfma_i8(as_v4i(sl.a0[r]), B0, zero);
+            g = mfma_i8(as_v4i(sl.a1[r]), B1, g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][r][i] += s2 * g[i];
         }
     }
 }
