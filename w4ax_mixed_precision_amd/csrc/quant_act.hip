@@ -773,10 +773,25 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_i8_kernel(const uint1
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
     float a = 0.0f;
-    for (int c = threadIdx.x; c < K; c += kTokThreads) {
-        const uint16_t h = xr[c];
-        row_lds[c] = h;
-        a = fmaxf(a, fabsf(h2f(h)));
+    if ((ldx & 7) == 0) {
+        // 16-byte loads, four in flight per thread (K is a multiple of 128,
+        // so the row is whole 16-byte words)
+        const uint4* x4 = reinterpret_cast<const uint4*>(xr);
+        uint4* l4 = reinterpret_cast<uint4*>(row_lds);
+#pragma unroll 4
+        for (int c = threadIdx.x; c < K / 8; c += kTokThreads) {
+            const uint4 v = x4[c];
+            l4[c] = v;
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(h2f(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))))));
+        }
+    } else {
+        for (int c = threadIdx.x; c < K; c += kTokThreads) {
+            const uint16_t h = xr[c];
+            row_lds[c] = h;
+            a = fmaxf(a, fabsf(h2f(h)));
+        }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
