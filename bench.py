@@ -381,11 +381,11 @@ def asym_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
     return out
 
 
-def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64), iters=20):
-    """QoQ's W4A8 variant (per-channel INT8 then per-group UINT4 weights,
-    dequantized to 8 bits in registers; per-token INT8 activations; one
-    integer sum over K) against the W4Ax path on the INT4 layout, at the
-    LLaMA-70B up_proj shape (K = 8192, N = 28672) for decode row counts:
+def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
+    """QoQ's W4A8 variant (per-channel INT8 then per-group UINT4 weights;
+    per-token INT8 activations; one integer sum over K) against the W4Ax path
+    on the INT4 layout (its tiled INT8 kernel for M > 64), at the LLaMA-70B
+    up_proj shape (K = 8192, N = 28672) for decode row counts and 4096 rows:
     quantizer + GEMM, HIP events around `iters` back-to-back pairs over weight
     copies of >= 1 GB; and each one's error against the unquantized product on
     16 rows."""
@@ -422,7 +422,7 @@ def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64), iters=20):
             comet.comet_quant_act_token_i8(X, w["perm"], Xq=Xq8, x_scale=xs8)
             comet.comet_w4a8_qoq_gemm(Xq8, xs8, w, M, Y=Y)
 
-        res = _time_variants(torch, (("w4ax", w4ax), ("qoq", qoq)), iters)
+        res = _time_variants(torch, (("w4ax", w4ax), ("qoq", qoq)), iters if M <= 64 else 5)
         out["per_M"][str(M)] = {"w4ax_us": res["w4ax"], "qoq_us": res["qoq"],
                                 "qoq_over_w4ax": res["qoq"] / res["w4ax"]}
     rows = 16

@@ -275,10 +275,13 @@ int comet_pack_weights_qoq(const uint16_t* W_fp16, int N, int K, const float* ch
 int comet_quant_act_token_i8(const void* X_fp16, int M, int K, int ldx, const int32_t* perm, void* Xq,
                              float* x_scale, void* stream);
 
-/* The QoQ GEMM, M <= 64 (weight-streaming decode shapes): the codes are
- * dequantized to s2 (u - z) in registers before the INT8 matrix instruction.
- * Y fp16 [M][ldy]. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 64, N % 128,
- * K > 32768), HIP. */
+/* The QoQ GEMM: Y fp16 [M][ldy] = fp16(fl(x_scale s1) float(P)). Per group of
+ * K the zero point comes off the codes in registers, the INT8 matrix
+ * instruction forms sum(q_a (u - z)), and s2 multiplies that group sum into
+ * the INT32 total (the same exact P as the page's dequantization to
+ * s2 (u - z) before the multiply). M <= 64: weight-streaming kernel; above: a
+ * 128 x 128 tiled kernel. Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (N % 128,
+ * K > 32768, M N beyond int32), HIP. */
 int comet_w4a8_qoq_gemm(const void* Xq, const float* x_scale, const void* Wu_packed, const uint16_t* s2z,
                         const uint16_t* s1_fp16, int M, int N, int K, void* Y_fp16, int ldy, void* stream);
 

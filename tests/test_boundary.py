@@ -293,6 +293,7 @@ def test_qoq_rejections():
     assert qt(K=33024, ldx=33024) == UNSUP and qt(Xq=MIS) == ALIGN
     assert gq(Y=None) == NULL and gq(s1=None) == NULL
     assert gq(M=0) == SHAPE and gq(ldy=500) == SHAPE and gq(K=100) == SHAPE
-    assert gq(M=65) == UNSUP and gq(N=200, ldy=200) == UNSUP and gq(K=33024) == UNSUP
+    assert gq(N=200, ldy=200) == UNSUP and gq(K=33024) == UNSUP
+    assert gq(M=1 << 20, N=1 << 12, ldy=1 << 12) == UNSUP
     assert gq(Wu=MIS) == ALIGN and gq(Y=MIS) == ALIGN and gq(s2z=MIS) == ALIGN
-    assert gqp(P=None) == NULL and gqp(P=MIS) == ALIGN and gqp(M=65) == UNSUP
+    assert gqp(P=None) == NULL and gqp(P=MIS) == ALIGN and gqp(N=96) == UNSUP

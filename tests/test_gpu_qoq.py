@@ -24,12 +24,23 @@ def torch():
     return t
 
 
-def check(torch, X, W, score, label):
+def check(torch, X, W, score, label, rows=None):
+    """rows: None for every row, else contiguous row ranges the oracle's product
+    is compared on (codes and scales are compared on every row)."""
     import w4ax_mixed_precision_amd as comet
     from oracle import oracle as O
     M, K = X.shape
     N = W.shape[0]
-    d = O.qoq_layer(X, W, score)
+    if rows is None:
+        d = O.qoq_layer(X, W, score)
+    else:
+        d = O.qoq_layer(X, W, score, rows[0])
+        for r in rows[1:]:
+            P2, y2, Y2, e2 = O.qoq_gemm(d["qa"], d["sa"], d["u"], d["s2"], d["z"], d["s1"], r)
+            d["P"] = np.concatenate([d["P"], P2])
+            d["Y16"] = np.concatenate([d["Y16"], Y2])
+            d["yexact"] = np.concatenate([d["yexact"], e2])
+    sel = np.arange(M) if rows is None else np.concatenate([np.arange(a, b) for a, b in rows])
     w = comet.upload_qoq(comet.comet_pack_weights_qoq(W, score))
     Xd = torch.from_numpy(X.view(np.float16)).cuda()
     Xq, xs = comet.comet_quant_act_token_i8(Xd, w["perm"])
@@ -38,8 +49,8 @@ def check(torch, X, W, score, label):
     torch.cuda.synchronize()
     assert np.array_equal(decode_xq_token_i8(Xq.cpu().numpy(), M, K), d["qa"]), f"{label}: codes"
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), d["sa"].view(np.uint32)), f"{label}: scales"
-    assert np.array_equal(P.cpu().numpy(), d["P"]), f"{label}: products"
-    yg = Y.cpu().numpy().view(np.uint16)
+    assert np.array_equal(P.cpu().numpy()[sel], d["P"]), f"{label}: products"
+    yg = Y.cpu().numpy().view(np.uint16)[sel]
     assert np.array_equal(yg, d["Y16"]), f"{label}: Y"
     rms = float(np.sqrt(np.mean(d["yexact"] ** 2)))
     rel = np.abs(G.f16(yg) - d["yexact"]) / np.maximum(np.abs(d["yexact"]), 1e-2 * rms + 1e-300)
@@ -66,4 +77,23 @@ def test_qoq_edge_shapes(torch, M, K, N):
     if M > 2:
         X[1] = 0
     W[5] = 0
+    check(torch, X, W, score, f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("name", ["q_proj_7b", "up_gate_7b", "prefill_up_70b"])
+def test_qoq_prefill_parity(torch, name):
+    """The tiled kernel (M > 64), in the launch configuration the benchmark
+    times; full-size layers compared on their first and last 16 rows."""
+    cfg = synth.CONFIGS[name]
+    G.log(f"[qoq prefill] {name}")
+    rows = None if cfg.M <= 128 else [(0, 16), (cfg.M - 16, cfg.M)]
+    check(torch, synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg), name, rows)
+
+
+@pytest.mark.parametrize("M,K,N", [(65, 256, 128), (100, 1024, 256), (130, 384, 384), (257, 2048, 128)])
+def test_qoq_prefill_edge_shapes(torch, M, K, N):
+    G.log(f"[qoq prefill edge] M={M} K={K} N={N}")
+    cfg = synth.LayerConfig("qoq_pedge", M, K, N, 5 * M + K)
+    X, W, score = synth.make_x(cfg), synth.make_w(cfg), synth.make_scores(cfg)
+    X[M - 1] = 0
     check(torch, X, W, score, f"M={M} K={K} N={N}")

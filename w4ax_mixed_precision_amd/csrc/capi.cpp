@@ -127,7 +127,8 @@ int qoq_check(const void* Xq, const float* x_scale, const void* Wu_packed, const
               const uint16_t* s1_fp16, int M, int N, int K) {
     if (!Xq || !x_scale || !Wu_packed || !s2z || !s1_fp16) return COMET_ERR_NULL;
     if (M < 1 || N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
-    if (N % 128 != 0 || M > 64 || K > 32768) return COMET_ERR_UNSUPPORTED;
+    if (N % 128 != 0 || K > 32768) return COMET_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(M) * N > std::numeric_limits<int32_t>::max()) return COMET_ERR_UNSUPPORTED;
     if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(Wu_packed) || !aligned16(s2z) || !aligned16(s1_fp16))
         return COMET_ERR_ALIGN;
     return COMET_OK;
