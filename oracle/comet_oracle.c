@@ -54,6 +54,16 @@
  *     before the multiply), and only a per-(token, channel) scale remains:
  *     Y = fp16( (s_x s1) * P ).
  *
+ *  9. KV4 decode attention (QoQ/QServe article, section "KV4注意力Kernel优化",
+ *     and section "运行时设计": per-head dynamic 4-bit KV quantization with an
+ *     fp16 scale and zero point stored beside the codes; COMET article: the
+ *     KV cache compressed to 4 bits). Each cached key and value vector of one
+ *     head (d channels of one token) is coded as asymmetric 4-bit codes with
+ *     the range widened to include 0 (as step 3b), its step kept in fp16;
+ *     decode attention then computes, per head, softmax(q . k / sqrt(d)) over
+ *     the cached tokens and the weighted sum of the values, on the
+ *     dequantized vectors s (u - z).
+ *
  *  6. RMS normalization before the quantizer (the next step the quantization
  *     fuses into). QoQ/QServe article, section "运行时设计": the activation
  *     quantization of the QKV projection and of the first FFN layer is fused
@@ -941,4 +951,106 @@ int orc_qoq_gemm(const int8_t *qa, const float *sa, const uint8_t *u, const uint
         }
     }
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 9. KV4 decode attention                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* One vector v[0..d) of one (token, head): range [lo, hi] = [min(0, min v),
+ * max(0, max v)]; if hi > lo: step s16 = fp16(d_ / 15) with d_ = hi - lo (the
+ * smallest fp16 subnormal if that rounds to 0), inv = 15 / d_ (binary32), z =
+ * clamp(round(-lo * inv), 0, 15), u = clamp(round(v * inv) + z, 0, 15); an
+ * all-zero vector gets s16 = 0, z = 0, u = 0. The value represented is
+ * float(s16) (u - z). */
+void orc_kv4_code_vector(const uint16_t *v, int d, uint8_t *u, uint16_t *s16, uint8_t *z)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        float x = orc_half_to_float(v[i]);
+        if (x < lo) lo = x;
+        if (x > hi) hi = x;
+    }
+    if (lo == hi) {
+        *s16 = 0;
+        *z = 0;
+        memset(u, 0, (size_t)d);
+        return;
+    }
+    float dd = hi - lo;
+    float inv = 15.0f / dd;
+    uint16_t h = orc_float_to_half(dd / 15.0f);
+    if (h == 0)
+        h = 1;
+    *s16 = h;
+    int zz = (int)rintf(-lo * inv);
+    zz = zz < 0 ? 0 : (zz > 15 ? 15 : zz);
+    *z = (uint8_t)zz;
+    for (int i = 0; i < d; ++i) {
+        int c = (int)rintf(orc_half_to_float(v[i]) * inv) + zz;
+        u[i] = (uint8_t)(c < 0 ? 0 : (c > 15 ? 15 : c));
+    }
+}
+
+/* A cache [n][d] of n vectors (one head's keys or values): codes [n][d],
+ * steps [n] (fp16 bits), zero points [n]. */
+int orc_kv4_quantize(const uint16_t *V, int n, int d, uint8_t *u, uint16_t *s16, uint8_t *z)
+{
+    if (n <= 0 || d <= 0)
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < n; ++t)
+        orc_kv4_code_vector(V + (size_t)t * d, d, u + (size_t)t * d, s16 + t, z + t);
+    return ORC_OK;
+}
+
+/* Decode attention for H heads (one query each) over T cached tokens, in
+ * double precision on the dequantized cache:
+ *   k_t = s_k[t] (uk[t] - zk[t]),  v_t = s_v[t] (uv[t] - zv[t]),
+ *   a_t = (q . k_t) / sqrt(d),  p_t = exp(a_t - max a) / sum exp(. - max a),
+ *   out = sum_t p_t v_t.
+ * q: fp16 [H][d]; codes [H][T][d]; steps fp16 [H][T]; zero points [H][T];
+ * out: double [H][d]. */
+int orc_kv4_attention(const uint16_t *q, const uint8_t *uk, const uint16_t *sk, const uint8_t *zk,
+                      const uint8_t *uv, const uint16_t *sv, const uint8_t *zv, int H, int T, int d,
+                      double *out)
+{
+    if (H <= 0 || T <= 0 || d <= 0)
+        return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int h = 0; h < H; ++h) {
+        double *a = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!a) {
+            bad = 1;
+            continue;
+        }
+        const uint16_t *qh = q + (size_t)h * d;
+        double amax = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            size_t o = ((size_t)h * T + t);
+            double sk_t = orc_half_to_float(sk[o]);
+            double dot = 0.0;
+            for (int i = 0; i < d; ++i)
+                dot += (double)orc_half_to_float(qh[i]) * sk_t * ((double)uk[o * d + i] - (double)zk[o]);
+            a[t] = dot / sqrt((double)d);
+            if (a[t] > amax)
+                amax = a[t];
+        }
+        double denom = 0.0;
+        for (int t = 0; t < T; ++t) {
+            a[t] = exp(a[t] - amax);
+            denom += a[t];
+        }
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int t = 0; t < T; ++t) {
+                size_t o = ((size_t)h * T + t);
+                acc += a[t] * (double)orc_half_to_float(sv[o]) * ((double)uv[o * d + i] - (double)zv[o]);
+            }
+            out[(size_t)h * d + i] = acc / denom;
+        }
+        free(a);
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
 }

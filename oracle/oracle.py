@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.orc_quantize_activations.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_block_partials.argtypes = [P, P, I, I, I, I, I, P]
         L.orc_qoq_group.argtypes = [P, I, P, P]
+        L.orc_kv4_code_vector.argtypes = [P, I, P, P, P]
+        L.orc_kv4_quantize.argtypes = [P, I, I, P, P, P]
+        L.orc_kv4_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, P]
         L.orc_qoq_quantize_weights.argtypes = [P, I, I, P, P, P, P, P, P]
         L.orc_qoq_quantize_activations.argtypes = [P, I, I, I, P, P, P]
         L.orc_qoq_gemm.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P]
@@ -421,3 +424,30 @@ def qoq_layer(X16, W16, score, rows=None):
     P, y32, Y16, ye = qoq_gemm(qa, sa, u, s2, z, s1, rows)
     return {"perm": perm, "s1": s1, "w8": w8, "s2": s2, "z": z, "u": u, "qa": qa, "sa": sa,
             "P": P, "y32": y32, "Y16": Y16, "yexact": ye}
+
+
+# ----------------------------------------------------------------------------
+# Step 9: KV4 decode attention
+# ----------------------------------------------------------------------------
+
+def kv4_quantize(V16: np.ndarray):
+    """Codes uint8 [n, d], steps fp16 bits [n], zero points uint8 [n] of n vectors."""
+    V16 = np.ascontiguousarray(V16, dtype=np.uint16)
+    n, d = V16.shape
+    u = np.zeros((n, d), np.uint8)
+    s16 = np.zeros(n, np.uint16)
+    z = np.zeros(n, np.uint8)
+    _check(lib().orc_kv4_quantize(_p(V16), n, d, _p(u), _p(s16), _p(z)), "kv4_quantize")
+    return u, s16, z
+
+
+def kv4_attention(q16, uk, sk, zk, uv, sv, zv):
+    """q16 fp16 bits [H, d]; codes [H, T, d]; steps [H, T]; zero points [H, T] ->
+    out float64 [H, d]."""
+    q16 = np.ascontiguousarray(q16, dtype=np.uint16)
+    H, d = q16.shape
+    T = uk.shape[1]
+    out = np.zeros((H, d), np.float64)
+    args = [np.ascontiguousarray(a) for a in (uk, sk, zk, uv, sv, zv)]
+    _check(lib().orc_kv4_attention(_p(q16), *[_p(a) for a in args], H, T, d, _p(out)), "kv4_attention")
+    return out
