@@ -47,11 +47,10 @@ WORKLOADS = {
 
 
 # Sources whose change invalidates counter data taken on the GEMM kernels of
-# a workload: the GEMM source of the layout the workload runs, plus what every
-# kernel includes and the build flags.
+# a workload: the GEMM source of the layout the workload runs and what every
+# kernel includes; the compiler flags are hashed with them.
 _COMMON_SOURCES = ["w4ax_mixed_precision_amd/csrc/device_util.h",
-                   "w4ax_mixed_precision_amd/csrc/comet_internal.h",
-                   "w4ax_mixed_precision_amd/build.py"]
+                   "w4ax_mixed_precision_amd/csrc/comet_internal.h"]
 KERNEL_SOURCES = {"int4": ["w4ax_mixed_precision_amd/csrc/w4ax_gemm.hip"] + _COMMON_SOURCES,
                   "fp6": ["w4ax_mixed_precision_amd/csrc/w4ax_gemm_fp6.hip"] + _COMMON_SOURCES}
 COPY_CAL_BYTES = 1 << 30
@@ -67,7 +66,8 @@ def synth_cfg(name):
 
 
 def kernel_sources_digest(workload):
-    h = hashlib.sha256()
+    from w4ax_mixed_precision_amd import build as _b
+    h = hashlib.sha256(repr(_b.FLAGS).encode())
     for rel in [r for lay in workload_layouts(workload) for r in KERNEL_SOURCES[lay]]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
@@ -440,6 +440,52 @@ def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
     return out
 
 
+def kv4_attention_measure(torch, comet, synth, T=4096, seqs=16, iters=20):
+    """KV4 decode attention (4-bit keys and values with an fp16 step and zero
+    point per head and token) for `seqs` sequences of T cached tokens, d = 128:
+    LLaMA-7B (32 heads, multi-head) and LLaMA-70B (64 query heads over 8 kv
+    heads). HIP events around `iters` back-to-back calls over cache copies that
+    together exceed the last-level cache. Algorithmic bytes: every cached code,
+    step and zero point of K and V read once, plus q and the fp16 output."""
+    out = {"timing": f"HIP events around {iters} back-to-back calls (split kernel + combine)", "shapes": {}}
+    d = 128
+    for name, hq_seq, group in (("llama7b_mha", 32, 1), ("llama70b_gqa8", 64, 8)):
+        Hq = seqs * hq_seq
+        H = Hq // group
+        q16, K16, V16 = synth.make_kv(77, T, H, d, Hq)
+        per_cache = H * T * (d // 2 + 3)
+        copies = max(1, -(-(1 << 30) // (2 * per_cache)))
+        caches = []
+        X = torch.from_numpy(K16.view(np.float16)).cuda()
+        Xv = torch.from_numpy(V16.view(np.float16)).cuda()
+        for _ in range(copies):
+            kc, vc = comet.kv4_cache(H, T, d), comet.kv4_cache(H, T, d)
+            comet.comet_kv4_quantize(X, kc, 0)
+            comet.comet_kv4_quantize(Xv, vc, 0)
+            caches.append((kc, vc))
+        del X, Xv
+        q = torch.from_numpy(q16.view(np.float16)).cuda()
+        o = torch.empty((Hq, d), dtype=torch.float16, device="cuda")
+        ws = torch.empty(comet.lib().comet_kv4_attention_workspace_bytes(Hq, d, T), dtype=torch.uint8,
+                         device="cuda")
+        it = {"i": 0}
+
+        def att():
+            kc, vc = caches[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_kv4_attention(q, kc, vc, T, group, out=o, workspace=ws)
+
+        us = _time_variants(torch, (("att", att),), iters)["att"]
+        nbytes = 2 * per_cache + 2 * Hq * d * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out["shapes"][name] = {"query_heads": Hq, "kv_heads": H, "T": T, "d": d, "us": us,
+                               "algorithmic_bytes": nbytes, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                               "cache_copies": copies}
+        del caches, q, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layers, budget_s):
     """The oracle as it stands, on a bounded sample of rows of every layer: host
     time of steps 3-5 (activation quantization, block partials, epilogue) with
@@ -548,6 +594,7 @@ def main():
     swi = swiglu_ablation(torch, comet, synth) if ablate else None
     asym = asym_ablation(torch, comet, synth) if ablate else None
     qoq = qoq_ablation(torch, comet, synth) if ablate else None
+    kv4 = kv4_attention_measure(torch, comet, synth) if ablate else None
 
     cpu = None
     if not args.no_cpu:
@@ -572,6 +619,7 @@ def main():
         "swiglu_quant_fusion": swi,
         "asym_activation_variant": asym,
         "qoq_w4a8_variant": qoq,
+        "kv4_decode_attention": kv4,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -47,6 +47,9 @@ STREAM_CHI = 6          # chi-square draws of the Student-t activations
 STREAM_CALIB_CHI = 7    # chi-square draws of the Student-t calibration batch
 STREAM_GATE = 8         # gate projection outputs (SwiGLU input)
 STREAM_UP = 9           # up projection outputs (SwiGLU input)
+STREAM_Q = 10           # decode queries of the KV4 attention
+STREAM_K = 11           # cached keys
+STREAM_V = 12           # cached values
 
 _CHUNK = 1 << 22        # values per generation chunk (bounds peak host memory)
 
@@ -270,3 +273,17 @@ def make_layer(cfg: LayerConfig) -> dict:
 
 def fp16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def make_kv(seed: int, ntok: int, H: int, d: int, Hq: int | None = None):
+    """Inputs of KV4 decode attention, fp16 bit patterns: queries [Hq, d] ~ N(0, 1),
+    keys and values [ntok, H d] (token rows, heads side by side, as the key and
+    value projections write them). Values ~ N(0, 1); keys ~ N(0, 1) with d / 16
+    outlier channels per head (channels 16 i + 3) scaled by 8, the fixed
+    large-magnitude key channels that make per-channel ranges uneven."""
+    Hq = H if Hq is None else Hq
+    q = normal(seed, STREAM_Q, Hq * d, dtype=np.float32).reshape(Hq, d)
+    k = normal(seed, STREAM_K, ntok * H * d, dtype=np.float32).reshape(ntok, H, d)
+    k[:, :, 3::16] *= 8.0
+    v = normal(seed, STREAM_V, ntok * H * d, dtype=np.float32).reshape(ntok, H * d)
+    return to_fp16(q), to_fp16(k.reshape(ntok, H * d)), to_fp16(v)

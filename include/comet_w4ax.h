@@ -290,6 +290,56 @@ int comet_w4a8_qoq_gemm_products(const void* Xq, const float* x_scale, const voi
                                  const uint16_t* s1_fp16, int M, int N, int K, int32_t* P, void* stream);
 
 /*
+ * KV4 cache (QoQ/QServe article, section "KV4注意力Kernel优化": keys and values
+ * quantized per head to 4 bits at run time, an fp16 scale and a zero point
+ * stored with the codes; COMET article: KV cache at 4 bits). For each (token,
+ * head) vector x of d channels: lo = min(0, min x), hi = max(0, max x),
+ * inv = 15 / (hi - lo) and step = fp16((hi - lo) / 15) (binary32 divisions; the
+ * smallest fp16 subnormal if the step rounds to 0), z = clamp(round(-lo inv)),
+ * u = clamp(round(x inv) + z), clamps to [0, 15], ties to even; value
+ * step (u - z). An all-zero vector stores step 0, z 0, codes 0.
+ *
+ * Cache layout per kv head h and slot t < tcap: codes [h][t][d/2] bytes
+ * (channel 2i in the low nibble of byte i, 2i+1 in the high nibble),
+ * step [h][t] fp16 bits, zero [h][t] bytes.
+ *
+ *   X_fp16     in   [ntok, ldx] fp16, device, 16-byte aligned, ldx % 8 == 0:
+ *                   row = token, head h at columns [h d, h d + d)
+ *   pos        in   cache slot of the first token (tokens go to pos .. pos+ntok-1)
+ *   tcap       in   slots per head in the cache
+ *   codes, step_fp16, zero   out (slots outside the range are untouched)
+ * Errors: NULL, SHAPE (ntok, H < 1, ldx < H d, pos < 0, pos + ntok > tcap),
+ * UNSUPPORTED (d not a power of two in [8, 512]), ALIGN, HIP.
+ */
+int comet_kv4_quantize(const void* X_fp16, int ntok, int H, int d, int ldx, int pos, int tcap, void* codes,
+                       uint16_t* step_fp16, uint8_t* zero, void* stream);
+
+/* Workspace bytes of comet_kv4_attention (0 for an invalid shape). */
+size_t comet_kv4_attention_workspace_bytes(int Hq, int d, int T);
+
+/*
+ * Decode attention over the KV4 cache (QoQ/QServe article, section
+ * "KV4注意力Kernel优化"): for each query head h, with kv head g = h / group,
+ * over the first T slots of g's cache, k_t and v_t the dequantized vectors,
+ *   a_t = q_h . k_t / sqrt(d),  p = softmax(a),  out_h = fp16(sum_t p_t v_t),
+ * in FP32 (a split over 256-token chunks, combined exactly as a softmax over
+ * the whole; the order of the sums differs from a plain loop).
+ *
+ *   q_fp16     in   [Hq][d] fp16, device, 16-byte aligned
+ *   k_*, v_*   in   caches of Hq / group kv heads, layout as comet_kv4_quantize
+ *   group      in   query heads per kv head (1 for multi-head attention)
+ *   T, tcap    in   tokens to attend (1 <= T <= tcap) and the cache's slots per head
+ *   out_fp16   out  [Hq][d] fp16, device, 2-byte aligned
+ *   workspace  in   device, 16-byte aligned, comet_kv4_attention_workspace_bytes()
+ * Errors: NULL, SHAPE (Hq < 1, group < 1, Hq % group, T < 1, tcap < T),
+ * UNSUPPORTED (d not a power of two in [8, 512]; Hq ceil(T / 256) beyond
+ * int32), WORKSPACE, ALIGN, HIP.
+ */
+int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t* k_step, const uint8_t* k_zero,
+                        const void* v_codes, const uint16_t* v_step, const uint8_t* v_zero, int Hq, int group, int d,
+                        int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP6 layout, sizes: bytes of Xq_fp6 for M rows (padded to a multiple of 16)
  * and of Wq_fp6 for N output channels (0 for an invalid shape).
  */

@@ -129,3 +129,17 @@ def decode_wq_fp6(WqF: np.ndarray, N: int, K: int, nb8: int) -> np.ndarray:
     blk = np.stack([lo, hi], axis=4)                                                # [b, c, g, n16, half, j]
     q[:, nb4 * 128:] = blk.transpose(1, 3, 0, 2, 4, 5).reshape(N, nb8 * 128)
     return q
+
+
+def pack_kv4_codes(u: np.ndarray) -> np.ndarray:
+    """Codes uint8 [..., d] -> bytes [..., d/2]: channel 2i in the low nibble of
+    byte i, 2i+1 in the high nibble."""
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_kv4_codes(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_kv4_codes."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out

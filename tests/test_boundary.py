@@ -297,3 +297,31 @@ def test_qoq_rejections():
     assert gq(M=1 << 20, N=1 << 12, ldy=1 << 12) == UNSUP
     assert gq(Wu=MIS) == ALIGN and gq(Y=MIS) == ALIGN and gq(s2z=MIS) == ALIGN
     assert gqp(P=None) == NULL and gqp(P=MIS) == ALIGN and gqp(N=96) == UNSUP
+
+
+def test_kv4_rejections():
+    L = comet.lib()
+
+    def kq(X=A, ntok=4, H=8, d=128, ldx=1024, pos=0, tcap=16, codes=A, step=A, zero=A):
+        return L.comet_kv4_quantize(X, ntok, H, d, ldx, pos, tcap, codes, step, zero, None)
+
+    def ka(q=A, kc=A, ks=A, kz=A, vc=A, vs=A, vz=A, Hq=8, group=2, d=128, T=300, tcap=300, out=A, ws=A,
+           wsb=1 << 20):
+        return L.comet_kv4_attention(q, kc, ks, kz, vc, vs, vz, Hq, group, d, T, tcap, out, ws, wsb, None)
+
+    assert kq(X=None) == NULL and kq(zero=None) == NULL and kq(codes=None) == NULL
+    assert kq(ntok=0) == SHAPE and kq(H=0) == SHAPE and kq(ldx=1000) == SHAPE and kq(pos=-1) == SHAPE
+    assert kq(pos=13) == SHAPE and kq(ntok=17) == SHAPE
+    assert kq(d=96, ldx=768) == UNSUP and kq(d=4, ldx=32) == UNSUP and kq(d=1024, ldx=8192) == UNSUP
+    assert kq(X=MIS) == ALIGN and kq(ldx=1028) == ALIGN and kq(step=MIS) == ALIGN
+    assert ka(out=None) == NULL and ka(ws=None) == NULL and ka(vz=None) == NULL
+    assert ka(Hq=0) == SHAPE and ka(group=0) == SHAPE and ka(group=3) == SHAPE
+    assert ka(T=0) == SHAPE and ka(tcap=299) == SHAPE
+    assert ka(d=100) == UNSUP and ka(d=1024) == UNSUP
+    assert ka(wsb=0) == WORKSPACE
+    assert ka(wsb=L.comet_kv4_attention_workspace_bytes(8, 128, 300) - 1) == WORKSPACE
+    assert ka(q=MIS) == ALIGN and ka(ws=MIS) == ALIGN and ka(kz=MIS) == ALIGN
+    assert L.comet_kv4_attention_workspace_bytes(8, 128, 300) == 8 * 2 * 130 * 4
+    assert L.comet_kv4_attention_workspace_bytes(512, 128, 4096) == 512 * 16 * 130 * 4
+    assert L.comet_kv4_attention_workspace_bytes(0, 128, 1) == 0
+    assert L.comet_kv4_attention_workspace_bytes(4, 96, 1) == 0

@@ -1,0 +1,141 @@
+"""GPU parity of KV4 decode attention (QoQ/QServe article, section
+"KV4注意力Kernel优化"; COMET article: KV cache at 4 bits) through the C ABI
+against the oracle's step 9.
+
+The cache quantizer is compared bit for bit (codes, fp16 steps, zero points),
+and slots outside the written range must stay untouched. The attention output
+is compared with the oracle's float64 result on the same codes within
+    |out - ref| <= 2^-11 |ref| + 2^-16 vmax_h,
+the fp16 rounding of the result plus an FP32 allowance: vmax_h is the largest
+dequantized value magnitude of the head, and 2^-16 vmax_h is several hundred
+FP32 rounding units of it, far above what the FP32 sums and the exponentials
+of the scores (relative error a few units) contribute, and far below the
+smallest structural mistake (one token of 4096 dropped, or a zero point off by
+one, moves the output by about 1e-3 and 0.1 vmax_h).
+"""
+import numpy as np
+import pytest
+
+from gen import synth
+from tests.layout import pack_kv4_codes, unpack_kv4_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    import w4ax_mixed_precision_amd as comet
+    comet.lib()
+    return t
+
+
+def oracle_cache(O, X16, H, d):
+    """X16 [ntok, H d] -> oracle codes [H, ntok, d], steps and zeros [H, ntok]."""
+    ntok = X16.shape[0]
+    per_head = X16.reshape(ntok, H, d).transpose(1, 0, 2).reshape(H * ntok, d)
+    u, s, z = O.kv4_quantize(np.ascontiguousarray(per_head))
+    return u.reshape(H, ntok, d), s.reshape(H, ntok), z.reshape(H, ntok)
+
+
+def gpu_cache(torch, comet, X16, H, d, tcap, pos=0, split=None):
+    """Quantize X16 into a fresh cache at pos (in two calls when split is given)."""
+    c = comet.kv4_cache(H, tcap, d)
+    c["codes"].fill_(0xAB)
+    c["step"].fill_(0x1234)
+    c["zero"].fill_(0xCD)
+    X = torch.from_numpy(X16.view(np.float16)).cuda()
+    if split is None:
+        comet.comet_kv4_quantize(X, c, pos)
+    else:
+        comet.comet_kv4_quantize(X[:split], c, pos)
+        comet.comet_kv4_quantize(X[split:], c, pos + split)
+    return c
+
+
+def read_cache(c):
+    H, tcap, d = c["H"], c["tcap"], c["d"]
+    b = c["codes"].cpu().numpy().reshape(H, tcap, d // 2)
+    s = c["step"].cpu().numpy().view(np.uint16).reshape(H, tcap)
+    z = c["zero"].cpu().numpy().reshape(H, tcap)
+    return b, s, z
+
+
+QUANT_CASES = [  # ntok, H, d, pos, tcap
+    (1, 32, 128, 7, 16), (37, 8, 128, 0, 40), (5, 4, 64, 3, 8), (3, 2, 256, 0, 3),
+    (2, 3, 8, 1, 4), (70, 2, 512, 5, 80), (513, 4, 128, 0, 513)]
+
+
+@pytest.mark.parametrize("ntok,H,d,pos,tcap", QUANT_CASES)
+def test_kv4_quantize_bit_exact(torch, ntok, H, d, pos, tcap):
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    _, K16, V16 = synth.make_kv(100 + ntok + d, ntok, H, d)
+    for X16 in (K16, V16):
+        X16 = X16.copy()
+        if ntok > 2:                         # special vectors: all zero, all non-negative
+            X16[1, :d] = 0
+            X16[2, -d:] = np.abs(X16[2, -d:].view(np.float16)).view(np.uint16)
+        u, s, z = oracle_cache(O, X16, H, d)
+        c = gpu_cache(torch, comet, X16, H, d, tcap, pos)
+        torch.cuda.synchronize()
+        b, gs, gz = read_cache(c)
+        w = slice(pos, pos + ntok)
+        assert np.array_equal(unpack_kv4_codes(b[:, w]), u), (ntok, H, d, "codes")
+        assert np.array_equal(gs[:, w], s), (ntok, H, d, "steps")
+        assert np.array_equal(gz[:, w], z), (ntok, H, d, "zeros")
+        outside = np.ones(tcap, bool)
+        outside[w] = False
+        assert (b[:, outside] == 0xAB).all() and (gs[:, outside] == 0x1234).all() and (gz[:, outside] == 0xCD).all()
+
+
+def check_attention(torch, Hq, group, d, T, seed, tcap=None, split=None):
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    H = Hq // group
+    tcap = T + 5 if tcap is None else tcap
+    q16, K16, V16 = synth.make_kv(seed, T, H, d, Hq)
+    Ku, Ks, Kz = oracle_cache(O, K16, H, d)
+    Vu, Vs, Vz = oracle_cache(O, V16, H, d)
+    rep = np.arange(Hq) // group
+    ref = O.kv4_attention(q16, Ku[rep], Ks[rep], Kz[rep], Vu[rep], Vs[rep], Vz[rep])
+    kc = gpu_cache(torch, comet, K16, H, d, tcap, 0, split)
+    vc = gpu_cache(torch, comet, V16, H, d, tcap, 0, split)
+    q = torch.from_numpy(q16.view(np.float16)).cuda()
+    out = comet.comet_kv4_attention(q, kc, vc, T, group)
+    out2 = comet.comet_kv4_attention(q, kc, vc, T, group)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), out2.cpu().numpy().view(np.uint16)), "determinism"
+    vd = np.abs(Vs.view(np.float16).astype(np.float64)[..., None] * (Vu.astype(np.float64) - Vz[..., None]))
+    vmax = vd.reshape(H, -1).max(axis=1)[rep][:, None]
+    tol = 2.0**-11 * np.abs(ref) + 2.0**-16 * vmax
+    err = np.abs(o - ref)
+    ratio = float((err / tol).max())
+    print(f"kv4 attention Hq={Hq} group={group} d={d} T={T}: max err {err.max():.3e}, "
+          f"max err/tol {ratio:.3f}", flush=True)
+    assert (err <= tol).all(), (Hq, group, d, T, ratio)
+    return ratio
+
+
+ATT_CASES = [  # Hq, group, d, T
+    (4, 1, 128, 1), (8, 1, 128, 255), (8, 2, 128, 256), (16, 8, 128, 257), (32, 1, 128, 1000),
+    (4, 1, 64, 513), (2, 1, 256, 300), (2, 1, 512, 70), (4, 1, 8, 33), (8, 1, 16, 700), (8, 1, 128, 4096)]
+
+
+@pytest.mark.parametrize("Hq,group,d,T", ATT_CASES)
+def test_kv4_attention_parity(torch, Hq, group, d, T):
+    check_attention(torch, Hq, group, d, T, seed=7 + T, split=(T - 1 if T > 1 else None))
+
+
+def test_kv4_attention_bench_size(torch):
+    """The measured decode workload in full: 16 sequences x 32 heads, 4096
+    cached tokens, d = 128 (LLaMA-7B attention), multi-head."""
+    check_attention(torch, 512, 1, 128, 4096, seed=2024, tcap=4096)
+
+
+def test_kv4_attention_gqa_bench_size(torch):
+    """16 sequences of LLaMA-70B's grouped-query attention: 64 query heads over
+    8 kv heads each, 4096 cached tokens."""
+    check_attention(torch, 1024, 8, 128, 4096, seed=2025, tcap=4096)

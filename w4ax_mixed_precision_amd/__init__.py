@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
     L.comet_w4a8_qoq_gemm.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
     L.comet_w4a8_qoq_gemm_products.argtypes = [P, P, P, P, P, I, I, I, P, P]
     L.comet_x_zero_bytes.argtypes = [I, I]
+    L.comet_kv4_quantize.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
+    L.comet_kv4_attention_workspace_bytes.argtypes = [I, I, I]
+    L.comet_kv4_attention_workspace_bytes.restype = Z
+    L.comet_kv4_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P]
     L.comet_x_zero_bytes.restype = Z
     L.comet_w4ax_gemm_asym.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, Z, P]
     L.comet_w4ax_gemm_asym_partials.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P]
@@ -84,7 +88,7 @@ def lib() -> ctypes.CDLL:
               "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
               "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
               "comet_pack_weights_qoq", "comet_quant_act_token_i8", "comet_w4a8_qoq_gemm",
-              "comet_w4a8_qoq_gemm_products"):
+              "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize", "comet_kv4_attention"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -98,7 +102,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
            "comet_w4ax_gemm_asym_partials", "comet_pack_weights_qoq", "comet_quant_act_token_i8",
-           "comet_w4a8_qoq_gemm", "comet_w4a8_qoq_gemm_products", "comet_status_string", "comet_version")
+           "comet_w4a8_qoq_gemm", "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize",
+           "comet_kv4_attention_workspace_bytes", "comet_kv4_attention", "comet_status_string", "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -320,6 +325,43 @@ def comet_w4a8_qoq_gemm_products(Xq, x_scale, w: dict, M: int, P=None, stream=No
                                             _stream(stream))
     _check("comet_w4a8_qoq_gemm_products", rc)
     return P
+
+
+def kv4_cache(H: int, tcap: int, d: int, device="cuda") -> dict:
+    """An empty KV4 cache of H heads and tcap slots (codes, step, zero)."""
+    import torch
+    return {"codes": torch.zeros(H * tcap * d // 2, dtype=torch.uint8, device=device),
+            "step": torch.zeros(H * tcap, dtype=torch.int16, device=device),
+            "zero": torch.zeros(H * tcap, dtype=torch.uint8, device=device),
+            "H": H, "tcap": tcap, "d": d}
+
+
+def comet_kv4_quantize(X, cache: dict, pos: int, stream=None):
+    """Quantize X fp16 [ntok, >= H d] (token rows, heads side by side) into
+    cache slots pos .. pos + ntok - 1 of every head."""
+    ntok = X.shape[0]
+    rc = lib().comet_kv4_quantize(_dev_ptr(X), ntok, cache["H"], cache["d"], X.stride(0), pos, cache["tcap"],
+                                  _dev_ptr(cache["codes"]), _dev_ptr(cache["step"]), _dev_ptr(cache["zero"]),
+                                  _stream(stream))
+    _check("comet_kv4_quantize", rc)
+
+
+def comet_kv4_attention(q, kcache: dict, vcache: dict, T: int, group: int = 1, out=None, workspace=None,
+                        stream=None):
+    """Decode attention of q fp16 [Hq, d] over the first T slots of the caches."""
+    import torch
+    Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float16, device=q.device)
+    nbytes = lib().comet_kv4_attention_workspace_bytes(Hq, d, T)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().comet_kv4_attention(_dev_ptr(q), _dev_ptr(kcache["codes"]), _dev_ptr(kcache["step"]),
+                                   _dev_ptr(kcache["zero"]), _dev_ptr(vcache["codes"]), _dev_ptr(vcache["step"]),
+                                   _dev_ptr(vcache["zero"]), Hq, group, d, T, kcache["tcap"], _dev_ptr(out),
+                                   _dev_ptr(workspace), workspace.numel(), _stream(stream))
+    _check("comet_kv4_attention", rc)
+    return out
 
 
 def comet_permute_channels(v: np.ndarray, perm: np.ndarray) -> np.ndarray:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcomet_w4ax.so")
-SOURCES = ["capi.cpp", "pack_weights.cpp", "quant_act.hip", "w4ax_gemm.hip", "w4ax_gemm_fp6.hip", "w4a8_qoq.hip"]
+SOURCES = ["capi.cpp", "pack_weights.cpp", "quant_act.hip", "w4ax_gemm.hip", "w4ax_gemm_fp6.hip", "w4a8_qoq.hip", "kv4_attention.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

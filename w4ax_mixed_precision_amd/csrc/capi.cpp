@@ -4,6 +4,7 @@
 #include <limits>
 
 #include "comet_internal.h"
+#include "kv4_internal.h"
 #include "qoq_internal.h"
 
 namespace {
@@ -157,6 +158,50 @@ int comet_w4a8_qoq_gemm_products(const void* Xq, const float* x_scale, const voi
     return hip_status(comet::launch_qoq_gemm(static_cast<const uint8_t*>(Xq), x_scale,
                                              static_cast<const uint8_t*>(Wu_packed), s2z, s1_fp16, M, N, K,
                                              nullptr, N, P, stream));
+}
+
+namespace {
+
+bool kv4_dim_ok(int d) { return d >= 8 && d <= 512 && (d & (d - 1)) == 0; }
+
+}  // namespace
+
+int comet_kv4_quantize(const void* X_fp16, int ntok, int H, int d, int ldx, int pos, int tcap, void* codes,
+                       uint16_t* step_fp16, uint8_t* zero, void* stream) {
+    if (!X_fp16 || !codes || !step_fp16 || !zero) return COMET_ERR_NULL;
+    if (ntok < 1 || H < 1 || d < 1 || pos < 0 || tcap < 1 || static_cast<int64_t>(ldx) < static_cast<int64_t>(H) * d)
+        return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(pos) + ntok > tcap) return COMET_ERR_SHAPE;
+    if (!kv4_dim_ok(d)) return COMET_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(ntok) * H > std::numeric_limits<int32_t>::max() - 4) return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(X_fp16) || ldx % 8 != 0 || !aligned16(codes) || !aligned16(step_fp16) || !aligned16(zero))
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_kv4_quantize(static_cast<const uint16_t*>(X_fp16), ntok, H, d, ldx, pos, tcap,
+                                                 static_cast<uint8_t*>(codes), step_fp16, zero, stream));
+}
+
+size_t comet_kv4_attention_workspace_bytes(int Hq, int d, int T) {
+    if (Hq < 1 || T < 1 || !kv4_dim_ok(d)) return 0;
+    return comet::kv4_workspace_bytes(Hq, d, T);
+}
+
+int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t* k_step, const uint8_t* k_zero,
+                        const void* v_codes, const uint16_t* v_step, const uint8_t* v_zero, int Hq, int group, int d,
+                        int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q_fp16 || !k_codes || !k_step || !k_zero || !v_codes || !v_step || !v_zero || !out_fp16 || !workspace)
+        return COMET_ERR_NULL;
+    if (Hq < 1 || group < 1 || Hq % group != 0 || d < 1 || T < 1 || tcap < T) return COMET_ERR_SHAPE;
+    if (!kv4_dim_ok(d)) return COMET_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(Hq) * comet::kv4_splits(T) > std::numeric_limits<int32_t>::max()) return COMET_ERR_UNSUPPORTED;
+    if (workspace_bytes < comet::kv4_workspace_bytes(Hq, d, T)) return COMET_ERR_WORKSPACE;
+    if (!aligned16(q_fp16) || !aligned16(k_codes) || !aligned16(k_step) || !aligned16(k_zero) ||
+        !aligned16(v_codes) || !aligned16(v_step) || !aligned16(v_zero) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(out_fp16) & 1u) != 0)
+        return COMET_ERR_ALIGN;
+    return hip_status(comet::launch_kv4_attention(
+        static_cast<const uint16_t*>(q_fp16), static_cast<const uint8_t*>(k_codes), k_step, k_zero,
+        static_cast<const uint8_t*>(v_codes), v_step, v_zero, Hq, group, d, T, tcap,
+        static_cast<uint16_t*>(out_fp16), static_cast<float*>(workspace), stream));
 }
 
 size_t comet_x_zero_bytes(int M, int K) {
