@@ -99,126 +99,223 @@ __global__ __launch_bounds__(kKvThreads) void kv4_quant_kernel(const uint16_t* _
     }
 }
 
-__device__ __forceinline__ float block_max(float v, float* wred) {
+// G per-query values reduced over the workgroup (maximum or sum), wave by
+// wave and then through LDS; every thread gets the results.
+template <int G, bool kMax>
+__device__ __forceinline__ void block_reduce(float* v, float (*wred)[4]) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = v;
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float x = __shfl_xor(v[g], o);
+            v[g] = kMax ? fmaxf(v[g], x) : v[g] + x;
+        }
+        if ((threadIdx.x & 63) == 0) wred[g][threadIdx.x >> 6] = v[g];
+    }
     __syncthreads();
-    v = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        v[g] = kMax ? fmaxf(fmaxf(wred[g][0], wred[g][1]), fmaxf(wred[g][2], wred[g][3]))
+                    : (wred[g][0] + wred[g][1]) + (wred[g][2] + wred[g][3]);
     __syncthreads();
-    return v;
 }
 
-__device__ __forceinline__ float block_sum(float v, float* wred) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-    __syncthreads();
-    return v;
+// CPL / 2 bytes of codes (CPL channels) at p, as 32-bit words.
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+    if constexpr (NW == 1) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (NW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    }
 }
 
-// One (query head, chunk of 256 tokens). Partial output (unnormalized), chunk
-// maximum and sum go to the workspace.
+__device__ __forceinline__ int nibble(const uint32_t* w, int c) { return static_cast<int>((w[c >> 3] >> (4 * (c & 7))) & 15u); }
+
+// One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
+// channels of one token (d / CPL lanes share a token); each code is converted
+// once and feeds the G queries, so a grouped-query cache is read once for G
+// heads. Loads are issued U steps at a time. Partial outputs (unnormalized),
+// chunk maxima and sums go to the workspace.
+template <int CPL, int G>
 __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int nsplit,
     float* __restrict__ part, float* __restrict__ ml) {
-    __shared__ float sc[kKvChunk];
-    __shared__ float red[4][512];
-    __shared__ float wred[4];
-    const int h = blockIdx.x / nsplit;
-    const int s = blockIdx.x - h * nsplit;
-    const int hk = h / group;
+    constexpr int NW = CPL / 8;                  // 32-bit code words per lane
+    constexpr int U = 4;                         // steps whose loads are in flight together
+    __shared__ float sc[G][kKvChunk];
+    __shared__ float red[G * 512];
+    __shared__ float wred[G][4];
+    const int rq = group / G;                    // workgroups per kv head and chunk
+    const int s = blockIdx.x % nsplit;
+    const int r = blockIdx.x / nsplit;
+    const int hk = r / rq;
+    const int h0 = hk * group + (r - hk * rq) * G;   // first query head
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int D = d >> 3;                        // lanes per token, power of two in [1, 64]
+    const int D = d / CPL;                       // lanes per token, power of two in [1, 64]
     const int TPW = 64 / D;                      // tokens per wave step
-    const int j = lane & (D - 1);                // code word of the token
+    const int j = lane & (D - 1);                // channel slice of the token
     const int sub = lane / D;                    // token slot within the wave step
     const int t0 = s * kKvChunk;
     const int nt = imin(kKvChunk, T - t0);       // >= 1
     const int rb = d >> 1;                       // bytes per cached vector
 
-    float qf[8];
-    unpack8(*reinterpret_cast<const uint4*>(q + static_cast<size_t>(h) * d + 8 * j), qf);
-    float qs = ((qf[0] + qf[1]) + (qf[2] + qf[3])) + ((qf[4] + qf[5]) + (qf[6] + qf[7]));
-    for (int o = 1; o < D; o <<= 1) qs += __shfl_xor(qs, o);
+    float qf[G][CPL], qs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const uint16_t* qg = q + static_cast<size_t>(h0 + g) * d + CPL * j;
+#pragma unroll
+        for (int k = 0; k < CPL / 8; ++k) unpack8(*reinterpret_cast<const uint4*>(qg + 8 * k), &qf[g][8 * k]);
+        float a = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) a += qf[g][c];
+        for (int o = 1; o < D; o <<= 1) a += __shfl_xor(a, o);
+        qs[g] = a;
+    }
 
     const size_t base = static_cast<size_t>(hk) * tcap + t0;   // slot of the chunk's first token
     const int per_step = 4 * TPW;
     const int niter = (nt + per_step - 1) / per_step;
+    const int first = wave * TPW + sub;
 
     // scores a_t = s_t (q . u_t - z_t sum q) / sqrt(d)
-#pragma unroll 2
-    for (int it = 0; it < niter; ++it) {
-        const int i = it * per_step + wave * TPW + sub;
-        const bool ok = i < nt;
-        uint32_t w = 0;
-        float st = 0.0f;
-        int zt = 0;
-        if (ok) {
-            const size_t sl = base + i;
-            w = *reinterpret_cast<const uint32_t*>(kc + sl * rb + 4 * j);
-            st = h2f(ks[sl]);
-            zt = kz[sl];
-        }
-        float dot = 0.0f;
+    for (int it0 = 0; it0 < niter; it0 += U) {
+        uint32_t w[U][NW];
+        float st[U];
+        int zt[U];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dot += qf[c] * static_cast<float>((w >> (4 * c)) & 15u);
-        for (int o = 1; o < D; o <<= 1) dot += __shfl_xor(dot, o);
-        if (ok && j == 0) sc[i] = st * (dot - static_cast<float>(zt) * qs) * scale;
+        for (int u = 0; u < U; ++u) {
+            const int i = (it0 + u) * per_step + first;
+#pragma unroll
+            for (int k = 0; k < NW; ++k) w[u][k] = 0;
+            st[u] = 0.0f;
+            zt[u] = 0;
+            if (i < nt) {
+                const size_t sl = base + i;
+                load_words<NW>(kc + sl * rb + (CPL / 2) * j, w[u]);
+                st[u] = h2f(ks[sl]);
+                zt[u] = kz[sl];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = (it0 + u) * per_step + first;
+            float dot[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) dot[g] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float x = static_cast<float>(nibble(w[u], c));
+#pragma unroll
+                for (int g = 0; g < G; ++g) dot[g] += qf[g][c] * x;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                for (int o = 1; o < D; o <<= 1) dot[g] += __shfl_xor(dot[g], o);
+            if (i < nt && j == 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) sc[g][i] = st[u] * (dot[g] - static_cast<float>(zt[u]) * qs[g]) * scale;
+            }
+        }
     }
     __syncthreads();
 
-    float m = -INFINITY;
-    for (int i = threadIdx.x; i < nt; i += kKvThreads) m = fmaxf(m, sc[i]);
-    m = block_max(m, wred);
-    float l = 0.0f;
-    for (int i = threadIdx.x; i < nt; i += kKvThreads) {
-        const float p = expf(sc[i] - m);
-        sc[i] = p;
-        l += p;
+    float m[G], l[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        for (int i = threadIdx.x; i < nt; i += kKvThreads) m[g] = fmaxf(m[g], sc[g][i]);
     }
-    l = block_sum(l, wred);                      // its barriers also publish sc
+    block_reduce<G, true>(m, wred);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = 0.0f;
+        for (int i = threadIdx.x; i < nt; i += kKvThreads) {
+            const float p = expf(sc[g][i] - m[g]);
+            sc[g][i] = p;
+            l[g] += p;
+        }
+    }
+    block_reduce<G, false>(l, wred);             // its barriers also publish sc
 
     // acc = sum_t p_t s_t (u_t - z_t)
-    float acc[8];
+    float acc[G][CPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-#pragma unroll 2
-    for (int it = 0; it < niter; ++it) {
-        const int i = it * per_step + wave * TPW + sub;
-        const bool ok = i < nt;
-        uint32_t w = 0;
-        float wt = 0.0f;
-        int zt = 0;
-        if (ok) {
-            const size_t sl = base + i;
-            w = *reinterpret_cast<const uint32_t*>(vc + sl * rb + 4 * j);
-            wt = sc[i] * h2f(vs[sl]);
-            zt = vz[sl];
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[g][c] = 0.0f;
+    for (int it0 = 0; it0 < niter; it0 += U) {
+        uint32_t w[U][NW];
+        float st[U];
+        int zt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = (it0 + u) * per_step + first;
+#pragma unroll
+            for (int k = 0; k < NW; ++k) w[u][k] = 0;
+            st[u] = 0.0f;
+            zt[u] = 0;
+            if (i < nt) {
+                const size_t sl = base + i;
+                load_words<NW>(vc + sl * rb + (CPL / 2) * j, w[u]);
+                st[u] = h2f(vs[sl]);
+                zt[u] = vz[sl];
+            }
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            acc[c] += wt * static_cast<float>(static_cast<int>((w >> (4 * c)) & 15u) - zt);
+        for (int u = 0; u < U; ++u) {
+            const int i = (it0 + u) * per_step + first;
+            float wt[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) wt[g] = i < nt ? sc[g][i] * st[u] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float x = static_cast<float>(nibble(w[u], c) - zt[u]);
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g][c] += wt[g] * x;
+            }
+        }
     }
     for (int o = D; o < 64; o <<= 1) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], o);
-    }
-    if (sub == 0) {
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) red[wave][8 * j + c] = acc[c];
+            for (int c = 0; c < CPL; ++c) acc[g][c] += __shfl_xor(acc[g][c], o);
     }
-    __syncthreads();
-    const size_t row = static_cast<size_t>(h) * nsplit + s;
-    for (int i = threadIdx.x; i < d; i += kKvThreads)
-        part[row * d + i] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
-    if (threadIdx.x == 0) {
-        ml[2 * row] = m;
-        ml[2 * row + 1] = l;
+    // waves in turn: ((w0 + w1) + w2) + w3, the same order on every run
+    for (int wv = 0; wv < 4; ++wv) {
+        if (wave == wv && sub == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int idx = g * d + CPL * j + c;
+                    red[idx] = wv == 0 ? acc[g][c] : red[idx] + acc[g][c];
+                }
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < G * d; i += kKvThreads) {
+        const int g = i / d;
+        part[(static_cast<size_t>(h0 + g) * nsplit + s) * d + (i - g * d)] = red[i];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (threadIdx.x == g) {
+            const size_t row = static_cast<size_t>(h0 + g) * nsplit + s;
+            ml[2 * row] = m[g];
+            ml[2 * row + 1] = l[g];
+        }
     }
 }
 
@@ -240,6 +337,8 @@ __global__ __launch_bounds__(128) void kv4_attn_combine_kernel(const float* __re
     }
 }
 
+inline int imin_host(int a, int b) { return a < b ? a : b; }
+
 }  // namespace
 
 int launch_kv4_quantize(const uint16_t* X, int ntok, int H, int d, int ldx, int pos, int tcap, uint8_t* codes,
@@ -259,8 +358,22 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     float* part = workspace;
     float* ml = workspace + static_cast<size_t>(Hq) * nsplit * d;
     const float scale = 1.0f / sqrtf(static_cast<float>(d));
-    kv4_attn_chunk_kernel<<<Hq * nsplit, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, tcap, scale,
-                                                              nsplit, part, ml);
+    const int G = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    const int cpl = imin_host(imin_host(32, 64 / G), d);
+    const int grid = (Hq / G) * nsplit;
+#define COMET_KV4_CHUNK(C, GG)                                                                              \
+    kv4_attn_chunk_kernel<C, GG><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, tcap, \
+                                                               scale, nsplit, part, ml)
+    if (G == 8) {
+        COMET_KV4_CHUNK(8, 8);
+    } else if (G == 4) {
+        if (cpl == 16) COMET_KV4_CHUNK(16, 4); else COMET_KV4_CHUNK(8, 4);
+    } else if (G == 2) {
+        if (cpl == 32) COMET_KV4_CHUNK(32, 2); else if (cpl == 16) COMET_KV4_CHUNK(16, 2); else COMET_KV4_CHUNK(8, 2);
+    } else {
+        if (cpl == 32) COMET_KV4_CHUNK(32, 1); else if (cpl == 16) COMET_KV4_CHUNK(16, 1); else COMET_KV4_CHUNK(8, 1);
+    }
+#undef COMET_KV4_CHUNK
     const int e = static_cast<int>(hipGetLastError());
     if (e != 0) return e;
     kv4_attn_combine_kernel<<<Hq, 128, 0, st>>>(part, ml, nsplit, d, out);
