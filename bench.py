@@ -529,6 +529,8 @@ def main():
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused-quantizer and asymmetric-variant ablations (outside the timed step)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kv4-only", action="store_true",
+                    help="only the KV4 decode attention measurement (its JSON object), for profiling")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -545,6 +547,9 @@ def main():
     from gen import synth
     comet.lib()
     assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.kv4_only:
+        print(json.dumps({"kv4_decode_attention": kv4_attention_measure(torch, comet, synth)}), flush=True)
+        return
 
     layers = [Layer(n, copies_for(synth.CONFIGS[n]), torch, comet, synth)
               for n in WORKLOADS[args.workload]]

@@ -15,14 +15,15 @@
 //
 // Attention: the page's point is that decode attention is memory bound, so
 // dequantization must cost few operations per code. Here a workgroup (4
-// waves) takes one query head and a chunk of 256 cached tokens; d/8 lanes
-// share a token, each reading one 32-bit word of its codes, so a wave load
-// covers 256 contiguous bytes of the cache. The zero point is taken out of
-// the key product as a whole, s (q.u - z sum(q)), so a key code costs one
-// conversion and one multiply-add; the value codes are weighted by p s and the
-// zero point subtracted per code. The chunk keeps its own maximum and sum, and
-// a second kernel combines the chunks (the split-softmax identity:
-// out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c).
+// waves) takes one kv head, the G query heads of it that it serves, and a
+// chunk of 256 cached tokens; d / CPL lanes share a token, each reading CPL
+// codes (16 bytes for d >= 32 when G <= 2), so a wave load covers contiguous
+// cache rows. The zero point comes out of both products as a whole: the key
+// product is s (q.u - z sum(q)) and the value sum is
+// sum p s u - sum p s z, so a code costs a byte-to-float conversion (shared by
+// the G queries) and one multiply-add per query. The chunk keeps its own
+// maximum and sum, and a second kernel combines the chunks (the split-softmax
+// identity: out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -33,6 +34,7 @@ namespace comet {
 namespace {
 
 constexpr int kKvThreads = 256;   // 4 waves
+constexpr int kKvChunkMax = 1024; // cached tokens per attention workgroup, at most
 
 __device__ __forceinline__ void unpack8(uint4 p, float* x) {
     const uint32_t w[4] = {p.x, p.y, p.z, p.w};
@@ -138,22 +140,96 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
     }
 }
 
-__device__ __forceinline__ int nibble(const uint32_t* w, int c) { return static_cast<int>((w[c >> 3] >> (4 * (c & 7))) & 15u); }
+// The CPL codes of NW words as floats: the even channels of a word are its low
+// nibbles and the odd channels its high nibbles, so two masks put each in a
+// byte of its own and one byte-to-float conversion takes each code.
+// (The byte conversions are written out: left to the compiler, the masks let
+// it narrow each byte to a 4-bit field extract followed by a conversion.)
+template <int B>
+__device__ __forceinline__ float ubyte_to_float(uint32_t x) {
+    float r;
+    if constexpr (B == 0)
+        asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (B == 1)
+        asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (B == 2)
+        asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+    else
+        asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+template <int NW>
+__device__ __forceinline__ void codes_to_float(const uint32_t* w, float* x) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const uint32_t ev = w[k] & 0x0F0F0F0Fu;
+        const uint32_t od = (w[k] >> 4) & 0x0F0F0F0Fu;
+        x[8 * k + 0] = ubyte_to_float<0>(ev);
+        x[8 * k + 1] = ubyte_to_float<0>(od);
+        x[8 * k + 2] = ubyte_to_float<1>(ev);
+        x[8 * k + 3] = ubyte_to_float<1>(od);
+        x[8 * k + 4] = ubyte_to_float<2>(ev);
+        x[8 * k + 5] = ubyte_to_float<2>(od);
+        x[8 * k + 6] = ubyte_to_float<3>(ev);
+        x[8 * k + 7] = ubyte_to_float<3>(od);
+    }
+}
+
+// v plus the value of lane (lane xor O): quad permutes for 1 and 2, a swizzle
+// within 32 lanes up to 16, a permute across the halves for 32.
+template <int O>
+__device__ __forceinline__ float xor_add(float v) {
+    const int x = __float_as_int(v);
+    int y;
+    if constexpr (O == 1)
+        y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+    else if constexpr (O == 2)
+        y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+    else if constexpr (O < 32)
+        y = __builtin_amdgcn_ds_swizzle(x, 0x1F | (O << 10));     // bitmask mode: lane ^ O
+    else
+        return v + __shfl_xor(v, O);
+    return v + __int_as_float(y);
+}
+
+// Sum over aligned groups of n lanes (n a power of two, uniform).
+__device__ __forceinline__ float group_sum(float v, int n) {
+    if (n > 1) v = xor_add<1>(v);
+    if (n > 2) v = xor_add<2>(v);
+    if (n > 4) v = xor_add<4>(v);
+    if (n > 8) v = xor_add<8>(v);
+    if (n > 16) v = xor_add<16>(v);
+    if (n > 32) v = xor_add<32>(v);
+    return v;
+}
+
+// Sum over the lanes that share lane mod n (n a power of two, uniform).
+__device__ __forceinline__ float stride_sum(float v, int n) {
+    if (n < 2) v = xor_add<1>(v);
+    if (n < 4) v = xor_add<2>(v);
+    if (n < 8) v = xor_add<4>(v);
+    if (n < 16) v = xor_add<8>(v);
+    if (n < 32) v = xor_add<16>(v);
+    if (n < 64) v = xor_add<32>(v);
+    return v;
+}
 
 // One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
 // channels of one token (d / CPL lanes share a token); each code is converted
 // once and feeds the G queries, so a grouped-query cache is read once for G
 // heads. Loads are issued U steps at a time. Partial outputs (unnormalized),
 // chunk maxima and sums go to the workspace.
-template <int CPL, int G>
+template <int CPL, int G, int kDim>              // kDim: d, or 0 for any d
 __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
-    const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int nsplit,
+    const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int chunk, int nsplit,
     float* __restrict__ part, float* __restrict__ ml) {
     constexpr int NW = CPL / 8;                  // 32-bit code words per lane
-    constexpr int U = 4;                         // steps whose loads are in flight together
-    __shared__ float sc[G][kKvChunk];
+    constexpr int U = NW == 4 ? 2 : 4;           // steps whose loads are in flight together
+    if constexpr (kDim != 0) d = kDim;
+    __shared__ float sc[G][kKvChunkMax];
     __shared__ float red[G * 512];
     __shared__ float wred[G][4];
     const int rq = group / G;                    // workgroups per kv head and chunk
@@ -166,8 +242,8 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const int TPW = 64 / D;                      // tokens per wave step
     const int j = lane & (D - 1);                // channel slice of the token
     const int sub = lane / D;                    // token slot within the wave step
-    const int t0 = s * kKvChunk;
-    const int nt = imin(kKvChunk, T - t0);       // >= 1
+    const int t0 = s * chunk;
+    const int nt = imin(chunk, T - t0);          // >= 1
     const int rb = d >> 1;                       // bytes per cached vector
 
     float qf[G][CPL], qs[G];
@@ -179,8 +255,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
         float a = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) a += qf[g][c];
-        for (int o = 1; o < D; o <<= 1) a += __shfl_xor(a, o);
-        qs[g] = a;
+        qs[g] = group_sum(a, D);
     }
 
     const size_t base = static_cast<size_t>(hk) * tcap + t0;   // slot of the chunk's first token
@@ -210,18 +285,17 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            float dot[G];
+            float dot[G], x[CPL];
+            codes_to_float<NW>(w[u], x);
 #pragma unroll
             for (int g = 0; g < G; ++g) dot[g] = 0.0f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float x = static_cast<float>(nibble(w[u], c));
 #pragma unroll
-                for (int g = 0; g < G; ++g) dot[g] += qf[g][c] * x;
+                for (int g = 0; g < G; ++g) dot[g] = fmaf(qf[g][c], x[c], dot[g]);
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-                for (int o = 1; o < D; o <<= 1) dot[g] += __shfl_xor(dot[g], o);
+            for (int g = 0; g < G; ++g) dot[g] = group_sum(dot[g], D);
             if (i < nt && j == 0) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) sc[g][i] = st[u] * (dot[g] - static_cast<float>(zt[u]) * qs[g]) * scale;
@@ -248,12 +322,14 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     }
     block_reduce<G, false>(l, wred);             // its barriers also publish sc
 
-    // acc = sum_t p_t s_t (u_t - z_t)
-    float acc[G][CPL];
+    // acc = sum_t p_t s_t u_t - sum_t p_t s_t z_t, the second sum once per token
+    float acc[G][CPL], wz[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+        wz[g] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[g][c] = 0.0f;
+    }
     for (int it0 = 0; it0 < niter; it0 += U) {
         uint32_t w[U][NW];
         float st[U];
@@ -275,23 +351,29 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            float wt[G];
+            float wt[G], x[CPL];
+            codes_to_float<NW>(w[u], x);
+            const float zf = static_cast<float>(zt[u]);
 #pragma unroll
-            for (int g = 0; g < G; ++g) wt[g] = i < nt ? sc[g][i] * st[u] : 0.0f;
+            for (int g = 0; g < G; ++g) {
+                wt[g] = i < nt ? sc[g][i] * st[u] : 0.0f;
+                wz[g] = fmaf(wt[g], zf, wz[g]);
+            }
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float x = static_cast<float>(nibble(w[u], c) - zt[u]);
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g][c] += wt[g] * x;
+                for (int g = 0; g < G; ++g) acc[g][c] = fmaf(wt[g], x[c], acc[g][c]);
             }
         }
     }
-    for (int o = D; o < 64; o <<= 1) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[g][c] += __shfl_xor(acc[g][c], o);
-    }
+        for (int c = 0; c < CPL; ++c) acc[g][c] -= wz[g];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[g][c] = stride_sum(acc[g][c], D);
     // waves in turn: ((w0 + w1) + w2) + w3, the same order on every run
     for (int wv = 0; wv < 4; ++wv) {
         if (wave == wv && sub == 0) {
@@ -354,16 +436,28 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const uint8_t* vc, const uint16_t* vs, const uint8_t* vz, int Hq, int group, int d, int T,
                          int tcap, uint16_t* out, float* workspace, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const int nsplit = kv4_splits(T);
+    // Tokens per workgroup: 256, or 512 / 1024 when the grid still has 2048
+    // workgroups (8 per CU), to spread the fixed cost of a chunk (the
+    // softmax reductions, the cross-lane sums, the partial outputs) over more
+    // tokens. Never more splits than kv4_splits(T), which sizes the workspace.
+    const int G = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    int chunk = kKvChunkMax;
+    while (chunk > kKvChunk && static_cast<int64_t>(Hq / G) * ((T + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    const int nsplit = (T + chunk - 1) / chunk;
     float* part = workspace;
     float* ml = workspace + static_cast<size_t>(Hq) * nsplit * d;
     const float scale = 1.0f / sqrtf(static_cast<float>(d));
-    const int G = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
     const int cpl = imin_host(imin_host(32, 64 / G), d);
     const int grid = (Hq / G) * nsplit;
-#define COMET_KV4_CHUNK(C, GG)                                                                              \
-    kv4_attn_chunk_kernel<C, GG><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, tcap, \
-                                                               scale, nsplit, part, ml)
+#define COMET_KV4_CHUNK(C, GG)                                                                                 \
+    do {                                                                                                       \
+        if (d == 128)                                                                                          \
+            kv4_attn_chunk_kernel<C, GG, 128><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, \
+                                                                          tcap, scale, chunk, nsplit, part, ml); \
+        else                                                                                                   \
+            kv4_attn_chunk_kernel<C, GG, 0><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T,   \
+                                                                        tcap, scale, chunk, nsplit, part, ml);   \
+    } while (0)
     if (G == 8) {
         COMET_KV4_CHUNK(8, 8);
     } else if (G == 4) {

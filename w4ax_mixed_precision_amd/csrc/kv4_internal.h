@@ -7,7 +7,7 @@
 
 namespace comet {
 
-constexpr int kKvChunk = 256;   // cached tokens per attention workgroup
+constexpr int kKvChunk = 256;   // cached tokens per attention workgroup, at least
 
 inline int kv4_splits(int T) { return (T + kKvChunk - 1) / kKvChunk; }
 
