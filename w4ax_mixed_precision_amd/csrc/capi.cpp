@@ -173,7 +173,7 @@ int comet_kv4_quantize(const void* X_fp16, int ntok, int H, int d, int ldx, int 
         return COMET_ERR_SHAPE;
     if (static_cast<int64_t>(pos) + ntok > tcap) return COMET_ERR_SHAPE;
     if (!kv4_dim_ok(d)) return COMET_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(ntok) * H > std::numeric_limits<int32_t>::max() - 4) return COMET_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(ntok) * H > std::numeric_limits<int32_t>::max() - 256) return COMET_ERR_UNSUPPORTED;
     if (!aligned16(X_fp16) || ldx % 8 != 0 || !aligned16(codes) || !aligned16(step_fp16) || !aligned16(zero))
         return COMET_ERR_ALIGN;
     return hip_status(comet::launch_kv4_quantize(static_cast<const uint16_t*>(X_fp16), ntok, H, d, ldx, pos, tcap,

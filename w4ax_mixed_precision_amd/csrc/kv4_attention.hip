@@ -10,8 +10,9 @@
 //          in the high nibble (one 32-bit word = 8 consecutive channels);
 //   step   [h][t] fp16 bits, zero [h][t] bytes.
 //
-// Quantizer: one wave per vector; a lane holds 8 channels (one 16-byte load,
-// one 32-bit code store), the range comes from two wave reductions.
+// Quantizer: d / 8 lanes per vector, each holding 8 channels (one 16-byte
+// load, one 32-bit code store); the range comes from min / max reductions
+// over those lanes.
 //
 // Attention: the page's point is that decode attention is memory bound, so
 // dequantization must cost few operations per code. Here a workgroup (4
@@ -46,21 +47,60 @@ __device__ __forceinline__ void unpack8(uint4 p, float* x) {
     }
 }
 
+// The value of lane (lane xor O): quad permutes for 1 and 2, a swizzle
+// within 32 lanes up to 16, a permute across the halves for 32.
+template <int O>
+__device__ __forceinline__ float xor_get(float v) {
+    const int x = __float_as_int(v);
+    if constexpr (O == 1)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));   // quad_perm [1, 0, 3, 2]
+    else if constexpr (O == 2)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));   // quad_perm [2, 3, 0, 1]
+    else if constexpr (O < 32)
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x1F | (O << 10)));     // bitmask mode: lane ^ O
+    else
+        return __shfl_xor(v, O);
+}
+
+template <int O>
+__device__ __forceinline__ float xor_add(float v) { return v + xor_get<O>(v); }
+
+// Minimum and maximum over aligned groups of n lanes (n a power of two, uniform).
+template <int O>
+__device__ __forceinline__ void xor_minmax(float& lo, float& hi) {
+    lo = fminf(lo, xor_get<O>(lo));
+    hi = fmaxf(hi, xor_get<O>(hi));
+}
+__device__ __forceinline__ void group_minmax(float& lo, float& hi, int n) {
+    if (n > 1) xor_minmax<1>(lo, hi);
+    if (n > 2) xor_minmax<2>(lo, hi);
+    if (n > 4) xor_minmax<4>(lo, hi);
+    if (n > 8) xor_minmax<8>(lo, hi);
+    if (n > 16) xor_minmax<16>(lo, hi);
+    if (n > 32) xor_minmax<32>(lo, hi);
+}
+
+// Cache quantizer: d / 8 lanes per vector (8 channels each, one 16-byte
+// load), 64 / (d / 8) vectors per wave; the range by a min / max reduction
+// over the vector's lanes.
 __global__ __launch_bounds__(kKvThreads) void kv4_quant_kernel(const uint16_t* __restrict__ X, int nvec, int H,
                                                                int d, int ldx, int pos, int tcap,
                                                                uint8_t* __restrict__ codes,
                                                                uint16_t* __restrict__ step,
                                                                uint8_t* __restrict__ zero) {
     const int lane = threadIdx.x & 63;
-    const int v = blockIdx.x * (kKvThreads / 64) + (threadIdx.x >> 6);
-    if (v >= nvec) return;                               // whole wave
-    const int tok = v / H, h = v - tok * H;
-    const int D = d >> 3;                                // 32-bit code words per vector
-    const bool act = lane < D;
+    const int D = d >> 3;                                // lanes (32-bit code words) per vector
+    const int vpw = 64 / D;                              // vectors per wave
+    const int first = (blockIdx.x * (kKvThreads / 64) + (threadIdx.x >> 6)) * vpw;
+    if (first >= nvec) return;                           // whole wave
+    const int v = first + lane / D;
+    const int j = lane & (D - 1);
+    const bool act = v < nvec;                           // whole groups of D lanes
+    const int tok = act ? v / H : 0, h = act ? v - tok * H : 0;
     float x[8];
     if (act) {
         unpack8(*reinterpret_cast<const uint4*>(X + static_cast<size_t>(tok) * ldx + static_cast<size_t>(h) * d +
-                                                8 * lane),
+                                                8 * j),
                 x);
     } else {
 #pragma unroll
@@ -72,11 +112,8 @@ __global__ __launch_bounds__(kKvThreads) void kv4_quant_kernel(const uint16_t* _
         lo = fminf(lo, x[c]);
         hi = fmaxf(hi, x[c]);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o));
-        hi = fmaxf(hi, __shfl_xor(hi, o));
-    }
+    group_minmax(lo, hi, D);
+    if (!act) return;
     const size_t slot = static_cast<size_t>(h) * tcap + pos + tok;
     uint32_t word = 0;
     uint16_t s16 = 0;
@@ -95,8 +132,8 @@ __global__ __launch_bounds__(kKvThreads) void kv4_quant_kernel(const uint16_t* _
             word |= static_cast<uint32_t>(u) << (4 * c);
         }
     }
-    if (act) *reinterpret_cast<uint32_t*>(codes + slot * static_cast<size_t>(d >> 1) + 4 * lane) = word;
-    if (lane == 0) {
+    *reinterpret_cast<uint32_t*>(codes + slot * static_cast<size_t>(d >> 1) + 4 * j) = word;
+    if (j == 0) {
         step[slot] = s16;
         zero[slot] = static_cast<uint8_t>(z);
     }
@@ -175,23 +212,6 @@ __device__ __forceinline__ void codes_to_float(const uint32_t* w, float* x) {
         x[8 * k + 6] = ubyte_to_float<3>(ev);
         x[8 * k + 7] = ubyte_to_float<3>(od);
     }
-}
-
-// v plus the value of lane (lane xor O): quad permutes for 1 and 2, a swizzle
-// within 32 lanes up to 16, a permute across the halves for 32.
-template <int O>
-__device__ __forceinline__ float xor_add(float v) {
-    const int x = __float_as_int(v);
-    int y;
-    if constexpr (O == 1)
-        y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
-    else if constexpr (O == 2)
-        y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
-    else if constexpr (O < 32)
-        y = __builtin_amdgcn_ds_swizzle(x, 0x1F | (O << 10));     // bitmask mode: lane ^ O
-    else
-        return v + __shfl_xor(v, O);
-    return v + __int_as_float(y);
 }
 
 // Sum over aligned groups of n lanes (n a power of two, uniform).
@@ -427,7 +447,7 @@ inline int imin_host(int a, int b) { return a < b ? a : b; }
 int launch_kv4_quantize(const uint16_t* X, int ntok, int H, int d, int ldx, int pos, int tcap, uint8_t* codes,
                         uint16_t* step, uint8_t* zero, void* stream) {
     const int nvec = ntok * H;
-    const int per_block = kKvThreads / 64;
+    const int per_block = (kKvThreads / 64) * (64 / (d >> 3));   // vectors per workgroup
     kv4_quant_kernel<<<(nvec + per_block - 1) / per_block, kKvThreads, 0, static_cast<hipStream_t>(stream)>>>(
         X, nvec, H, d, ldx, pos, tcap, codes, step, zero);
     return static_cast<int>(hipGetLastError());
