@@ -22,12 +22,15 @@
  * device memory, asynchronous on a HIP stream). The *_fp6 calls are the same
  * three steps on a second operand layout (FP6-encoded 4-bit codes) that the
  * prefill GEMM kernel consumes directly; the INT4 layout is the smaller one
- * and serves the weight-bandwidth-bound decode shapes.
+ * and serves the weight-bandwidth-bound decode shapes. Further down: the
+ * quantizer fused into the RMSNorm or SwiGLU before it, QUIK's asymmetric
+ * 4-bit activations, QoQ's W4A8 variant, and a 4-bit KV cache with decode
+ * attention over it.
  *
  * Shared rules
  *   - Every function returns a comet_status. Nothing throws across the ABI.
  *   - The caller owns every buffer. The online calls never allocate; the GEMM
- *     uses only the workspace the caller passes.
+ *     and the KV4 attention use only the workspace the caller passes.
  *   - All argument checks run before any HIP call, so a rejected call has no
  *     effect on the device and needs no GPU.
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. The
@@ -35,7 +38,8 @@
  *     kernels themselves surface at the caller's next synchronization.
  *   - Calls on different streams with disjoint outputs may run concurrently.
  *     Two GEMM calls that share one workspace must be ordered by the caller.
- *   - Device pointers must be 16-byte aligned.
+ *   - Device pointers must be 16-byte aligned, except where a call states
+ *     2 bytes (comet_rmsnorm, comet_swiglu, the output of comet_kv4_attention).
  *
  * Notation: nb = K / 128 blocks; nb8 = n_int8_blocks; nb4 = nb - nb8. The
  * 8-bit blocks are always the LAST nb8 blocks of the permuted channel order
