@@ -239,7 +239,7 @@ __device__ __forceinline__ float stride_sum(float v, int n) {
 // One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
 // channels of one token (d / CPL lanes share a token); each code is converted
 // once and feeds the G queries, so a grouped-query cache is read once for G
-// heads. Loads are issued U steps at a time. Partial outputs (unnormalized),
+// heads. Partial outputs (unnormalized),
 // chunk maxima and sums go to the workspace.
 template <int CPL, int G, int kDim>              // kDim: d, or 0 for any d
 __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
@@ -248,7 +248,11 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int chunk, int nsplit,
     float* __restrict__ part, float* __restrict__ ml) {
     constexpr int NW = CPL / 8;                  // 32-bit code words per lane
-    constexpr int U = NW == 4 ? 2 : 4;           // steps whose loads are in flight together
+    // Steps whose loads are issued together: one for 16-byte slices (more
+    // steps in flight would hold more registers than the occupancy they cost
+    // is worth: LLaMA-7B / -70B decode shapes 81.4 / 87.3 us with one, 83-86 /
+    // 103-104 with two, 124 / 131 with four), four for the narrow slices.
+    constexpr int U = NW == 4 ? 1 : 4;
     if constexpr (kDim != 0) d = kDim;
     __shared__ float sc[G][kKvChunkMax];
     __shared__ float red[G * 512];
