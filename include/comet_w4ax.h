@@ -199,9 +199,11 @@ size_t comet_w4ax_gemm_workspace_bytes(int M, int N, int K, int n_int8_blocks);
 /*
  * Debug variant of the GEMM: writes the exact INT32 block partials of rows
  * [m_begin, m_begin + m_count) instead of Y, as P[m - m_begin][n][b] (int32,
- * [m_count][N][K/128], device). The partials do not depend on tiling, so any
- * row range gives the values the full GEMM uses. Same inputs and errors as
- * comet_w4ax_gemm (no workspace); SHAPE also covers a row range outside [0, M).
+ * [m_count][N][K/128], device). It launches the kernel that comet_w4ax_gemm
+ * launches for the same (M, N, K), with the same tile shape, block split and
+ * pipeline, over the tiles that hold those rows; only the epilogue is
+ * replaced by the stores of P. Same inputs and errors as comet_w4ax_gemm (no
+ * workspace); SHAPE also covers a row range outside [0, M).
  */
 int comet_w4ax_gemm_partials(const void* Xq, const float* x_scale, const void* Wq_packed,
                              const uint16_t* w_scale_fp16, const int16_t* w_sum,
@@ -395,7 +397,8 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
 
 /*
  * Debug variant of comet_w4ax_gemm_fp6: the exact INT32 block partials of rows
- * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], like
+ * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], from the kernel and
+ * launch configuration comet_w4ax_gemm_fp6 uses for the same (M, N, K), like
  * comet_w4ax_gemm_partials.
  */
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
@@ -410,17 +413,12 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
  * section "核融合": one kernel reads the input, takes its statistics and
  * quantizes. The normalization (RMSNorm, as in the LLaMA models the pages
  * evaluate) of row m:
- *   S  = sum over k of x_k^2 in binary64, in this order: the channels fall
- *        in chunks of 512 (chunk c = channels 512c .. 512c + 511); partial
- *        (w, j), w = 0..7, j = 0..63, adds x_k^2 for k = 512c + 8j + e over
- *        the chunks c = w, w + 8, w + 16, ... and e = 0..7 (increasing c,
- *        then e); for each w the 64 partials are halved with strides 32, 16,
- *        ..., 1 (partial j += partial j + stride for j < stride), and the 8
- *        results with strides 4, 2, 1;
+ *   S  = sum over k of x_k^2, the exact real sum rounded once to binary64
+ *        (nearest, ties to even); no summation order enters it;
  *   r  = binary32( 1 / sqrt(S / K + eps) ), the root and quotient in binary64;
  *   xn_k = fp16( (x_k * r) * gamma_k ), two binary32 products, nearest-even.
- * Every kernel of the library forms S the same way, so the fused calls give
- * exactly the codes and scales of comet_rmsnorm followed by comet_quant_act.
+ * Every kernel of the library forms this S, so the fused calls give exactly
+ * the codes and scales of comet_rmsnorm followed by comet_quant_act.
  * Normalized values must stay finite (|gamma| sqrt(K) < 65504); eps must be a
  * positive finite float.
  * ------------------------------------------------------------------------ */

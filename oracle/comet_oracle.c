@@ -590,42 +590,40 @@ int orc_epilogue(const int32_t *P, const float *sa, const uint16_t *sw16, int ro
 /* 6. RMS normalization (the step before the quantizer)                      */
 /* ------------------------------------------------------------------------ */
 
-/* Row statistic, in the order this library defines it (the pages fix none).
- * The row is cut into chunks of 512 channels, c = 0, 1, ...; lane j (0..63)
- * of virtual wave w (0..7) owns channels 512c + 8j + e (e = 0..7) of the
- * chunks c = w, w + 8, w + 16, ...; its partial adds x_k^2 over those chunks
- * in increasing c and, inside a chunk, increasing e (channels k >= K add
- * nothing). The 64 lane partials of a wave are then halved with strides 32,
- * 16, ..., 1 (partial j += partial j + stride for j < stride), and the 8 wave
- * results with strides 4, 2, 1. All in binary64, where every square of a
- * binary16 value is exact. */
+/* binary64 nearest to a non-negative 128-bit integer, ties to even: keep the
+ * 53 leading bits, look at the bits cut off (above, at or below half a unit
+ * of the kept last bit) and round the kept part up where the rule says so. */
+static double orc_u128_to_double(unsigned __int128 v)
+{
+    if ((v >> 53) == 0)
+        return (double)(uint64_t)v; /* fits the significand: exact */
+    int n = 0; /* bit length of v */
+    for (unsigned __int128 t = v; t != 0; t >>= 1)
+        ++n;
+    int cut = n - 53;
+    unsigned __int128 kept = v >> cut;
+    unsigned __int128 rest = v - (kept << cut);
+    unsigned __int128 half = (unsigned __int128)1 << (cut - 1);
+    if (rest > half || (rest == half && (kept & 1)))
+        kept += 1; /* may reach 2^53: still exact in binary64 */
+    return ldexp((double)(uint64_t)kept, cut);
+}
+
+/* Row statistic S = sum over k of x_k^2, the exact real sum rounded once to
+ * binary64 (nearest, ties to even). The pages fix no precision or order for
+ * it; the exact sum is the one value that needs neither. Every binary16 value
+ * is an integer multiple of 2^-24 (|x| = n 2^-24 with n < 2^40), so every
+ * square is n^2 2^-48 with n^2 < 2^80, and the integers n^2 add up exactly in
+ * 128 bits for any row this library accepts (K < 2^47). */
 double orc_rms_sumsq(const uint16_t *x, int K)
 {
-    double wave[8];
-    int chunks = (K + 511) / 512;
-    for (int w = 0; w < 8; ++w) {
-        double lane[64];
-        for (int j = 0; j < 64; ++j) {
-            double s = 0.0;
-            for (int c = w; c < chunks; c += 8)
-                for (int e = 0; e < 8; ++e) {
-                    int k = 512 * c + 8 * j + e;
-                    if (k < K) {
-                        double v = (double)orc_half_to_float(x[k]);
-                        s = s + v * v;
-                    }
-                }
-            lane[j] = s;
-        }
-        for (int stride = 32; stride >= 1; stride /= 2)
-            for (int j = 0; j < stride; ++j)
-                lane[j] = lane[j] + lane[j + stride];
-        wave[w] = lane[0];
+    unsigned __int128 acc = 0;
+    for (int k = 0; k < K; ++k) {
+        double v = fabs((double)orc_half_to_float(x[k])); /* exact */
+        uint64_t n = (uint64_t)ldexp(v, 24);              /* exact integer */
+        acc += (unsigned __int128)n * n;
     }
-    for (int stride = 4; stride >= 1; stride /= 2)
-        for (int w = 0; w < stride; ++w)
-            wave[w] = wave[w] + wave[w + stride];
-    return wave[0];
+    return ldexp(orc_u128_to_double(acc), -48); /* a power-of-two scaling: exact */
 }
 
 /* Xn[m][k] = fp16( (x * r) * gamma_k ) with r = binary32( 1 / sqrt(S / K +

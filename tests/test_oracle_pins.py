@@ -552,24 +552,63 @@ def _exact_sumsq(x16):
 
 
 def test_rms_sumsq_exact_on_dyadic_rows(orc):
-    """Rows of multiples of 2^-8 in [-4, 4]: every partial sum is exact in
-    binary64, so the statistic equals the exact rational sum of squares
-    whatever the order."""
+    """Rows of multiples of 2^-8 in [-4, 4]: the exact sum of squares is a
+    binary64 value, so the statistic is that rational exactly."""
     rng = np.random.default_rng(11)
     for K in (128, 1000, 8192, 28672):
         x = (rng.integers(-1024, 1025, K) / 256.0).astype(np.float16).view(np.uint16)
         assert Fraction(orc.rms_sumsq(x)) == _exact_sumsq(x), K
 
 
-def test_rms_sumsq_close_to_exact_on_wide_rows(orc):
-    """Heavy-tailed rows spanning many binades: within binary64 rounding of the
-    exact sum (no term dropped, none counted twice)."""
+def test_rms_sumsq_correctly_rounded_on_wide_rows(orc):
+    """Heavy-tailed rows over many binades (subnormal to 65504): the statistic
+    is the exact rational sum of squares rounded once to binary64, which
+    Python's float() of a Fraction does (nearest, ties to even)."""
     rng = np.random.default_rng(12)
-    for K in (512, 4096, 11008):
-        x = (rng.standard_t(3, K) * 10.0 ** rng.uniform(-3, 2, K)).astype(np.float16).view(np.uint16)
-        exact = _exact_sumsq(x)
-        got = Fraction(orc.rms_sumsq(x))
-        assert abs(got - exact) <= exact * Fraction(K, 2 ** 52), K
+    for K in (512, 4096, 11008, 28672):
+        x = np.clip(rng.standard_t(3, K) * 10.0 ** rng.uniform(-9, 4, K), -65504, 65504).astype(np.float16)
+        x[: K // 64] = rng.choice([65504.0, -65504.0, 6.1e-5, -3e-8, 0.0], K // 64)
+        x = x.view(np.uint16)
+        assert orc.rms_sumsq(x) == float(_exact_sumsq(x)), K
+
+
+def test_rms_sumsq_small_terms_and_ties(orc):
+    """Closed forms where a binary64 running sum and the exact sum differ:
+    one large square (2^30) followed by many squares each below half a unit
+    in the last place of 2^30 (dropped one by one by a running sum, not by the
+    exact sum); and sums that fall exactly halfway between two binary64
+    values, which must round to the even neighbour."""
+    big = np.float16(32768.0)                      # 2^15, square 2^30
+    tiny = np.float16(2.0 ** -14)                  # square 2^-28 < 2^-23
+    x = np.array([big] + [tiny] * 8191, np.float16).view(np.uint16)
+    exact = Fraction(2) ** 30 + 8191 * Fraction(2) ** -28
+    assert orc.rms_sumsq(x) == float(exact)
+    assert orc.rms_sumsq(x) != 2.0 ** 30          # the running sum's value
+    # 2^30 + 2^-23: halfway between 2^30 and 2^30 + 2^-22; the even one is 2^30
+    h = np.array([big, 2.0 ** -12, 2.0 ** -12], np.float16).view(np.uint16)
+    assert orc.rms_sumsq(h) == 2.0 ** 30
+    # 2^30 + 2^-22 + 2^-23: halfway above an odd last bit: rounds up
+    h = np.array([big, 2.0 ** -11, 2.0 ** -12, 2.0 ** -12], np.float16).view(np.uint16)
+    assert orc.rms_sumsq(h) == 2.0 ** 30 + 2.0 ** -21
+    # just past the midpoint: up; just short of it: down
+    h = np.array([big, 2.0 ** -12, 2.0 ** -12, 2.0 ** -24], np.float16).view(np.uint16)
+    assert orc.rms_sumsq(h) == 2.0 ** 30 + 2.0 ** -22
+    # smallest subnormal squared, alone: 2^-48 exactly
+    assert orc.rms_sumsq(np.array([1], np.uint16)) == 2.0 ** -48
+    # 128-bit range: 28672 copies of 65504 (sum near 2^46.8)
+    x = np.full(28672, 65504.0, np.float16).view(np.uint16)
+    assert orc.rms_sumsq(x) == float(28672 * Fraction(65504) ** 2)
+
+
+def test_rms_sumsq_order_free(orc):
+    """The statistic does not depend on the order of the row (an exact sum
+    rounded once): every shuffle gives the same bits."""
+    rng = np.random.default_rng(16)
+    x = np.clip(rng.standard_t(2, 4096) * 10.0 ** rng.uniform(-6, 4, 4096), -65504, 65504)
+    x = x.astype(np.float16).view(np.uint16)
+    base = orc.rms_sumsq(x)
+    for _ in range(5):
+        assert orc.rms_sumsq(rng.permutation(x)) == base
 
 
 def test_rmsnorm_against_float64_formula(orc):

@@ -34,12 +34,13 @@
 // the layer norm before it). The row is already staged once for the gather,
 // so the statistic costs one more pass over LDS, and the normalized row never
 // goes to memory: xn = fp16((x r) gamma), r = binary32(1 / sqrt(S / K + eps)),
-// S a binary64 sum of squares in a fixed order that follows the staging: the
-// wave that loads a 512-channel chunk also sums its squares (8 consecutive
-// channels per lane), so each wave's part needs no barrier, and the parts of
-// the 8 (virtual) waves meet at the barrier the row needs anyway. Every kernel
-// here forms S the same way, so the fused codes equal those of normalizing
-// first and quantizing after.
+// S the exact sum of squares rounded once to binary64. The squares are summed
+// as integers (units of 2^-48) while the row is staged: the wave that loads a
+// 512-channel chunk also adds its squares, so each wave's part needs no
+// barrier, and the parts meet at the barrier the row needs anyway. Integer
+// sums do not depend on the order, so every kernel here, and any other exact
+// implementation, gets the same S, and the fused codes equal those of
+// normalizing first and quantizing after.
 //
 // The same kernels also fuse the SwiGLU before the down projection (QoQ/QServe
 // article, section "运行时设计": the quantization of the second FFN layer's
@@ -82,16 +83,53 @@ __device__ __forceinline__ void load_positions(const int32_t* __restrict__ perm,
     for (int k = 0; k < 8; ++k) p[k] = src[k];
 }
 
-// Row statistic S = sum of x_k^2 in binary64, in this fixed order: chunk c
-// holds channels 512c .. 512c + 511; lane j of virtual wave w (0..7) adds the
-// squares of channels 512c + 8j + e (e = 0..7) over the chunks c = w, w + 8,
-// ... in increasing c, then e; the 64 lane sums are halved with strides 32 ..
-// 1 and the 8 wave sums with strides 4, 2, 1. A workgroup's wave w stages the
-// chunks c = w mod (waves) itself, so it can form its part as soon as its own
-// direct loads have landed. The xor butterfly gives every lane the halving
-// result (each of its additions has the operands of a halving step).
-__device__ __forceinline__ double wave_sumsq(const uint16_t* row, int K, int w, int lane) {
-    double s = 0.0;
+// Row statistic S = the exact sum of x_k^2, rounded once to binary64. Every
+// binary16 value is n 2^-24 with n < 2^40, so x^2 is the integer n^2 < 2^80
+// in units of 2^-48; those integers add up exactly in 128 bits (two 64-bit
+// words), in whatever order the lanes and waves take them, and the total is
+// rounded to binary64 once at the end. Staging and reduction order therefore
+// do not change a bit of S.
+struct SumSq {
+    uint64_t lo, hi;
+};
+
+// a += x^2 for the binary16 value with bits h (finite): |x| = s 2^(max(e,1) - 25)
+// with s the significand (the implicit bit for e > 0), so x^2 = s^2 2^sh in
+// units of 2^-48 with sh = 2 max(e, 1) - 2 <= 58 and s^2 < 2^22.
+__device__ __forceinline__ void sumsq_add(SumSq& a, uint32_t h) {
+    const uint32_t e = (h >> 10) & 31u;
+    const uint32_t s = (h & 1023u) | (e != 0u ? 1024u : 0u);
+    const uint32_t sh = e != 0u ? 2u * e - 2u : 0u;
+    const uint64_t s2 = static_cast<uint64_t>(s * s);
+    const uint64_t lo = s2 << sh;                       // the bits below 2^64
+    const uint64_t hi = (s2 >> 1) >> (63u - sh);        // the bits at and above 2^64
+    a.lo += lo;
+    a.hi += hi + (a.lo < lo ? 1u : 0u);
+}
+
+__device__ __forceinline__ void sumsq_merge(SumSq& a, uint64_t lo, uint64_t hi) {
+    a.lo += lo;
+    a.hi += hi + (a.lo < lo ? 1u : 0u);
+}
+
+// binary64 value of a sum (nearest, ties to even). Below 2^64 the 64-bit
+// integer converts with one rounding (two exact 32-bit conversions, one
+// exact scaling, one addition); above, the 64 leading bits are kept and the
+// bits shifted out are folded into the lowest kept bit (a sticky bit), which
+// keeps every rounding decision of the full value.
+__device__ __forceinline__ double sumsq_value(const SumSq& a) {
+    if (a.hi == 0) return __builtin_ldexp(static_cast<double>(a.lo), -48);
+    const int n = 64 - __clzll(static_cast<long long>(a.hi));     // 1 .. 47
+    const uint64_t top = (a.hi << (64 - n)) | (a.lo >> n);
+    const uint64_t sticky = (a.lo << (64 - n)) != 0 ? 1u : 0u;
+    return __builtin_ldexp(static_cast<double>(top | sticky), n - 48);
+}
+
+// This lane's part of the sum over the chunks c = w, w + 8, ... (chunk c
+// holds channels 512c .. 512c + 511, 8 consecutive channels per lane), then
+// summed over the 64 lanes of the wave (every lane gets the total).
+__device__ __forceinline__ SumSq wave_sumsq(const uint16_t* row, int K, int w, int lane) {
+    SumSq s = {0u, 0u};
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     const int chunks = (K + 511) / 512;
     for (int c = w; c < chunks; c += 8) {
@@ -100,38 +138,36 @@ __device__ __forceinline__ double wave_sumsq(const uint16_t* row, int K, int w, 
             const uint4 q = *reinterpret_cast<const uint4*>(row + k0);
             const uint32_t h[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double v = h2f(static_cast<uint16_t>(h[e >> 1] >> (16 * (e & 1))));
-                s = s + v * v;                  // v * v is exact in binary64
-            }
+            for (int e = 0; e < 8; ++e) sumsq_add(s, (h[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         } else {
-            for (int e = 0; e < 8 && k0 + e < K; ++e) {
-                const double v = h2f(row[k0 + e]);
-                s = s + v * v;
-            }
+            for (int e = 0; e < 8 && k0 + e < K; ++e) sumsq_add(s, row[k0 + e]);
         }
     }
 #pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) s = s + __shfl_xor(s, st);
+    for (int st = 32; st >= 1; st >>= 1)
+        sumsq_merge(s, static_cast<uint64_t>(__shfl_xor(static_cast<unsigned long long>(s.lo), st)),
+                    static_cast<uint64_t>(__shfl_xor(static_cast<unsigned long long>(s.hi), st)));
     return s;
 }
 
-// r = binary32(1 / sqrt(S / K + eps)) from the 8 wave sums (LDS, published).
-__device__ __forceinline__ float rms_from_waves(const double* red, int K, float eps) {
-    const double b0 = red[0] + red[4], b1 = red[1] + red[5], b2 = red[2] + red[6], b3 = red[3] + red[7];
-    const double c0 = b0 + b2, c1 = b1 + b3;
-    const double S = c0 + c1;
+// r = binary32(1 / sqrt(S / K + eps)) from the 8 wave parts (LDS, published),
+// the quotient and root in binary64.
+__device__ __forceinline__ float rms_from_waves(const SumSq* red, int K, float eps) {
+    SumSq s = red[0];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) sumsq_merge(s, red[v].lo, red[v].hi);
+    const double S = sumsq_value(s);
     return static_cast<float>(1.0 / __builtin_sqrt(S / static_cast<double>(K) + static_cast<double>(eps)));
 }
 
-// The 8 wave sums of a row by the T / 64 waves of a workgroup (wave i forms
-// virtual waves i, i + T / 64, ...), written to `red`; the caller publishes
-// them with a barrier.
+// The 8 wave parts of a row by the T / 64 waves of a workgroup (wave i forms
+// parts i, i + T / 64, ...), written to `red`; the caller publishes them with
+// a barrier.
 template <int T>
-__device__ __forceinline__ void wave_sums(const uint16_t* row, int K, double* red) {
+__device__ __forceinline__ void wave_sums(const uint16_t* row, int K, SumSq* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int v = wave; v < 8; v += T / 64) {
-        const double W = wave_sumsq(row, K, v, lane);
+        const SumSq W = wave_sumsq(row, K, v, lane);
         if (lane == 0) red[v] = W;
     }
 }
@@ -397,9 +433,9 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // whole 1 KB direct-load chunks of one staged row
     const size_t row_bytes = static_cast<size_t>((K + 511) / 512) * 1024;
-    // the row statistic's 8 wave sums (kNorm), or the SwiGLU fix-up queue
+    // the row statistic's 8 wave parts (kNorm), or the SwiGLU fix-up queue
     // (kSwi), follow the staged row
-    double* red = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(row_lds) + (kRowInLds ? row_bytes : 0));
+    SumSq* red = reinterpret_cast<SumSq*>(reinterpret_cast<uint8_t*>(row_lds) + (kRowInLds ? row_bytes : 0));
     bool sums_done = false;
 
     const int Mp = (M + 15) & ~15;        // FP6 layout: rows padded to whole 16-row tiles
@@ -555,8 +591,8 @@ __device__ __forceinline__ void row_step(const uint16_t* next_row, uint8_t* __re
                                          const int4 (&pos)[row_passes<kWaves>()][8],
                                          int K, int nb, int nb4, int M, int Mp, int m, int wave, int lane,
                                          uint8_t* __restrict__ Xq, float* __restrict__ x_scale,
-                                         const uint16_t* __restrict__ gperm, float eps, const double* red_cur,
-                                         double* red_nxt) {
+                                         const uint16_t* __restrict__ gperm, float eps, const SumSq* red_cur,
+                                         SumSq* red_nxt) {
     if (next_row) stage_row<kWaves>(next_row, K, wave, lane, nxt_buf);
     float rs = 0.0f;
     if constexpr (kNorm) rs = rms_from_waves(red_cur, K, eps);
@@ -600,7 +636,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_rows_kernel(
         const int b = (p * kWaves + wave) * 16 + (lane >> 2);
         load_positions(perm, imin(b, nb - 1), lane & 3, pos[p]);
     }
-    double* red = reinterpret_cast<double*>(bufs + 2 * static_cast<size_t>(row_bytes));
+    SumSq* red = reinterpret_cast<SumSq*>(bufs + 2 * static_cast<size_t>(row_bytes));
     stage_row<kWaves>(X + static_cast<size_t>(first) * ldx, K, wave, lane, bufs);
     if constexpr (kNorm) {
         COMET_VMCNT(0);
@@ -657,7 +693,7 @@ int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb
     dim3 grid(rows_per_xcd > 0 ? 8 * rows_per_xcd : M, groups);
     hipStream_t s = static_cast<hipStream_t>(stream);
     // wave sums of the row statistic, or the SwiGLU fix-up queue and its count
-    const size_t red = kNorm ? 16 * sizeof(double) : kSwi ? (T / 64) * kSwiWaveQueue * sizeof(int) : 0;
+    const size_t red = kNorm ? 16 * sizeof(SumSq) : kSwi ? (T / 64) * kSwiWaveQueue * sizeof(int) : 0;
     const size_t row_lds = static_cast<size_t>((K + 511) / 512) * 1024;   // whole 1 KB direct-load chunks
     const size_t buf = row_lds;
     constexpr size_t kLds = 160 * 1024;
@@ -704,7 +740,7 @@ constexpr int kNormThreads = 512;
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* __restrict__ X, int K, int ldx,
                                                                const uint16_t* __restrict__ gamma, float eps,
                                                                uint16_t* __restrict__ Xn, int ldn) {
-    __shared__ double red[8];
+    __shared__ SumSq red[8];
     const int m = blockIdx.x;
     const uint16_t* xr = X + static_cast<size_t>(m) * ldx;
     wave_sums<kNormThreads>(xr, K, red);
