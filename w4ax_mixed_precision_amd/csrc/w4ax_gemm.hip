@@ -260,7 +260,7 @@ __device__ __forceinline__ void tiled_block(const GemmProblem& p, int b, int m0,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = m0 + 64 * wr + 16 * r + 4 * g + i;
-                    if (row < row_hi)
+                    if (row >= row_lo && row < row_hi)
                         p.P[(static_cast<size_t>(row - row_lo) * N + ncol) * nb + b] = acc[i] >> 4;
                 }
             } else {
@@ -293,13 +293,17 @@ __global__ __launch_bounds__(kThreads, COMET_TILED_WG_PER_CU) void gemm_tiled_ke
     __shared__ __attribute__((aligned(1024))) uint8_t stage3[kSt];
 #endif
 
+    // the partials variant runs the tiles of the full launch (128-row tiles
+    // from row 0) that hold rows of [m_begin, m_begin + m_count), and stores
+    // only those rows
     const int row_lo = kDump ? p.m_begin : 0;
     const int row_hi = kDump ? p.m_begin + p.m_count : p.M;
-    const int tiles_m = (row_hi - row_lo + kTM - 1) / kTM;
+    const int tm_lo = row_lo / kTM;
+    const int tiles_m = (row_hi + kTM - 1) / kTM - tm_lo;
     const int tiles_n = p.N / kTN;
     int tm, tn;
     if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
-    const int m0 = row_lo + tm * kTM;
+    const int m0 = (tm_lo + tm) * kTM;
     const int n0 = tn * kTN;
 
     const int lane = threadIdx.x & 63;
@@ -397,6 +401,19 @@ __device__ __forceinline__ uint32_t zero_word(const GemmProblem& p, int b, int r
 
 
 
+// The partials variant of a streaming kernel: the exact P of block b for this
+// lane's four outputs of row tile r (rows 16r + 4g .. 16r + 4g + 3, column
+// `col`), from the accumulator (16 P), in place of the epilogue. Rows outside
+// [m_begin, m_begin + m_count) are not written.
+__device__ __forceinline__ void dump_tile(const GemmProblem& p, int b, int col, int r, int g, const v4i& acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * r + 4 * g + i;
+        if (row >= p.m_begin && row < p.m_begin + p.m_count)
+            p.P[(static_cast<size_t>(row - p.m_begin) * p.N + col) * p.nb + b] = acc[i] >> 4;
+    }
+}
+
 // Everything block b needs except the weight word: activation words of the
 // lane's rows, activation scale of row `srow`, weight scale and sum of its
 // column. MR == 1 issues exactly five loads.
@@ -446,9 +463,9 @@ __device__ __forceinline__ Rsrc stream_xq_rsrc(const GemmProblem& p) {
 
 // One block from a slot. `valid` is false for the clamped refetches past the
 // wave's last block: they get a zero scale product, which adds exactly zero.
-template <int MR, bool kAsym = false>
+template <int MR, bool kAsym = false, bool kDump = false>
 __device__ __forceinline__ void stream_compute(bool valid, bool is4, const StreamSlot<MR>& sl,
-                                               float (&y)[MR][4]) {
+                                               float (&y)[MR][4], const GemmProblem& p, int b, int col) {
     const v4i B0 = widen_weights_lo(sl.w);
     const v4i B1 = widen_weights_hi(sl.w);
     const float sw = valid ? h2f(static_cast<uint16_t>(sl.hs)) * 0.0625f : 0.0f;
@@ -470,12 +487,17 @@ __device__ __forceinline__ void stream_compute(bool valid, bool is4, const Strea
         }
         v4i acc = mfma_i8(A0, B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
         acc = mfma_i8(A1, B1, acc);
+        if constexpr (kDump) {
+            if (valid) dump_tile(p, b, col, r, (threadIdx.x & 63) >> 4, acc);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[r][i]);
+            for (int i = 0; i < 4; ++i)
+                y[r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[r][i]);
+        }
     }
 }
 
-template <int MR, int kD, int kSplit, bool kAsym = false>
+template <int MR, int kD, int kSplit, bool kAsym = false, bool kDump = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p) {
     __shared__ float red[kSplit][MR * 4][64];
     const int lane = threadIdx.x & 63;
@@ -513,12 +535,13 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_kernel(GemmProblem p)
 #pragma unroll
             for (int u = 0; u < kD; ++u) {
                 const int b = b0 + u;
-                stream_compute<MR, kAsym>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                stream_compute<MR, kAsym, kDump>(b < b_end, imin(b, last) < nb4, slot[u], y, p, b, grp * 16 + l16);
                 if (b0 + kD < b_end)
                     stream_fetch<MR, kAsym>(p, xq, imin(b + kD, last), grp, lane, srow, arow, slot[u]);
             }
         }
     }
+    if constexpr (kDump) return;
 
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -594,9 +617,9 @@ __device__ __forceinline__ void stream_fetch_g(const GemmProblem& p, Rsrc xq, in
     }
 }
 
-template <int MR, int G, bool kAsym = false>
+template <int MR, int G, bool kAsym = false, bool kDump = false>
 __device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlotG<MR, G>& sl,
-                                                 float (&y)[G][MR][4]) {
+                                                 float (&y)[G][MR][4], const GemmProblem& p, int b, int grp0) {
     // 4-bit rows: the one word holds both halves of the lane's 32 positions;
     // widen it in place into the two operand words an 8-bit row loads
     if (is4) {
@@ -624,14 +647,19 @@ __device__ __forceinline__ void stream_compute_g(bool valid, bool is4, StreamSlo
         for (int r = 0; r < MR; ++r) {
             v4i acc = mfma_i8(as_v4i(sl.a0[r]), B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
             acc = mfma_i8(as_v4i(sl.a1[r]), B1, acc);
+            if constexpr (kDump) {
+                const int lane = threadIdx.x & 63;
+                if (valid) dump_tile(p, b, (grp0 + j) * 16 + (lane & 15), r, lane >> 4, acc);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+                for (int i = 0; i < 4; ++i)
+                    y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+            }
         }
     }
 }
 
-template <int MR, int G, int kD, int kSplit, bool kAsym = false>
+template <int MR, int G, int kD, int kSplit, bool kAsym = false, bool kDump = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem p) {
     __shared__ float red[kSplit][MR * 4][64];
     const int lane = threadIdx.x & 63;
@@ -671,12 +699,13 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_g_kernel(GemmProblem 
 #pragma unroll
             for (int u = 0; u < kD; ++u) {
                 const int b = b0 + u;
-                stream_compute_g<MR, G, kAsym>(b < b_end, imin(b, last) < nb4, slot[u], y);
+                stream_compute_g<MR, G, kAsym, kDump>(b < b_end, imin(b, last) < nb4, slot[u], y, p, b, grp0);
                 if (b0 + kD < b_end)
                     stream_fetch_g<MR, G, kAsym>(p, xq, imin(b + kD, last), grp0, lane, srow, arow, slot[u]);
             }
         }
     }
+    if constexpr (kDump) return;
 
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -732,7 +761,7 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
     (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int NBW, int kSplit, bool kAsym = false>
+template <int NBW, int kSplit, bool kAsym = false, bool kDump = false>
 __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProblem p) {
     constexpr int MR = 1;
     __shared__ float red[kSplit][4][64];
@@ -773,11 +802,12 @@ __global__ __launch_bounds__(64 * kSplit) void gemm_stream_lds_kernel(GemmProble
         COMET_VMCNT(lds_loads_after(i, NBW, kAsym));
         StreamSlot<MR>& sl = slot[i % kRingA];
         sl.w = *reinterpret_cast<const uint4*>(my + (i % kRingR) * kFragBytes + 16 * lane);
-        stream_compute<MR, kAsym>(true, b_begin + i < nb4, sl, y);
+        stream_compute<MR, kAsym, kDump>(true, b_begin + i < nb4, sl, y, p, b_begin + i, grp * 16 + l16);
         // the ring slot just read is refilled only after its word is used
         if (i + kRingA < NBW) stream_fetch_aux<MR, kAsym>(p, xq, b_begin + i + kRingA, grp, lane, srow, arow, sl);
         if (i + kRingR < NBW) fragment(i + kRingR);
     }, std::make_integer_sequence<int, NBW>{});
+    if constexpr (kDump) return;
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][i][lane] = y[0][i];
@@ -861,9 +891,9 @@ __device__ __forceinline__ void stream_fetch_aux_g(const GemmProblem& p, Rsrc xq
     }
 }
 
-template <int MR, int G, bool kAsym = false>
+template <int MR, int G, bool kAsym = false, bool kDump = false>
 __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, kAsym>& sl, const uint8_t* frags, int lane,
-                                                     float (&y)[G][MR][4]) {
+                                                     float (&y)[G][MR][4], const GemmProblem& p, int b, int grp0) {
     // branch-free operand words (a branch on the block kind splits the
     // straight-line block sequence, and the compiler then waits for every
     // outstanding load before the next LDS read): a 4-bit row's second word
@@ -898,14 +928,18 @@ __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, k
         for (int r = 0; r < MR; ++r) {
             v4i acc = mfma_i8(A0[r], B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
             acc = mfma_i8(A1[r], B1, acc);
+            if constexpr (kDump) {
+                dump_tile(p, b, (grp0 + j) * 16 + (lane & 15), r, lane >> 4, acc);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+                for (int i = 0; i < 4; ++i)
+                    y[j][r][i] = __builtin_fmaf(t[4 * r + i], static_cast<float>(acc[i]), y[j][r][i]);
+            }
         }
     }
 }
 
-template <int MR, int G, int NBW, int kSplit, int kRA, int kRR, bool kAsym = false>
+template <int MR, int G, int NBW, int kSplit, int kRA, int kRR, bool kAsym = false, bool kDump = false>
 __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_lds_g_kernel(GemmProblem p) {
     // two LDS objects: the compiler can then tell ring reads from other LDS
     // accesses and waits only for the direct loads a read depends on (with
@@ -961,11 +995,13 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
         constexpr int i = decltype(ic)::value;
         COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR, kAsym>(i, NBW)));
         AuxSlotG<MR, G, kAsym>& sl = slot[i % kRA];
-        stream_compute_lds_g<MR, G, kAsym>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y);
+        stream_compute_lds_g<MR, G, kAsym, kDump>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y,
+                                                  p, b_begin + i, grp0);
         if (i + kRA < NBW) stream_fetch_aux_g<MR, G, kAsym>(p, xq, b_begin + i + kRA, grp0, lane, srow, arow, sl);
         // the ring slot just read is refilled only after its words are used
         if (i + kRR < NBW) fragments(i + kRR);
     }, std::make_integer_sequence<int, NBW>{});
+    if constexpr (kDump) return;
 
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -999,10 +1035,10 @@ bool use_stream(int M) { return M <= 64; }
 // kernel (below); otherwise one channel group per workgroup, its blocks split
 // over the waves: the LDS-ring kernel for 32, 64 and 128 blocks, the register
 // kernel (four blocks in flight, 120 VGPRs) otherwise.
-template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym>
+template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st);
 
-template <bool kAsym>
+template <bool kAsym, bool kDump>
 int launch_stream1(const GemmProblem& p, hipStream_t st) {
     // 64 blocks: the multi-group LDS-ring kernel in its narrow form (two
     // groups per wave, eight waves of 8 blocks), except where its grid of
@@ -1013,26 +1049,26 @@ int launch_stream1(const GemmProblem& p, hipStream_t st) {
     // against 12.8-13.4 us, which stays on the one-group kernel.
     const int narrow_units = p.N / 32;
     if (p.nb == 64 && !(narrow_units > 256 && narrow_units < 512))
-        return launch_stream_lds_g_cfg<1, 2, 8, 4, 2, kAsym>(p, st);
+        return launch_stream_lds_g_cfg<1, 2, 8, 4, 2, kAsym, kDump>(p, st);
     constexpr int kD = COMET_STREAM_DEPTH;
     const int groups = p.N / 16;
     const int grid = 8 * ((groups + 7) / 8);     // XCD-aware order; surplus workgroups exit
     if (p.nb == 32) {
-        gemm_stream_lds_kernel<8, 4, kAsym><<<grid, 256, 0, st>>>(p);
+        gemm_stream_lds_kernel<8, 4, kAsym, kDump><<<grid, 256, 0, st>>>(p);
     } else if (p.nb == 64 && groups * 8 < 2 * COMET_STREAM_TARGET_WAVES) {
-        gemm_stream_lds_kernel<8, 8, kAsym><<<grid, 512, 0, st>>>(p);
+        gemm_stream_lds_kernel<8, 8, kAsym, kDump><<<grid, 512, 0, st>>>(p);
     } else if (p.nb == 64) {
-        gemm_stream_lds_kernel<16, 4, kAsym><<<grid, 256, 0, st>>>(p);
+        gemm_stream_lds_kernel<16, 4, kAsym, kDump><<<grid, 256, 0, st>>>(p);
     } else if (p.nb == 128) {
-        gemm_stream_lds_kernel<16, 8, kAsym><<<grid, 512, 0, st>>>(p);
+        gemm_stream_lds_kernel<16, 8, kAsym, kDump><<<grid, 512, 0, st>>>(p);
     } else if (groups * 4 >= COMET_STREAM_TARGET_WAVES || p.nb < 8 * kD) {
         // split the blocks of a channel group over enough waves to keep
         // many weight fragments in flight across the chip
-        gemm_stream_kernel<1, kD, 4, kAsym><<<grid, 256, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 4, kAsym, kDump><<<grid, 256, 0, st>>>(p);
     } else if (groups * 8 >= COMET_STREAM_TARGET_WAVES || p.nb < 16 * kD) {
-        gemm_stream_kernel<1, kD, 8, kAsym><<<grid, 512, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 8, kAsym, kDump><<<grid, 512, 0, st>>>(p);
     } else {
-        gemm_stream_kernel<1, kD, 16, kAsym><<<grid, 1024, 0, st>>>(p);
+        gemm_stream_kernel<1, kD, 16, kAsym, kDump><<<grid, 1024, 0, st>>>(p);
     }
     return static_cast<int>(hipGetLastError());
 }
@@ -1040,24 +1076,24 @@ int launch_stream1(const GemmProblem& p, hipStream_t st) {
 // Register multi-group kernel, any block count. Measured against the
 // one-group kernel on the K = 8192 decode shapes it is faster in 11 of 12
 // (N = 10240, M = 64: 34 against 32 us).
-template <int MR, int G, int kSplit, bool kAsym>
+template <int MR, int G, int kSplit, bool kAsym, bool kDump>
 int launch_stream_g_cfg(const GemmProblem& p, hipStream_t st) {
     constexpr int kD = 2;
     const int units = p.N / (16 * G);
     const int grid = 8 * ((units + 7) / 8);
-    gemm_stream_g_kernel<MR, G, kD, kSplit, kAsym><<<grid, 64 * kSplit, 0, st>>>(p);
+    gemm_stream_g_kernel<MR, G, kD, kSplit, kAsym, kDump><<<grid, 64 * kSplit, 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int MR, bool kAsym>
+template <int MR, bool kAsym, bool kDump>
 int launch_stream_g(const GemmProblem& p, hipStream_t st) {
     const int groups = p.N / 16;
     // four groups per workgroup while that still leaves about two four-wave
     // workgroups per CU; else two groups, with eight waves per workgroup when
     // four-wave workgroups alone would not cover the CUs
-    if (groups / 4 >= 384) return launch_stream_g_cfg<MR, 4, 4, kAsym>(p, st);
-    if (groups / 2 >= 384) return launch_stream_g_cfg<MR, 2, 4, kAsym>(p, st);
-    return launch_stream_g_cfg<MR, 2, 8, kAsym>(p, st);
+    if (groups / 4 >= 384) return launch_stream_g_cfg<MR, 4, 4, kAsym, kDump>(p, st);
+    if (groups / 2 >= 384) return launch_stream_g_cfg<MR, 2, 4, kAsym, kDump>(p, st);
+    return launch_stream_g_cfg<MR, 2, 8, kAsym, kDump>(p, st);
 }
 
 // LDS-ring multi-group kernel, 64 blocks. Two configurations, chosen by
@@ -1070,45 +1106,46 @@ int launch_stream_g(const GemmProblem& p, hipStream_t st) {
 // faster when it still yields about 1.5 workgroups per CU (N >= 24576), and
 // at M > 32 from 160 workgroups on (N = 10240, M = 64: 23 against 26 us); the
 // narrow one has twice the waves and wins on the smaller grids.
-template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym>
+template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st) {
     const int units = p.N / (16 * G);
     const int grid = 8 * ((units + 7) / 8);
-    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR, kAsym><<<grid, 64 * kSplit, 0, st>>>(p);
+    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR, kAsym, kDump><<<grid, 64 * kSplit, 0, st>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int MR, bool kAsym>
+template <int MR, bool kAsym, bool kDump>
 int launch_stream_lds_g(const GemmProblem& p, hipStream_t st) {
     const int wide_units = p.N / 64;
     const bool wide = wide_units >= 384 || (p.M > 32 && wide_units >= 160);
-    if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2, kAsym>(p, st);
-    return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2, kAsym>(p, st);
+    if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2, kAsym, kDump>(p, st);
+    return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2, kAsym, kDump>(p, st);
 }
 
 // Two to four row tiles (16 < M <= 64): several channel groups per wave.
-template <int MR, bool kAsym>
+template <int MR, bool kAsym, bool kDump>
 int launch_stream(const GemmProblem& p, hipStream_t st) {
-    if (p.nb == 64) return launch_stream_lds_g<MR, kAsym>(p, st);
-    return launch_stream_g<MR, kAsym>(p, st);
+    if (p.nb == 64) return launch_stream_lds_g<MR, kAsym, kDump>(p, st);
+    return launch_stream_g<MR, kAsym, kDump>(p, st);
 }
 
-template <bool kAsym>
+// One kernel choice for both variants: the partials entry points (kDump)
+// launch exactly the kernel, launch shape and block split that produce Y for
+// the same (M, N, K), with the epilogue replaced by stores of P.
+template <bool kAsym, bool kDump>
 int launch_gemm(const GemmProblem& p, hipStream_t s) {
-    if (p.P) {
-        const int tiles = ((p.m_count + kTM - 1) / kTM) * (p.N / kTN);
-        gemm_tiled_kernel<true, kAsym><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
-        return static_cast<int>(hipGetLastError());
-    }
     if (use_stream(p.M)) {
         const int mr = (p.M + 15) / 16;
-        if (mr == 1) return launch_stream1<kAsym>(p, s);
-        if (mr == 2) return launch_stream<2, kAsym>(p, s);
-        if (mr == 3) return launch_stream<3, kAsym>(p, s);
-        return launch_stream<4, kAsym>(p, s);
+        if (mr == 1) return launch_stream1<kAsym, kDump>(p, s);
+        if (mr == 2) return launch_stream<2, kAsym, kDump>(p, s);
+        if (mr == 3) return launch_stream<3, kAsym, kDump>(p, s);
+        return launch_stream<4, kAsym, kDump>(p, s);
     }
-    const int tiles = ((p.M + kTM - 1) / kTM) * (p.N / kTN);
-    gemm_tiled_kernel<false, kAsym><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
+    // the tiles of the full launch that hold rows of the partials' range
+    const int tm_lo = kDump ? p.m_begin / kTM : 0;
+    const int tm_hi = kDump ? (p.m_begin + p.m_count + kTM - 1) / kTM : (p.M + kTM - 1) / kTM;
+    const int tiles = (tm_hi - tm_lo) * (p.N / kTN);
+    gemm_tiled_kernel<kDump, kAsym><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -1118,7 +1155,8 @@ size_t gemm_workspace_bytes(int, int, int, int) { return 0; }
 
 int launch_w4ax_gemm(const GemmProblem& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return p.x_zero ? launch_gemm<true>(p, s) : launch_gemm<false>(p, s);
+    if (p.P) return p.x_zero ? launch_gemm<true, true>(p, s) : launch_gemm<false, true>(p, s);
+    return p.x_zero ? launch_gemm<true, false>(p, s) : launch_gemm<false, false>(p, s);
 }
 
 }  // namespace comet
