@@ -159,8 +159,11 @@ class Layer:
         self.Xq = torch.empty(nxq, dtype=torch.uint8, device="cuda")
         self.xs = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
         self.Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        need = comet.workspace_bytes(M, N, K, cfg.nb8)
-        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
+        need = (comet.workspace_bytes(M, N, K, cfg.nb8) if self.layout == "int4"
+                else comet.fp6_workspace_bytes(M, N, K, cfg.nb8))
+        # zeroed once: the library leaves it zeroed after every call
+        self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
+        self.ws_bytes = need
         self.ops = 2.0 * M * N * K
         self.gbytes = gemm_bytes(M, N, K, cfg.nb8, self.layout)
         self.qbytes = quant_bytes(M, K, cfg.nb8, self.layout)
@@ -180,7 +183,7 @@ class Layer:
         if self.layout == "int4":
             comet.comet_w4ax_gemm(self.Xq, self.xs, w, self.cfg.M, Y=self.Y, workspace=self.ws)
         else:
-            comet.comet_w4ax_gemm_fp6(self.Xq, self.xs, w, self.cfg.M, Y=self.Y)
+            comet.comet_w4ax_gemm_fp6(self.Xq, self.xs, w, self.cfg.M, Y=self.Y, workspace=self.ws)
 
 
 def copies_for(cfg, target_bytes=1 << 30):

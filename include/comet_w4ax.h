@@ -382,28 +382,56 @@ int comet_quant_act_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t
  * partials P (4-bit blocks on the FP6 matrix instruction, whose FP32 result
  * is exact for these integer products; 8-bit blocks on the INT8 one), then
  * y = sum over blocks of (x_scale * w_scale) * P in FP32 and Y = fp16(y).
- * Needs no workspace and no weight sums. UNSUPPORTED also covers
+ * No weight sums (the codes are signed). UNSUPPORTED also covers
  * Mp * K > 2^31 - 1 (the kernel's 32-bit offsets into Xq_fp6).
+ *
+ * Scheduling (COMET article, section "2.混合精度计算的动态调度": tiles are
+ * not bound to compute units; idle units take over their neighbours' work).
+ * A grid of at least one wave of whole output tiles (two per CU) runs one
+ * tile per workgroup and needs no workspace. A smaller grid splits each
+ * tile's blocks into runs of about equal cost (an 8-bit block counts twice)
+ * and runs them as the work items of a persistent grid with per-XCD work
+ * queues (atomic counters; an idle workgroup takes from the fullest queue);
+ * each run stores its FP32 partial tile, and a second kernel adds them in
+ * split order and writes Y. Y is deterministic: the same inputs give the same
+ * bits whatever the timing (no floating-point atomics); the sum over blocks
+ * is then grouped by runs, which is one of the orders the definition allows.
  *
  *   Xq_fp6, x_scale   in   from comet_quant_act_fp6
  *   Wq_fp6            in   from comet_repack_weights_fp6, on device
  *   w_scale_fp16      in   from comet_pack_weights, on device
  *   Y_fp16            out  device, [M][ldy] fp16, ldy >= N
- * Errors: NULL, SHAPE, ALIGN, ARG, UNSUPPORTED, HIP.
+ *   workspace         in/out  device, 16-byte aligned, at least
+ *                     comet_w4ax_gemm_fp6_workspace_bytes(M, N, K, nb8) bytes
+ *                     (may be NULL when that is 0). Its first 256 bytes (the
+ *                     queue counters) must be zero before its first use (e.g.
+ *                     allocated zeroed); every call returns them to zero before
+ *                     it ends, so calls of any shape ordered on one stream can
+ *                     share the workspace. Calls that may run at the same time
+ *                     need workspaces of their own.
+ * Errors: NULL, SHAPE, ALIGN, ARG, WORKSPACE, UNSUPPORTED, HIP.
  */
 int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                         const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
-                        void* Y_fp16, int ldy, void* stream);
+                        void* Y_fp16, int ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes comet_w4ax_gemm_fp6 (and its partials variant) needs for
+ * this shape: 0 for grids of a wave of tiles or more; otherwise the work
+ * queue's counters and the runs' FP32 partial tiles. A function of the shape
+ * only (no device is queried); 0 for an invalid shape. */
+size_t comet_w4ax_gemm_fp6_workspace_bytes(int M, int N, int K, int n_int8_blocks);
 
 /*
  * Debug variant of comet_w4ax_gemm_fp6: the exact INT32 block partials of rows
- * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], from the kernel and
- * launch configuration comet_w4ax_gemm_fp6 uses for the same (M, N, K), like
- * comet_w4ax_gemm_partials.
+ * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], from the kernel, tile
+ * shape, block runs and work queue comet_w4ax_gemm_fp6 uses for the same
+ * (M, N, K), over the tiles that hold those rows; each run stores the
+ * partials of its own blocks (no fix-up). Workspace as comet_w4ax_gemm_fp6.
  */
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N,
-                                 int K, int m_begin, int m_count, int32_t* P, void* stream);
+                                 int K, int m_begin, int m_count, int32_t* P, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * RMS normalization fused into the activation quantizer. QoQ/QServe article

@@ -61,12 +61,36 @@ def qf(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, Xq=A, xs=A):
     return comet.lib().comet_quant_act_fp6(X, M, K, ldx, perm, nb8, Xq, xs, None)
 
 
-def gf(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512):
-    return comet.lib().comet_w4ax_gemm_fp6(Xq, xs, Wq, ws, nb8, M, N, K, Y, ldy, None)
+def gf(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512, work=A, wbytes=1 << 40):
+    return comet.lib().comet_w4ax_gemm_fp6(Xq, xs, Wq, ws, nb8, M, N, K, Y, ldy, work, wbytes, None)
 
 
-def gfp(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A):
-    return comet.lib().comet_w4ax_gemm_fp6_partials(Xq, xs, Wq, ws, nb8, M, N, K, m0, mc, P, None)
+def gfp(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A, work=A, wbytes=1 << 40):
+    return comet.lib().comet_w4ax_gemm_fp6_partials(Xq, xs, Wq, ws, nb8, M, N, K, m0, mc, P, work, wbytes,
+                                                    None)
+
+
+def test_fp6_workspace_contract():
+    """The FP6 GEMM's workspace: a function of the shape only (no device
+    needed), none for grids of a wave of whole tiles or more (the 70B prefill
+    layers, the 7B up/gate layer's 688 tiles), the split runs' partial tiles
+    for smaller grids (q_proj_7b: 32 tiles x 8 runs; down_7b: 256 x 2); a
+    missing, small or misaligned workspace is rejected before any HIP call."""
+    L = comet.lib()
+    wb = L.comet_w4ax_gemm_fp6_workspace_bytes
+    assert wb(4096, 8192, 28672, 67) == 0 and wb(4096, 28672, 8192, 7) == 0 and wb(1024, 11008, 4096, 4) == 0
+    tile = 128 * 128 * 4
+    assert wb(128, 4096, 4096, 4) == 256 + 32 * 8 * tile
+    assert wb(1024, 4096, 11008, 22) == 256 + 256 * 2 * tile
+    for M, N, K, nb8 in ((128, 4096, 4096, 4), (1024, 4096, 11008, 22), (16, 512, 512, 1)):
+        need = wb(M, N, K, nb8)
+        assert need > 0 and need % 16 == 0, (M, N, K)
+        assert comet.fp6_workspace_bytes(M, N, K, nb8) == need
+        assert gf(M=M, N=N, K=K, nb8=nb8, ldy=N, work=None, wbytes=0) == NULL
+        assert gf(M=M, N=N, K=K, nb8=nb8, ldy=N, wbytes=need - 1) == WORKSPACE
+        assert gf(M=M, N=N, K=K, nb8=nb8, ldy=N, work=MIS, wbytes=need) == ALIGN
+        assert gfp(M=M, N=N, K=K, nb8=nb8, mc=1, work=None, wbytes=0) == NULL
+    assert wb(16, 512, 500, 1) == 0 and wb(0, 512, 512, 1) == 0 and wb(16, 512, 512, 9) == 0
 
 
 def test_fp6_rejections():

@@ -55,8 +55,10 @@ def lib() -> ctypes.CDLL:
     L.comet_wq_fp6_bytes.restype = Z
     L.comet_repack_weights_fp6.argtypes = [P, I, I, I, P]
     L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
-    L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
-    L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P]
+    L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P, Z, P]
+    L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, Z, P]
+    L.comet_w4ax_gemm_fp6_workspace_bytes.argtypes = [I, I, I, I]
+    L.comet_w4ax_gemm_fp6_workspace_bytes.restype = Z
     L.comet_quant_act_asym.argtypes = [P, I, I, I, P, I, P, P, P, P]
     L.comet_pack_weights_qoq.argtypes = [P, I, I, P, P, P, P, P]
     L.comet_quant_act_token_i8.argtypes = [P, I, I, I, P, P, P, P]
@@ -83,7 +85,8 @@ def lib() -> ctypes.CDLL:
     L.comet_version.restype = ctypes.c_char_p
     for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
               "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
-              "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_rmsnorm_quant_act",
+              "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_w4ax_gemm_fp6_workspace_bytes",
+              "comet_rmsnorm_quant_act",
               "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels",
               "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
               "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
@@ -98,6 +101,7 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_w4ax_gemm_workspace_bytes", "comet_w4ax_gemm_partials",
            "comet_xq_fp6_bytes", "comet_wq_fp6_bytes", "comet_repack_weights_fp6",
            "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
+           "comet_w4ax_gemm_fp6_workspace_bytes",
            "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
            "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
@@ -495,30 +499,64 @@ def comet_quant_act_fp6(X, perm, nb8: int, Xq=None, x_scale=None, stream=None):
     return Xq, x_scale
 
 
-def comet_w4ax_gemm_fp6(Xq, x_scale, w: dict, M: int, Y=None, stream=None):
-    """Y fp16 [M, N] from FP6-layout activations and the bundle's FP6 weights."""
+def fp6_workspace_bytes(M: int, N: int, K: int, nb8: int) -> int:
+    return int(lib().comet_w4ax_gemm_fp6_workspace_bytes(M, N, K, int(nb8)))
+
+
+_WS_CACHE: dict = {}
+
+
+def fp6_workspace(M: int, N: int, K: int, nb8: int, device):
+    """A zeroed device workspace for comet_w4ax_gemm_fp6 of this shape (None if
+    the shape needs none), kept per device and reused: the library returns it
+    to zero at the end of every call, so calls ordered on one stream can share
+    it (calls that may overlap need workspaces of their own)."""
+    import torch
+    need = fp6_workspace_bytes(M, N, K, nb8)
+    if need == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def comet_w4ax_gemm_fp6(Xq, x_scale, w: dict, M: int, Y=None, workspace=None, stream=None):
+    """Y fp16 [M, N] from FP6-layout activations and the bundle's FP6 weights.
+    `workspace`: a zeroed uint8 device tensor of at least fp6_workspace_bytes()
+    (by default a shared one from fp6_workspace())."""
     import torch
     N, K, nb8 = w["N"], w["K"], w["nb8"]
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    if workspace is None:
+        workspace = fp6_workspace(M, N, K, nb8, Xq.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().comet_w4ax_gemm_fp6(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
                                    _dev_ptr(w["w_scale"]), int(nb8), M, N, K, _dev_ptr(Y), Y.stride(0),
-                                   _stream(stream))
+                                   None if workspace is None else _dev_ptr(workspace), wsz, _stream(stream))
     _check("comet_w4ax_gemm_fp6", rc)
     return Y
 
 
 def comet_w4ax_gemm_fp6_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
-                                 m_count: int | None = None, P=None, stream=None):
+                                 m_count: int | None = None, P=None, workspace=None, stream=None):
     """Exact block partials of the FP6-layout GEMM, [m_count, N, nb] int32."""
     import torch
     N, K, nb8 = w["N"], w["K"], w["nb8"]
     m_count = M - m_begin if m_count is None else m_count
     if P is None:
         P = torch.empty((m_count, N, K // 128), dtype=torch.int32, device=Xq.device)
+    if workspace is None:
+        workspace = fp6_workspace(M, N, K, nb8, Xq.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().comet_w4ax_gemm_fp6_partials(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
                                             _dev_ptr(w["w_scale"]), int(nb8), M, N, K, m_begin,
-                                            m_count, _dev_ptr(P), _stream(stream))
+                                            m_count, _dev_ptr(P), None if workspace is None else _dev_ptr(workspace),
+                                            wsz, _stream(stream))
     _check("comet_w4ax_gemm_fp6_partials", rc)
     return P
 

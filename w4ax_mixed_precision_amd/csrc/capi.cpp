@@ -428,19 +428,34 @@ int comet_permute_channels(const uint16_t* v, const int32_t* perm, int K, uint16
     return COMET_OK;
 }
 
-int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
-                        const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
-                        void* Y_fp16, int ldy, void* stream) {
-    if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !Y_fp16) return COMET_ERR_NULL;
+size_t comet_w4ax_gemm_fp6_workspace_bytes(int M, int N, int K, int n_int8_blocks) {
+    if (check_online_shape(M, N, K, n_int8_blocks) != COMET_OK) return 0;
+    return comet::gemm_fp6_workspace_bytes(M, N, K, n_int8_blocks);
+}
+
+namespace {
+
+// Checks shared by the FP6 GEMM and its partials variant (workspace included).
+int check_fp6_gemm(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6, const uint16_t* w_scale_fp16,
+                   int n_int8_blocks, int M, int N, int K, void* workspace, size_t workspace_bytes) {
+    if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16) return COMET_ERR_NULL;
     int st = check_online_shape(M, N, K, n_int8_blocks);
     if (st != COMET_OK) return st;
     if (!fp6_offsets_fit(M, K)) return COMET_ERR_UNSUPPORTED;
-    if (ldy < N) return COMET_ERR_SHAPE;
-    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
-        return COMET_ERR_UNSUPPORTED;
-    if (!aligned16(Xq_fp6) || !aligned16(x_scale) || !aligned16(Wq_fp6) || !aligned16(w_scale_fp16) ||
-        !aligned16(Y_fp16))
+    const size_t need = comet::gemm_fp6_workspace_bytes(M, N, K, n_int8_blocks);
+    if (need > 0) {
+        if (!workspace) return COMET_ERR_NULL;
+        if (workspace_bytes < need) return COMET_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return COMET_ERR_ALIGN;
+    }
+    if (!aligned16(Xq_fp6) || !aligned16(x_scale) || !aligned16(Wq_fp6) || !aligned16(w_scale_fp16))
         return COMET_ERR_ALIGN;
+    return COMET_OK;
+}
+
+comet::GemmProblem fp6_problem(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                               const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                               void* workspace, size_t workspace_bytes) {
     comet::GemmProblem p{};
     p.Xq = static_cast<const uint8_t*>(Xq_fp6);
     p.x_scale = x_scale;
@@ -452,6 +467,26 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
     p.K = K;
     p.nb = K / kBlock;
     p.nb4 = p.nb - n_int8_blocks;
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    return p;
+}
+
+}  // namespace
+
+int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                        const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                        void* Y_fp16, int ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!Y_fp16) return COMET_ERR_NULL;
+    int st = check_fp6_gemm(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace,
+                            workspace_bytes);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Y_fp16)) return COMET_ERR_ALIGN;
+    comet::GemmProblem p =
+        fp6_problem(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace, workspace_bytes);
     p.Y = static_cast<uint16_t*>(Y_fp16);
     p.ldy = ldy;
     p.P = nullptr;
@@ -462,28 +497,18 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
 
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
-                                 int m_begin, int m_count, int32_t* P, void* stream) {
-    if (!Xq_fp6 || !x_scale || !Wq_fp6 || !w_scale_fp16 || !P) return COMET_ERR_NULL;
-    int st = check_online_shape(M, N, K, n_int8_blocks);
+                                 int m_begin, int m_count, int32_t* P, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    if (!P) return COMET_ERR_NULL;
+    int st = check_fp6_gemm(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace,
+                            workspace_bytes);
     if (st != COMET_OK) return st;
-    if (!fp6_offsets_fit(M, K)) return COMET_ERR_UNSUPPORTED;
     if (m_begin < 0 || m_count < 1 || m_begin > M - m_count) return COMET_ERR_SHAPE;
     if (static_cast<int64_t>(m_count) * N * (K / kBlock) > std::numeric_limits<int32_t>::max())
         return COMET_ERR_UNSUPPORTED;
-    if (!aligned16(Xq_fp6) || !aligned16(x_scale) || !aligned16(Wq_fp6) || !aligned16(w_scale_fp16) ||
-        !aligned16(P))
-        return COMET_ERR_ALIGN;
-    comet::GemmProblem p{};
-    p.Xq = static_cast<const uint8_t*>(Xq_fp6);
-    p.x_scale = x_scale;
-    p.Wq = static_cast<const uint8_t*>(Wq_fp6);
-    p.w_scale = w_scale_fp16;
-    p.w_sum = nullptr;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.nb = K / kBlock;
-    p.nb4 = p.nb - n_int8_blocks;
+    if (!aligned16(P)) return COMET_ERR_ALIGN;
+    comet::GemmProblem p =
+        fp6_problem(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace, workspace_bytes);
     p.Y = nullptr;
     p.ldy = N;
     p.P = P;

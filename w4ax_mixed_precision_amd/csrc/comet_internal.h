@@ -68,6 +68,9 @@ struct GemmProblem {
 size_t gemm_workspace_bytes(int M, int N, int K, int nb8);
 int launch_w4ax_gemm(const GemmProblem& p, void* stream);
 int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream);   // FP6 layout; w_sum unused
+// Workspace of the FP6 GEMM (work queue, tile counts, split partial tiles);
+// a function of the shape only (no device query).
+size_t gemm_fp6_workspace_bytes(int M, int N, int K, int nb8);
 
 // Compute units of the current device (quant_act.hip; read once per process).
 int cu_count();

@@ -15,8 +15,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Integer minimum by value (a reference-returning min leaves stack slots behind).
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+// Integer minimum and maximum by value (a reference-returning min leaves stack
+// slots behind).
+__host__ __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 

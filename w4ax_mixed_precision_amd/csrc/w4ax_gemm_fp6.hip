@@ -147,13 +147,13 @@ __device__ __forceinline__ void issue(const GemmProblem& p, const Inputs& in, in
     }
 }
 
-// End of block b: block b+1 has landed once only the loads of the blocks
-// issued after it may still be in flight; the barrier publishes it and frees
-// block b's stage.
+// End of block b (of a run of blocks ending before b_end): block b+1 has
+// landed once only the loads of the blocks issued after it may still be in
+// flight; the barrier publishes it and frees block b's stage.
 template <int kWC>
-__device__ __forceinline__ void end_block(int b, int nb) {
+__device__ __forceinline__ void end_block(int b, int b_end) {
     using C = Cfg<kWC>;
-    if (C::kAhead == 2 && b + 2 < nb) COMET_VMCNT(C::kLoads);
+    if (C::kAhead == 2 && b + 2 < b_end) COMET_VMCNT(C::kLoads);
     else COMET_VMCNT(0);
     __builtin_amdgcn_s_barrier();
 }
@@ -213,13 +213,13 @@ __device__ __forceinline__ void epilogue(const GemmProblem& p, const v16f& t, co
 // `nxt`, then the matrix work of column tile c followed by the epilogue of
 // tile c-1.
 template <bool kDump, int kWC>
-__device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in, int b, int m0, int n0,
+__device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in, int b, int b_end, int m0, int n0,
                                           int row_lo, int row_hi, int wave, int lane, uint32_t sc,
                                           const uint8_t* __restrict__ st, uint8_t* __restrict__ nxt,
                                           float (&y)[4][kWC][4]) {
     constexpr int kAhead = Cfg<kWC>::kAhead;
     const int wr = wave >> 1, wc = wave & 1;
-    if (b + kAhead < p.nb) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
+    if (b + kAhead < b_end) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
     const int row0 = m0 + 64 * wr + 4 * (lane >> 4);
     const int col0 = n0 + 16 * kWC * wc + (lane & 15);
     Scales<kWC> s;
@@ -235,9 +235,6 @@ __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in
 #pragma unroll
         for (int r = 0; r < 4; ++r) Dp[r] = mfma_fp6(A[r], B);
     }
-    // Each column tile is one scheduling region: without the fences the
-    // scheduler pulls a tile's epilogue up behind its own matrix instructions,
-    // so the multiply-adds wait on results still in flight.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 1; c < kWC; ++c) {
@@ -252,19 +249,19 @@ __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in
         __builtin_amdgcn_sched_barrier(0);
     }
     epilogue<kDump, kWC>(p, tp, Dp, kWC - 1, b, row0, col0, row_lo, row_hi, y);
-    end_block<kWC>(b, p.nb);
+    end_block<kWC>(b, b_end);
 }
 
 // One 8-bit block: INT8 matrix instruction, weights widened to 16 q_w, so the
 // accumulator holds 16 P; the row scales are divided by 16 (exactly).
 template <bool kDump, int kWC>
-__device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& in, int b, int m0, int n0,
+__device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& in, int b, int b_end, int m0, int n0,
                                            int row_lo, int row_hi, int wave, int lane, uint32_t sc,
                                            const uint8_t* __restrict__ st, uint8_t* __restrict__ nxt,
                                            float (&y)[4][kWC][4]) {
     constexpr int kAhead = Cfg<kWC>::kAhead;
     const int wr = wave >> 1, wc = wave & 1;
-    if (b + kAhead < p.nb) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
+    if (b + kAhead < b_end) issue<kWC>(p, in, b + kAhead, m0, n0, wave, lane, sc, nxt);
     const int row0 = m0 + 64 * wr + 4 * (lane >> 4);
     const int col0 = n0 + 16 * kWC * wc + (lane & 15);
     Scales<kWC> s;
@@ -299,107 +296,368 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
         tp = tc;
     }
     epilogue<kDump, kWC>(p, tp, Dp, kWC - 1, b, row0, col0, row_lo, row_hi, y);
-    end_block<kWC>(b, p.nb);
+    end_block<kWC>(b, b_end);
 }
 
+// ---------------------------------------------------------------------------
+// Tile scheduling (COMET article, mmssai.com/?p=43269, section
+// "2.混合精度计算的动态调度": tiles are not bound to compute units; work is
+// balanced between units even though 8-bit blocks cost more than 4-bit ones).
+//
+// A grid of at least one wave of 128-row tiles (two workgroups per CU) runs as
+// it is: one tile per workgroup, XCD-aware order (tile_of). A smaller grid
+// cannot fill 256 CUs with whole tiles, so each tile's blocks are split into
+// S runs of equal cost (an 8-bit block costs twice a 4-bit one: twice the
+// matrix instructions, plus widening and conversion), S chosen so the runs
+// fill about one wave, and the runs are the work items of a persistent grid:
+//   * the items are dealt in the XCD-aware tile order into 8 contiguous
+//     ranges, one per XCD (workgroup w runs on XCD w mod 8); workgroup j of an
+//     XCD starts on item j of its range without any atomic, and a range
+//     longer than its XCD's workgroups hands out the rest with an atomic
+//     counter (the workgroups that finish first take them);
+//   * each run stores its FP32 partial tile in the workspace; a second kernel
+//     adds the runs of every tile in split order, y_0 + y_1 + ... + y_{S-1},
+//     writes Y and clears the counters for the next call. The kernel
+//     boundary publishes the partial tiles: no device-scope fence, no
+//     floating-point atomics, no workgroup waiting for another, and Y does
+//     not depend on timing.
+// Measured on MI355X and kept out: a fix-up inside the kernel by the last
+// run to finish (its device-scope fences write back and invalidate L2:
+// down_7b 256 us against 64), idle workgroups taking items from other XCDs'
+// ranges (the cross-XCD takes doubled the time of every grid that used them:
+// up_gate_7b split 101 us against 64 without), and splitting grids of one
+// wave or more (up_gate_7b, 688 tiles: whole tiles 58 us, the tiles past the
+// first wave split 64 us).
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxSplits = 8;
+
+struct Sched {
+    uint32_t* queue;       // [0..7] per-XCD counters; nullptr: one tile per workgroup
+    float* partials;       // [tiles][splits][kTM * 32 kWC] FP32 partial tiles
+    int tiles_m, tiles_n, tm0;   // tiles launched (row tiles tm0 .. tm0 + tiles_m - 1)
+    int splits;
+    int items, per_xcd;    // runs in all, and per XCD range (rounded up)
+    int wg_per_xcd;        // workgroups per XCD: the first that many items of a range are
+                           // dealt one per workgroup, the rest by the range's counter
+    int bounds[kMaxSplits + 1];  // run s covers blocks [bounds[s], bounds[s + 1])
+};
+
+// Workspace: the 8 queue counters in the first kCtrlBytes (the same place for
+// every shape, zero between calls), then the partial tiles.
+constexpr size_t kCtrlBytes = 256;
+
+// Row and column tile of tile t in the XCD-aware order of tile_of (8-row-tile
+// groups walked column by column).
+__host__ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    constexpr int G = 8;
+    const int group = t / (G * tiles_n);
+    const int first = group * G;
+    const int gh = imin(G, tiles_m - first);
+    const int in = t - group * G * tiles_n;
+    tn = in / gh;
+    tm = first + in % gh;
+}
+
+// The range counters are taken and cleared at system scope: the take is then
+// coherent whichever XCD a workgroup actually runs on, so every item goes to
+// exactly one workgroup.
+__device__ __forceinline__ uint32_t take_counter(uint32_t* a) {
+    return __hip_atomic_fetch_add(a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Number of items in XCD x's range: [x per_xcd, x per_xcd + count).
+__device__ __forceinline__ int range_count(const Sched& sc, int x) {
+    return imax(0, imin(sc.per_xcd, sc.items - x * sc.per_xcd));
+}
+
+// Next item for a workgroup of XCD x after its first, or -1: the range's
+// items past the first wg_per_xcd go out in order of the counter (one thread
+// calls this).
+__device__ __forceinline__ int next_item(const Sched& sc, int x) {
+    const int n = range_count(sc, x) - sc.wg_per_xcd;
+    if (n <= 0) return -1;
+    const int h = static_cast<int>(take_counter(&sc.queue[x]));
+    return h < n ? x * sc.per_xcd + sc.wg_per_xcd + h : -1;
+}
+
+// The blocks [b_begin, b_end) of the tile at rows m0, columns n0, into y (or
+// the partials of those blocks, kDump). Stages are used from stage 0 on; at
+// the end every wave is past the last barrier, so the stages are free again.
 template <bool kDump, int kWC>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p) {
+__device__ __forceinline__ void run_blocks(const GemmProblem& p, const Inputs& in, int b_begin, int b_end, int m0,
+                                           int n0, int row_lo, int row_hi, int wave, int lane, uint32_t sc,
+                                           uint8_t* smem, float (&y)[4][kWC][4]) {
     using C = Cfg<kWC>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStage];
-
-    // the partials variant covers rows [m_begin, m_begin + m_count) with tiles
-    // that start on a 16-row boundary
-    const int row_lo = kDump ? p.m_begin : 0;
-    const int row_hi = kDump ? p.m_begin + p.m_count : p.M;
-    const int base = row_lo & ~15;
-    const int tiles_m = (row_hi - base + kTM - 1) / kTM;
-    const int tiles_n = p.N / C::kTN;
-    int tm, tn;
-    if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
-    const int m0 = base + tm * kTM;
-    const int n0 = tn * C::kTN;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wr = wave >> 1, wc = wave & 1;
-    const int g = lane >> 4, l16 = lane & 15;
-    const int nb = p.nb, nb4 = p.nb4;
-    const Inputs in = make_inputs(p);
-    const uint32_t sc = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
-
-    float y[4][kWC][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < kWC; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[r][c][i] = 0.0f;
+    if (b_begin >= b_end) return;
 
-    // prologue: blocks 0 .. kAhead-1 in flight; wait for block 0
-    issue<kWC>(p, in, 0, m0, n0, wave, lane, sc, smem);
-    if (C::kAhead == 2 && 1 < nb) {
-        issue<kWC>(p, in, 1, m0, n0, wave, lane, sc, smem + C::kStage);
+    // prologue: blocks b_begin .. b_begin + kAhead - 1 in flight; wait for the first
+    issue<kWC>(p, in, b_begin, m0, n0, wave, lane, sc, smem);
+    if (C::kAhead == 2 && b_begin + 1 < b_end) {
+        issue<kWC>(p, in, b_begin + 1, m0, n0, wave, lane, sc, smem + C::kStage);
         COMET_VMCNT(C::kLoads);
     } else {
         COMET_VMCNT(0);
     }
     __builtin_amdgcn_s_barrier();
 
-    // Block b lives in stage b mod kStages and block b+kAhead is loaded into
-    // stage (b + kAhead) mod kStages. The stage pointers are restrict-qualified
+    // Block b lives in stage (b - b_begin) mod kStages and block b+kAhead is
+    // loaded into the stage after it. The stage pointers are restrict-qualified
     // in the block functions: an LDS read of one stage does not wait for the
     // direct loads in flight into another. The 4-bit blocks come first in the
     // permuted order, the 8-bit ones last.
     int cur = 0;
-    for (int b = 0; b < nb4; ++b) {
+    const int end4 = imin(b_end, p.nb4);
+    for (int b = b_begin; b < end4; ++b) {
         const int nxt = cur == 0 ? C::kStages - 1 : cur - 1;
-        block_fp6<kDump, kWC>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
+        block_fp6<kDump, kWC>(p, in, b, b_end, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
                               smem + nxt * C::kStage, y);
         cur = cur == C::kStages - 1 ? 0 : cur + 1;
     }
-    for (int b = nb4; b < nb; ++b) {
+    for (int b = imax(b_begin, p.nb4); b < b_end; ++b) {
         const int nxt = cur == 0 ? C::kStages - 1 : cur - 1;
-        block_int8<kDump, kWC>(p, in, b, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
+        block_int8<kDump, kWC>(p, in, b, b_end, m0, n0, row_lo, row_hi, wave, lane, sc, smem + cur * C::kStage,
                                smem + nxt * C::kStage, y);
         cur = cur == C::kStages - 1 ? 0 : cur + 1;
     }
+}
 
-    if constexpr (!kDump) {
+// Y of the tile from y (rows below row_hi).
+template <int kWC>
+__device__ __forceinline__ void store_y(const GemmProblem& p, int m0, int n0, int row_hi, int wave, int lane,
+                                        const float (&y)[4][kWC][4]) {
+    const int wr = wave >> 1, wc = wave & 1, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = m0 + 64 * wr + 16 * r + 4 * g + i;
-                if (row < row_hi) {
-                    uint16_t* yrow = p.Y + static_cast<size_t>(row) * p.ldy + n0 + 16 * kWC * wc + l16;
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + 64 * wr + 16 * r + 4 * g + i;
+            if (row < row_hi) {
+                uint16_t* yrow = p.Y + static_cast<size_t>(row) * p.ldy + n0 + 16 * kWC * wc + l16;
 #pragma unroll
-                    for (int c = 0; c < kWC; ++c) yrow[16 * c] = __half_as_ushort(__float2half_rn(y[r][c][i]));
-                }
+                for (int c = 0; c < kWC; ++c) yrow[16 * c] = __half_as_ushort(__float2half_rn(y[r][c][i]));
             }
+        }
+}
+
+// Partial tile of run s of a tile: the float4 y[r][c][0..3] of thread t at
+// index (r kWC + c) 256 + t, so each float4 store or load of a workgroup is
+// one contiguous 4 KB run.
+template <int kWC>
+__host__ __device__ __forceinline__ size_t slot_offset(int tile, int splits, int s) {
+    return (static_cast<size_t>(tile) * splits + s) * (kTM * 32 * kWC / 4);
+}
+
+template <int kWC>
+__device__ __forceinline__ void store_partial(const Sched& sc, int tile, int s, const float (&y)[4][kWC][4]) {
+    float4* own = reinterpret_cast<float4*>(sc.partials) + slot_offset<kWC>(tile, sc.splits, s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < kWC; ++c)
+            own[(r * kWC + c) * kThreads + threadIdx.x] = make_float4(y[r][c][0], y[r][c][1], y[r][c][2], y[r][c][3]);
+}
+
+template <bool kDump, int kWC>
+__global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p, Sched sc) {
+    using C = Cfg<kWC>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStage];
+    __shared__ int item_lds;
+
+    // the partials variant runs the tiles of the full launch (128-row tiles
+    // from row 0) that hold rows of [m_begin, m_begin + m_count), and stores
+    // only those rows
+    const int row_lo = kDump ? p.m_begin : 0;
+    const int row_hi = kDump ? p.m_begin + p.m_count : p.M;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const Inputs in = make_inputs(p);
+    float y[4][kWC][4];
+
+    if (kWC != 4 || sc.queue == nullptr) {
+        // one tile per workgroup, all blocks (the work queue serves the
+        // 128 x 128 tiles only: the wide tile is chosen for large grids)
+        int tm, tn;
+        if (!tile_of(blockIdx.x, sc.tiles_m, sc.tiles_n, tm, tn)) return;
+        const int m0 = (sc.tm0 + tm) * kTM;
+        const int n0 = tn * C::kTN;
+        const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
+        run_blocks<kDump, kWC>(p, in, 0, p.nb, m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
+        if constexpr (!kDump) store_y<kWC>(p, m0, n0, row_hi, wave, lane, y);
+        return;
     }
+
+    // persistent: item j of the XCD's range to its workgroup j, then (when
+    // the range is longer than the XCD's workgroups) items from the counter
+    const int xcd = blockIdx.x & 7;
+    const bool queued = sc.per_xcd > sc.wg_per_xcd;
+    int item = static_cast<int>(blockIdx.x >> 3) < range_count(sc, xcd) ? xcd * sc.per_xcd + (blockIdx.x >> 3) : -1;
+    while (item >= 0) {
+        const int tile = item / sc.splits, s = item - tile * sc.splits;
+        int tm, tn;
+        tile_coords(tile, sc.tiles_m, sc.tiles_n, tm, tn);
+        const int m0 = (sc.tm0 + tm) * kTM;
+        const int n0 = tn * C::kTN;
+        const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
+        run_blocks<kDump, kWC>(p, in, sc.bounds[s], sc.bounds[s + 1], m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
+        if constexpr (!kDump) store_partial<kWC>(sc, tile, s, y);
+        if (!queued) break;
+        if (threadIdx.x == 0) item_lds = next_item(sc, xcd);
+        __syncthreads();
+        item = item_lds;
+        __syncthreads();         // every wave has the item before thread 0 may overwrite it
+    }
+}
+
+// The second kernel of a split grid: four workgroups per tile (one per row
+// tile r of each wave's 64 rows) add the tile's partial tiles in split order
+// and write Y. Threads are numbered as in the GEMM's workgroup, so thread t
+// reads what thread t stored; each thread first issues the loads of every
+// run (kWC float4 per run, all in flight at once), then adds them in order.
+// Workgroup 0 also clears the queue counters. With `tiles` = 0 it only clears
+// them (the partials variant, which stores no partial tiles).
+template <int kWC>
+__global__ __launch_bounds__(kThreads) void gemm_fp6_splits_kernel(GemmProblem p, Sched sc, int tiles) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) sc.queue[threadIdx.x] = 0u;
+    const int tile = blockIdx.x >> 2, r = blockIdx.x & 3;
+    if (tile >= tiles) return;
+    int tm, tn;
+    tile_coords(tile, sc.tiles_m, sc.tiles_n, tm, tn);
+    const int t = threadIdx.x;
+    const float4* base = reinterpret_cast<const float4*>(sc.partials);
+    float4 v[kMaxSplits][kWC];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < sc.splits)
+#pragma unroll
+            for (int c = 0; c < kWC; ++c) v[s][c] = base[slot_offset<kWC>(tile, sc.splits, s) + (r * kWC + c) * kThreads + t];
+    float y[kWC][4];
+#pragma unroll
+    for (int c = 0; c < kWC; ++c) {
+        float4 a = v[0][c];
+#pragma unroll
+        for (int s = 1; s < kMaxSplits; ++s)
+            if (s < sc.splits) {
+                a.x += v[s][c].x;
+                a.y += v[s][c].y;
+                a.z += v[s][c].z;
+                a.w += v[s][c].w;
+            }
+        y[c][0] = a.x;
+        y[c][1] = a.y;
+        y[c][2] = a.z;
+        y[c][3] = a.w;
+    }
+    const int wave = t >> 6, lane = t & 63;
+    const int wr = wave >> 1, wc = wave & 1, g = lane >> 4, l16 = lane & 15;
+    const int m0 = (sc.tm0 + tm) * kTM, n0 = tn * Cfg<kWC>::kTN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 64 * wr + 16 * r + 4 * g + i;
+        if (row < p.M) {
+            uint16_t* yrow = p.Y + static_cast<size_t>(row) * p.ldy + n0 + 16 * kWC * wc + l16;
+#pragma unroll
+            for (int c = 0; c < kWC; ++c) yrow[16 * c] = __half_as_ushort(__float2half_rn(y[c][i]));
+        }
+    }
+}
+
+// Launch plan of a shape; the same for both variants (Y and the partials).
+struct Plan {
+    int wc;                  // column tiles per wave: 8 (128 x 256 tiles) or 4 (128 x 128)
+    int tiles_m, tiles_n;    // of the full launch
+    int splits;              // runs per tile; 1: one tile per workgroup, no workspace
+    int bounds[kMaxSplits + 1];
+    size_t ws_bytes;         // workspace the plan needs
+};
+
+// The plan (and so the workspace size) depends on the shape only: it is made
+// for the 256 CUs of an MI355X, so a workspace query needs no device. The
+// persistent grid itself is sized from the device's CU count.
+constexpr int kPlanCUs = 256;
+
+Plan make_plan(int M, int N, int K, int nb8) {
+    Plan pl{};
+    const int nb = K / kBlock, nb4 = nb - nb8;
+    pl.tiles_m = (M + kTM - 1) / kTM;
+    const int slots = 2 * kPlanCUs;      // two workgroups per CU
+    const int wide_tiles = N % Cfg<8>::kTN == 0 ? pl.tiles_m * (N / Cfg<8>::kTN) : 0;
+    pl.wc = wide_tiles >= 2 * slots ? 8 : 4;
+    pl.tiles_n = N / (32 * pl.wc);
+    const int tiles = pl.tiles_m * pl.tiles_n;
+    pl.splits = 1;
+    // below one wave of whole tiles: runs that fill about one wave, at least
+    // two blocks each (more runs only add partial-tile traffic: down_7b with
+    // 4 runs per tile took 101 us against 64 with 2)
+    if (pl.wc == 4 && tiles < slots) {
+        const int want = (slots + tiles / 2) / tiles;
+        pl.splits = imax(1, imin(imin(kMaxSplits, want), nb / 2));
+    }
+    // runs of about equal cost: a 4-bit block 1, an 8-bit block 2 (the 8-bit
+    // blocks are the last nb8); every run holds at least one block
+    auto cost_to = [nb4](int b) { return imin(b, nb4) + 2 * imax(0, b - nb4); };
+    const int cost = cost_to(nb);
+    pl.bounds[0] = 0;
+    for (int s = 1; s < pl.splits; ++s) {
+        const int goal = (cost * s + pl.splits / 2) / pl.splits;
+        int b = pl.bounds[s - 1] + 1;
+        while (b < nb && cost_to(b + 1) <= goal) ++b;
+        pl.bounds[s] = imin(b, nb - (pl.splits - s));
+    }
+    pl.bounds[pl.splits] = nb;
+    if (pl.splits > 1)
+        pl.ws_bytes = kCtrlBytes + static_cast<size_t>(tiles) * pl.splits * kTM * 32 * pl.wc * 4;
+    return pl;
+}
+
+template <bool kDump, int kWC>
+int launch_plan(const GemmProblem& p, const Plan& pl, hipStream_t s) {
+    Sched sc{};
+    sc.splits = pl.splits;
+    for (int i = 0; i <= pl.splits; ++i) sc.bounds[i] = pl.bounds[i];
+    sc.tiles_n = pl.tiles_n;
+    // the partials variant: the row tiles that hold [m_begin, m_begin + m_count)
+    sc.tm0 = kDump ? p.m_begin / kTM : 0;
+    sc.tiles_m = kDump ? (p.m_begin + p.m_count + kTM - 1) / kTM - sc.tm0 : pl.tiles_m;
+    const int tiles = sc.tiles_m * sc.tiles_n;
+    if (pl.splits == 1) {
+        gemm_fp6_kernel<kDump, kWC><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p, sc);
+        return static_cast<int>(hipGetLastError());
+    }
+    uint8_t* ws = static_cast<uint8_t*>(p.workspace);
+    sc.queue = reinterpret_cast<uint32_t*>(ws);
+    sc.partials = reinterpret_cast<float*>(ws + kCtrlBytes);
+    sc.items = tiles * sc.splits;
+    sc.per_xcd = (sc.items + 7) / 8;
+    sc.wg_per_xcd = imin(sc.per_xcd, imax(1, 2 * cu_count() / 8));
+    gemm_fp6_kernel<kDump, kWC><<<8 * sc.wg_per_xcd, kThreads, 0, s>>>(p, sc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return static_cast<int>(e);
+    gemm_fp6_splits_kernel<kWC><<<kDump ? 1 : 4 * tiles, kThreads, 0, s>>>(p, sc, kDump ? 0 : tiles);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <bool kDump>
+int launch_fp6(const GemmProblem& p, hipStream_t s) {
+    const Plan pl = make_plan(p.M, p.N, p.K, p.nb - p.nb4);
+    return pl.wc == 8 ? launch_plan<kDump, 8>(p, pl, s) : launch_plan<kDump, 4>(p, pl, s);
 }
 
 }  // namespace
 
+size_t gemm_fp6_workspace_bytes(int M, int N, int K, int nb8) {
+    return make_plan(M, N, K, nb8).ws_bytes;
+}
+
 int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.P != nullptr) {
-        const int rows = p.m_begin + p.m_count - (p.m_begin & ~15);
-        const int tiles = ((rows + kTM - 1) / kTM) * (p.N / Cfg<4>::kTN);
-        gemm_fp6_kernel<true, 4><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
-        return static_cast<int>(hipGetLastError());
-    }
-    // the wide tile when N allows it and the grid still covers every CU's two
-    // workgroup slots about twice
-    const int tiles_m = (p.M + kTM - 1) / kTM;
-    const int wide = p.N % Cfg<8>::kTN == 0 ? tiles_m * (p.N / Cfg<8>::kTN) : 0;
-    if (wide >= 4 * cu_count()) {
-        gemm_fp6_kernel<false, 8><<<8 * ((wide + 7) / 8), kThreads, 0, s>>>(p);
-    } else {
-        const int tiles = tiles_m * (p.N / Cfg<4>::kTN);
-        gemm_fp6_kernel<false, 4><<<8 * ((tiles + 7) / 8), kThreads, 0, s>>>(p);
-    }
-    return static_cast<int>(hipGetLastError());
+    return p.P != nullptr ? launch_fp6<true>(p, s) : launch_fp6<false>(p, s);
 }
 
 }  // namespace comet
