@@ -422,6 +422,22 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
 size_t comet_w4ax_gemm_fp6_workspace_bytes(int M, int N, int K, int n_int8_blocks);
 
 /*
+ * comet_w4ax_gemm_fp6 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a fixed array of
+ * COMET_NOALLOC_SCRATCH_BYTES in device memory inside the library, one per
+ * GPU, held until the process ends; this call allocates nothing. Calls on one
+ * GPU share that array, so calls that may overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller. Same result, kernels
+ * and errors as comet_w4ax_gemm_fp6; WORKSPACE when the shape needs more than
+ * COMET_NOALLOC_SCRATCH_BYTES (comet_w4ax_gemm_fp6_workspace_bytes tells).
+ */
+#define COMET_NOALLOC_SCRATCH_BYTES (36u << 20)
+int comet_w4ax_gemm_fp6_noalloc(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                                const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                                void* Y_fp16, int ldy, void* stream);
+
+/*
  * Debug variant of comet_w4ax_gemm_fp6: the exact INT32 block partials of rows
  * [m_begin, m_begin + m_count) as P[m - m_begin][n][b], from the kernel, tile
  * shape, block runs and work queue comet_w4ax_gemm_fp6 uses for the same

@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
     L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
     L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P, Z, P]
     L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, Z, P]
+    L.comet_w4ax_gemm_fp6_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_workspace_bytes.argtypes = [I, I, I, I]
     L.comet_w4ax_gemm_fp6_workspace_bytes.restype = Z
     L.comet_quant_act_asym.argtypes = [P, I, I, I, P, I, P, P, P, P]
@@ -86,7 +87,7 @@ def lib() -> ctypes.CDLL:
     for f in ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
               "comet_w4ax_gemm_partials", "comet_repack_weights_fp6", "comet_quant_act_fp6",
               "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials", "comet_w4ax_gemm_fp6_workspace_bytes",
-              "comet_rmsnorm_quant_act",
+              "comet_w4ax_gemm_fp6_noalloc", "comet_rmsnorm_quant_act",
               "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm", "comet_permute_channels",
               "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
               "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
@@ -101,7 +102,7 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_w4ax_gemm_workspace_bytes", "comet_w4ax_gemm_partials",
            "comet_xq_fp6_bytes", "comet_wq_fp6_bytes", "comet_repack_weights_fp6",
            "comet_quant_act_fp6", "comet_w4ax_gemm_fp6", "comet_w4ax_gemm_fp6_partials",
-           "comet_w4ax_gemm_fp6_workspace_bytes",
+           "comet_w4ax_gemm_fp6_workspace_bytes", "comet_w4ax_gemm_fp6_noalloc",
            "comet_rmsnorm_quant_act", "comet_rmsnorm_quant_act_fp6", "comet_rmsnorm",
            "comet_permute_channels", "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
@@ -539,6 +540,23 @@ def comet_w4ax_gemm_fp6(Xq, x_scale, w: dict, M: int, Y=None, workspace=None, st
                                    _dev_ptr(w["w_scale"]), int(nb8), M, N, K, _dev_ptr(Y), Y.stride(0),
                                    None if workspace is None else _dev_ptr(workspace), wsz, _stream(stream))
     _check("comet_w4ax_gemm_fp6", rc)
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 36 << 20      # COMET_NOALLOC_SCRATCH_BYTES of the header
+
+
+def comet_w4ax_gemm_fp6_noalloc(Xq, x_scale, w: dict, M: int, Y=None, stream=None):
+    """comet_w4ax_gemm_fp6 on the library's fixed per-GPU scratch (no workspace
+    argument; the call itself allocates nothing)."""
+    import torch
+    N, K, nb8 = w["N"], w["K"], w["nb8"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    rc = lib().comet_w4ax_gemm_fp6_noalloc(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
+                                           _dev_ptr(w["w_scale"]), int(nb8), M, N, K, _dev_ptr(Y), Y.stride(0),
+                                           _stream(stream))
+    _check("comet_w4ax_gemm_fp6_noalloc", rc)
     return Y
 
 

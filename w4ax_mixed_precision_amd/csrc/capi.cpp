@@ -495,6 +495,29 @@ int comet_w4ax_gemm_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq
     return hip_status(comet::launch_w4ax_gemm_fp6(p, stream));
 }
 
+int comet_w4ax_gemm_fp6_noalloc(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                                const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
+                                void* Y_fp16, int ldy, void* stream) {
+    if (!Y_fp16) return COMET_ERR_NULL;
+    // the fixed scratch array stands in for the workspace (16-byte aligned)
+    static uint8_t* const kScratchStandIn = reinterpret_cast<uint8_t*>(static_cast<uintptr_t>(256));
+    int st = check_fp6_gemm(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, kScratchStandIn,
+                            COMET_NOALLOC_SCRATCH_BYTES);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max())
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Y_fp16)) return COMET_ERR_ALIGN;
+    comet::GemmProblem p =
+        fp6_problem(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, nullptr, 0);
+    p.Y = static_cast<uint16_t*>(Y_fp16);
+    p.ldy = ldy;
+    p.P = nullptr;
+    p.m_begin = 0;
+    p.m_count = M;
+    return hip_status(comet::launch_w4ax_gemm_fp6_noalloc(p, stream));
+}
+
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
                                  int m_begin, int m_count, int32_t* P, void* workspace, size_t workspace_bytes,

@@ -71,6 +71,9 @@ int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream);   // FP6 layout; w
 // Workspace of the FP6 GEMM (work queue, tile counts, split partial tiles);
 // a function of the shape only (no device query).
 size_t gemm_fp6_workspace_bytes(int M, int N, int K, int nb8);
+// The FP6 GEMM with the library's fixed per-device scratch array as its
+// workspace (p.workspace is ignored); the shape's workspace must fit it.
+int launch_w4ax_gemm_fp6_noalloc(GemmProblem p, void* stream);
 
 // Compute units of the current device (quant_act.hip; read once per process).
 int cu_count();

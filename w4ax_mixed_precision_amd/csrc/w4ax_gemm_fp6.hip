@@ -51,6 +51,8 @@
 //     for positions 32g + 16h ..); B at 16384, the tile's 2 kWC INT4 fragments.
 //   then the block's 128 activation scales (f32) and 32 kWC weight scales
 //   (fp16), and a pad that receives the balancing loads.
+#include <mutex>
+
 #include "comet_internal.h"
 #include "device_util.h"
 
@@ -658,6 +660,65 @@ size_t gemm_fp6_workspace_bytes(int M, int N, int K, int nb8) {
 int launch_w4ax_gemm_fp6(const GemmProblem& p, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     return p.P != nullptr ? launch_fp6<true>(p, s) : launch_fp6<false>(p, s);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form of the FP6 GEMM, for callers that cannot allocate
+// (code under HIP graph capture, serving loops, harnesses that forbid
+// allocation): the workspace is a fixed array in device memory, one per GPU,
+// held until the process ends. In host code the array's name is only a
+// host-side stand-in, so its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// passed on. Calls on one GPU share the array: calls that may overlap on one
+// GPU race. The queue counters at its start are zero when the code object is
+// loaded, each call leaves them zero, and the first call on a device clears
+// them again with a small kernel (no memset node, should that call be
+// captured).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[COMET_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_cleared[kMaxDevices] = {};
+
+__global__ void clear_words_kernel(uint32_t* w, int n) {
+    if (static_cast<int>(threadIdx.x) < n) w[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+int launch_w4ax_gemm_fp6_noalloc(GemmProblem p, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+    bool clear = false;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_ptr[dev] == nullptr) {
+            void* ptr = nullptr;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return static_cast<int>(e);
+            g_scratch_ptr[dev] = ptr;
+        }
+        if (!g_scratch_cleared[dev]) {
+            g_scratch_cleared[dev] = true;
+            clear = true;
+        }
+        p.workspace = g_scratch_ptr[dev];
+    }
+    p.workspace_bytes = COMET_NOALLOC_SCRATCH_BYTES;
+    if (clear) {
+        clear_words_kernel<<<1, 64, 0, s>>>(static_cast<uint32_t*>(p.workspace), static_cast<int>(kCtrlBytes / 4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return static_cast<int>(e);
+    }
+    return launch_w4ax_gemm_fp6(p, stream);
 }
 
 }  // namespace comet
