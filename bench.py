@@ -489,6 +489,136 @@ def kv4_attention_measure(torch, comet, synth, T=4096, seqs=16, iters=20):
     return out
 
 
+def _per_call_us(torch, fn, iters):
+    """Mean microseconds per call of fn(i), i = 0 .. iters-1: HIP events on the
+    launch stream around `iters` back-to-back calls, after 3 untimed ones."""
+    for i in range(3):
+        fn(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(iters):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+def decode_sweep(torch, comet, synth, iters=60):
+    """The LLaMA-70B decode sweep (M in {1, 4, 16, 64}, K = 8192, N in {10240,
+    8192, 28672}) on the INT4 layout: comet_w4ax_gemm, comet_quant_act and the
+    pair, each timed over `iters` back-to-back calls that rotate through weight
+    copies of >= 1 GB (the 256 MB last-level cache cannot serve them). HBM
+    fraction of the GEMM from its algorithmic bytes (weight codes, scales and
+    sums, activation codes and scales, fp16 Y) against 8 TB/s."""
+    out = {"timing": f"HIP events around {iters} back-to-back calls per figure, weights rotated "
+                     f"over copies of >= 1 GB", "shapes": {}}
+    for N in (10240, 8192, 28672):
+        cfg1 = synth.CONFIGS[f"decode_70b_n{N}_m1"]
+        K, nb8 = cfg1.K, cfg1.nb8
+        pk = comet.comet_pack_weights(synth.make_w(cfg1), synth.make_scores(cfg1), nb8)
+        w0 = comet.upload_weights(pk)
+        copies = copies_for(cfg1)
+        ws = [w0] + [{k: (v.clone() if hasattr(v, "clone") else v) for k, v in w0.items()}
+                     for _ in range(copies - 1)]
+        for m in (1, 4, 16, 64):
+            cfg = synth.CONFIGS[f"decode_70b_n{N}_m{m}"]
+            X = torch.from_numpy(synth.make_x(cfg).view(np.float16)).cuda()
+            Xq, xs = comet.comet_quant_act(X, w0["perm"], nb8)
+            Y = torch.empty((m, N), dtype=torch.float16, device="cuda")
+            g = _per_call_us(torch, lambda i: comet.comet_w4ax_gemm(Xq, xs, ws[i % copies], m, Y=Y), iters)
+            q = _per_call_us(torch, lambda i: comet.comet_quant_act(X, ws[i % copies]["perm"], nb8, Xq=Xq,
+                                                                    x_scale=xs), iters)
+
+            def pair(i):
+                w = ws[i % copies]
+                comet.comet_quant_act(X, w["perm"], nb8, Xq=Xq, x_scale=xs)
+                comet.comet_w4ax_gemm(Xq, xs, w, m, Y=Y)
+
+            pq = _per_call_us(torch, pair, iters)
+            nbytes = gemm_bytes(m, N, K, nb8, "int4")
+            gbs = nbytes / (g * 1e-6) / 1e9
+            out["shapes"][f"m{m}_n{N}"] = {
+                "M": m, "N": N, "K": K, "int8_blocks": nb8, "gemm_us": g, "quant_us": q, "pair_us": pq,
+                "gemm_bytes": nbytes, "gemm_gbs": gbs, "gemm_hbm_frac": gbs / PEAK_HBM_GBS,
+                "gemm_tops": 2.0 * m * N * K / (g * 1e-6) / 1e12, "weight_copies": copies}
+            log(f"[bench] decode m={m} n={N}: gemm {g:.1f} us ({gbs:.0f} GB/s, "
+                f"{gbs / PEAK_HBM_GBS:.2f} of HBM), quant {q:.1f} us, pair {pq:.1f} us")
+        del ws, w0
+        torch.cuda.empty_cache()
+    return out
+
+
+def layer_configs(torch, comet, synth, iters=50):
+    """LLaMA-7B layers: q_proj (128 tokens; HBM binds: op/B below the ridge)
+    and the MLP pair up/gate + down (1024 tokens; the matrix unit binds), on
+    the FP6 layout with the split-K work queue where a grid is below one wave.
+    GEMM and quantizer each over `iters` back-to-back calls, weights rotated
+    over copies of >= 1 GB. Fractions against the instruction-mix peak (FP6
+    for 4-bit blocks, INT8 for 8-bit ones), the dense INT8 peak, and HBM."""
+    res = {"timing": f"HIP events around {iters} back-to-back calls per figure, weights rotated over "
+                     f"copies of >= 1 GB"}
+    for group, names in (("q_proj_7b", ["q_proj_7b"]), ("mlp_7b", ["up_gate_7b", "down_7b"])):
+        g_out = {"layers": {}}
+        tot_ops = tot_us = 0.0
+        for name in names:
+            l = Layer(name, copies_for(synth.CONFIGS[name]), torch, comet, synth)
+            l.quant(l.w[0])
+            gu = _per_call_us(torch, lambda i: l.gemm(l.w[i % len(l.w)]), iters)
+            qu = _per_call_us(torch, lambda i: l.quant(l.w[i % len(l.w)]), iters)
+            tops = l.ops / (gu * 1e-6) / 1e12
+            gbs = l.gbytes / (gu * 1e-6) / 1e9
+            bound = "hbm" if l.gbytes / (PEAK_HBM_GBS * 1e9) > l.ops / (l.peak * 1e12) else "mfma"
+            g_out["layers"][name] = {
+                "M": l.cfg.M, "N": l.cfg.N, "K": l.cfg.K, "int8_blocks": l.cfg.nb8, "gemm_us": gu,
+                "quant_us": qu, "gemm_tops": tops, "gemm_gbs": gbs, "bound": bound,
+                "frac_vs_mix_peak": tops / l.peak, "frac_vs_int8_peak": tops / PEAK_INT8_TOPS,
+                "hbm_frac": gbs / PEAK_HBM_GBS, "mix_peak_tops": l.peak,
+                "workspace_bytes": l.ws_bytes, "weight_copies": len(l.w)}
+            log(f"[bench] {name}: gemm {gu:.1f} us ({tops:.0f} TOPS, {tops / l.peak:.3f} of the mix peak, "
+                f"{gbs:.0f} GB/s), quant {qu:.1f} us")
+            tot_ops += l.ops
+            tot_us += gu
+            del l
+            torch.cuda.empty_cache()
+        g_out["gemm_us"] = tot_us
+        g_out["gemm_tops"] = tot_ops / (tot_us * 1e-6) / 1e12
+        res[group] = g_out
+    return res
+
+
+def cpu_single_core(budget_s=12.0):
+    """The oracle on one core for the small configurations: a bounded sample of
+    rows of tiny, q_proj_7b, up_gate_7b, down_7b and the decode layers (M = 1),
+    steps 3-5 (activation quantization, block partials, epilogue) with the
+    weights quantized beforehand."""
+    from gen import synth
+    from oracle import oracle as O
+    O.build(force=False)
+    before = O.threads()
+    O.set_threads(1)
+    names = ["tiny", "q_proj_7b", "up_gate_7b", "down_7b"] + [f"decode_70b_n{n}_m1" for n in (10240, 8192, 28672)]
+    per = budget_s / len(names)
+    out = {}
+    try:
+        for name in names:
+            cfg = synth.CONFIGS[name]
+            X, W, score = synth.make_x(cfg, rows=min(cfg.M, 64)), synth.make_w(cfg), synth.make_scores(cfg)
+            perm, flags = O.channel_order(score, cfg.nb8)
+            qw, sw16, _ = O.quantize_weights(W, perm)
+            rows, spent = 0, 0.0
+            while rows < X.shape[0] and spent < per:
+                t = time.perf_counter()
+                O.forward_rows(X, perm, flags, qw, sw16, (rows, rows + 1))
+                spent += time.perf_counter() - t
+                rows += 1
+            out[name] = {"rows": rows, "of_rows": cfg.M, "seconds": spent,
+                         "tops": 2.0 * rows * cfg.N * cfg.K / spent / 1e12}
+    finally:
+        O.set_threads(before)
+    return out
+
+
 def cpu_baseline(layers, budget_s):
     """The oracle as it stands, on a bounded sample of rows of every layer: host
     time of steps 3-5 (activation quantization, block partials, epilogue) with
@@ -534,6 +664,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv4-only", action="store_true",
                     help="only the KV4 decode attention measurement (its JSON object), for profiling")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode sweep and the LLaMA-7B layers (outside the timed step)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the decode sweep and the LLaMA-7B layers (their JSON objects), for profiling")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -553,6 +687,10 @@ def main():
     if args.kv4_only:
         print(json.dumps({"kv4_decode_attention": kv4_attention_measure(torch, comet, synth)}), flush=True)
         return
+    if args.configs_only:
+        print(json.dumps({"decode_70b": decode_sweep(torch, comet, synth),
+                          "llama7b_layers": layer_configs(torch, comet, synth)}), flush=True)
+        return
 
     layers = [Layer(n, copies_for(synth.CONFIGS[n]), torch, comet, synth)
               for n in WORKLOADS[args.workload]]
@@ -571,9 +709,12 @@ def main():
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": achieved_tops, "peak": peak_tops,
                 "unit": "TFLOP/s", "frac": achieved_tops / peak_tops,
+                "frac_vs_mix_peak": achieved_tops / peak_tops,
+                "frac_vs_int8_peak": achieved_tops / PEAK_INT8_TOPS,
                 "peak_basis": "dense MFMA peak of the instruction mix: FP6 10.1 POPS for 4-bit "
                               "blocks, INT8 5.0 POPS for 8-bit blocks (and for every block on "
-                              "the INT4 layout)"}
+                              "the INT4 layout); frac_vs_int8_peak is against the dense INT8 "
+                              "peak (5.0 POPS) alone"}
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS}
@@ -604,15 +745,22 @@ def main():
     qoq = qoq_ablation(torch, comet, synth) if ablate else None
     kv4 = kv4_attention_measure(torch, comet, synth) if ablate else None
 
+    configs = None
+    if args.workload == "prefill_70b" and not args.no_configs:
+        configs = {"decode_70b": decode_sweep(torch, comet, synth),
+                   "llama7b_layers": layer_configs(torch, comet, synth)}
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(layers, args.cpu_seconds)
+        if args.workload == "prefill_70b":
+            cpu["single_core"] = cpu_single_core()
 
     out = {
         "metric": "W4Ax GEMM effective TOPS + % INT8-MFMA/HBM roofline, LLaMA-70B layer shapes",
         "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8+fp6(e2m3 exact int4 codes)",
         "data": "synthetic (seeded LLaMA-shaped activations with planted outlier channels, "
                 "N(0,0.02) weights)",
         "config": {"workload": args.workload,
@@ -628,6 +776,7 @@ def main():
         "asym_activation_variant": asym,
         "qoq_w4a8_variant": qoq,
         "kv4_decode_attention": kv4,
+        "configs": configs,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -781,6 +781,17 @@ int orc_threads(void)
 #endif
 }
 
+/* Threads the OpenMP loops use from now on (for timing on one core). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* 8. QoQ progressive group quantization (W4A8)                             */
 /* ------------------------------------------------------------------------ */

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.orc_silu_mul_array.restype = None
         L.orc_swiglu_rows.argtypes = [P, P, I, I, I, P, I]
         L.orc_threads.restype = I
+        L.orc_set_threads.argtypes = [I]
+        L.orc_set_threads.restype = None
         L.orc_half_to_float_array.restype = None
         L.orc_half_to_float_array.argtypes = [P, P, ctypes.c_int64]
         L.orc_float_to_half_array.restype = None
@@ -324,6 +326,11 @@ def swiglu(G16: np.ndarray, U16: np.ndarray) -> np.ndarray:
 
 def threads() -> int:
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on."""
+    lib().orc_set_threads(int(n))
 
 
 def quantize_layer(X16, W16, score, nb8):
