@@ -443,11 +443,16 @@ int comet_w4ax_gemm_fp6_noalloc(const void* Xq_fp6, const float* x_scale, const 
  * shape, block runs and work queue comet_w4ax_gemm_fp6 uses for the same
  * (M, N, K), over the tiles that hold those rows; each run stores the
  * partials of its own blocks (no fix-up). Workspace as comet_w4ax_gemm_fp6.
+ * max_workgroups: 0 runs the grid the Y call runs; n > 0 caps a split plan's
+ * persistent grid at about n workgroups (8 at least, one per XCD), so that
+ * the work-queue counters deal most items (a check of the queue, which on a
+ * full MI355X only deals the items a plan has beyond its resident grid).
+ * Errors as comet_w4ax_gemm_fp6, plus SHAPE (row range), ARG (max_workgroups < 0).
  */
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N,
-                                 int K, int m_begin, int m_count, int32_t* P, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 int K, int m_begin, int m_count, int32_t* P, int max_workgroups,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * RMS normalization fused into the activation quantizer. QoQ/QServe article

@@ -65,24 +65,49 @@ def gf(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, Y=A, ldy=512, work=A, 
     return comet.lib().comet_w4ax_gemm_fp6(Xq, xs, Wq, ws, nb8, M, N, K, Y, ldy, work, wbytes, None)
 
 
-def gfp(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A, work=A, wbytes=1 << 40):
-    return comet.lib().comet_w4ax_gemm_fp6_partials(Xq, xs, Wq, ws, nb8, M, N, K, m0, mc, P, work, wbytes,
+def gfp(Xq=A, xs=A, Wq=A, ws=A, nb8=1, M=16, N=512, K=512, m0=0, mc=16, P=A, cap=0, work=A, wbytes=1 << 40):
+    return comet.lib().comet_w4ax_gemm_fp6_partials(Xq, xs, Wq, ws, nb8, M, N, K, m0, mc, P, cap, work, wbytes,
                                                     None)
+
+
+def test_fp6_workspace_bounds_and_noalloc_limit():
+    """Split plans hold at most two waves of runs (1024 partial tiles of
+    64 KiB, plus the counters), over a sweep of shapes; the allocation-free
+    call's fixed scratch holds every one-wave plan (the 7B layers, the 70B
+    decode shapes on this layout) and rejects a larger one with
+    COMET_ERR_WORKSPACE before any HIP call."""
+    L = comet.lib()
+    wb = L.comet_w4ax_gemm_fp6_workspace_bytes
+    worst = 0
+    for M in (1, 16, 64, 100, 128, 256, 384, 512, 1024, 2048, 4096):
+        for N in (128, 512, 1024, 2048, 4096, 5120, 8192, 10240, 11008, 12800, 28672):
+            for K in (128, 512, 1024, 4096, 8192, 11008, 28672):
+                nb = K // 128
+                for nb8 in {0, nb // 4, nb}:
+                    worst = max(worst, wb(M, N, K, nb8))
+    assert 0 < worst <= 256 + 1024 * 128 * 128 * 4
+    for M, N, K, nb8 in ((128, 4096, 4096, 4), (1024, 4096, 11008, 22), (64, 10240, 8192, 7)):
+        assert 0 < wb(M, N, K, nb8) <= comet.NOALLOC_SCRATCH_BYTES
+    M, N, K, nb8 = 256, 12800, 28672, 0                     # 200 tiles x 5 runs: 62.5 MiB
+    assert wb(M, N, K, nb8) > comet.NOALLOC_SCRATCH_BYTES
+    assert L.comet_w4ax_gemm_fp6_noalloc(A, A, A, A, nb8, M, N, K, A, N, None) == WORKSPACE
 
 
 def test_fp6_workspace_contract():
     """The FP6 GEMM's workspace: a function of the shape only (no device
     needed), none for grids of a wave of whole tiles or more (the 70B prefill
-    layers, the 7B up/gate layer's 688 tiles), the split runs' partial tiles
-    for smaller grids (q_proj_7b: 32 tiles x 8 runs; down_7b: 256 x 2); a
-    missing, small or misaligned workspace is rejected before any HIP call."""
+    layers, the 7B up/gate layer's 688 tiles) or where splitting does not pay
+    (short K, or a grid close to a wave), the split runs' partial tiles
+    otherwise (q_proj_7b: 32 tiles x 8 runs; down_7b: 256 x 2); a missing,
+    small or misaligned workspace is rejected before any HIP call."""
     L = comet.lib()
     wb = L.comet_w4ax_gemm_fp6_workspace_bytes
     assert wb(4096, 8192, 28672, 67) == 0 and wb(4096, 28672, 8192, 7) == 0 and wb(1024, 11008, 4096, 4) == 0
     tile = 128 * 128 * 4
     assert wb(128, 4096, 4096, 4) == 256 + 32 * 8 * tile
     assert wb(1024, 4096, 11008, 22) == 256 + 256 * 2 * tile
-    for M, N, K, nb8 in ((128, 4096, 4096, 4), (1024, 4096, 11008, 22), (16, 512, 512, 1)):
+    assert wb(16, 512, 512, 1) == 0 and wb(384, 12800, 1024, 2) == 0        # splitting would not pay
+    for M, N, K, nb8 in ((128, 4096, 4096, 4), (1024, 4096, 11008, 22), (64, 10240, 8192, 7)):
         need = wb(M, N, K, nb8)
         assert need > 0 and need % 16 == 0, (M, N, K)
         assert comet.fp6_workspace_bytes(M, N, K, nb8) == need
@@ -101,7 +126,7 @@ def test_fp6_rejections():
     assert gf(nb8=5) == ARG and gf(N=200, ldy=200) == UNSUP
     assert gf(Wq=MIS) == ALIGN and gf(Y=MIS) == ALIGN and gf(xs=MIS) == ALIGN
     assert gf(M=1 << 20, N=1 << 12, ldy=1 << 12) == UNSUP
-    assert gfp(P=None) == NULL and gfp(m0=10, mc=7) == SHAPE and gfp(P=MIS) == ALIGN
+    assert gfp(P=None) == NULL and gfp(m0=10, mc=7) == SHAPE and gfp(P=MIS) == ALIGN and gfp(cap=-1) == ARG
     L = comet.lib()
     assert L.comet_xq_fp6_bytes(16, 512, 1) == comet.xq_fp6_bytes(16, 512, 1) == 16 * (96 * 3 + 128)
     assert L.comet_wq_fp6_bytes(256, 512, 1) == comet.wq_fp6_bytes(256, 512, 1) == 256 * (96 * 3 + 64)

@@ -62,10 +62,12 @@ def test_layer_parity_fp6(torch, name):
     (1, 128, 128, 0), (1, 128, 128, 1), (3, 256, 256, 2), (17, 512, 384, 0),
     (33, 384, 640, 3), (100, 1024, 512, 1), (130, 640, 256, 5), (257, 896, 384, 2),
     (5, 33024, 128, 4),   # K > 32768: global gather path of the quantizer
-    # split grids whose runs outnumber the persistent grid, so the range
-    # counters deal the rest: 300 tiles x 2 runs and 110 tiles x 5 runs, with
-    # 8-bit blocks inside and across runs
+    # grids below a wave that the cost model keeps whole (short K)
     (384, 1024, 12800, 2), (128, 1280, 14080, 3),
+    # split grids: 80 tiles x 6 runs (8-bit blocks inside and across runs),
+    # 40 tiles x 6 runs with a ragged row tile, and 130 tiles x 7 runs: more
+    # runs than the resident grid, so the work queue deals the rest
+    (64, 8192, 10240, 7), (100, 4096, 5120, 3), (64, 6144, 16640, 12),
 ])
 def test_edge_shapes_fp6(torch, M, K, N, nb8):
     import w4ax_mixed_precision_amd as comet
@@ -131,6 +133,32 @@ def test_fp6_matches_int4_layout(torch):
     for Y in (Y4, Y6):
         y1, y2_ok, _ = G.gate_y(G.f16(Y.cpu().numpy().view(np.uint16)), ye, tabs, cfg.nb)
         assert y1 <= 1e-3 and y2_ok
+
+
+@pytest.mark.parametrize("name", ["q_proj_7b", "decode_70b_n10240_m64"])
+def test_fp6_work_queue(torch, name):
+    """The work queue dealing most of a split plan's runs: the partials call
+    capped at 8 workgroups (one per XCD: each takes its first run directly
+    and the rest from its XCD's counter) gives the oracle's partials bit for
+    bit, the same as the uncapped call, and leaves the counters at zero."""
+    import w4ax_mixed_precision_amd as comet
+    G.log(f"[fp6 queue] {name}")
+    d = G.host_layer(name)
+    cfg = d["cfg"]
+    need = comet.fp6_workspace_bytes(cfg.M, cfg.N, cfg.K, cfg.nb8)
+    assert need > 0, "a split plan"
+    X, w = G.device_layer(d, d["pk"])
+    Xq, xs = comet.comet_quant_act_fp6(X, w["perm"], cfg.nb8)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    P8 = comet.comet_w4ax_gemm_fp6_partials(Xq, xs, w, cfg.M, workspace=ws, max_workgroups=8)
+    torch.cuda.synchronize()
+    assert int(ws[:256].count_nonzero()) == 0
+    P = comet.comet_w4ax_gemm_fp6_partials(Xq, xs, w, cfg.M, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(P8, P)
+    rows = np.arange(cfg.M)
+    P_o = G.oracle_rows(d, rows)[0]
+    assert np.array_equal(P8.cpu().numpy(), P_o)
 
 
 def test_fp6_workspace_shared_across_shapes(torch):

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
     L.comet_repack_weights_fp6.argtypes = [P, I, I, I, P]
     L.comet_quant_act_fp6.argtypes = [P, I, I, I, P, I, P, P, P]
     L.comet_w4ax_gemm_fp6.argtypes = [P, P, P, P, I, I, I, I, P, I, P, Z, P]
-    L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, Z, P]
+    L.comet_w4ax_gemm_fp6_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]
     L.comet_w4ax_gemm_fp6_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_workspace_bytes.argtypes = [I, I, I, I]
     L.comet_w4ax_gemm_fp6_workspace_bytes.restype = Z
@@ -561,7 +561,8 @@ def comet_w4ax_gemm_fp6_noalloc(Xq, x_scale, w: dict, M: int, Y=None, stream=Non
 
 
 def comet_w4ax_gemm_fp6_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
-                                 m_count: int | None = None, P=None, workspace=None, stream=None):
+                                 m_count: int | None = None, P=None, workspace=None, stream=None,
+                                 max_workgroups: int = 0):
     """Exact block partials of the FP6-layout GEMM, [m_count, N, nb] int32."""
     import torch
     N, K, nb8 = w["N"], w["K"], w["nb8"]
@@ -573,8 +574,9 @@ def comet_w4ax_gemm_fp6_partials(Xq, x_scale, w: dict, M: int, m_begin: int = 0,
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().comet_w4ax_gemm_fp6_partials(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
                                             _dev_ptr(w["w_scale"]), int(nb8), M, N, K, m_begin,
-                                            m_count, _dev_ptr(P), None if workspace is None else _dev_ptr(workspace),
-                                            wsz, _stream(stream))
+                                            m_count, _dev_ptr(P), int(max_workgroups),
+                                            None if workspace is None else _dev_ptr(workspace), wsz,
+                                            _stream(stream))
     _check("comet_w4ax_gemm_fp6_partials", rc)
     return P
 

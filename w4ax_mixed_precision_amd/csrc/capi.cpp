@@ -520,18 +520,20 @@ int comet_w4ax_gemm_fp6_noalloc(const void* Xq_fp6, const float* x_scale, const 
 
 int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
                                  const uint16_t* w_scale_fp16, int n_int8_blocks, int M, int N, int K,
-                                 int m_begin, int m_count, int32_t* P, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 int m_begin, int m_count, int32_t* P, int max_workgroups, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
     if (!P) return COMET_ERR_NULL;
     int st = check_fp6_gemm(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace,
                             workspace_bytes);
     if (st != COMET_OK) return st;
     if (m_begin < 0 || m_count < 1 || m_begin > M - m_count) return COMET_ERR_SHAPE;
+    if (max_workgroups < 0) return COMET_ERR_ARG;
     if (static_cast<int64_t>(m_count) * N * (K / kBlock) > std::numeric_limits<int32_t>::max())
         return COMET_ERR_UNSUPPORTED;
     if (!aligned16(P)) return COMET_ERR_ALIGN;
     comet::GemmProblem p =
         fp6_problem(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, K, workspace, workspace_bytes);
+    p.max_wg = max_workgroups;
     p.Y = nullptr;
     p.ldy = N;
     p.P = P;

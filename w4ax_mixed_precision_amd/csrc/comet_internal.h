@@ -63,6 +63,7 @@ struct GemmProblem {
     int m_begin, m_count;    // row range of the partials output
     void* workspace;
     size_t workspace_bytes;
+    int max_wg;              // FP6 partials only: cap on the persistent grid (0: none)
 };
 
 size_t gemm_workspace_bytes(int M, int N, int K, int nb8);

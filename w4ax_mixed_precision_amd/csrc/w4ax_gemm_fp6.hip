@@ -333,6 +333,9 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxSplits = 8;
+#ifndef COMET_FP6_SPLITS_CAP
+#define COMET_FP6_SPLITS_CAP kMaxSplits
+#endif
 
 struct Sched {
     uint32_t* queue;       // [0..7] per-XCD counters; nullptr: one tile per workgroup
@@ -594,12 +597,28 @@ Plan make_plan(int M, int N, int K, int nb8) {
     pl.tiles_n = N / (32 * pl.wc);
     const int tiles = pl.tiles_m * pl.tiles_n;
     pl.splits = 1;
-    // below one wave of whole tiles: runs that fill about one wave, at least
-    // two blocks each (more runs only add partial-tile traffic: down_7b with
-    // 4 runs per tile took 101 us against 64 with 2)
+    // Split only where the cost model says it pays: time in block-steps of
+    // a 4-bit block with two workgroups per CU (an 8-bit block costs 2), a
+    // workgroup alone on its CU about 1.3x faster, each run paying about 2
+    // block-steps of its own (pipeline start, partial tile store) and a split
+    // plan about 15 more for the second kernel, and at most two waves of
+    // runs. Calibrated on the 7B layers (whole tiles against runs): q_proj_7b
+    // 24 against 16 us (8 runs), down_7b 72 against 63 us (2 runs); a
+    // 300-tile grid of 8 blocks 14 against 28 us (2 runs: it stays whole).
     if (pl.wc == 4 && tiles < slots) {
-        const int want = (slots + tiles / 2) / tiles;
-        pl.splits = imax(1, imin(imin(kMaxSplits, want), nb / 2));
+        const double c = nb4 + 2.0 * nb8;
+        auto run_cost = [&](int items, double per_item) {
+            if (items <= kPlanCUs) return per_item / 1.3;
+            return per_item * ((items + slots - 1) / slots);
+        };
+        double best = run_cost(tiles, c);
+        for (int sp = 2; sp <= imin(COMET_FP6_SPLITS_CAP, nb / 2) && tiles * sp <= 2 * slots; ++sp) {
+            const double t = run_cost(tiles * sp, c / sp + 2.0) + 15.0;
+            if (t < best) {
+                best = t;
+                pl.splits = sp;
+            }
+        }
     }
     // runs of about equal cost: a 4-bit block 1, an 8-bit block 2 (the 8-bit
     // blocks are the last nb8); every run holds at least one block
@@ -638,6 +657,7 @@ int launch_plan(const GemmProblem& p, const Plan& pl, hipStream_t s) {
     sc.items = tiles * sc.splits;
     sc.per_xcd = (sc.items + 7) / 8;
     sc.wg_per_xcd = imin(sc.per_xcd, imax(1, 2 * cu_count() / 8));
+    if (kDump && p.max_wg > 0) sc.wg_per_xcd = imin(sc.wg_per_xcd, imax(1, p.max_wg / 8));
     gemm_fp6_kernel<kDump, kWC><<<8 * sc.wg_per_xcd, kThreads, 0, s>>>(p, sc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return static_cast<int>(e);
