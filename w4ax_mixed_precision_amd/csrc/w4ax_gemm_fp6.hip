@@ -310,8 +310,8 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
 // it is: one tile per workgroup, XCD-aware order (tile_of). A smaller grid
 // cannot fill 256 CUs with whole tiles, so each tile's blocks are split into
 // S runs of equal cost (an 8-bit block costs twice a 4-bit one: twice the
-// matrix instructions, plus widening and conversion), S chosen so the runs
-// fill about one wave, and the runs are the work items of a persistent grid:
+// matrix instructions, plus widening and conversion), S chosen by the cost
+// model of make_plan, and the runs are the work items of a persistent grid:
 //   * the items are dealt in the XCD-aware tile order into 8 contiguous
 //     ranges, one per XCD (workgroup w runs on XCD w mod 8); workgroup j of an
 //     XCD starts on item j of its range without any atomic, and a range
