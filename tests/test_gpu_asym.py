@@ -19,7 +19,7 @@ from tests.layout import decode_xq
 pytestmark = pytest.mark.gpu
 
 LAYERS = ["tiny", "q_proj_7b", "down_7b", "decode_70b_n8192_m1", "decode_70b_n10240_m16",
-          "decode_70b_n8192_m64", "decode_70b_n28672_m64", "prefill_up_70b"]
+          "decode_70b_n8192_m64", "decode_70b_n10240_m64", "decode_70b_n28672_m64", "prefill_up_70b"]
 
 
 @pytest.fixture(scope="module")

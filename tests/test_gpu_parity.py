@@ -97,8 +97,9 @@ def _custom_layer(M, K, N, nb8, seed, zero_rows=(), zero_block_rows=(), ldx=None
     (2, 4096, 384, 3), (16, 8192, 1152, 7), (9, 16384, 128, 20),
     # decode kernels for 17..64 rows, several channel groups per wave: the
     # LDS-ring form at 64 blocks (narrow: two groups, eight waves; wide: four
-    # groups, four waves) and the register form at other block counts
-    (24, 8192, 1152, 7), (64, 8192, 640, 0), (40, 8192, 10240, 64),
+    # groups, four waves; wide with eight waves on grids below one
+    # workgroup per CU) and the register form at other block counts
+    (24, 8192, 1152, 7), (64, 8192, 640, 0), (40, 8192, 10240, 64), (57, 8192, 12288, 5),
     (20, 1024, 24576, 1), (48, 2048, 1024, 16),
 ])
 def test_edge_shapes(torch, M, K, N, nb8):

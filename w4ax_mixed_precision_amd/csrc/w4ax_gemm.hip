@@ -944,6 +944,11 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
     // two LDS objects: the compiler can then tell ring reads from other LDS
     // accesses and waits only for the direct loads a read depends on (with
     // one object it waits for every outstanding load before each read)
+    // the wait before block i counts the loads issued after block i's aux
+    // loads, so block i's fragments must have gone out before them
+    static_assert(kRR > kRA, "the fragments of a block are issued before its aux loads");
+    // at most 63 loads may be outstanding behind a wait
+    static_assert(lds_g_loads_after<MR, G, kRA, kRR, kAsym>(0, NBW) <= 63, "vmcnt range");
     __shared__ float red[kSplit][MR * 4][64];
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kSplit][kRR * G][kFragBytes];
     const int lane = threadIdx.x & 63;
@@ -1096,16 +1101,22 @@ int launch_stream_g(const GemmProblem& p, hipStream_t st) {
     return launch_stream_g_cfg<MR, 2, 8, kAsym, kDump>(p, st);
 }
 
-// LDS-ring multi-group kernel, 64 blocks. Two configurations, chosen by
+// LDS-ring multi-group kernel, 64 blocks. Three configurations, chosen by
 // measurement on the LLaMA-70B decode shapes (K = 8192; N = 8192, 10240,
 // 28672; M = 17 .. 64):
 //   wide:   G = 4, four waves of 16 blocks, 4-block ring (64 KB, plus 16 KB
 //           for the reduction: two workgroups per CU);
 //   narrow: G = 2, eight waves of 8 blocks, 4-block ring (64 KB + 32 KB).
+//   wide8:  G = 4, eight waves of 8 blocks, 3-block ring (96 KB + up to
+//           32 KB), one workgroup per CU.
 // The wide form reads each activation word for twice the channels and is
 // faster when it still yields about 1.5 workgroups per CU (N >= 24576), and
 // at M > 32 from 160 workgroups on (N = 10240, M = 64: 23 against 26 us); the
-// narrow one has twice the waves and wins on the smaller grids.
+// narrow one has twice the waves and wins on the smaller grids. A wide grid
+// of fewer workgroups than CUs leaves one wave per SIMD on the CUs it uses;
+// there the eight-wave form hides more latency (N = 10240, M = 33 / 48 / 64:
+// 16.8 / 17.3 / 19.9 against 18.9 / 19.2 / 22.4 us), while on grids of more
+// workgroups than CUs it is slower (N = 28672, M = 64: 41.9 against 37.3 us).
 template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st) {
     const int units = p.N / (16 * G);
@@ -1118,6 +1129,7 @@ template <int MR, bool kAsym, bool kDump>
 int launch_stream_lds_g(const GemmProblem& p, hipStream_t st) {
     const int wide_units = p.N / 64;
     const bool wide = wide_units >= 384 || (p.M > 32 && wide_units >= 160);
+    if (wide && wide_units < 256) return launch_stream_lds_g_cfg<MR, 4, 8, 3, 2, kAsym, kDump>(p, st);
     if (wide) return launch_stream_lds_g_cfg<MR, 4, 4, 4, 2, kAsym, kDump>(p, st);
     return launch_stream_lds_g_cfg<MR, 2, 8, 4, 2, kAsym, kDump>(p, st);
 }
