@@ -131,7 +131,13 @@ ATT_CASES = [  # Hq, group, d, T
     # enough heads for 512- and 1024-token chunks, each with a ragged last chunk
     (1024, 1, 64, 700), (2048, 1, 128, 1500), (2048, 2, 64, 2100), (4096, 4, 32, 1100),
     # two query heads per workgroup at every lane-slice width the launcher picks
-    (8, 2, 16, 300), (8, 2, 8, 257), (4, 2, 256, 300), (4, 2, 512, 70)]
+    (8, 2, 16, 300), (8, 2, 8, 257), (4, 2, 256, 300), (4, 2, 512, 70),
+    # the matrix-instruction kernel (d = 128, groups of 2 to 16): 8- and
+    # 16-row query tiles, groups that are not powers of two, one token,
+    # partial score tiles and value steps, 512-token chunks with one token in
+    # the last
+    (16, 16, 128, 300), (12, 12, 128, 33), (24, 3, 128, 1), (10, 5, 128, 257), (64, 8, 128, 1000),
+    (4096, 2, 128, 513)]
 
 
 @pytest.mark.parametrize("Hq,group,d,T", ATT_CASES)

@@ -25,6 +25,9 @@
 // the G queries) and one multiply-add per query. The chunk keeps its own
 // maximum and sum, and a second kernel combines the chunks (the split-softmax
 // identity: out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c).
+// Grouped-query heads at d = 128 take a matrix-instruction form instead
+// (kv4_attn_mfma_kernel below), which converts each code once for all the
+// query heads of its kv head.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -36,6 +39,10 @@ namespace {
 
 constexpr int kKvThreads = 256;   // 4 waves
 constexpr int kKvChunkMax = 1024; // cached tokens per attention workgroup, at most
+// Smallest query-head group on the matrix-instruction kernel: with one query
+// head per kv head the 16-row tile is 15/16 empty and the vector kernel is
+// faster (LLaMA-7B multi-head decode shape: 94-98 against 78-82 us).
+constexpr int kKvMfmaMinGroup = 2;
 
 
 __device__ __forceinline__ void unpack8(uint4 p, float* x) {
@@ -426,21 +433,355 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     }
 }
 
+// kBase2: the chunk maxima are in base-2 units (the matrix-instruction kernel).
+// One workgroup per query head: the weights e^(m_c - M) of its chunks go to
+// LDS 128 at a time (M and the sum L over all chunks first, by a workgroup
+// reduction), then every thread adds its channels' partial outputs in chunk
+// order.
+template <bool kBase2>
 __global__ __launch_bounds__(128) void kv4_attn_combine_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ ml, int nsplit, int d,
                                                               uint16_t* __restrict__ out) {
+    __shared__ float fs[128];
+    __shared__ float red2[2];
     const int h = blockIdx.x;
+    const int tid = threadIdx.x;
     const float* mh = ml + static_cast<size_t>(h) * nsplit * 2;
+    auto ex = [](float x) { return kBase2 ? exp2f(x) : expf(x); };
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mh[2 * s]);
+    for (int s = tid; s < nsplit; s += 128) M = fmaxf(M, mh[2 * s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if ((tid & 63) == 0) red2[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red2[0], red2[1]);
+    __syncthreads();
     float L = 0.0f;
-    for (int s = 0; s < nsplit; ++s) L += expf(mh[2 * s] - M) * mh[2 * s + 1];
-    const float invL = 1.0f / L;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    for (int s = tid; s < nsplit; s += 128) L += ex(mh[2 * s] - M) * mh[2 * s + 1];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    if ((tid & 63) == 0) red2[tid >> 6] = L;
+    __syncthreads();
+    const float invL = 1.0f / (red2[0] + red2[1]);
+    const float* ph = part + static_cast<size_t>(h) * nsplit * d;
+    for (int i0 = 0; i0 < d; i0 += 128) {
+        const int i = i0 + tid;
         float a = 0.0f;
-        for (int s = 0; s < nsplit; ++s)
-            a += expf(mh[2 * s] - M) * part[(static_cast<size_t>(h) * nsplit + s) * d + i];
-        out[static_cast<size_t>(h) * d + i] = __half_as_ushort(__float2half_rn(a * invL));
+        for (int s0 = 0; s0 < nsplit; s0 += 128) {
+            const int n = imin(128, nsplit - s0);
+            __syncthreads();                 // the previous batch is read
+            if (tid < n) fs[tid] = ex(mh[2 * (s0 + tid)] - M);
+            __syncthreads();
+            if (i < d) {
+                int s = 0;
+                for (; s + 4 <= n; s += 4) {
+                    const float p0 = ph[static_cast<size_t>(s0 + s) * d + i];
+                    const float p1 = ph[static_cast<size_t>(s0 + s + 1) * d + i];
+                    const float p2 = ph[static_cast<size_t>(s0 + s + 2) * d + i];
+                    const float p3 = ph[static_cast<size_t>(s0 + s + 3) * d + i];
+                    a += fs[s] * p0;
+                    a += fs[s + 1] * p1;
+                    a += fs[s + 2] * p2;
+                    a += fs[s + 3] * p3;
+                }
+                for (; s < n; ++s) a += fs[s] * ph[static_cast<size_t>(s0 + s) * d + i];
+            }
+        }
+        if (i < d) out[static_cast<size_t>(h) * d + i] = __half_as_ushort(__float2half_rn(a * invL));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped-query heads on the matrix unit (d = 128). The vector-unit kernel
+// above converts each code once per workgroup and then spends one
+// multiply-add per code and query head; with 8 query heads per kv head that
+// is most of its time. Here one workgroup takes a kv head, all of its query
+// heads (up to GQ, the rows of a 16 x 16 tile past the group held at zero) and
+// a chunk of CH tokens, and both products run as 16x16x32 fp16 matrix
+// instructions:
+//   scores  S[h][t] = s_t sum_c q_hc (u_tc - z_t) / sqrt(d): A = the queries,
+//           B = the codes of 16 tokens;
+//   values  acc[h][c] = sum_t w_ht (u_tc - z_t), w_ht = p_ht s_t: A = w as two
+//           fp16 parts (w = hi + lo to about 2^-22, after scaling by a power of
+//           two that puts the chunk's largest step near 2^14, so no weight
+//           underflows), B = the codes of 32 tokens.
+// Every operand value is exact: q is fp16, u - z an integer in [-15, 15]. A
+// code becomes fp16 u - z in about 1.4 operations: one byte permute places
+// it under the fp16 exponent of 1024 (0x64NN = 1024 + NN), one packed fp16
+// add (two codes) subtracts 1024 + z exactly. The k index of a lane's 8
+// operand values is a fixed permutation of the channels (scores) or the 8
+// consecutive tokens (values), the same for A and B. For the values, output
+// column n of tile j is channel 8 n + j, so a lane reads one 32-bit word (8
+// channels) per token and the cache needs no transpose.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kBias64 = 0x64646464u;   // fp16 bits 0x64NN = 1024 + NN for NN < 1024
+
+// (a + b) on packed fp16 pairs: (1024 + u) - (1024 + z), exact.
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
+    const v2h r = __builtin_bit_cast(v2h, a) + __builtin_bit_cast(v2h, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// fp16 bits of -(1024 + z) in both halves.
+__device__ __forceinline__ uint32_t neg_bias(int z) { return static_cast<uint32_t>(0xE400 + z) * 0x00010001u; }
+__device__ __forceinline__ uint32_t neg_bias2(int z0, int z1) {
+    return static_cast<uint32_t>(0xE400 + z0) | (static_cast<uint32_t>(0xE400 + z1) << 16);
+}
+__device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(v8h, v4u{a, b, c, d});
+}
+
+// Maximum and sum over the 16 lanes of a row of the wave (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, xor_get<1>(v));
+    v = fmaxf(v, xor_get<2>(v));
+    v = fmaxf(v, xor_get<4>(v));
+    return fmaxf(v, xor_get<8>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v = xor_add<1>(v);
+    v = xor_add<2>(v);
+    v = xor_add<4>(v);
+    return xor_add<8>(v);
+}
+
+template <int GQ, int CH>
+__global__ __launch_bounds__(kKvThreads) void kv4_attn_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
+    const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
+    const uint8_t* __restrict__ vz, int group, int T, int tcap, float scale, int nsplit,
+    float* __restrict__ part, float* __restrict__ ml) {
+    constexpr int D = 128;         // head dimension
+    constexpr int RB = D / 2;      // bytes per cached vector
+    constexpr int TW = CH / 64;    // 16-token score tiles per wave
+    constexpr int SW = CH / 128;   // 32-token value steps per wave
+    static_assert(CH % kKvThreads == 0 && (GQ == 8 || GQ == 16), "chunk and query tile");
+    __shared__ __attribute__((aligned(16))) _Float16 whi[GQ][CH];   // value weights, two fp16 parts
+    __shared__ __attribute__((aligned(16))) _Float16 wlo[GQ][CH];
+    __shared__ __attribute__((aligned(16))) float vst[CH];
+    __shared__ __attribute__((aligned(16))) uint8_t vzt[CH];
+    __shared__ __attribute__((aligned(16))) float red[4][GQ][D];
+    __shared__ float wmax[4][16], wsum[4][16], wsmax[4];
+    const int s = blockIdx.x % nsplit;
+    const int hk = blockIdx.x / nsplit;
+    const int h0 = hk * group;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int t0 = s * CH;
+    const int nt = imin(CH, T - t0);                    // >= 1
+    const size_t base = static_cast<size_t>(hk) * tcap + t0;
+    // buffer resources over the chunk's nt tokens: loads past them read 0
+    const Rsrc rkc = make_rsrc(kc + base * RB, static_cast<uint32_t>(nt) * RB);
+    const Rsrc rks = make_rsrc(ks + base, static_cast<uint32_t>(nt) * 2u);
+    const Rsrc rkz = make_rsrc(kz + base, static_cast<uint32_t>(nt));
+    const Rsrc rvc = make_rsrc(vc + base * RB, static_cast<uint32_t>(nt) * RB);
+    const Rsrc rvs = make_rsrc(vs + base, static_cast<uint32_t>(nt) * 2u);
+    const Rsrc rvz = make_rsrc(vz + base, static_cast<uint32_t>(nt));
+
+    // key slices of the wave's score tiles, then value steps and zero points
+    // to LDS (their largest step by wave)
+    uint4 kw[TW];
+    float kst[TW];
+    int kzt[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const uint32_t t = static_cast<uint32_t>((wave + 4 * i) * 16 + col);
+        kw[i] = buf_load16(rkc, t * RB + 16u * g);
+        kst[i] = h2f(__builtin_amdgcn_raw_buffer_load_b16(rks, 2u * t, 0, 0));
+        kzt[i] = __builtin_amdgcn_raw_buffer_load_b8(rkz, t, 0, 0);
+    }
+    float smx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CH / kKvThreads; ++k) {
+        const uint32_t i = threadIdx.x + k * kKvThreads;
+        const float st = h2f(__builtin_amdgcn_raw_buffer_load_b16(rvs, 2u * i, 0, 0));
+        vst[i] = st;
+        vzt[i] = __builtin_amdgcn_raw_buffer_load_b8(rvz, i, 0, 0);
+        smx = fmaxf(smx, st);
+    }
+
+    // queries as A operands: row col (query head h0 + col; zero past the
+    // group), step kk: channels 32 g + 8 kk + {0, 2, 4, 6, 1, 3, 5, 7}
+    v8h qa[4];
+    {
+        const bool real = col < group;
+        const uint16_t* qr = q + static_cast<size_t>(h0 + (real ? col : 0)) * D + 32 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint4 v = real ? *reinterpret_cast<const uint4*>(qr + 8 * kk) : uint4{0u, 0u, 0u, 0u};
+            qa[kk] = as_v8h(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                            __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+        }
+    }
+
+    // scores: lane (col, g) holds token col of the tile, channels 32 g + 8 kk
+    // + {0, 2, 4, 6, 1, 3, 5, 7} of step kk (word kk of its 16-byte slice);
+    // the result holds query 4 g + r, token col. Kept in registers (-inf
+    // outside the chunk and the group).
+    float sr[TW][4];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int tile = wave + 4 * i;
+        const uint32_t nz = neg_bias(kzt[i]);
+        const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (tile * 16 < nt) {                            // uniform in the wave
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t x = w4[kk] & 0x0F0F0F0Fu, y = (w4[kk] >> 4) & 0x0F0F0F0Fu;
+                const v8h b = as_v8h(pk_add_f16(__builtin_amdgcn_perm(kBias64, x, 0x04010400u), nz),
+                                     pk_add_f16(__builtin_amdgcn_perm(kBias64, x, 0x04030402u), nz),
+                                     pk_add_f16(__builtin_amdgcn_perm(kBias64, y, 0x04010400u), nz),
+                                     pk_add_f16(__builtin_amdgcn_perm(kBias64, y, 0x04030402u), nz));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, acc, 0, 0, 0);
+            }
+        }
+        const bool tin = tile * 16 + col < nt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sr[i][r] = (tin && 4 * g + r < group) ? kst[i] * acc[r] * scale : -INFINITY;
+    }
+
+    // value words of the wave's steps: lane (col, g) reads word col (channels
+    // 8 col .. 8 col + 7) of tokens 8 g + e; issued here, they arrive under
+    // the softmax
+    uint32_t vw[SW][8];
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t t = static_cast<uint32_t>((wave + 4 * i) * 32 + 8 * g + e);
+            vw[i][e] = __builtin_amdgcn_raw_buffer_load_b32(rvc, t * RB + 4u * col, 0, 0);
+        }
+
+    // softmax of the chunk (scores in base-2 units: `scale` holds log2(e) /
+    // sqrt(d)): row maxima by wave, then over the waves
+    float mr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = sr[0][r];
+#pragma unroll
+        for (int i = 1; i < TW; ++i) v = fmaxf(v, sr[i][r]);
+        mr[r] = row16_max(v);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) smx = fmaxf(smx, __shfl_xor(smx, o));
+    if (col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wmax[wave][4 * g + r] = mr[r];
+    }
+    if (lane == 0) wsmax[wave] = smx;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * g + r;
+        mr[r] = fmaxf(fmaxf(wmax[0][h], wmax[1][h]), fmaxf(wmax[2][h], wmax[3][h]));
+    }
+    const float smax = fmaxf(fmaxf(wsmax[0], wsmax[1]), fmaxf(wsmax[2], wsmax[3]));
+    int ex = 0;
+    if (smax > 0.0f) frexpf(smax, &ex);
+    const int k2 = 14 - ex;                              // w 2^k2 < 2^14: p <= 1, s < 2^ex
+    // p = 2^(score - max) (scores are in base-2 units), and the value weight
+    // w = p s 2^k2 as two fp16 parts, once per (query, token); zero past the
+    // chunk and the group
+    float lr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (4 * g < GQ) {
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int t = (wave + 4 * i) * 16 + col;
+            const float sv = ldexpf(vst[t], k2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool in = t < nt && 4 * g + r < group;
+                const float p = in ? exp2f(sr[i][r] - mr[r]) : 0.0f;
+                lr[r] += p;
+                const float w = p * sv;
+                const _Float16 h = static_cast<_Float16>(w);
+                whi[4 * g + r][t] = h;
+                wlo[4 * g + r][t] = static_cast<_Float16>(w - static_cast<float>(h));
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lr[r] = row16_sum(lr[r]);
+    if (col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wsum[wave][4 * g + r] = lr[r];
+    }
+    __syncthreads();
+
+    // values: lane (col, g) holds tokens 8 g + e of the step (k index e) and
+    // channels 8 col + j (column col of tile j)
+    v4f acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < SW; ++i) {
+        const int tb = (wave + 4 * i) * 32;
+        if (tb >= nt) break;                             // uniform in the wave
+        const int t8 = tb + 8 * g;
+        // A: the weights of query col for tokens t8 .. t8 + 7 (rows past
+        // GQ are zero)
+        v8h ahi = {}, alo = {};
+        if (col < GQ) {
+            ahi = *reinterpret_cast<const v8h*>(&whi[col < GQ ? col : 0][t8]);
+            alo = *reinterpret_cast<const v8h*>(&wlo[col < GQ ? col : 0][t8]);
+        }
+        const uint2 zz = *reinterpret_cast<const uint2*>(&vzt[t8]);
+        uint32_t nz[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t zw = p < 2 ? zz.x : zz.y;
+            const int sh = 16 * (p & 1);
+            nz[p] = neg_bias2(static_cast<int>((zw >> sh) & 0xFFu), static_cast<int>((zw >> (sh + 8)) & 0xFFu));
+        }
+        // token pairs (2p, 2p + 1) interleaved by byte: il[p][0] = low
+        // nibbles of bytes 0-1, il[p][1] of bytes 2-3, il[p][2..3] the high nibbles
+        uint32_t il[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t xa = vw[i][2 * p] & 0x0F0F0F0Fu, xb = vw[i][2 * p + 1] & 0x0F0F0F0Fu;
+            const uint32_t ya = (vw[i][2 * p] >> 4) & 0x0F0F0F0Fu, yb = (vw[i][2 * p + 1] >> 4) & 0x0F0F0F0Fu;
+            il[p][0] = __builtin_amdgcn_perm(xb, xa, 0x05010400u);
+            il[p][1] = __builtin_amdgcn_perm(xb, xa, 0x07030602u);
+            il[p][2] = __builtin_amdgcn_perm(yb, ya, 0x05010400u);
+            il[p][3] = __builtin_amdgcn_perm(yb, ya, 0x07030602u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // channel 8 col + j: nibble j of the word, i.e. byte j / 2, low
+            // nibble for even j; bytes 0-1 in il[.][0 | 2], 2-3 in il[.][1 | 3]
+            const int src = (j & 1 ? 2 : 0) + (j >= 4 ? 1 : 0);
+            const uint32_t sel = (j >> 1) & 1 ? 0x04030402u : 0x04010400u;
+            const v8h b = as_v8h(pk_add_f16(__builtin_amdgcn_perm(kBias64, il[0][src], sel), nz[0]),
+                                 pk_add_f16(__builtin_amdgcn_perm(kBias64, il[1][src], sel), nz[1]),
+                                 pk_add_f16(__builtin_amdgcn_perm(kBias64, il[2][src], sel), nz[2]),
+                                 pk_add_f16(__builtin_amdgcn_perm(kBias64, il[3][src], sel), nz[3]));
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, b, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, b, acc[j], 0, 0, 0);
+        }
+    }
+    // the waves' sums in a fixed order ((w0 + w1) + w2) + w3; result: query
+    // 4 g + r, channel 8 col + j
+    if (4 * g < GQ) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][4 * g + r][8 * col + j] = acc[j][r];
+    }
+    __syncthreads();
+    const float unscale = ldexpf(1.0f, -k2);
+    for (int i = threadIdx.x; i < group * D; i += kKvThreads) {
+        const int h = i / D, c = i - h * D;
+        part[(static_cast<size_t>(h0 + h) * nsplit + s) * D + c] =
+            (((red[0][h][c] + red[1][h][c]) + red[2][h][c]) + red[3][h][c]) * unscale;
+    }
+    if (threadIdx.x < group) {
+        const int h = threadIdx.x;
+        const size_t row = static_cast<size_t>(h0 + h) * nsplit + s;
+        ml[2 * row] = fmaxf(fmaxf(wmax[0][h], wmax[1][h]), fmaxf(wmax[2][h], wmax[3][h]));
+        ml[2 * row + 1] = ((wsum[0][h] + wsum[1][h]) + wsum[2][h]) + wsum[3][h];
     }
 }
 
@@ -461,17 +802,43 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
                          const uint8_t* vc, const uint16_t* vs, const uint8_t* vz, int Hq, int group, int d, int T,
                          int tcap, uint16_t* out, float* workspace, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    // Tokens per workgroup: 256, or 512 / 1024 when the grid still has 2048
-    // workgroups (8 per CU), to spread the fixed cost of a chunk (the
-    // softmax reductions, the cross-lane sums, the partial outputs) over more
-    // tokens. Never more splits than kv4_splits(T), which sizes the workspace.
-    // Query heads per workgroup: two when the group allows. The kernel is
-    // bound by the vector unit per (query head, code), so sharing the code
-    // conversion between two queries pays, while more queries per workgroup
-    // need narrower code slices per lane (registers) and more cross-lane sums
-    // per score than they save (measured on the LLaMA-70B grouped-query
-    // shape: 101.6 us with two, 137.0 with four, 160.7 with eight, 119.5 with
-    // one).
+    // Grouped-query heads at d = 128: the matrix-instruction kernel, one
+    // workgroup per (kv head, chunk) for all the group's query heads; chunks
+    // of 512 tokens while that still gives 1024 workgroups (four per CU, one
+    // round), else 256 (LLaMA-70B grouped-query shape: 28.5 us with 512,
+    // 30.6 with 256, 31 with 1024; its value loads issued with the key loads
+    // instead of after the scores: 31-34 us). Never more splits than
+    // kv4_splits(T), which sizes the workspace.
+    const int Hk = Hq / group;
+    if (d == 128 && group >= kKvMfmaMinGroup && group <= 16 && static_cast<int64_t>(tcap) * 64 < (1ll << 31)) {
+        const int ch = static_cast<int64_t>(Hk) * ((T + 511) / 512) >= 1024 ? 512 : 256;
+        const int ns = (T + ch - 1) / ch;
+        float* pt = workspace;
+        float* mlp = workspace + static_cast<size_t>(Hq) * ns * d;
+        const float sc = 1.4426950408889634f / sqrtf(static_cast<float>(d));   // log2(e) / sqrt(d)
+        const int grid = Hk * ns;
+        if (group <= 8) {
+            if (ch == 512) kv4_attn_mfma_kernel<8, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+            else kv4_attn_mfma_kernel<8, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+        } else {
+            if (ch == 512) kv4_attn_mfma_kernel<16, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+            else kv4_attn_mfma_kernel<16, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+        }
+        const int e = static_cast<int>(hipGetLastError());
+        if (e != 0) return e;
+        kv4_attn_combine_kernel<true><<<Hq, 128, 0, st>>>(pt, mlp, ns, d, out);
+        return static_cast<int>(hipGetLastError());
+    }
+    // The vector kernel. Tokens per workgroup: 256, or 512 / 1024 when the
+    // grid still has 2048 workgroups (8 per CU), to spread the fixed cost of
+    // a chunk (the softmax reductions, the cross-lane sums, the partial
+    // outputs) over more tokens. Query heads per workgroup: two when the
+    // group allows. The kernel is bound by the vector unit per (query head,
+    // code), so sharing the code conversion between two queries pays, while
+    // more queries per workgroup need narrower code slices per lane
+    // (registers) and more cross-lane sums per score than they save
+    // (measured on the LLaMA-70B grouped-query shape: 101.6 us with two,
+    // 137.0 with four, 160.7 with eight, 119.5 with one).
     const int G = group % 2 == 0 ? 2 : 1;
     int chunk = kKvChunkMax;
     while (chunk > kKvChunk && static_cast<int64_t>(Hq / G) * ((T + chunk - 1) / chunk) < 2048) chunk >>= 1;
@@ -498,7 +865,7 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
 #undef COMET_KV4_CHUNK
     const int e = static_cast<int>(hipGetLastError());
     if (e != 0) return e;
-    kv4_attn_combine_kernel<<<Hq, 128, 0, st>>>(part, ml, nsplit, d, out);
+    kv4_attn_combine_kernel<false><<<Hq, 128, 0, st>>>(part, ml, nsplit, d, out);
     return static_cast<int>(hipGetLastError());
 }
 
