@@ -455,6 +455,77 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * QUIK's fp16 outlier columns on the FP6 layout (QUIK blog,
+ * deep-paper.org/paper/2310.09259, section "第一步: 识别与重排": the outlier
+ * columns, found offline from calibration, are moved to the end of W; section
+ * "第二步: 前向传播 (在线)": the activations split into a quantized part and
+ * the fp16 outlier part, each multiplied on its own path, and the results are
+ * added). With the channel order of comet_pack_weights (ascending score), the
+ * last n_fp16 channels (the highest scores) keep their fp16 values in X and
+ * W; the first K - n_fp16 are the quantized channels of the three calls
+ * above (their last nb8 blocks 8-bit). Then
+ *   y = (the FP32 block sum of comet_w4ax_gemm over the quantized channels)
+ *       + sum over the fp16 channels j of x_j * w_j     in FP32
+ * (a product of two fp16 values is exact in FP32), Y = fp16(y). The two
+ * parts are summed in the same FP32 accumulators inside the GEMM kernel.
+ * n_fp16 is a multiple of 128 with K - n_fp16 >= 128 (0 gives the plain
+ * FP6 path).
+ *
+ * Fp16 operand layouts (fp16 bits, 1 KB pieces = 16 rows or output channels
+ * x 32 channels, the operand order of the 16x16x32 fp16 matrix instruction):
+ *   Xf  [Mp/16][n_fp16/32] tiles (Mp = M rounded up to 16): tile (t, s) at
+ *       half (t * (n_fp16/32) + s) * 512; half 8l + e (l in 0..63, e in 0..7)
+ *       is row 16t + (l mod 16), outlier channel 32s + 8(l/16) + e; rows
+ *       past M are zero. comet_xf_bytes(M, n_fp16) bytes.
+ *   Wf  [N/16][n_fp16/32] fragments: fragment (c, s) at half
+ *       (c * (n_fp16/32) + s) * 512; half 8l + e is output channel
+ *       16c + (l mod 16), outlier channel 32s + 8(l/16) + e. N * n_fp16 * 2
+ *       bytes.
+ * Outlier channel j is original channel perm[K - n_fp16 + j].
+ */
+
+/*
+ * Offline, host memory: channel order, quantized pack of the first K - n_fp16
+ * permuted channels (exactly comet_pack_weights' Wq, w_scale and w_sum for
+ * them; repack Wq to the FP6 layout with comet_repack_weights_fp6(Wq, N,
+ * K - n_fp16, nb8)) and the fp16 fragments of the rest.
+ *   perm        out  int32 [K]
+ *   Wq_packed   out  N*(K - n_fp16)/2 bytes;  w_scale_fp16, w_sum  out  [(K - n_fp16)/128][N]
+ *   Wf_fp16     out  N * n_fp16 halves, layout above (may be NULL if n_fp16 = 0)
+ * Errors: NULL, SHAPE (N < 1, K % 128 != 0), UNSUPPORTED (N % 128 != 0),
+ * ARG (n_fp16 not a multiple of 128 or above K - 128; non-finite score or weight).
+ */
+int comet_pack_weights_quik(const uint16_t* W_fp16, int N, int K, const float* chan_score, int n_fp16,
+                            int32_t* perm, uint8_t* Wq_packed, uint16_t* w_scale_fp16, int16_t* w_sum,
+                            uint16_t* Wf_fp16);
+
+/* Bytes of Xf for M rows (0 for an invalid argument). */
+size_t comet_xf_bytes(int M, int n_fp16);
+
+/*
+ * Online: comet_quant_act_fp6 over the quantized channels perm[0 .. K - n_fp16)
+ * (Xq_fp6 and x_scale of K - n_fp16 channels), and Xf, the fp16 values of the
+ * outlier channels perm[K - n_fp16 .. K).
+ * Errors: NULL, SHAPE (M < 1, K % 128 != 0, ldx < K), ARG (n_fp16 or nb8
+ * range), ALIGN, HIP.
+ */
+int comet_quant_act_quik_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t* perm, int n_int8_blocks,
+                             int n_fp16, void* Xq_fp6, float* x_scale, void* Xf_fp16, void* stream);
+
+/*
+ * Online: Y of the QUIK split (above) from the FP6-layout quantized operands
+ * (K - n_fp16 channels) and the fp16 outlier operands. K is the full channel
+ * count. workspace as comet_w4ax_gemm_fp6 with K - n_fp16 channels
+ * (comet_w4ax_gemm_fp6_workspace_bytes(M, N, K - n_fp16, nb8) bytes).
+ * Errors: NULL, SHAPE, ARG (n_fp16 or nb8 range), ALIGN, WORKSPACE,
+ * UNSUPPORTED (as comet_w4ax_gemm_fp6, or Xf / Wf of 2 GB or more), HIP.
+ */
+int comet_w4ax_gemm_quik_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                             const uint16_t* w_scale_fp16, int n_int8_blocks, const void* Xf_fp16,
+                             const void* Wf_fp16, int n_fp16, int M, int N, int K, void* Y_fp16, int ldy,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * RMS normalization fused into the activation quantizer. QoQ/QServe article
  * (youleyou.com/wenzhang/3078652.html), section "运行时设计": the activation
  * quantization of the QKV projection and of the first FFN layer is fused into

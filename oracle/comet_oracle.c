@@ -64,6 +64,18 @@
  *     the cached tokens and the weighted sum of the values, on the
  *     dequantized vectors s (u - z).
  *
+ * 10. QUIK's FP16 outlier columns (QUIK blog, section "第一步: 识别与重排":
+ *     the outlier columns, chosen offline from calibration, go to the end of
+ *     W; section "第二步: 前向传播 (在线)": the activations split into a
+ *     quantized part and the FP16 outlier part, the two are multiplied on
+ *     their own paths and the results are added). The last nf channels of
+ *     the permuted order (step 1's ascending-score order, so the
+ *     highest-scoring ones) keep their fp16 values in both X and W; the first
+ *     K - nf channels go through steps 2-5 (their last nb8 blocks 8-bit).
+ *     y = (step 5's FP32 sum over the blocks) + the FP32 sum of the fp16
+ *     products x_j w_j in channel order; a product of two fp16 values is
+ *     exact in FP32. Y = fp16(y).
+ *
  *  6. RMS normalization before the quantizer (the next step the quantization
  *     fuses into). QoQ/QServe article, section "运行时设计": the activation
  *     quantization of the QKV projection and of the first FFN layer is fused
@@ -1062,4 +1074,38 @@ int orc_kv4_attention(const uint16_t *q, const uint8_t *uk, const uint16_t *sk, 
         free(a);
     }
     return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 10. QUIK's FP16 outlier columns                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Add the FP16 outlier part to step 5's results for `rows` rows: Xf [rows][nf]
+ * and Wf [N][nf] hold the fp16 bits of the last nf permuted channels; y32 and
+ * yexact come from orc_epilogue over the quantized channels and are updated in
+ * place (y32 in channel order, one FP32 addition per channel of the exact
+ * product), Y16 = fp16(y32). */
+int orc_quik_outlier_add(const uint16_t *Xf, const uint16_t *Wf, int rows, int N, int nf, float *y32,
+                         uint16_t *Y16, double *yexact)
+{
+    if (rows <= 0 || N <= 0 || nf < 0)
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        for (int n = 0; n < N; ++n) {
+            size_t o = (size_t)r * N + n;
+            float y = y32[o];
+            double ye = yexact[o];
+            for (int j = 0; j < nf; ++j) {
+                float x = orc_half_to_float(Xf[(size_t)r * nf + j]);
+                float w = orc_half_to_float(Wf[(size_t)n * nf + j]);
+                y = y + x * w;
+                ye += (double)x * (double)w;
+            }
+            y32[o] = y;
+            yexact[o] = ye;
+            if (Y16) Y16[o] = orc_float_to_half(y);
+        }
+    }
+    return ORC_OK;
 }

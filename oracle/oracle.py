@@ -363,6 +363,64 @@ def reference(X16, W16, score, nb8, rows=None):
 
 
 # ----------------------------------------------------------------------------
+# Step 10: QUIK's FP16 outlier columns
+# ----------------------------------------------------------------------------
+
+def quik_split(score: np.ndarray, nb8: int, nf: int):
+    """(perm [K], flags [nb'] of the K' = K - nf quantized channels): step 1's
+    order over all K; the last nf positions stay fp16, the last nb8 blocks of
+    the first K' are 8-bit."""
+    K = int(score.shape[0])
+    assert nf % 128 == 0 and 0 <= nf < K
+    perm, _ = channel_order(score, 0)
+    kq = K - nf
+    flags = np.zeros(kq // 128, np.uint8)
+    if nb8:
+        flags[-nb8:] = 1
+    return perm, flags
+
+
+def quik_outlier_add(Xf16, Wf16, y32, yexact):
+    """Step 10's merge, in place on copies: (y32, Y16, yexact) with the fp16
+    outlier part added to step 5's results."""
+    Xf = np.ascontiguousarray(Xf16, dtype=np.uint16)
+    Wf = np.ascontiguousarray(Wf16, dtype=np.uint16)
+    y = np.array(y32, dtype=np.float32, copy=True)
+    ye = np.array(yexact, dtype=np.float64, copy=True)
+    rows, N = y.shape
+    nf = Xf.shape[1]
+    assert Xf.shape == (rows, nf) and Wf.shape == (N, nf)
+    Y16 = np.zeros((rows, N), np.uint16)
+    _check(lib().orc_quik_outlier_add(_p(Xf), _p(Wf), rows, N, nf, _p(y), _p(Y16), _p(ye)),
+           "quik_outlier_add")
+    return y, Y16, ye
+
+
+def quik_layer(X16, W16, score, nb8, nf, rows=None):
+    """Every logical array of the QUIK variant and its result for rows
+    (default all): the quantized part over perm[:K - nf] (steps 2-5), Xf / Wf
+    the fp16 columns perm[K - nf:], and the merged y32, Y16, yexact."""
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    M, K = X16.shape
+    perm, flags = quik_split(score, nb8, nf)
+    kq = K - nf
+    pq = np.ascontiguousarray(perm[:kq])
+    pf = perm[kq:]
+    qw, sw16, wsum = quantize_weights(np.ascontiguousarray(W16[:, pq]), np.arange(kq, dtype=np.int32))
+    qa, sa = quantize_activations(np.ascontiguousarray(X16[:, pq]), np.arange(kq, dtype=np.int32), flags)
+    m0, m1 = rows if rows is not None else (0, M)
+    P = block_partials(qa, qw, (m0, m1))
+    y32, _, ye = epilogue(P, sa[m0:m1], sw16)
+    Xf = np.ascontiguousarray(X16[m0:m1][:, pf])
+    Wf = np.ascontiguousarray(W16[:, pf])
+    y32, Y16, ye = quik_outlier_add(Xf, Wf, y32, ye)
+    return {"perm": perm, "flags": flags, "qw": qw, "sw16": sw16, "wsum": wsum, "qa": qa, "sa": sa,
+            "Xf_all": np.ascontiguousarray(X16[:, pf]), "Wf": Wf, "P": P, "y32": y32, "Y16": Y16,
+            "yexact": ye, "rows": (m0, m1)}
+
+
+# ----------------------------------------------------------------------------
 # Step 8: QoQ progressive group quantization (W4A8)
 # ----------------------------------------------------------------------------
 

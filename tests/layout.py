@@ -143,3 +143,19 @@ def unpack_kv4_codes(b: np.ndarray) -> np.ndarray:
     out[..., 0::2] = b & 15
     out[..., 1::2] = b >> 4
     return out
+
+
+def decode_xf(Xf: np.ndarray, M: int, nf: int) -> np.ndarray:
+    """fp16 bits [M, nf] from the QUIK outlier tiles: tile (t, s) at half
+    (t (nf/32) + s) 512, half 8l + e = row 16t + l mod 16, channel 32s + 8(l/16) + e."""
+    steps = nf // 32
+    mp = (M + 15) // 16 * 16
+    h = np.asarray(Xf).view(np.uint16)[: mp * nf].reshape(mp // 16, steps, 4, 16, 8)   # t, s, l/16, l%16, e
+    out = h.transpose(0, 3, 1, 2, 4).reshape(mp, nf)       # row = 16t + l%16, channel = 32s + 8(l/16) + e
+    return out[:M]
+
+
+def decode_wf(Wf: np.ndarray, N: int, nf: int) -> np.ndarray:
+    """fp16 bits [N, nf] from the QUIK outlier weight fragments (same order as
+    decode_xf with output channels for rows)."""
+    return decode_xf(Wf, N, nf)

@@ -374,3 +374,37 @@ def test_kv4_rejections():
     assert L.comet_kv4_attention_workspace_bytes(512, 128, 4096) == 512 * 16 * 130 * 4
     assert L.comet_kv4_attention_workspace_bytes(0, 128, 1) == 0
     assert L.comet_kv4_attention_workspace_bytes(4, 96, 1) == 0
+
+
+def qq(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, nf=128, Xq=A, xs=A, Xf=A):
+    return comet.lib().comet_quant_act_quik_fp6(X, M, K, ldx, perm, nb8, nf, Xq, xs, Xf, None)
+
+
+def gq(Xq=A, xs=A, Wq=A, ws=A, nb8=1, Xf=A, Wf=A, nf=128, M=16, N=512, K=512, Y=A, ldy=512, work=A,
+       wbytes=1 << 40):
+    return comet.lib().comet_w4ax_gemm_quik_fp6(Xq, xs, Wq, ws, nb8, Xf, Wf, nf, M, N, K, Y, ldy, work, wbytes,
+                                                None)
+
+
+def test_quik_rejections():
+    """QUIK's split: n_fp16 a multiple of 128 leaving a quantized block, nb8
+    within the quantized blocks; the fp16 operands required only when
+    n_fp16 > 0; every check before any HIP call."""
+    assert qq(X=None) == NULL and qq(Xf=None) == NULL and qq(M=0) == SHAPE and qq(ldx=500) == SHAPE
+    assert qq(nf=100) == ARG and qq(nf=512) == ARG and qq(nf=-128) == ARG and qq(nb8=4) == ARG
+    assert qq(Xf=MIS) == ALIGN and qq(Xq=MIS) == ALIGN
+    assert gq(Xf=None) == NULL and gq(Wf=None) == NULL and gq(Y=None) == NULL
+    assert gq(nf=64) == ARG and gq(nf=512) == ARG and gq(nb8=4) == ARG and gq(K=500) == SHAPE
+    assert gq(M=0) == SHAPE and gq(ldy=500) == SHAPE and gq(N=200, ldy=200) == UNSUP
+    assert gq(Xf=MIS) == ALIGN and gq(Wf=MIS) == ALIGN and gq(Y=MIS) == ALIGN
+    # the quantized part's workspace is that of the plain FP6 call over K - n_fp16 channels
+    need = comet.lib().comet_w4ax_gemm_fp6_workspace_bytes(128, 4096, 4096 - 256, 4)
+    if need:
+        assert gq(M=128, N=4096, K=4096, nf=256, nb8=4, ldy=4096, wbytes=need - 1) == WORKSPACE
+    L = comet.lib()
+    assert L.comet_xf_bytes(17, 256) == 32 * 256 * 2 and L.comet_xf_bytes(16, 100) == 0
+    p = ctypes.c_void_p(A)
+    assert L.comet_pack_weights_quik(None, 128, 512, p, 128, p, p, p, p, p) == NULL
+    assert L.comet_pack_weights_quik(p, 128, 500, p, 128, p, p, p, p, p) == SHAPE
+    assert L.comet_pack_weights_quik(p, 128, 512, p, 512, p, p, p, p, p) == ARG
+    assert L.comet_pack_weights_quik(p, 100, 512, p, 128, p, p, p, p, p) == UNSUP

@@ -93,3 +93,25 @@ def test_qoq_pack_matches_oracle(name):
     assert np.array_equal((pk["s2z"] & 0xFF).T, s2)
     assert np.array_equal((pk["s2z"] >> 8).T, z)
     assert np.array_equal(decode_wu(pk["Wu"], cfg.N, cfg.K), u)
+
+
+@pytest.mark.parametrize("nb8,nf", [(0, 128), (1, 256), (2, 0)])
+def test_pack_quik_matches_oracle(orc, nb8, nf):
+    """QUIK's split pack: the perm, the quantized part (decoded) and the fp16
+    outlier fragments (decoded) against the oracle's step 10 arrays."""
+    from tests.layout import decode_wf, decode_wq_fp6
+    cfg = synth.CONFIGS["q_proj_7b"]
+    W = synth.make_w(cfg)[:256]
+    score = synth.make_scores(cfg)
+    N, K = W.shape
+    pk = comet.comet_pack_weights_quik(W, score, nb8, nf)
+    perm, flags = orc.quik_split(score, nb8, nf)
+    kq = K - nf
+    qw, sw16, wsum = orc.quantize_weights(np.ascontiguousarray(W[:, perm[:kq]]), np.arange(kq, dtype=np.int32))
+    assert np.array_equal(pk["perm"], perm)
+    assert np.array_equal(pk["w_scale"].T, sw16)
+    assert np.array_equal(pk["w_sum"].T.astype(np.int32), wsum)
+    assert np.array_equal(decode_wq(pk["Wq"], N, kq), qw)
+    assert np.array_equal(decode_wq_fp6(pk["WqF"], N, kq, nb8), qw)
+    if nf:
+        assert np.array_equal(decode_wf(pk["Wf"], N, nf), W[:, perm[kq:]])

@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
     L.comet_w4ax_gemm_fp6_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     L.comet_w4ax_gemm_fp6_workspace_bytes.argtypes = [I, I, I, I]
     L.comet_w4ax_gemm_fp6_workspace_bytes.restype = Z
+    L.comet_pack_weights_quik.argtypes = [P, I, I, P, I, P, P, P, P, P]
+    L.comet_xf_bytes.argtypes = [I, I]
+    L.comet_xf_bytes.restype = Z
+    L.comet_quant_act_quik_fp6.argtypes = [P, I, I, I, P, I, I, P, P, P, P]
+    L.comet_w4ax_gemm_quik_fp6.argtypes = [P, P, P, P, I, P, P, I, I, I, I, P, I, P, Z, P]
     L.comet_quant_act_asym.argtypes = [P, I, I, I, P, I, P, P, P, P]
     L.comet_pack_weights_qoq.argtypes = [P, I, I, P, P, P, P, P]
     L.comet_quant_act_token_i8.argtypes = [P, I, I, I, P, P, P, P]
@@ -92,7 +97,8 @@ def lib() -> ctypes.CDLL:
               "comet_swiglu_quant_act", "comet_swiglu_quant_act_fp6", "comet_swiglu",
               "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
               "comet_pack_weights_qoq", "comet_quant_act_token_i8", "comet_w4a8_qoq_gemm",
-              "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize", "comet_kv4_attention"):
+              "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize", "comet_kv4_attention",
+              "comet_pack_weights_quik", "comet_quant_act_quik_fp6", "comet_w4ax_gemm_quik_fp6"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -108,7 +114,9 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
            "comet_w4ax_gemm_asym_partials", "comet_pack_weights_qoq", "comet_quant_act_token_i8",
            "comet_w4a8_qoq_gemm", "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize",
-           "comet_kv4_attention_workspace_bytes", "comet_kv4_attention", "comet_status_string", "comet_version")
+           "comet_kv4_attention_workspace_bytes", "comet_kv4_attention", "comet_pack_weights_quik",
+           "comet_xf_bytes", "comet_quant_act_quik_fp6", "comet_w4ax_gemm_quik_fp6", "comet_status_string",
+           "comet_version")
 
 
 def _check(call: str, rc: int):
@@ -196,8 +204,36 @@ def upload_weights(packed: dict, device="cuda") -> dict:
         d["Wq"] = torch.from_numpy(packed["Wq"]).to(device)
     if "WqF" in packed:
         d["WqF"] = torch.from_numpy(packed["WqF"]).to(device)
+    if packed.get("nf", 0) > 0:
+        d["Wf"] = torch.from_numpy(packed["Wf"].view(np.int16)).to(device)
     d.update({k: packed[k] for k in ("N", "K", "nb8")})
+    d["nf"] = packed.get("nf", 0)
     return d
+
+
+def comet_pack_weights_quik(W16: np.ndarray, score: np.ndarray, nb8: int, nf: int) -> dict:
+    """QUIK's split (host): perm int32 [K]; the quantized pack of the first
+    K - nf permuted channels (Wq, w_scale, w_sum, and its FP6 repack WqF with
+    nb8 8-bit blocks); Wf uint16 [N * nf], the fp16 outlier fragments."""
+    W16 = np.ascontiguousarray(W16, dtype=np.uint16)
+    score = np.ascontiguousarray(score, dtype=np.float32)
+    N, K = W16.shape
+    if score.shape != (K,):
+        raise ValueError("score must have K entries")
+    kq = K - int(nf)
+    nbq = max(kq // 128, 1)
+    out = {"perm": np.zeros(K, np.int32), "Wq": np.zeros(N * max(kq, 0) // 2, np.uint8),
+           "w_scale": np.zeros((nbq, N), np.uint16), "w_sum": np.zeros((nbq, N), np.int16),
+           "Wf": np.zeros(max(N * int(nf), 1), np.uint16)}
+    rc = lib().comet_pack_weights_quik(_np_ptr(W16), N, K, _np_ptr(score), int(nf), _np_ptr(out["perm"]),
+                                       _np_ptr(out["Wq"]), _np_ptr(out["w_scale"]), _np_ptr(out["w_sum"]),
+                                       _np_ptr(out["Wf"]))
+    _check("comet_pack_weights_quik", rc)
+    WqF = np.zeros(wq_fp6_bytes(N, kq, nb8), np.uint8)
+    _check("comet_repack_weights_fp6",
+           lib().comet_repack_weights_fp6(_np_ptr(out["Wq"]), N, kq, int(nb8), _np_ptr(WqF)))
+    out.update({"WqF": WqF, "N": N, "K": kq, "K_full": K, "nb8": int(nb8), "nf": int(nf)})
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -540,6 +576,47 @@ def comet_w4ax_gemm_fp6(Xq, x_scale, w: dict, M: int, Y=None, workspace=None, st
                                    _dev_ptr(w["w_scale"]), int(nb8), M, N, K, _dev_ptr(Y), Y.stride(0),
                                    None if workspace is None else _dev_ptr(workspace), wsz, _stream(stream))
     _check("comet_w4ax_gemm_fp6", rc)
+    return Y
+
+
+def xf_bytes(M: int, nf: int) -> int:
+    return int(lib().comet_xf_bytes(M, int(nf)))
+
+
+def comet_quant_act_quik_fp6(X, perm, nb8: int, nf: int, stream=None):
+    """QUIK's split of the activations: the FP6-layout codes of the channels
+    perm[:K - nf] and the fp16 outlier tiles of perm[K - nf:].
+    Returns (Xq, x_scale float32 [(K - nf) / 128, M], Xf int16 tiles)."""
+    import torch
+    M, ldx = X.shape
+    K = perm.shape[0]
+    kq = K - int(nf)
+    Xq = torch.empty(xq_fp6_bytes(M, kq, nb8), dtype=torch.uint8, device=X.device)
+    x_scale = torch.empty((kq // 128, M), dtype=torch.float32, device=X.device)
+    Xf = torch.empty(max(xf_bytes(M, nf) // 2, 8), dtype=torch.int16, device=X.device)
+    rc = lib().comet_quant_act_quik_fp6(_dev_ptr(X), M, K, X.stride(0), _dev_ptr(perm), int(nb8), int(nf),
+                                        _dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(Xf), _stream(stream))
+    _check("comet_quant_act_quik_fp6", rc)
+    return Xq, x_scale, Xf
+
+
+def comet_w4ax_gemm_quik_fp6(Xq, x_scale, Xf, w: dict, M: int, Y=None, workspace=None, stream=None):
+    """Y fp16 [M, N] of QUIK's split from comet_quant_act_quik_fp6's outputs and
+    an uploaded comet_pack_weights_quik bundle (w["K"] = K - nf)."""
+    import torch
+    N, kq, nb8, nf = w["N"], w["K"], w["nb8"], w["nf"]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    if workspace is None:
+        workspace = fp6_workspace(M, N, kq, nb8, Xq.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().comet_w4ax_gemm_quik_fp6(_dev_ptr(Xq), _dev_ptr(x_scale), _dev_ptr(w["WqF"]),
+                                        _dev_ptr(w["w_scale"]), int(nb8), _dev_ptr(Xf),
+                                        _dev_ptr(w["Wf"]) if nf else None, int(nf), M, N, kq + int(nf),
+                                        _dev_ptr(Y), Y.stride(0),
+                                        None if workspace is None else _dev_ptr(workspace), wsz,
+                                        _stream(stream))
+    _check("comet_w4ax_gemm_quik_fp6", rc)
     return Y
 
 

@@ -542,6 +542,78 @@ int comet_w4ax_gemm_fp6_partials(const void* Xq_fp6, const float* x_scale, const
     return hip_status(comet::launch_w4ax_gemm_fp6(p, stream));
 }
 
+// QUIK's fp16 outlier channels: n_fp16 a multiple of 128 leaving at least one
+// quantized block, nb8 within the quantized blocks.
+static bool quik_split_ok(int K, int n_fp16, int n_int8_blocks) {
+    return n_fp16 >= 0 && n_fp16 % kBlock == 0 && n_fp16 <= K - kBlock && n_int8_blocks >= 0 &&
+           n_int8_blocks <= (K - n_fp16) / kBlock;
+}
+
+int comet_pack_weights_quik(const uint16_t* W_fp16, int N, int K, const float* chan_score, int n_fp16,
+                            int32_t* perm, uint8_t* Wq_packed, uint16_t* w_scale_fp16, int16_t* w_sum,
+                            uint16_t* Wf_fp16) {
+    if (!W_fp16 || !chan_score || !perm || !Wq_packed || !w_scale_fp16 || !w_sum || (n_fp16 > 0 && !Wf_fp16))
+        return COMET_ERR_NULL;
+    if (N < 1 || K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (!quik_split_ok(K, n_fp16, 0)) return COMET_ERR_ARG;
+    if (N % 128 != 0) return COMET_ERR_UNSUPPORTED;
+    return comet::pack_weights_quik(W_fp16, N, K, chan_score, n_fp16, perm, Wq_packed, w_scale_fp16, w_sum,
+                                    Wf_fp16);
+}
+
+size_t comet_xf_bytes(int M, int n_fp16) {
+    if (M < 1 || n_fp16 < 0 || n_fp16 % kBlock != 0) return 0;
+    return comet::xf_bytes(M, n_fp16);
+}
+
+int comet_quant_act_quik_fp6(const void* X_fp16, int M, int K, int ldx, const int32_t* perm, int n_int8_blocks,
+                             int n_fp16, void* Xq_fp6, float* x_scale, void* Xf_fp16, void* stream) {
+    if (!X_fp16 || !perm || !Xq_fp6 || !x_scale || (n_fp16 > 0 && !Xf_fp16)) return COMET_ERR_NULL;
+    if (M < 1 || K < kBlock || K % kBlock != 0 || ldx < K) return COMET_ERR_SHAPE;
+    if (!quik_split_ok(K, n_fp16, n_int8_blocks)) return COMET_ERR_ARG;
+    if (!aligned16(X_fp16) || !aligned16(perm) || !aligned16(Xq_fp6) || !aligned16(x_scale) ||
+        (n_fp16 > 0 && !aligned16(Xf_fp16)))
+        return COMET_ERR_ALIGN;
+    const int Kq = K - n_fp16;
+    int e = comet::launch_quant_act_fp6(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm, n_int8_blocks,
+                                        static_cast<uint8_t*>(Xq_fp6), x_scale, stream, Kq);
+    if (e != 0 || n_fp16 == 0) return hip_status(e);
+    return hip_status(comet::launch_gather_outliers(static_cast<const uint16_t*>(X_fp16), M, ldx, perm + Kq,
+                                                    n_fp16, static_cast<uint16_t*>(Xf_fp16), stream));
+}
+
+int comet_w4ax_gemm_quik_fp6(const void* Xq_fp6, const float* x_scale, const void* Wq_fp6,
+                             const uint16_t* w_scale_fp16, int n_int8_blocks, const void* Xf_fp16,
+                             const void* Wf_fp16, int n_fp16, int M, int N, int K, void* Y_fp16, int ldy,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!Y_fp16 || (n_fp16 > 0 && (!Xf_fp16 || !Wf_fp16))) return COMET_ERR_NULL;
+    if (K < kBlock || K % kBlock != 0) return COMET_ERR_SHAPE;
+    if (!quik_split_ok(K, n_fp16, n_int8_blocks)) return COMET_ERR_ARG;
+    const int Kq = K - n_fp16;
+    int st = check_fp6_gemm(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, Kq, workspace,
+                            workspace_bytes);
+    if (st != COMET_OK) return st;
+    if (ldy < N) return COMET_ERR_SHAPE;
+    if (static_cast<int64_t>(M) * ldy > std::numeric_limits<int32_t>::max()) return COMET_ERR_UNSUPPORTED;
+    // the fp16 operands are read through 32-bit buffer offsets
+    if (comet::xf_bytes(M, n_fp16) >= (1ull << 31) ||
+        static_cast<uint64_t>(N) * static_cast<uint64_t>(n_fp16) * 2u >= (1ull << 31))
+        return COMET_ERR_UNSUPPORTED;
+    if (!aligned16(Y_fp16) || (n_fp16 > 0 && (!aligned16(Xf_fp16) || !aligned16(Wf_fp16))))
+        return COMET_ERR_ALIGN;
+    comet::GemmProblem p =
+        fp6_problem(Xq_fp6, x_scale, Wq_fp6, w_scale_fp16, n_int8_blocks, M, N, Kq, workspace, workspace_bytes);
+    p.Y = static_cast<uint16_t*>(Y_fp16);
+    p.ldy = ldy;
+    p.P = nullptr;
+    p.m_begin = 0;
+    p.m_count = M;
+    p.xf = static_cast<const uint16_t*>(Xf_fp16);
+    p.wf = static_cast<const uint16_t*>(Wf_fp16);
+    p.nf = n_fp16;
+    return hip_status(comet::launch_w4ax_gemm_fp6(p, stream));
+}
+
 const char* comet_status_string(int status) {
     switch (status) {
         case COMET_OK: return "ok";

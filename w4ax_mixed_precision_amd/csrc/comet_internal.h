@@ -34,8 +34,20 @@ int launch_quant_act(const uint16_t* X, int M, int K, int ldx, const int32_t* pe
 int launch_quant_act_asym(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                           uint8_t* Xq, float* x_scale, uint8_t* x_zero, void* stream);
 
+// kq > 0: quantize only the first kq permuted channels (QUIK's split; the
+// rows are still staged K channels wide, since perm reaches any of them).
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
-                         uint8_t* Xq, float* x_scale, void* stream);
+                         uint8_t* Xq, float* x_scale, void* stream, int kq = 0);
+// QUIK's fp16 outlier channels: Xf tiles (GemmProblem::xf layout) of columns
+// perm_f[0 .. nf) of X, rows past M zero.
+int launch_gather_outliers(const uint16_t* X, int M, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
+                           void* stream);
+
+// Bytes of the QUIK fp16 outlier tiles of M rows.
+inline size_t xf_bytes(int M, int nf) {
+    const size_t mp = (static_cast<size_t>(M) + 15u) & ~static_cast<size_t>(15);
+    return mp * static_cast<size_t>(nf) * 2u;
+}
 
 // RMS normalization fused into the quantizer (either layout), and on its own.
 int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma_perm, float eps,
@@ -64,6 +76,12 @@ struct GemmProblem {
     void* workspace;
     size_t workspace_bytes;
     int max_wg;              // FP6 partials only: cap on the persistent grid (0: none)
+    // FP6 layout only: QUIK's fp16 outlier channels after the K quantized ones
+    // (nf = 0: none). xf: [Mp/16][nf/32] 1 KB tiles (16 rows x 32 channels, Mp
+    // = M rounded up to 16); wf: [N/16][nf/32] 1 KB fragments.
+    const uint16_t* xf;
+    const uint16_t* wf;
+    int nf;
 };
 
 size_t gemm_workspace_bytes(int M, int N, int K, int nb8);
@@ -82,6 +100,8 @@ int cu_count();
 // Host packer (pack_weights.cpp).
 int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
                  uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum);
+int pack_weights_quik(const uint16_t* W, int N, int K, const float* score, int nf, int32_t* perm, uint8_t* Wq,
+                      uint16_t* w_scale, int16_t* w_sum, uint16_t* Wf);
 // INT4 fragments to the FP6 layout (pack_weights.cpp).
 void repack_fp6(const uint8_t* Wq, int N, int K, int nb8, uint8_t* WqF);
 

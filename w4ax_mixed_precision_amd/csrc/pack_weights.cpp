@@ -146,19 +146,25 @@ void repack_fp6(const uint8_t* Wq, int N, int K, int nb8, uint8_t* WqF) {
     for (auto& th : pool) th.join();
 }
 
-int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
-                 uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum) {
-    const int nb = K / kBlock;
-    for (int k = 0; k < K; ++k)
-        if (!std::isfinite(score[k])) return COMET_ERR_ARG;
+namespace {
 
+// Channel order: stable ascending sort by score (the highest-scoring channels
+// last). False on a non-finite score.
+bool channel_order(const float* score, int K, int32_t* perm) {
+    for (int k = 0; k < K; ++k)
+        if (!std::isfinite(score[k])) return false;
     std::vector<int32_t> order(K);
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(),
                      [score](int32_t x, int32_t y) { return score[x] < score[y]; });
     std::copy(order.begin(), order.end(), perm);
-    for (int b = 0; b < nb; ++b) flags[b] = static_cast<uint8_t>(b >= nb - nb8);
+    return true;
+}
 
+// Quantize and pack the channels perm[0 .. Kq) of every row of W ([N][K]),
+// threaded over rows. False on a non-finite weight.
+bool pack_rows(const uint16_t* W, int N, int K, int Kq, const int32_t* perm, uint8_t* Wq, uint16_t* w_scale,
+               int16_t* w_sum) {
     unsigned hw = std::thread::hardware_concurrency();
     const int threads = static_cast<int>(std::max(1u, std::min(hw ? hw : 1u, 32u)));
     const int per = (N + threads - 1) / threads;
@@ -169,7 +175,7 @@ int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, i
         if (n0 >= n1) break;
         pool.emplace_back([=, &ok] {
             for (int n = n0; n < n1; ++n)
-                if (!pack_row(W + static_cast<size_t>(n) * K, N, K, perm, n, Wq, w_scale, w_sum)) {
+                if (!pack_row(W + static_cast<size_t>(n) * K, N, Kq, perm, n, Wq, w_scale, w_sum)) {
                     ok[t] = 0;
                     return;
                 }
@@ -177,7 +183,44 @@ int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, i
     }
     for (auto& th : pool) th.join();
     for (char c : ok)
-        if (!c) return COMET_ERR_ARG;
+        if (!c) return false;
+    return true;
+}
+
+}  // namespace
+
+int pack_weights(const uint16_t* W, int N, int K, const float* score, int nb8, int32_t* perm,
+                 uint8_t* flags, uint8_t* Wq, uint16_t* w_scale, int16_t* w_sum) {
+    const int nb = K / kBlock;
+    if (!channel_order(score, K, perm)) return COMET_ERR_ARG;
+    for (int b = 0; b < nb; ++b) flags[b] = static_cast<uint8_t>(b >= nb - nb8);
+    return pack_rows(W, N, K, K, perm, Wq, w_scale, w_sum) ? COMET_OK : COMET_ERR_ARG;
+}
+
+// QUIK's outlier columns (QUIK blog, sections "第一步: 识别与重排" and "第二步:
+// 前向传播 (在线)"): the same channel order; the first K - nf channels are
+// quantized and packed as by pack_weights (their last nb8 blocks 8-bit), the
+// last nf (the highest scores) keep their fp16 values in 1 KB fragments of
+// 16 output channels x 32 channels, the operand order of the fp16 matrix
+// instruction: fragment (c, s) at half (c * (nf / 32) + s) * 512 holds, at
+// half 8 l + e, W[16 c + l mod 16][perm[K - nf + 32 s + 8 (l / 16) + e]].
+int pack_weights_quik(const uint16_t* W, int N, int K, const float* score, int nf, int32_t* perm, uint8_t* Wq,
+                      uint16_t* w_scale, int16_t* w_sum, uint16_t* Wf) {
+    if (!channel_order(score, K, perm)) return COMET_ERR_ARG;
+    const int Kq = K - nf;
+    if (!pack_rows(W, N, K, Kq, perm, Wq, w_scale, w_sum)) return COMET_ERR_ARG;
+    const int steps = nf / 32;
+    for (int c = 0; c < N / 16; ++c)
+        for (int s = 0; s < steps; ++s) {
+            uint16_t* frag = Wf + (static_cast<size_t>(c) * steps + s) * 512;
+            for (int l = 0; l < 64; ++l)
+                for (int e = 0; e < 8; ++e) {
+                    const int n = 16 * c + (l & 15);
+                    const uint16_t w = W[static_cast<size_t>(n) * K + perm[Kq + 32 * s + 8 * (l >> 4) + e]];
+                    if (!std::isfinite(half_bits_to_float(w))) return COMET_ERR_ARG;
+                    frag[8 * l + e] = w;
+                }
+        }
     return COMET_OK;
 }
 

@@ -673,10 +673,13 @@ hipError_t allow_lds(int bytes) {
     return attr;
 }
 
+// K: the channels of X a row stages (the gather reads any of them); kq > 0:
+// only the first kq permuted channels are quantized (QUIK's split), else K.
 template <bool kFp6, bool kNorm, bool kSwi = false>
 int launch(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8, uint8_t* Xq,
-           float* x_scale, const uint16_t* gperm, float eps, void* stream, const uint16_t* U = nullptr) {
-    const int nb = K / kBlock;
+           float* x_scale, const uint16_t* gperm, float eps, void* stream, const uint16_t* U = nullptr,
+           int kq = 0) {
+    const int nb = (kq > 0 ? kq : K) / kBlock;
     const int nb4 = nb - nb8;
     // Enough workgroups to cover the chip even for a handful of rows: split the
     // blocks of a row over gridDim.y workgroups (each stages the whole row).
@@ -906,8 +909,47 @@ int launch_quant_act_asym(const uint16_t* X, int M, int K, int ldx, const int32_
 }
 
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
-                         uint8_t* Xq, float* x_scale, void* stream) {
-    return launch<true, false>(X, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream);
+                         uint8_t* Xq, float* x_scale, void* stream, int kq) {
+    return launch<true, false>(X, M, K, ldx, perm, nb8, Xq, x_scale, nullptr, 0.0f, stream, nullptr, kq);
+}
+
+namespace {
+
+// QUIK's fp16 outlier channels (QUIK blog, section "第二步: 前向传播 (在线)":
+// the activations split into the quantized part and the FP16 outlier
+// columns): the columns perm_f[0 .. nf) of X as 16-row x 32-channel tiles in
+// the operand order of the fp16 matrix instruction. One thread per lane slot
+// of a tile (8 halves): tile (t, s) at half (t (nf / 32) + s) 512, lane l at
+// + 8 l, row 16 t + l mod 16, channels 32 s + 8 (l / 16) .. + 7; rows past M
+// are zero.
+__global__ __launch_bounds__(256) void gather_outliers_kernel(const uint16_t* __restrict__ X, int M, int ldx,
+                                                              const int32_t* __restrict__ perm_f, int nf,
+                                                              uint16_t* __restrict__ Xf, uint32_t slots) {
+    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
+    if (item >= slots) return;
+    const uint32_t steps = static_cast<uint32_t>(nf) / 32u;
+    const uint32_t l = item & 63u, ts = item >> 6;
+    const uint32_t st = ts % steps, t = ts / steps;
+    const int row = static_cast<int>(16u * t + (l & 15u));
+    const int32_t* pc = perm_f + 32u * st + 8u * (l >> 4);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (row < M) {
+        const uint16_t* xr = X + static_cast<size_t>(row) * ldx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = static_cast<uint32_t>(xr[pc[2 * e]]) | (static_cast<uint32_t>(xr[pc[2 * e + 1]]) << 16);
+    }
+    *reinterpret_cast<uint4*>(Xf + static_cast<size_t>(item) * 8u) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+}  // namespace
+
+int launch_gather_outliers(const uint16_t* X, int M, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
+                           void* stream) {
+    const uint32_t slots = static_cast<uint32_t>((M + 15) / 16) * static_cast<uint32_t>(nf / 32) * 64u;
+    gather_outliers_kernel<<<(slots + 255u) / 256u, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        X, M, ldx, perm_f, nf, Xf, slots);
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_rmsnorm_quant_act(const uint16_t* X, int M, int K, int ldx, const uint16_t* gamma_perm, float eps,

@@ -301,6 +301,46 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
     end_block<kWC>(b, b_end);
 }
 
+// QUIK's fp16 outlier channels (QUIK blog, section "第二步: 前向传播 (在线)":
+// the outlier columns are multiplied in FP16 on their own path and the two
+// results added). Here the two paths meet in the tile's FP32 accumulators:
+// after the quantized blocks, each 32-channel step of the outlier part is one
+// 16x16x32 fp16 matrix instruction per 16x16 tile, accumulating straight into
+// y (the products of two fp16 values are exact in FP32). The operands come
+// from L2 as 16 bytes per lane (a 1 KB tile or fragment per wave); row tiles
+// past the padded rows read 0 through the buffer's range check.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+template <int kWC>
+__device__ __forceinline__ void fp16_tail(const GemmProblem& p, int m0, int n0, int wave, int lane,
+                                          float (&y)[4][kWC][4]) {
+    const int wr = wave >> 1, wc = wave & 1;
+    const uint32_t steps = static_cast<uint32_t>(p.nf) / 32u;
+    const uint32_t mp = (static_cast<uint32_t>(p.M) + 15u) & ~15u;
+    const Rsrc rx = make_rsrc(p.xf, mp * static_cast<uint32_t>(p.nf) * 2u);
+    const Rsrc rw = make_rsrc(p.wf, static_cast<uint32_t>(p.N) * static_cast<uint32_t>(p.nf) * 2u);
+    const uint32_t t0 = static_cast<uint32_t>(m0 + 64 * wr) / 16u;            // the wave's first row tile
+    const uint32_t c0 = static_cast<uint32_t>(n0 + 16 * kWC * wc) / 16u;      // and column tile
+    for (uint32_t s = 0; s < steps; ++s) {
+        v8h a[4], b[kWC];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            a[r] = __builtin_bit_cast(v8h, buf_load16(rx, ((t0 + r) * steps + s) * 1024u + 16u * lane));
+#pragma unroll
+        for (int c = 0; c < kWC; ++c)
+            b[c] = __builtin_bit_cast(v8h, buf_load16(rw, ((c0 + c) * steps + s) * 1024u + 16u * lane));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < kWC; ++c) {
+                v4f acc = {y[r][c][0], y[r][c][1], y[r][c][2], y[r][c][3]};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], b[c], acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[r][c][i] = acc[i];
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Tile scheduling (COMET article, mmssai.com/?p=43269, section
 // "2.混合精度计算的动态调度": tiles are not bound to compute units; work is
@@ -494,7 +534,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p, Sc
         const int n0 = tn * C::kTN;
         const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
         run_blocks<kDump, kWC>(p, in, 0, p.nb, m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
-        if constexpr (!kDump) store_y<kWC>(p, m0, n0, row_hi, wave, lane, y);
+        if constexpr (!kDump) {
+            if (p.nf > 0) fp16_tail<kWC>(p, m0, n0, wave, lane, y);
+            store_y<kWC>(p, m0, n0, row_hi, wave, lane, y);
+        }
         return;
     }
 
@@ -511,7 +554,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p, Sc
         const int n0 = tn * C::kTN;
         const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
         run_blocks<kDump, kWC>(p, in, sc.bounds[s], sc.bounds[s + 1], m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
-        if constexpr (!kDump) store_partial<kWC>(sc, tile, s, y);
+        if constexpr (!kDump) {
+            if (p.nf > 0 && s == sc.splits - 1) fp16_tail<kWC>(p, m0, n0, wave, lane, y);   // the last run
+            store_partial<kWC>(sc, tile, s, y);
+        }
         if (!queued) break;
         if (threadIdx.x == 0) item_lds = next_item(sc, xcd);
         __syncthreads();
