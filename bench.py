@@ -384,6 +384,67 @@ def asym_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
     return out
 
 
+def quik_ablation(torch, comet, synth, Ms=(16, 4096), iters=20):
+    """QUIK's split (the top nf channels in fp16 on their own path, every other
+    block 4-bit) against the COMET form (the same layer with its 8-bit
+    blocks), all on the FP6 layout, at the LLaMA-70B up_proj shape (K = 8192,
+    N = 28672, 7 8-bit blocks): nf = 896 keeps exactly the channels of the 8-bit
+    blocks in fp16, nf = 256 is QUIK's usual outlier count. Quantizer + GEMM,
+    HIP events around `iters` back-to-back pairs over weight copies of >= 1 GB;
+    and each one's error against the unquantized product on 16 rows."""
+    cfg0 = synth.CONFIGS["prefill_up_70b"]
+    K, N, nb8 = cfg0.K, cfg0.N, cfg0.nb8
+    W, score = synth.make_w(cfg0), synth.make_scores(cfg0)
+    copies = copies_for(synth.LayerConfig("quik", 1, K, N, 0, int8_frac=None))
+
+    def clone(w):
+        return {k: (v.clone() if hasattr(v, "clone") else v) for k, v in w.items()}
+
+    def replicas(w0):
+        return [w0] + [clone(w0) for _ in range(copies - 1)]
+    variants = {"comet": (replicas(comet.upload_weights(
+        comet.comet_repack_weights_fp6(comet.comet_pack_weights(W, score, nb8)))), 0)}
+    for nf in (128 * nb8, 256):
+        variants[f"quik_nf{nf}"] = (replicas(comet.upload_weights(comet.comet_pack_weights_quik(W, score, 0, nf))), nf)
+    Xall = synth.make_x(cfg0)
+    out = {"shape": {"K": K, "N": N, "comet_int8_blocks": nb8, "layout": "fp6"}, "per_M": {},
+           "timing": f"HIP events around {iters} back-to-back quantizer + GEMM pairs, {copies} weight copies"}
+
+    def pair(name, X, M, Y, i):
+        ws, nf = variants[name]
+        w = ws[i % copies]
+        if nf == 0:
+            Xq, xs = comet.comet_quant_act_fp6(X, w["perm"], nb8)
+            return comet.comet_w4ax_gemm_fp6(Xq, xs, w, M, Y=Y)
+        Xq, xs, Xf = comet.comet_quant_act_quik_fp6(X, w["perm"], 0, nf)
+        return comet.comet_w4ax_gemm_quik_fp6(Xq, xs, Xf, w, M, Y=Y)
+
+    for M in Ms:
+        X = torch.from_numpy(Xall[:M].view(np.float16)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fns = []
+        for name in variants:
+            it = {"i": 0}
+
+            def fn(name=name, it=it):
+                pair(name, X, M, Y, it["i"])
+                it["i"] += 1
+            fns.append((name, fn))
+        res = _time_variants(torch, fns, iters if M <= 64 else 5)
+        out["per_M"][str(M)] = {f"{k}_us": v for k, v in res.items()}
+    rows = 16
+    X = torch.from_numpy(Xall[:rows].view(np.float16)).cuda()
+    ref = Xall[:rows].view(np.float16).astype(np.float64) @ W.view(np.float16).astype(np.float64).T
+    err = {}
+    for name in variants:
+        y = pair(name, X, rows, None, 0).float().cpu().numpy().astype(np.float64)
+        err[name] = float(np.sqrt(np.mean((y - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+    out["rel_rms_err_vs_unquantized"] = err
+    del variants
+    torch.cuda.empty_cache()
+    return out
+
+
 def qoq_ablation(torch, comet, synth, Ms=(1, 16, 64, 4096), iters=20):
     """QoQ's W4A8 variant (per-channel INT8 then per-group UINT4 weights;
     per-token INT8 activations; one integer sum over K) against the W4Ax path
@@ -743,6 +804,7 @@ def main():
     swi = swiglu_ablation(torch, comet, synth) if ablate else None
     asym = asym_ablation(torch, comet, synth) if ablate else None
     qoq = qoq_ablation(torch, comet, synth) if ablate else None
+    quik = quik_ablation(torch, comet, synth) if ablate else None
     kv4 = kv4_attention_measure(torch, comet, synth) if ablate else None
 
     configs = None
@@ -775,6 +837,7 @@ def main():
         "swiglu_quant_fusion": swi,
         "asym_activation_variant": asym,
         "qoq_w4a8_variant": qoq,
+        "quik_fp16_outlier_variant": quik,
         "kv4_decode_attention": kv4,
         "configs": configs,
         "gpu": torch.cuda.get_device_name(0),
