@@ -578,7 +578,7 @@ int comet_quant_act_quik_fp6(const void* X_fp16, int M, int K, int ldx, const in
     int e = comet::launch_quant_act_fp6(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm, n_int8_blocks,
                                         static_cast<uint8_t*>(Xq_fp6), x_scale, stream, Kq);
     if (e != 0 || n_fp16 == 0) return hip_status(e);
-    return hip_status(comet::launch_gather_outliers(static_cast<const uint16_t*>(X_fp16), M, ldx, perm + Kq,
+    return hip_status(comet::launch_gather_outliers(static_cast<const uint16_t*>(X_fp16), M, K, ldx, perm + Kq,
                                                     n_fp16, static_cast<uint16_t*>(Xf_fp16), stream));
 }
 

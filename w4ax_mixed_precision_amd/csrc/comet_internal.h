@@ -39,8 +39,8 @@ int launch_quant_act_asym(const uint16_t* X, int M, int K, int ldx, const int32_
 int launch_quant_act_fp6(const uint16_t* X, int M, int K, int ldx, const int32_t* perm, int nb8,
                          uint8_t* Xq, float* x_scale, void* stream, int kq = 0);
 // QUIK's fp16 outlier channels: Xf tiles (GemmProblem::xf layout) of columns
-// perm_f[0 .. nf) of X, rows past M zero.
-int launch_gather_outliers(const uint16_t* X, int M, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
+// perm_f[0 .. nf) of X (rows of K channels), rows past M zero.
+int launch_gather_outliers(const uint16_t* X, int M, int K, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
                            void* stream);
 
 // Bytes of the QUIK fp16 outlier tiles of M rows.

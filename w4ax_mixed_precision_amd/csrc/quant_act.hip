@@ -918,37 +918,69 @@ namespace {
 // QUIK's fp16 outlier channels (QUIK blog, section "第二步: 前向传播 (在线)":
 // the activations split into the quantized part and the FP16 outlier
 // columns): the columns perm_f[0 .. nf) of X as 16-row x 32-channel tiles in
-// the operand order of the fp16 matrix instruction. One thread per lane slot
-// of a tile (8 halves): tile (t, s) at half (t (nf / 32) + s) 512, lane l at
-// + 8 l, row 16 t + l mod 16, channels 32 s + 8 (l / 16) .. + 7; rows past M
-// are zero.
-__global__ __launch_bounds__(256) void gather_outliers_kernel(const uint16_t* __restrict__ X, int M, int ldx,
-                                                              const int32_t* __restrict__ perm_f, int nf,
-                                                              uint16_t* __restrict__ Xf, uint32_t slots) {
-    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
-    if (item >= slots) return;
-    const uint32_t steps = static_cast<uint32_t>(nf) / 32u;
-    const uint32_t l = item & 63u, ts = item >> 6;
-    const uint32_t st = ts % steps, t = ts / steps;
-    const int row = static_cast<int>(16u * t + (l & 15u));
-    const int32_t* pc = perm_f + 32u * st + 8u * (l >> 4);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (row < M) {
-        const uint16_t* xr = X + static_cast<size_t>(row) * ldx;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(xr[pc[2 * e]]) | (static_cast<uint32_t>(xr[pc[2 * e + 1]]) << 16);
+// the operand order of the fp16 matrix instruction: tile (t, s) at half
+// (t (nf / 32) + s) 512, lane slot l at + 8 l, row 16 t + l mod 16, channels
+// 32 s + 8 (l / 16) .. + 7. One workgroup per row (and per padding row, which
+// is written as zeros): the row is staged in LDS with coalesced 16-byte loads
+// (the quantizer has just read it, so it comes from the last-level cache),
+// then each thread gathers 8 consecutive outlier channels from LDS and writes
+// them with one 16-byte store.
+constexpr int kGatherThreads = 256;
+
+template <bool kLds>
+__global__ __launch_bounds__(kGatherThreads) void gather_outliers_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                                         int ldx, const int32_t* __restrict__ perm_f,
+                                                                         int nf, uint16_t* __restrict__ Xf) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t row_lds[];
+    const int m = blockIdx.x;
+    const bool real = m < M;
+    const uint16_t* xr = X + static_cast<size_t>(real ? m : 0) * ldx;
+    if constexpr (kLds) {
+        if (real) {
+            // K and ldx are multiples of 8 on this path: whole 16-byte words
+            for (int k = 8 * threadIdx.x; k < K; k += 8 * kGatherThreads)
+                *reinterpret_cast<uint4*>(row_lds + k) = *reinterpret_cast<const uint4*>(xr + k);
+        }
+        __syncthreads();
     }
-    *reinterpret_cast<uint4*>(Xf + static_cast<size_t>(item) * 8u) = uint4{w[0], w[1], w[2], w[3]};
+    const uint32_t steps = static_cast<uint32_t>(nf) / 32u;
+    const uint32_t t = static_cast<uint32_t>(m) / 16u, r = static_cast<uint32_t>(m) & 15u;
+    for (int j0 = 8 * threadIdx.x; j0 < nf; j0 += 8 * kGatherThreads) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (real) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c0 = perm_f[j0 + 2 * e], c1 = perm_f[j0 + 2 * e + 1];
+                const uint16_t v0 = kLds ? row_lds[c0] : xr[c0];
+                const uint16_t v1 = kLds ? row_lds[c1] : xr[c1];
+                w[e] = static_cast<uint32_t>(v0) | (static_cast<uint32_t>(v1) << 16);
+            }
+        }
+        const uint32_t st = static_cast<uint32_t>(j0) / 32u;
+        const uint32_t l = r + 16u * ((static_cast<uint32_t>(j0) & 31u) / 8u);
+        *reinterpret_cast<uint4*>(Xf + ((static_cast<size_t>(t) * steps + st) * 64u + l) * 8u) =
+            uint4{w[0], w[1], w[2], w[3]};
+    }
 }
 
 }  // namespace
 
-int launch_gather_outliers(const uint16_t* X, int M, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
+int launch_gather_outliers(const uint16_t* X, int M, int K, int ldx, const int32_t* perm_f, int nf, uint16_t* Xf,
                            void* stream) {
-    const uint32_t slots = static_cast<uint32_t>((M + 15) / 16) * static_cast<uint32_t>(nf / 32) * 64u;
-    gather_outliers_kernel<<<(slots + 255u) / 256u, 256, 0, static_cast<hipStream_t>(stream)>>>(
-        X, M, ldx, perm_f, nf, Xf, slots);
+    const int mp = (M + 15) / 16 * 16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool lds = K <= kMaxLdsRowChannels && (ldx & 7) == 0 &&
+                     (reinterpret_cast<uintptr_t>(X) & 15u) == 0;
+    if (lds) {
+        const size_t bytes = static_cast<size_t>(K) * 2u;
+        if (bytes > 64 * 1024) {
+            const hipError_t attr = allow_lds<&gather_outliers_kernel<true>>(160 * 1024);
+            if (attr != hipSuccess) return static_cast<int>(attr);
+        }
+        gather_outliers_kernel<true><<<mp, kGatherThreads, bytes, s>>>(X, M, K, ldx, perm_f, nf, Xf);
+    } else {
+        gather_outliers_kernel<false><<<mp, kGatherThreads, 0, s>>>(X, M, K, ldx, perm_f, nf, Xf);
+    }
     return static_cast<int>(hipGetLastError());
 }
 

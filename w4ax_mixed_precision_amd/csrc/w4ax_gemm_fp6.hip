@@ -306,29 +306,55 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
 // results added). Here the two paths meet in the tile's FP32 accumulators:
 // after the quantized blocks, each 32-channel step of the outlier part is one
 // 16x16x32 fp16 matrix instruction per 16x16 tile, accumulating straight into
-// y (the products of two fp16 values are exact in FP32). The operands come
-// from L2 as 16 bytes per lane (a 1 KB tile or fragment per wave); row tiles
-// past the padded rows read 0 through the buffer's range check.
+// y (the products of two fp16 values are exact in FP32). A step's operands
+// are the workgroup's 8 row-tile pieces and 2 kWC column-tile pieces of 1 KB;
+// the waves share them out of LDS (the main loop's ring, free by now), two
+// steps in flight, each piece one direct load by one wave. Row tiles past the
+// padded rows read 0 through the buffer's range check.
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 template <int kWC>
 __device__ __forceinline__ void fp16_tail(const GemmProblem& p, int m0, int n0, int wave, int lane,
-                                          float (&y)[4][kWC][4]) {
+                                          uint8_t* smem, float (&y)[4][kWC][4]) {
+    constexpr int kRowPieces = kTM / 16;
+    constexpr int kPieces = kRowPieces + 2 * kWC;
+    constexpr int kPerWave = kPieces / 4;                 // direct loads per wave and step
+    static_assert(kPieces % 4 == 0 && 2 * kPieces * 1024 <= Cfg<kWC>::kStages * Cfg<kWC>::kStage, "tail stages");
     const int wr = wave >> 1, wc = wave & 1;
     const uint32_t steps = static_cast<uint32_t>(p.nf) / 32u;
     const uint32_t mp = (static_cast<uint32_t>(p.M) + 15u) & ~15u;
     const Rsrc rx = make_rsrc(p.xf, mp * static_cast<uint32_t>(p.nf) * 2u);
     const Rsrc rw = make_rsrc(p.wf, static_cast<uint32_t>(p.N) * static_cast<uint32_t>(p.nf) * 2u);
-    const uint32_t t0 = static_cast<uint32_t>(m0 + 64 * wr) / 16u;            // the wave's first row tile
-    const uint32_t c0 = static_cast<uint32_t>(n0 + 16 * kWC * wc) / 16u;      // and column tile
+    const uint32_t tr0 = static_cast<uint32_t>(m0) / 16u, tc0 = static_cast<uint32_t>(n0) / 16u;
+    auto issue = [&](uint32_t s, uint8_t* st) {
+#pragma unroll
+        for (int k = 0; k < kPerWave; ++k) {
+            const int q = wave + 4 * k;                   // piece q: row tiles first, then column tiles
+            if (q < kRowPieces)
+                lds_buf16(rx, 16u * lane, ((tr0 + q) * steps + s) * 1024u, st + q * 1024);
+            else
+                lds_buf16(rw, 16u * lane, ((tc0 + q - kRowPieces) * steps + s) * 1024u, st + q * 1024);
+        }
+    };
+    COMET_VMCNT(0);
+    __syncthreads();                                      // the last block's LDS reads are done
+    issue(0, smem);
     for (uint32_t s = 0; s < steps; ++s) {
+        uint8_t* cur = smem + (s & 1u) * kPieces * 1024;
+        if (s + 1 < steps) {
+            issue(s + 1, smem + ((s + 1) & 1u) * kPieces * 1024);
+            COMET_VMCNT(kPerWave);                        // this wave's pieces of step s
+        } else {
+            COMET_VMCNT(0);
+        }
+        __syncthreads();                                  // every wave's pieces of step s
         v8h a[4], b[kWC];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            a[r] = __builtin_bit_cast(v8h, buf_load16(rx, ((t0 + r) * steps + s) * 1024u + 16u * lane));
+            a[r] = *reinterpret_cast<const v8h*>(cur + (4 * wr + r) * 1024 + 16 * lane);
 #pragma unroll
         for (int c = 0; c < kWC; ++c)
-            b[c] = __builtin_bit_cast(v8h, buf_load16(rw, ((c0 + c) * steps + s) * 1024u + 16u * lane));
+            b[c] = *reinterpret_cast<const v8h*>(cur + (kRowPieces + kWC * wc + c) * 1024 + 16 * lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -338,6 +364,7 @@ __device__ __forceinline__ void fp16_tail(const GemmProblem& p, int m0, int n0, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[r][c][i] = acc[i];
             }
+        __syncthreads();                                  // step s read before its buffer is refilled
     }
 }
 
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p, Sc
         const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
         run_blocks<kDump, kWC>(p, in, 0, p.nb, m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
         if constexpr (!kDump) {
-            if (p.nf > 0) fp16_tail<kWC>(p, m0, n0, wave, lane, y);
+            if (p.nf > 0) fp16_tail<kWC>(p, m0, n0, wave, lane, smem, y);
             store_y<kWC>(p, m0, n0, row_hi, wave, lane, y);
         }
         return;
@@ -555,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp6_kernel(GemmProblem p, Sc
         const uint32_t scw = wave < 2 ? static_cast<uint32_t>(imin(m0 + 64 * wave + lane, p.M - 1)) * 4u : 4u * lane;
         run_blocks<kDump, kWC>(p, in, sc.bounds[s], sc.bounds[s + 1], m0, n0, row_lo, row_hi, wave, lane, scw, smem, y);
         if constexpr (!kDump) {
-            if (p.nf > 0 && s == sc.splits - 1) fp16_tail<kWC>(p, m0, n0, wave, lane, y);   // the last run
+            if (p.nf > 0 && s == sc.splits - 1) fp16_tail<kWC>(p, m0, n0, wave, lane, smem, y);   // the last run
             store_partial<kWC>(sc, tile, s, y);
         }
         if (!queued) break;
