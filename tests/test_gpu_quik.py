@@ -77,9 +77,11 @@ def _run(torch, M, K, N, nb8, nf, seed):
 
 
 # (M, K, N, nb8, nf): one 16-row tile; a split plan with the work queue
-# (q_proj_7b-like); ragged rows; one row; the 128 x 256 tile over 1024 tiles
+# (q_proj_7b-like); ragged rows; one row; the 128 x 256 tile over 1024 tiles;
+# rows wider than the LDS staging (the quantizer's and the gather's global
+# paths)
 SHAPES = [(16, 512, 512, 0, 128), (128, 4096, 4096, 4, 256), (100, 1024, 512, 1, 256), (1, 8192, 1024, 2, 128),
-          (4096, 2048, 8192, 2, 256)]
+          (4096, 2048, 8192, 2, 256), (5, 33280, 256, 3, 256)]
 
 
 @pytest.mark.parametrize("M,K,N,nb8,nf", SHAPES)
