@@ -77,6 +77,7 @@ def test_asym_layer_parity(torch, name):
     (1, 128, 128, 0), (3, 256, 256, 1), (16, 8192, 1152, 7), (17, 512, 384, 0),
     (24, 8192, 1152, 7), (33, 384, 640, 3), (40, 8192, 10240, 0), (64, 8192, 640, 64),
     (48, 2048, 1024, 2), (100, 1024, 512, 1), (130, 640, 256, 2), (5, 33024, 128, 4),
+    (2, 8192, 14336, 3),
 ])
 def test_asym_edge_shapes(torch, M, K, N, nb8):
     """Every kernel path (one- and multi-group streaming, LDS ring and register

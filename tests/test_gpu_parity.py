@@ -101,6 +101,8 @@ def _custom_layer(M, K, N, nb8, seed, zero_rows=(), zero_block_rows=(), ldx=None
     # workgroup per CU) and the register form at other block counts
     (24, 8192, 1152, 7), (64, 8192, 640, 0), (40, 8192, 10240, 64), (57, 8192, 12288, 5),
     (20, 1024, 24576, 1), (48, 2048, 1024, 16),
+    # half-group units (N = 2048 H): H = 5 at one to four row tiles, H = 7 at one
+    (16, 8192, 10240, 64), (25, 8192, 10240, 0), (3, 8192, 14336, 7), (64, 8192, 10240, 9),
 ])
 def test_edge_shapes(torch, M, K, N, nb8):
     import w4ax_mixed_precision_amd as comet

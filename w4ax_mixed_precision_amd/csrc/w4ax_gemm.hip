@@ -891,9 +891,12 @@ __device__ __forceinline__ void stream_fetch_aux_g(const GemmProblem& p, Rsrc xq
     }
 }
 
+// `half_j` names the group of which this workgroup owns only the channels of
+// lanes with `own` set (-1: none); partials of the other half are not stored.
 template <int MR, int G, bool kAsym = false, bool kDump = false>
 __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, kAsym>& sl, const uint8_t* frags, int lane,
-                                                     float (&y)[G][MR][4], const GemmProblem& p, int b, int grp0) {
+                                                     float (&y)[G][MR][4], const GemmProblem& p, int b, int grp0,
+                                                     int half_j = -1, bool own = true) {
     // branch-free operand words (a branch on the block kind splits the
     // straight-line block sequence, and the compiler then waits for every
     // outstanding load before the next LDS read): a 4-bit row's second word
@@ -929,7 +932,7 @@ __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, k
             v4i acc = mfma_i8(A0[r], B0, kAsym ? COMET_ACC_START_ASYM(zmul, sl.zw[r]) : cinit);
             acc = mfma_i8(A1[r], B1, acc);
             if constexpr (kDump) {
-                dump_tile(p, b, (grp0 + j) * 16 + (lane & 15), r, lane >> 4, acc);
+                if (j != half_j || own) dump_tile(p, b, (grp0 + j) * 16 + (lane & 15), r, lane >> 4, acc);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -939,8 +942,17 @@ __device__ __forceinline__ void stream_compute_lds_g(bool is4, AuxSlotG<MR, G, k
     }
 }
 
-template <int MR, int G, int NBW, int kSplit, int kRA, int kRR, bool kAsym = false, bool kDump = false>
+// H > 0: half-group units. Unit u owns the half-groups [H u, H u + H) (H odd,
+// half-group h = channels 8 (h mod 2) .. + 8 of group h / 2), so 2 N / (16 H)
+// units split the channels evenly over that many CUs where whole groups would
+// not (N = 10240: 640 groups are 2.5 per CU; 256 units of five halves). The
+// unit's G = (H + 1) / 2 groups are whole but one, whose other half belongs to
+// the neighbouring unit: its lanes of the other half load nothing (an offset
+// past the buffer reads zeros, no memory access) and store nothing. A group's
+// columns depend only on its own weight columns, so the owned half is exact.
+template <int MR, int G, int NBW, int kSplit, int kRA, int kRR, bool kAsym = false, bool kDump = false, int H = 0>
 __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_lds_g_kernel(GemmProblem p) {
+    static_assert(H == 0 || (H % 2 == 1 && G == (H + 1) / 2), "a unit of H half-groups spans (H + 1) / 2 groups");
     // two LDS objects: the compiler can then tell ring reads from other LDS
     // accesses and waits only for the direct loads a read depends on (with
     // one object it waits for every outstanding load before each read)
@@ -954,11 +966,16 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int units = p.N / (16 * G);
+    const int units = H > 0 ? p.N / (8 * H) : p.N / (16 * G);
     const int per = (units + 7) / 8;
     const int unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (unit >= units) return;      // whole workgroup, before any barrier
-    const int grp0 = unit * G;
+    const int grp0 = H > 0 ? (H * unit) / 2 : unit * G;
+    // the shared group: first of the unit when it starts on a second half,
+    // else its last (first half)
+    const int hh = H > 0 ? (H * unit) & 1 : 0;
+    const int half_j = H > 0 ? (hh ? 0 : G - 1) : -1;
+    const bool own = ((lane & 15) >> 3) == hh;
     const int nb4 = p.nb4, M = p.M;
     const int b_begin = wave * NBW;
     int arow[MR];
@@ -972,9 +989,14 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
     // ring slot i mod kRR
     auto fragments = [&](int i) {
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-            lds_buf16(wq, 16u * lane, (static_cast<uint32_t>(grp0 + j) * p.nb + b_begin + i) * kFragBytes,
-                      my + ((i % kRR) * G + j) * kFragBytes);
+        for (int j = 0; j < G; ++j) {
+            const uint32_t off = (static_cast<uint32_t>(grp0 + j) * p.nb + b_begin + i) * kFragBytes;
+            if constexpr (H > 0)
+                lds_buf16(wq, j != half_j || own ? 16u * lane + off : kOutOfRange, 0u,
+                          my + ((i % kRR) * G + j) * kFragBytes);
+            else
+                lds_buf16(wq, 16u * lane, off, my + ((i % kRR) * G + j) * kFragBytes);
+        }
     };
 
     float y[G][MR][4];
@@ -1001,7 +1023,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
         COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR, kAsym>(i, NBW)));
         AuxSlotG<MR, G, kAsym>& sl = slot[i % kRA];
         stream_compute_lds_g<MR, G, kAsym, kDump>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y,
-                                                  p, b_begin + i, grp0);
+                                                  p, b_begin + i, grp0, half_j, own);
         if (i + kRA < NBW) stream_fetch_aux_g<MR, G, kAsym>(p, xq, b_begin + i + kRA, grp0, lane, srow, arow, sl);
         // the ring slot just read is refilled only after its words are used
         if (i + kRR < NBW) fragments(i + kRR);
@@ -1021,7 +1043,7 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
             for (int w2 = 1; w2 < kSplit; ++w2) v += red[w2][q][lane];
             const int row = 16 * (q >> 2) + 4 * g + (q & 3);
-            if (row < M)
+            if (row < M && (j != half_j || own))
                 p.Y[static_cast<size_t>(row) * p.ldy + (grp0 + j) * 16 + l16] = __half_as_ushort(__float2half_rn(v));
         }
     }
@@ -1043,15 +1065,47 @@ bool use_stream(int M) { return M <= 64; }
 template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st);
 
+// Half-group units (see gemm_stream_lds_g_kernel) where N = 2048 H, H = 5 or
+// 7: 256 units of H half-groups, one per CU, every CU the same load, where
+// whole groups leave some CUs a third more work than others. Measured at K =
+// 8192 against the whole-group kernels (60 back-to-back calls, medians): N =
+// 10240, M = 1 / 4 / 16 11.8 / 11.5 / 11.6 against 12.8 / 12.7 / 13.3 us,
+// M = 32 / 48 / 64 13.5 / 15.9 / 18.6 against 16.6 / 17.4 / 20.1 us; N =
+// 14336, M = 1 / 4 / 16 15.2 / 15.2 / 14.7 against 16.8 / 16.6 / 17.2 us.
+// Not used where it was not faster: H = 3 (N = 6144, equal), and H = 7 above
+// 16 rows (M = 48 / 64 19.0 / 22.2 against 18.8 / 21.9 us).
+template <int MR, int H, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
+int launch_stream_lds_half_cfg(const GemmProblem& p, hipStream_t st) {
+    constexpr int G = (H + 1) / 2;
+    const int units = p.N / (8 * H);
+    const int grid = 8 * ((units + 7) / 8);
+    gemm_stream_lds_g_kernel<MR, G, 64 / kSplit, kSplit, kRA, kRR, kAsym, kDump, H><<<grid, 64 * kSplit, 0, st>>>(p);
+    return static_cast<int>(hipGetLastError());
+}
+
+bool half_units(const GemmProblem& p, int mr) {
+    const int h = p.N / 2048;
+    return p.nb == 64 && p.N % 2048 == 0 && (h == 5 || (h == 7 && mr == 1));
+}
+
+template <int MR, bool kAsym, bool kDump>
+int launch_stream_lds_half(const GemmProblem& p, hipStream_t st) {
+    if constexpr (MR == 1)
+        if (p.N == 7 * 2048) return launch_stream_lds_half_cfg<1, 7, 8, 4, 2, kAsym, kDump>(p, st);
+    return launch_stream_lds_half_cfg<MR, 5, 8, 4, 2, kAsym, kDump>(p, st);
+}
+
 template <bool kAsym, bool kDump>
 int launch_stream1(const GemmProblem& p, hipStream_t st) {
+    if (half_units(p, 1)) return launch_stream_lds_half<1, kAsym, kDump>(p, st);
     // 64 blocks: the multi-group LDS-ring kernel in its narrow form (two
     // groups per wave, eight waves of 8 blocks), except where its grid of
     // N / 32 workgroups falls between one and two per CU and leaves the CUs
     // unevenly loaded. Measured at K = 8192, M = 1..16 against the one-group
     // kernels below: N = 8192 9.3-9.5 against 10.8-11.2 us, N = 28672
     // 24.7-26.5 against 29.1-31.8 us; N = 10240 (320 workgroups) 13.1-13.5
-    // against 12.8-13.4 us, which stays on the one-group kernel.
+    // against 12.8-13.4 us. N = 10240 and 14336 now take the half-group
+    // units above; other such grids stay on the one-group kernel.
     const int narrow_units = p.N / 32;
     if (p.nb == 64 && !(narrow_units > 256 && narrow_units < 512))
         return launch_stream_lds_g_cfg<1, 2, 8, 4, 2, kAsym, kDump>(p, st);
@@ -1117,6 +1171,7 @@ int launch_stream_g(const GemmProblem& p, hipStream_t st) {
 // there the eight-wave form hides more latency (N = 10240, M = 33 / 48 / 64:
 // 16.8 / 17.3 / 19.9 against 18.9 / 19.2 / 22.4 us), while on grids of more
 // workgroups than CUs it is slower (N = 28672, M = 64: 41.9 against 37.3 us).
+// (N = 10240 itself has since moved to the half-group units.)
 template <int MR, int G, int kSplit, int kRR, int kRA, bool kAsym, bool kDump>
 int launch_stream_lds_g_cfg(const GemmProblem& p, hipStream_t st) {
     const int units = p.N / (16 * G);
@@ -1137,6 +1192,7 @@ int launch_stream_lds_g(const GemmProblem& p, hipStream_t st) {
 // Two to four row tiles (16 < M <= 64): several channel groups per wave.
 template <int MR, bool kAsym, bool kDump>
 int launch_stream(const GemmProblem& p, hipStream_t st) {
+    if (half_units(p, MR)) return launch_stream_lds_half<MR, kAsym, kDump>(p, st);
     if (p.nb == 64) return launch_stream_lds_g<MR, kAsym, kDump>(p, st);
     return launch_stream_g<MR, kAsym, kDump>(p, st);
 }
