@@ -79,10 +79,13 @@
  *     to a multiple of 16, block-major, in 16-row tiles (rows M .. Mp-1 are
  *     padding, never written and never used). 4-bit block b lives at byte
  *     b*Mp*96; its tile t (rows 16t .. 16t+15) at + t*1536 holds the head of
- *     group g of row 16t + r at byte 256g + 16r and its tail at
- *     1024 + 128g + 8r. 8-bit block b lives at byte nb4*Mp*96 + (b - nb4)*Mp*128;
- *     its tile t at + t*2048 holds the int8 codes of block positions
- *     32g + 16h .. 32g + 16h + 15 of row 16t + r at byte 1024h + 256g + 16r.
+ *     group g of row 16t + r at byte H(r, g) = 64r + 16(g ^ h(r)) and its
+ *     tail at 1024 + 32r + 8(g ^ u(r)), with h(r) = (r >> 1) & 3
+ *     and u(r) = (r >> 2) & 3 (a row's bytes contiguous; the slot
+ *     permutation keeps the kernel's LDS reads free of bank conflicts).
+ *     8-bit block b lives at byte nb4*Mp*96 + (b - nb4)*Mp*128; its tile t at
+ *     + t*2048 holds the int8 codes of block positions 32g + 16h' .. 32g +
+ *     16h' + 15 of row 16t + r at byte 1024h' + H(r, g).
  *   Wq_fp6, N * (96 * nb4 + 64 * nb8) bytes, block-major: for a 4-bit block b
  *     the N/16 fragments of 1536 bytes start at byte b*(N/16)*1536; fragment c
  *     (channels 16c .. 16c+15) holds, for lane l in 0..63 (channel

@@ -86,6 +86,20 @@ def _fp6_ints(codes: np.ndarray) -> np.ndarray:
     return v.astype(np.int8)
 
 
+def _tile_rows_index():
+    """Byte offsets in a 16-row activation tile of the FP6 layout: row r's
+    16-byte piece of group g at 64 r + 16 (g ^ h(r)), its 8-byte tail at
+    1024 + 32 r + 8 (g ^ t(r)), h(r) = (r >> 1) & 3,
+    t(r) = (r >> 2) & 3. Returns head [16, 4, 16] and tail [16, 4, 8] indices."""
+    r = np.arange(16)[:, None]
+    g = np.arange(4)[None, :]
+    h = (r >> 1) & 3
+    t = (r >> 2) & 3
+    head = (64 * r + 16 * (g ^ h))[:, :, None] + np.arange(16)
+    tail = (1024 + 32 * r + 8 * (g ^ t))[:, :, None] + np.arange(8)
+    return head, tail
+
+
 def decode_xq_fp6(Xq: np.ndarray, M: int, K: int, nb8: int) -> np.ndarray:
     """Xq_fp6 bytes (16-row tiles, rows padded to Mp) -> q_a int8 [M, K] in
     permuted channel order."""
@@ -95,17 +109,16 @@ def decode_xq_fp6(Xq: np.ndarray, M: int, K: int, nb8: int) -> np.ndarray:
     T = Mp // 16
     Xq = np.asarray(Xq, dtype=np.uint8)
     assert Xq.size == Mp * (96 * nb4 + 128 * nb8)
+    head, tail = _tile_rows_index()
     q = np.empty((M, K), np.int8)
     tiles = Xq[: nb4 * Mp * 96].reshape(nb4, T, 1536)
-    heads = tiles[:, :, :1024].reshape(nb4, T, 4, 16, 16)                          # [b, t, g, r, 16]
-    tails = tiles[:, :, 1024:].reshape(nb4, T, 4, 16, 8)                           # [b, t, g, r, 8]
-    groups = np.concatenate([heads, tails], axis=-1)                               # [b, t, g, r, 24]
-    codes = _codes_from_groups(groups).transpose(0, 1, 3, 2, 4)                    # [b, t, r, g, 32]
-    codes = codes.reshape(nb4, Mp, 128)[:, :M]                                     # padding rows dropped
+    groups = np.concatenate([tiles[:, :, head], tiles[:, :, tail]], axis=-1)      # [b, t, r, g, 24]
+    codes = _codes_from_groups(groups).reshape(nb4, Mp, 128)[:, :M]               # padding rows dropped
     vals = _fp6_ints(codes)                                                        # [b, m, 32g + j]
     q[:, : nb4 * 128] = vals.transpose(1, 0, 2).reshape(M, nb4 * 128)
-    t8 = Xq[nb4 * Mp * 96:].view(np.int8).reshape(nb8, T, 2, 4, 16, 16)            # [b, t, h, g, r, j]
-    v8 = t8.transpose(0, 1, 4, 3, 2, 5).reshape(nb8, Mp, 128)[:, :M]               # [b, m, 32g + 16h + j]
+    t8 = Xq[nb4 * Mp * 96:].view(np.int8).reshape(nb8, T, 2, 1024)                 # [b, t, half, byte]
+    v8 = t8[:, :, :, head]                                                         # [b, t, h, r, g, j]
+    v8 = v8.transpose(0, 1, 3, 4, 2, 5).reshape(nb8, Mp, 128)[:, :M]               # [b, m, 32g + 16h + j]
     q[:, nb4 * 128:] = v8.transpose(1, 0, 2).reshape(M, nb8 * 128)
     return q
 

@@ -22,6 +22,20 @@ __host__ __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : 
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
+// Byte offsets inside a 16-row activation tile of the FP6 layout. Row r keeps
+// its bytes together: the 16-byte pieces of its four 32-channel groups g (the
+// FP6 heads, or an 8-bit block's half-group) at 64 r + 16 (g ^ h(r)), the
+// 8-byte FP6 tails at 1024 + 32 r + 8 (g ^ t(r)). The quantizer, which codes
+// one row at a time, then writes a row's groups as one 64-byte and one
+// 32-byte run. The slot permutations h(r) = (r >> 1) & 3 and t(r) =
+// (r >> 2) & 3 were chosen by measurement (LDS bank-conflict counter of a
+// probe that reads candidate layouts in the matrix-operand lane order, lane
+// 16 g + r): with them the 16-byte and 8-byte operand reads run without bank
+// conflicts, as the lane-order layout does; the other permutations tried
+// (no permutation, r & 3, r >> 2, ...) cost a second cycle per read.
+__host__ __device__ constexpr int tile_head(int r, int g) { return 64 * r + 16 * (g ^ ((r >> 1) & 3)); }
+__host__ __device__ constexpr int tile_tail(int r, int g) { return 1024 + 32 * r + 8 * (g ^ ((r >> 2) & 3)); }
+
 // The value unchanged but opaque to the optimizer. A binary32 product that is
 // then rounded to fp16 must stay a product: otherwise the compiler folds the
 // two into one mixed-precision FMA (v_fma_mixlo_f16) that rounds once,

@@ -365,8 +365,8 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
             }
             const v6i c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
             uint8_t* tile = Xq + static_cast<size_t>(bc) * Mp * 96 + static_cast<size_t>(m >> 4) * 1536;
-            *reinterpret_cast<uint4*>(tile + 256 * g + 16 * (m & 15)) = make_uint4(c[0], c[1], c[2], c[3]);
-            *reinterpret_cast<uint2*>(tile + 1024 + 128 * g + 8 * (m & 15)) = make_uint2(c[4], c[5]);
+            *reinterpret_cast<uint4*>(tile + tile_head(m & 15, g)) = make_uint4(c[0], c[1], c[2], c[3]);
+            *reinterpret_cast<uint2*>(tile + tile_tail(m & 15, g)) = make_uint2(c[4], c[5]);
         } else if (!is8) {
             uint32_t w[4];
 #pragma unroll
@@ -394,12 +394,12 @@ __device__ __forceinline__ void code_block(const uint16_t* __restrict__ row, con
             }
             if constexpr (kFp6) {
                 // 16-row tiles of 2048 bytes: positions 32g + 16h + j of
-                // row r at tile byte 1024h + 256g + 16r + j
+                // row r at tile byte 1024h + tile_head(r, g) + j
                 uint8_t* tile = Xq + static_cast<size_t>(nb4) * Mp * 96 +
                                 static_cast<size_t>(bc - nb4) * Mp * 128 + static_cast<size_t>(m >> 4) * 2048;
-                *reinterpret_cast<uint4*>(tile + 256 * g + 16 * (m & 15)) = make_uint4(w[0], w[1], w[2], w[3]);
-                *reinterpret_cast<uint4*>(tile + 1024 + 256 * g + 16 * (m & 15)) =
-                    make_uint4(w[4], w[5], w[6], w[7]);
+                const int head = tile_head(m & 15, g);
+                *reinterpret_cast<uint4*>(tile + head) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4*>(tile + 1024 + head) = make_uint4(w[4], w[5], w[6], w[7]);
             } else {
                 uint8_t* dst = Xq + static_cast<size_t>(nb4) * M * 64 +
                                static_cast<size_t>(bc - nb4) * M * 128 + static_cast<size_t>(m) * 128 + 32 * g;

@@ -28,10 +28,12 @@
 // bytes land at LDS base + lane * size) into a ring of stages ahead of the
 // compute: three stages two blocks ahead for kWC = 4, two stages one block
 // ahead for kWC = 8 (whose stage is half again as large and whose block takes
-// twice as long). Both operand layouts are 16-row (16-channel) tiles in the
-// order a wave reads them, so every direct load is a contiguous copy and
-// every LDS read of a 16-lane k-group is one contiguous 256-byte run (no bank
-// conflicts). Each wave issues the same number of direct loads per block of
+// twice as long). Both operand layouts are 16-row (16-channel) tiles, so
+// every direct load is a contiguous copy. The weight tiles are in the order a
+// wave reads them (every LDS read of a 16-lane k-group one contiguous 256-byte
+// run); the activation tiles keep each row's bytes together for the
+// quantizer's stores, with a per-row slot permutation that keeps the reads
+// free of bank conflicts (tile_head, tile_tail). Each wave issues the same number of direct loads per block of
 // either kind (one scale word, then A and B, plus a balancing load where the
 // kinds differ), so a single partial wait at the end of a block publishes the
 // next one.
@@ -45,10 +47,12 @@
 // instructions of tile c+1, so it never waits on a result just produced.
 //
 // LDS stage (kWC = 4: 25.6 KB, kWC = 8: 38 KB):
-//   4-bit block: A at 0, eight 16-row tiles of 1536 bytes (heads: 256g + 16r,
-//     tails: 1024 + 128g + 8r); B at 12288, the tile's 2 kWC FP6 fragments.
-//   8-bit block: A at 0, eight 16-row tiles of 2048 bytes (1024h + 256g + 16r
-//     for positions 32g + 16h ..); B at 16384, the tile's 2 kWC INT4 fragments.
+//   4-bit block: A at 0, eight 16-row tiles of 1536 bytes (row-contiguous:
+//     heads at tile_head(r, g), tails at tile_tail(r, g)); B at 12288, the
+//     tile's 2 kWC FP6 fragments (lane order: 16 lane, 1024 + 8 lane).
+//   8-bit block: A at 0, eight 16-row tiles of 2048 bytes (1024h +
+//     tile_head(r, g) for positions 32g + 16h ..); B at 16384, the tile's
+//     2 kWC INT4 fragments.
 //   then the block's 128 activation scales (f32) and 32 kWC weight scales
 //   (fp16), and a pad that receives the balancing loads.
 #include <mutex>
@@ -192,6 +196,15 @@ __device__ __forceinline__ v8i fp6_operand(const uint8_t* tile, int lane) {
     return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)t.x, (int)t.y, 0, 0};
 }
 
+// The activation operand of lane 16 g + r from a row-contiguous tile
+// (tile_head / tile_tail).
+__device__ __forceinline__ v8i fp6_operand_rows(const uint8_t* tile, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const uint4 h = *reinterpret_cast<const uint4*>(tile + tile_head(r, g));
+    const uint2 t = *reinterpret_cast<const uint2*>(tile + tile_tail(r, g));
+    return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)t.x, (int)t.y, 0, 0};
+}
+
 // Epilogue of column tile c: y += t P, or the partials themselves.
 template <bool kDump, int kWC>
 __device__ __forceinline__ void epilogue(const GemmProblem& p, const v16f& t, const v4f (&D)[4], int c, int b,
@@ -228,7 +241,7 @@ __device__ __forceinline__ void block_fp6(const GemmProblem& p, const Inputs& in
     read_scales<kWC>(st, wr, wc, lane, 1.0f, s);
     v8i A[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) A[r] = fp6_operand(st + (4 * wr + r) * kTileF6, lane);
+    for (int r = 0; r < 4; ++r) A[r] = fp6_operand_rows(st + (4 * wr + r) * kTileF6, lane);
     v4f Dp[4], Dc[4];
     v16f tp = {}, tc = {};
     if constexpr (!kDump) tp = scale_products<kWC>(s, 0);
@@ -271,9 +284,9 @@ __device__ __forceinline__ void block_int8(const GemmProblem& p, const Inputs& i
     v4i A0[4], A1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint8_t* t = st + (4 * wr + r) * kTileI8;
-        A0[r] = as_v4i(*reinterpret_cast<const uint4*>(t + 16 * lane));
-        A1[r] = as_v4i(*reinterpret_cast<const uint4*>(t + 1024 + 16 * lane));
+        const uint8_t* t = st + (4 * wr + r) * kTileI8 + tile_head(lane & 15, lane >> 4);
+        A0[r] = as_v4i(*reinterpret_cast<const uint4*>(t));
+        A1[r] = as_v4i(*reinterpret_cast<const uint4*>(t + 1024));
     }
     const v4i zero = {0, 0, 0, 0};
     v4f Dp[4], Dc[4];
