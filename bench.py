@@ -565,6 +565,37 @@ def _per_call_us(torch, fn, iters):
     return a.elapsed_time(b) * 1e3 / iters
 
 
+def _graph_per_call_us(torch, fn, reps, check):
+    """Mean microseconds per call of fn(i), i = 0 .. reps-1, captured once in a
+    HIP graph and replayed (no host launch cost per call). `check()` runs after
+    every replay, with the eager work and synchronization in between, and must
+    return True (the replay reproduced the eager result); None if it does not."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        if not check():
+            return None
+        times.append(a.elapsed_time(b) * 1e3 / reps)
+    del g
+    return float(np.median(times))
+
+
 def decode_sweep(torch, comet, synth, iters=60):
     """The LLaMA-70B decode sweep (M in {1, 4, 16, 64}, K = 8192, N in {10240,
     8192, 28672}) on the INT4 layout: comet_w4ax_gemm, comet_quant_act and the
@@ -573,7 +604,9 @@ def decode_sweep(torch, comet, synth, iters=60):
     fraction of the GEMM from its algorithmic bytes (weight codes, scales and
     sums, activation codes and scales, fp16 Y) against 8 TB/s."""
     out = {"timing": f"HIP events around {iters} back-to-back calls per figure, weights rotated "
-                     f"over copies of >= 1 GB", "shapes": {}}
+                     f"over copies of >= 1 GB; the *_graph_us figures replay the same {iters} calls from "
+                     f"one captured HIP graph (no host launch cost; every replay checked against the "
+                     f"eager result, null if one differed)", "shapes": {}}
     for N in (10240, 8192, 28672):
         cfg1 = synth.CONFIGS[f"decode_70b_n{N}_m1"]
         K, nb8 = cfg1.K, cfg1.nb8
@@ -597,14 +630,28 @@ def decode_sweep(torch, comet, synth, iters=60):
                 comet.comet_w4ax_gemm(Xq, xs, w, m, Y=Y)
 
             pq = _per_call_us(torch, pair, iters)
+            # the same calls from a captured HIP graph: the kernels' own rate,
+            # without the Python binding's launch cost per call
+            pair(0)
+            torch.cuda.synchronize()
+            Y_ref, Xq_ref, xs_ref = Y.clone(), Xq.clone(), xs.clone()
+
+            def same():
+                return bool(torch.equal(Y, Y_ref) and torch.equal(Xq, Xq_ref) and torch.equal(xs, xs_ref))
+
+            qg = _graph_per_call_us(torch, lambda i: comet.comet_quant_act(X, ws[i % copies]["perm"], nb8, Xq=Xq,
+                                                                           x_scale=xs), iters, same)
+            pg = _graph_per_call_us(torch, pair, iters, same)
             nbytes = gemm_bytes(m, N, K, nb8, "int4")
             gbs = nbytes / (g * 1e-6) / 1e9
             out["shapes"][f"m{m}_n{N}"] = {
                 "M": m, "N": N, "K": K, "int8_blocks": nb8, "gemm_us": g, "quant_us": q, "pair_us": pq,
+                "quant_graph_us": qg, "pair_graph_us": pg,
                 "gemm_bytes": nbytes, "gemm_gbs": gbs, "gemm_hbm_frac": gbs / PEAK_HBM_GBS,
                 "gemm_tops": 2.0 * m * N * K / (g * 1e-6) / 1e12, "weight_copies": copies}
             log(f"[bench] decode m={m} n={N}: gemm {g:.1f} us ({gbs:.0f} GB/s, "
-                f"{gbs / PEAK_HBM_GBS:.2f} of HBM), quant {q:.1f} us, pair {pq:.1f} us")
+                f"{gbs / PEAK_HBM_GBS:.2f} of HBM), quant {q:.1f} us, pair {pq:.1f} us; from a graph: "
+                f"quant {qg if qg is None else round(qg, 1)} us, pair {pg if pg is None else round(pg, 1)} us")
         del ws, w0
         torch.cuda.empty_cache()
     return out
