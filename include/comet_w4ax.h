@@ -349,6 +349,29 @@ int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t*
                         int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * comet_kv4_attention over sequences of different lengths in one call (a
+ * decode batch: each sequence its own kv heads, each at its own position; the
+ * serving KV cache of QoQ/QServe article, section "运行时设计", holds many
+ * sequences, each with its own length):
+ * kv head g attends to its first T_kv[g] slots, the same formula as
+ * comet_kv4_attention with T = T_kv[g].
+ *
+ *   T_kv       in   device, 4-byte aligned, int32 [Hq / group]: tokens of each kv
+ *                   head; values are clamped to [0, T_max] on the device, and
+ *                   a head with 0 tokens gives an all-zero output
+ *   T_max      in   the largest T_kv (1 <= T_max <= tcap): it sizes the split
+ *                   and the workspace, comet_kv4_attention_workspace_bytes(Hq, d,
+ *                   T_max); chunks past a head's tokens exit at once
+ * Other arguments, layouts and errors as comet_kv4_attention (T_max in the
+ * place of T); NULL also for a null T_kv, ALIGN for a misaligned one. With
+ * every T_kv[g] = T_max the output is bit for bit that of comet_kv4_attention.
+ */
+int comet_kv4_attention_varlen(const void* q_fp16, const void* k_codes, const uint16_t* k_step,
+                               const uint8_t* k_zero, const void* v_codes, const uint16_t* v_step,
+                               const uint8_t* v_zero, int Hq, int group, int d, const int32_t* T_kv, int T_max,
+                               int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP6 layout, sizes: bytes of Xq_fp6 for M rows (padded to a multiple of 16)
  * and of Wq_fp6 for N output channels (0 for an invalid shape).
  */

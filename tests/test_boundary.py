@@ -375,6 +375,15 @@ def test_kv4_rejections():
     assert L.comet_kv4_attention_workspace_bytes(0, 128, 1) == 0
     assert L.comet_kv4_attention_workspace_bytes(4, 96, 1) == 0
 
+    def kv(Tkv=A, Tmax=300, tcap=300, q=A, Hq=8, group=2, d=128, wsb=1 << 20):
+        return L.comet_kv4_attention_varlen(q, A, A, A, A, A, A, Hq, group, d, Tkv, Tmax, tcap, A, A, wsb, None)
+
+    assert kv(Tkv=None) == NULL and kv(q=None) == NULL
+    assert kv(Tmax=0) == SHAPE and kv(tcap=299) == SHAPE and kv(group=3) == SHAPE
+    assert kv(d=100) == UNSUP
+    assert kv(wsb=L.comet_kv4_attention_workspace_bytes(8, 128, 300) - 1) == WORKSPACE
+    assert kv(Tkv=A + 2) == ALIGN and kv(q=MIS) == ALIGN
+
 
 def qq(X=A, M=16, K=512, ldx=512, perm=A, nb8=1, nf=128, Xq=A, xs=A, Xf=A):
     return comet.lib().comet_quant_act_quik_fp6(X, M, K, ldx, perm, nb8, nf, Xq, xs, Xf, None)

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 from gen import synth
+from tests import gpu_common as G
 from tests.layout import pack_kv4_codes, unpack_kv4_codes
 
 pytestmark = pytest.mark.gpu
@@ -155,3 +156,56 @@ def test_kv4_attention_gqa_bench_size(torch):
     """16 sequences of LLaMA-70B's grouped-query attention: 64 query heads over
     8 kv heads each, 4096 cached tokens."""
     check_attention(torch, 1024, 8, 128, 4096, seed=2025, tcap=4096)
+
+
+VARLEN_CASES = [  # Hq, group, d, T_max: the vector kernel (one and two query heads per
+    # workgroup, narrow slices), the matrix kernel (256- and 512-token chunks)
+    (32, 1, 128, 1000), (16, 2, 64, 700), (8, 1, 16, 300), (64, 8, 128, 1000), (256, 8, 128, 2048)]
+
+
+@pytest.mark.parametrize("Hq,group,d,Tmax", VARLEN_CASES)
+def test_kv4_attention_varlen(torch, Hq, group, d, Tmax):
+    """Sequences of different lengths in one call: kv head g attends to its
+    first T_kv[g] slots (clamped to [0, T_max]; an empty head gives zeros).
+    Each head against the oracle over its own prefix, and with every length at
+    T_max the output equals comet_kv4_attention's bit for bit."""
+    import w4ax_mixed_precision_amd as comet
+    from oracle import oracle as O
+    H = Hq // group
+    G.log(f"[kv4 varlen] Hq={Hq} group={group} d={d} Tmax={Tmax}")
+    rng = np.random.default_rng(Hq * 131 + d + Tmax)
+    # empty, one token, full, chunk edges, past T_max (clamped), negative (empty)
+    special = [v for v in (0, 1, Tmax, 255, 256, 257, 511, 512, 513, Tmax + 77, -3) if v <= Tmax + 77]
+    lens = rng.integers(0, Tmax + 1, size=H)
+    k = min(H, len(special))
+    lens[:k] = special[:k]
+    q16, K16, V16 = synth.make_kv(Hq + Tmax, Tmax, H, d, Hq)
+    Ku, Ks, Kz = oracle_cache(O, K16, H, d)
+    Vu, Vs, Vz = oracle_cache(O, V16, H, d)
+    kc = gpu_cache(torch, comet, K16, H, d, Tmax + 3)
+    vc = gpu_cache(torch, comet, V16, H, d, Tmax + 3)
+    q = torch.from_numpy(q16.view(np.float16)).cuda()
+    Tkv = torch.from_numpy(lens.astype(np.int32)).cuda()
+    out = comet.comet_kv4_attention_varlen(q, kc, vc, Tkv, Tmax, group).cpu().numpy()
+    o = out.astype(np.float64)
+    worst = 0.0
+    for g in range(H):
+        T = int(min(max(lens[g], 0), Tmax))
+        hq = slice(g * group, (g + 1) * group)
+        if T == 0:
+            assert (out[hq].view(np.uint16) == 0).all(), f"head {g}: no tokens must give zeros"
+            continue
+        sel = [g] * group
+        ref = O.kv4_attention(q16[hq], Ku[sel, :T], Ks[sel, :T], Kz[sel, :T], Vu[sel, :T], Vs[sel, :T], Vz[sel, :T])
+        step = np.abs(Vs[g, :T].view(np.float16).astype(np.float64))
+        dev = np.abs(Vu[g, :T].astype(np.int16) - Vz[g, :T, None].astype(np.int16)).max(axis=-1)
+        vmax = (step * dev).max()
+        tol = 2.0**-11 * np.abs(ref) + 2.0**-16 * vmax
+        err = np.abs(o[hq] - ref)
+        worst = max(worst, float((err / tol).max()))
+        assert (err <= tol).all(), (g, T, float((err / tol).max()))
+    print(f"kv4 varlen Hq={Hq} group={group} d={d} Tmax={Tmax}: max err/tol {worst:.3f}", flush=True)
+    full = torch.full((H,), Tmax, dtype=torch.int32, device="cuda")
+    a = comet.comet_kv4_attention_varlen(q, kc, vc, full, Tmax, group)
+    b = comet.comet_kv4_attention(q, kc, vc, Tmax, group)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "all lengths at T_max must equal the uniform call"

@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L.comet_kv4_attention_workspace_bytes.argtypes = [I, I, I]
     L.comet_kv4_attention_workspace_bytes.restype = Z
     L.comet_kv4_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P]
+    L.comet_kv4_attention_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, P, I, I, P, P, Z, P]
     L.comet_x_zero_bytes.restype = Z
     L.comet_w4ax_gemm_asym.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, P, Z, P]
     L.comet_w4ax_gemm_asym_partials.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P]
@@ -98,7 +99,7 @@ def lib() -> ctypes.CDLL:
               "comet_quant_act_asym", "comet_w4ax_gemm_asym", "comet_w4ax_gemm_asym_partials",
               "comet_pack_weights_qoq", "comet_quant_act_token_i8", "comet_w4a8_qoq_gemm",
               "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize", "comet_kv4_attention",
-              "comet_pack_weights_quik", "comet_quant_act_quik_fp6", "comet_w4ax_gemm_quik_fp6"):
+              "comet_kv4_attention_varlen", "comet_pack_weights_quik", "comet_quant_act_quik_fp6", "comet_w4ax_gemm_quik_fp6"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -114,7 +115,8 @@ EXPORTS = ("comet_pack_weights", "comet_quant_act", "comet_w4ax_gemm",
            "comet_quant_act_asym", "comet_x_zero_bytes", "comet_w4ax_gemm_asym",
            "comet_w4ax_gemm_asym_partials", "comet_pack_weights_qoq", "comet_quant_act_token_i8",
            "comet_w4a8_qoq_gemm", "comet_w4a8_qoq_gemm_products", "comet_kv4_quantize",
-           "comet_kv4_attention_workspace_bytes", "comet_kv4_attention", "comet_pack_weights_quik",
+           "comet_kv4_attention_workspace_bytes", "comet_kv4_attention", "comet_kv4_attention_varlen",
+           "comet_pack_weights_quik",
            "comet_xf_bytes", "comet_quant_act_quik_fp6", "comet_w4ax_gemm_quik_fp6", "comet_status_string",
            "comet_version")
 
@@ -402,6 +404,26 @@ def comet_kv4_attention(q, kcache: dict, vcache: dict, T: int, group: int = 1, o
                                    _dev_ptr(vcache["zero"]), Hq, group, d, T, kcache["tcap"], _dev_ptr(out),
                                    _dev_ptr(workspace), workspace.numel(), _stream(stream))
     _check("comet_kv4_attention", rc)
+    return out
+
+
+def comet_kv4_attention_varlen(q, kcache: dict, vcache: dict, T_kv, T_max: int, group: int = 1, out=None,
+                               workspace=None, stream=None):
+    """Decode attention of q fp16 [Hq, d]; kv head g over its first T_kv[g]
+    slots (T_kv: int32 cuda tensor [Hq / group], values clamped to [0, T_max])."""
+    import torch
+    Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float16, device=q.device)
+    nbytes = lib().comet_kv4_attention_workspace_bytes(Hq, d, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().comet_kv4_attention_varlen(_dev_ptr(q), _dev_ptr(kcache["codes"]), _dev_ptr(kcache["step"]),
+                                          _dev_ptr(kcache["zero"]), _dev_ptr(vcache["codes"]),
+                                          _dev_ptr(vcache["step"]), _dev_ptr(vcache["zero"]), Hq, group, d,
+                                          _dev_ptr(T_kv), T_max, kcache["tcap"], _dev_ptr(out), _dev_ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    _check("comet_kv4_attention_varlen", rc)
     return out
 
 

@@ -185,9 +185,12 @@ size_t comet_kv4_attention_workspace_bytes(int Hq, int d, int T) {
     return comet::kv4_workspace_bytes(Hq, d, T);
 }
 
-int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t* k_step, const uint8_t* k_zero,
-                        const void* v_codes, const uint16_t* v_step, const uint8_t* v_zero, int Hq, int group, int d,
-                        int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int kv4_attention_impl(const void* q_fp16, const void* k_codes, const uint16_t* k_step, const uint8_t* k_zero,
+                       const void* v_codes, const uint16_t* v_step, const uint8_t* v_zero, int Hq, int group, int d,
+                       int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream,
+                       const int32_t* T_kv) {
     if (!q_fp16 || !k_codes || !k_step || !k_zero || !v_codes || !v_step || !v_zero || !out_fp16 || !workspace)
         return COMET_ERR_NULL;
     if (Hq < 1 || group < 1 || Hq % group != 0 || d < 1 || T < 1 || tcap < T) return COMET_ERR_SHAPE;
@@ -196,12 +199,30 @@ int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t*
     if (workspace_bytes < comet::kv4_workspace_bytes(Hq, d, T)) return COMET_ERR_WORKSPACE;
     if (!aligned16(q_fp16) || !aligned16(k_codes) || !aligned16(k_step) || !aligned16(k_zero) ||
         !aligned16(v_codes) || !aligned16(v_step) || !aligned16(v_zero) || !aligned16(workspace) ||
-        (reinterpret_cast<uintptr_t>(out_fp16) & 1u) != 0)
+        (reinterpret_cast<uintptr_t>(out_fp16) & 1u) != 0 || (reinterpret_cast<uintptr_t>(T_kv) & 3u) != 0)
         return COMET_ERR_ALIGN;
     return hip_status(comet::launch_kv4_attention(
         static_cast<const uint16_t*>(q_fp16), static_cast<const uint8_t*>(k_codes), k_step, k_zero,
         static_cast<const uint8_t*>(v_codes), v_step, v_zero, Hq, group, d, T, tcap,
-        static_cast<uint16_t*>(out_fp16), static_cast<float*>(workspace), stream));
+        static_cast<uint16_t*>(out_fp16), static_cast<float*>(workspace), stream, T_kv));
+}
+
+}  // namespace
+
+int comet_kv4_attention(const void* q_fp16, const void* k_codes, const uint16_t* k_step, const uint8_t* k_zero,
+                        const void* v_codes, const uint16_t* v_step, const uint8_t* v_zero, int Hq, int group, int d,
+                        int T, int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream) {
+    return kv4_attention_impl(q_fp16, k_codes, k_step, k_zero, v_codes, v_step, v_zero, Hq, group, d, T, tcap,
+                              out_fp16, workspace, workspace_bytes, stream, nullptr);
+}
+
+int comet_kv4_attention_varlen(const void* q_fp16, const void* k_codes, const uint16_t* k_step,
+                               const uint8_t* k_zero, const void* v_codes, const uint16_t* v_step,
+                               const uint8_t* v_zero, int Hq, int group, int d, const int32_t* T_kv, int T_max,
+                               int tcap, void* out_fp16, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!T_kv) return COMET_ERR_NULL;
+    return kv4_attention_impl(q_fp16, k_codes, k_step, k_zero, v_codes, v_step, v_zero, Hq, group, d, T_max, tcap,
+                              out_fp16, workspace, workspace_bytes, stream, T_kv);
 }
 
 size_t comet_x_zero_bytes(int M, int K) {

@@ -248,12 +248,17 @@ __device__ __forceinline__ float stride_sum(float v, int n) {
 // once and feeds the G queries, so a grouped-query cache is read once for G
 // heads. Partial outputs (unnormalized),
 // chunk maxima and sums go to the workspace.
+// Tokens of kv head hk: T, or with per-head lengths Tk[hk] clamped to [0, T].
+__device__ __forceinline__ int head_tokens(const int* Tk, int hk, int T) {
+    return Tk ? imin(imax(Tk[hk], 0), T) : T;
+}
+
 template <int CPL, int G, int kDim>              // kDim: d, or 0 for any d
 __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int chunk, int nsplit,
-    float* __restrict__ part, float* __restrict__ ml) {
+    float* __restrict__ part, float* __restrict__ ml, const int* __restrict__ Tk) {
     constexpr int NW = CPL / 8;                  // 32-bit code words per lane
     // Steps whose loads are issued together: one for 16-byte slices (more
     // steps in flight would hold more registers than the occupancy they cost
@@ -275,7 +280,9 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const int j = lane & (D - 1);                // channel slice of the token
     const int sub = lane / D;                    // token slot within the wave step
     const int t0 = s * chunk;
-    const int nt = imin(chunk, T - t0);          // >= 1
+    const int Th = head_tokens(Tk, hk, T);
+    if (t0 >= Th) return;                        // a chunk past this head's tokens (whole workgroup)
+    const int nt = imin(chunk, Th - t0);         // >= 1
     const int rb = d >> 1;                       // bytes per cached vector
 
     float qf[G][CPL], qs[G];
@@ -441,15 +448,23 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
 template <bool kBase2>
 __global__ __launch_bounds__(128) void kv4_attn_combine_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ ml, int nsplit, int d,
-                                                              uint16_t* __restrict__ out) {
+                                                              uint16_t* __restrict__ out, const int* __restrict__ Tk,
+                                                              int group, int chunk, int T) {
     __shared__ float fs[128];
     __shared__ float red2[2];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
     const float* mh = ml + static_cast<size_t>(h) * nsplit * 2;
+    // the chunks that hold this head's tokens (no partials exist past them)
+    const int Th = head_tokens(Tk, h / group, T);
+    if (Th == 0) {                               // no tokens: the output is zero
+        for (int i = tid; i < d; i += 128) out[static_cast<size_t>(h) * d + i] = 0;
+        return;
+    }
+    const int ns = (Th + chunk - 1) / chunk;
     auto ex = [](float x) { return kBase2 ? exp2f(x) : expf(x); };
     float M = -INFINITY;
-    for (int s = tid; s < nsplit; s += 128) M = fmaxf(M, mh[2 * s]);
+    for (int s = tid; s < ns; s += 128) M = fmaxf(M, mh[2 * s]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     if ((tid & 63) == 0) red2[tid >> 6] = M;
@@ -457,7 +472,7 @@ __global__ __launch_bounds__(128) void kv4_attn_combine_kernel(const float* __re
     M = fmaxf(red2[0], red2[1]);
     __syncthreads();
     float L = 0.0f;
-    for (int s = tid; s < nsplit; s += 128) L += ex(mh[2 * s] - M) * mh[2 * s + 1];
+    for (int s = tid; s < ns; s += 128) L += ex(mh[2 * s] - M) * mh[2 * s + 1];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     if ((tid & 63) == 0) red2[tid >> 6] = L;
@@ -467,8 +482,8 @@ __global__ __launch_bounds__(128) void kv4_attn_combine_kernel(const float* __re
     for (int i0 = 0; i0 < d; i0 += 128) {
         const int i = i0 + tid;
         float a = 0.0f;
-        for (int s0 = 0; s0 < nsplit; s0 += 128) {
-            const int n = imin(128, nsplit - s0);
+        for (int s0 = 0; s0 < ns; s0 += 128) {
+            const int n = imin(128, ns - s0);
             __syncthreads();                 // the previous batch is read
             if (tid < n) fs[tid] = ex(mh[2 * (s0 + tid)] - M);
             __syncthreads();
@@ -552,7 +567,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const uint8_t* __restrict__ vz, int group, int T, int tcap, float scale, int nsplit,
-    float* __restrict__ part, float* __restrict__ ml) {
+    float* __restrict__ part, float* __restrict__ ml, const int* __restrict__ Tk) {
     constexpr int D = 128;         // head dimension
     constexpr int RB = D / 2;      // bytes per cached vector
     constexpr int TW = CH / 64;    // 16-token score tiles per wave
@@ -570,7 +585,9 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_mfma_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int t0 = s * CH;
-    const int nt = imin(CH, T - t0);                    // >= 1
+    const int Th = head_tokens(Tk, hk, T);
+    if (t0 >= Th) return;                               // past this head's tokens (whole workgroup)
+    const int nt = imin(CH, Th - t0);                   // >= 1
     const size_t base = static_cast<size_t>(hk) * tcap + t0;
     // buffer resources over the chunk's nt tokens: loads past them read 0
     const Rsrc rkc = make_rsrc(kc + base * RB, static_cast<uint32_t>(nt) * RB);
@@ -800,7 +817,7 @@ int launch_kv4_quantize(const uint16_t* X, int ntok, int H, int d, int ldx, int 
 
 int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* kz,
                          const uint8_t* vc, const uint16_t* vs, const uint8_t* vz, int Hq, int group, int d, int T,
-                         int tcap, uint16_t* out, float* workspace, void* stream) {
+                         int tcap, uint16_t* out, float* workspace, void* stream, const int* Tk) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     // Grouped-query heads at d = 128: the matrix-instruction kernel, one
     // workgroup per (kv head, chunk) for all the group's query heads; chunks
@@ -818,15 +835,15 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
         const float sc = 1.4426950408889634f / sqrtf(static_cast<float>(d));   // log2(e) / sqrt(d)
         const int grid = Hk * ns;
         if (group <= 8) {
-            if (ch == 512) kv4_attn_mfma_kernel<8, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
-            else kv4_attn_mfma_kernel<8, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+            if (ch == 512) kv4_attn_mfma_kernel<8, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp, Tk);
+            else kv4_attn_mfma_kernel<8, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp, Tk);
         } else {
-            if (ch == 512) kv4_attn_mfma_kernel<16, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
-            else kv4_attn_mfma_kernel<16, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp);
+            if (ch == 512) kv4_attn_mfma_kernel<16, 512><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp, Tk);
+            else kv4_attn_mfma_kernel<16, 256><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, T, tcap, sc, ns, pt, mlp, Tk);
         }
         const int e = static_cast<int>(hipGetLastError());
         if (e != 0) return e;
-        kv4_attn_combine_kernel<true><<<Hq, 128, 0, st>>>(pt, mlp, ns, d, out);
+        kv4_attn_combine_kernel<true><<<Hq, 128, 0, st>>>(pt, mlp, ns, d, out, Tk, group, ch, T);
         return static_cast<int>(hipGetLastError());
     }
     // The vector kernel. Tokens per workgroup: 256, or 512 / 1024 when the
@@ -852,10 +869,10 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     do {                                                                                                       \
         if (d == 128)                                                                                          \
             kv4_attn_chunk_kernel<C, GG, 128><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, \
-                                                                          tcap, scale, chunk, nsplit, part, ml); \
+                                                                          tcap, scale, chunk, nsplit, part, ml, Tk); \
         else                                                                                                   \
             kv4_attn_chunk_kernel<C, GG, 0><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T,   \
-                                                                        tcap, scale, chunk, nsplit, part, ml);   \
+                                                                        tcap, scale, chunk, nsplit, part, ml, Tk); \
     } while (0)
     if (G == 2) {
         if (cpl == 32) COMET_KV4_CHUNK(32, 2); else if (cpl == 16) COMET_KV4_CHUNK(16, 2); else COMET_KV4_CHUNK(8, 2);
@@ -865,7 +882,7 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
 #undef COMET_KV4_CHUNK
     const int e = static_cast<int>(hipGetLastError());
     if (e != 0) return e;
-    kv4_attn_combine_kernel<false><<<Hq, 128, 0, st>>>(part, ml, nsplit, d, out);
+    kv4_attn_combine_kernel<false><<<Hq, 128, 0, st>>>(part, ml, nsplit, d, out, Tk, group, chunk, T);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -23,8 +23,10 @@ int launch_kv4_quantize(const uint16_t* X, int ntok, int H, int d, int ldx, int 
                         uint16_t* step, uint8_t* zero, void* stream);
 
 // q fp16 [Hq][d]; out fp16 [Hq][d]; query head h reads kv head h / group.
+// Tk (device, Hq / group int32) or null: kv head g attends to its first
+// min(max(Tk[g], 0), T) slots (an empty head gives zeros), else all T.
 int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* kz,
                          const uint8_t* vc, const uint16_t* vs, const uint8_t* vz, int Hq, int group, int d, int T,
-                         int tcap, uint16_t* out, float* workspace, void* stream);
+                         int tcap, uint16_t* out, float* workspace, void* stream, const int* Tk = nullptr);
 
 }  // namespace comet
