@@ -545,6 +545,23 @@ def kv4_attention_measure(torch, comet, synth, T=4096, seqs=16, iters=20):
         out["shapes"][name] = {"query_heads": Hq, "kv_heads": H, "T": T, "d": d, "us": us,
                                "algorithmic_bytes": nbytes, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                                "cache_copies": copies}
+        # the same batch with the sequences at different positions (a decode
+        # batch): lengths drawn uniformly from [T/8, T] per sequence, one call
+        seq_T = np.random.default_rng(78).integers(T // 8, T + 1, size=seqs).astype(np.int32)
+        Tkv = torch.from_numpy(np.repeat(seq_T, H // seqs)).cuda()
+
+        def att_var():
+            kc, vc = caches[it["i"] % copies]
+            it["i"] += 1
+            comet.comet_kv4_attention_varlen(q, kc, vc, Tkv, T, group, out=o, workspace=ws)
+
+        usv = _time_variants(torch, (("att", att_var),), iters)["att"]
+        vbytes = 2 * (H // seqs) * int(seq_T.sum()) * (d // 2 + 3) + 2 * Hq * d * 2
+        gbsv = vbytes / (usv * 1e-6) / 1e9
+        out["shapes"][name + "_varlen"] = {"query_heads": Hq, "kv_heads": H, "T_max": T,
+                                           "seq_tokens": [int(x) for x in seq_T], "d": d, "us": usv,
+                                           "algorithmic_bytes": vbytes, "gbs": gbsv,
+                                           "hbm_frac": gbsv / PEAK_HBM_GBS, "cache_copies": copies}
         del caches, q, o, ws
         torch.cuda.empty_cache()
     return out
