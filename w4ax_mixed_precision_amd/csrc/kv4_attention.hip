@@ -270,8 +270,12 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     __shared__ float red[G * 512];
     __shared__ float wred[G][4];
     const int rq = group / G;                    // workgroups per kv head and chunk
-    const int s = blockIdx.x % nsplit;
-    const int r = blockIdx.x / nsplit;
+    // chunk-major order: consecutive workgroups (which the dispatcher deals
+    // round-robin to the XCDs) take the same chunk of different heads, so
+    // with per-head lengths the chunks that hold tokens spread over the XCDs
+    const int nr = gridDim.x / nsplit;
+    const int s = blockIdx.x / nr;
+    const int r = blockIdx.x - s * nr;
     const int hk = r / rq;
     const int h0 = hk * group + (r - hk * rq) * G;   // first query head
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -579,8 +583,10 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t vzt[CH];
     __shared__ __attribute__((aligned(16))) float red[4][GQ][D];
     __shared__ float wmax[4][16], wsum[4][16], wsmax[4];
-    const int s = blockIdx.x % nsplit;
-    const int hk = blockIdx.x / nsplit;
+    // chunk-major order (see kv4_attn_chunk_kernel)
+    const int nhk = gridDim.x / nsplit;
+    const int s = blockIdx.x / nhk;
+    const int hk = blockIdx.x - s * nhk;
     const int h0 = hk * group;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
