@@ -115,3 +115,21 @@ def test_pack_quik_matches_oracle(orc, nb8, nf):
     assert np.array_equal(decode_wq_fp6(pk["WqF"], N, kq, nb8), qw)
     if nf:
         assert np.array_equal(decode_wf(pk["Wf"], N, nf), W[:, perm[kq:]])
+
+
+def test_fp6_activation_tile_covers_every_byte_once():
+    """The FP6 activation tile (the quantizer writes it, the GEMM and the test
+    decoder read it): every byte of a 1536-byte tile belongs to exactly one
+    (row, group, byte), a row's heads form one 64-byte run and its tails one
+    32-byte run, and the 8-bit tile's two 1 KB halves use the heads' map."""
+    from tests.layout import _tile_rows_index
+    head, tail = _tile_rows_index()
+    seen = np.zeros(1536, np.int32)
+    np.add.at(seen, head.ravel(), 1)
+    np.add.at(seen, tail.ravel(), 1)
+    assert (seen == 1).all()
+    for r in range(16):
+        assert sorted(head[r].ravel()) == list(range(64 * r, 64 * r + 64))
+        assert sorted(tail[r].ravel()) == list(range(1024 + 32 * r, 1024 + 32 * r + 32))
+    # a lane's 16-byte head and 8-byte tail stay aligned for the 128- and 64-bit LDS reads
+    assert (head[:, :, 0] % 16 == 0).all() and (tail[:, :, 0] % 8 == 0).all()
