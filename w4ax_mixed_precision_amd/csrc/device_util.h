@@ -107,13 +107,6 @@ __device__ __forceinline__ void lds_buf16(Rsrc r, uint32_t voff, uint32_t soff, 
         r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_piece)), 16,
         voff, soff, 0, 0);
 }
-// The same with the non-temporal hint (the data is read once: the L2 keeps
-// it only with low priority).
-__device__ __forceinline__ void lds_buf16_nt(Rsrc r, uint32_t voff, uint32_t soff, uint8_t* lds_piece) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_piece)), 16,
-        voff, soff, 0, 2);
-}
 __device__ __forceinline__ void lds_buf4(Rsrc r, uint32_t voff, uint32_t soff, uint8_t* lds_piece) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_piece)), 4,

@@ -575,6 +575,14 @@ __global__ __launch_bounds__(T) void quant_act_kernel(
 template <int kWaves>
 constexpr int row_passes() { return kWaves == 8 ? 2 : 1; }
 
+// lds_buf16 with the non-temporal hint (data read once: the L2 keeps it only
+// with low priority).
+__device__ __forceinline__ void lds_buf16_nt(Rsrc r, uint32_t voff, uint32_t soff, uint8_t* lds_piece) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_piece)), 16,
+        voff, soff, 0, 2);
+}
+
 template <int kWaves>
 __device__ __forceinline__ void stage_row(const uint16_t* xr, int K, int wave, int lane, uint8_t* __restrict__ buf) {
     const Rsrc r = make_rsrc(xr, 2u * static_cast<uint32_t>(K));
