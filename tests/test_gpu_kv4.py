@@ -5,8 +5,9 @@ against the oracle's step 9.
 The cache quantizer is compared bit for bit (codes, fp16 steps, zero points),
 and slots outside the written range must stay untouched. The attention output
 is compared with the oracle's float64 result on the same codes within
-    |out - ref| <= 2^-11 |ref| + 2^-16 vmax_h,
-the fp16 rounding of the result plus an FP32 allowance: vmax_h is the largest
+    |out - ref| <= 2^-11 |ref| + 2^-25 + 2^-16 vmax_h,
+the fp16 rounding of the result (2^-25, half the spacing of fp16 subnormals,
+bounds it below 2^-14) plus an FP32 allowance: vmax_h is the largest
 dequantized value magnitude of the head, and 2^-16 vmax_h is several hundred
 FP32 rounding units of it, far above what the FP32 sums and the exponentials
 of the scores (relative error a few units) contribute, and far below the
@@ -91,12 +92,21 @@ def test_kv4_quantize_bit_exact(torch, ntok, H, d, pos, tcap):
         assert (b[:, outside] == 0xAB).all() and (gs[:, outside] == 0x1234).all() and (gz[:, outside] == 0xCD).all()
 
 
-def check_attention(torch, Hq, group, d, T, seed, tcap=None, split=None):
+def rescale16(x16, f):
+    """fp16 bit patterns times f, rounded to fp16 (to nearest even)."""
+    return (x16.view(np.float16).astype(np.float64) * f).astype(np.float16).view(np.uint16)
+
+
+def check_attention(torch, Hq, group, d, T, seed, tcap=None, split=None, qscale=1.0, vscale=1.0):
     import w4ax_mixed_precision_amd as comet
     from oracle import oracle as O
     H = Hq // group
     tcap = T + 5 if tcap is None else tcap
     q16, K16, V16 = synth.make_kv(seed, T, H, d, Hq)
+    if qscale != 1.0:
+        q16 = rescale16(q16, qscale)
+    if vscale != 1.0:
+        V16 = rescale16(V16, vscale)
     Ku, Ks, Kz = oracle_cache(O, K16, H, d)
     Vu, Vs, Vz = oracle_cache(O, V16, H, d)
     rep = np.arange(Hq) // group
@@ -117,7 +127,7 @@ def check_attention(torch, Hq, group, d, T, seed, tcap=None, split=None):
         u = Vu[h0:h0 + 64].astype(np.int16)
         dev[h0:h0 + 64] = np.abs(u - Vz[h0:h0 + 64, :, None].astype(np.int16)).max(axis=-1)
     vmax = (step * dev).max(axis=1)[rep][:, None]
-    tol = 2.0**-11 * np.abs(ref) + 2.0**-16 * vmax
+    tol = 2.0**-11 * np.abs(ref) + 2.0**-25 + 2.0**-16 * vmax
     err = np.abs(o - ref)
     ratio = float((err / tol).max())
     print(f"kv4 attention Hq={Hq} group={group} d={d} T={T}: max err {err.max():.3e}, "
@@ -144,6 +154,28 @@ ATT_CASES = [  # Hq, group, d, T
 @pytest.mark.parametrize("Hq,group,d,T", ATT_CASES)
 def test_kv4_attention_parity(torch, Hq, group, d, T):
     check_attention(torch, Hq, group, d, T, seed=7 + T, split=(T - 1 if T > 1 else None))
+
+
+SCALE_CASES = [  # Hq, group, d, T, query scale, value scale
+    # a near one-hot softmax (weights from 1 down to underflow in one chunk)
+    (8, 1, 128, 700, 16.0, 1.0), (4, 2, 256, 300, 16.0, 1.0),
+    # value steps in the fp16 subnormal range (the outputs too: there the
+    # fp16 rounding of the result, 2^-25, bounds what can be checked), and
+    # near the top of fp16
+    (8, 1, 128, 513, 1.0, 2.0**-18), (8, 1, 128, 513, 16.0, 2.0**-13), (4, 2, 256, 300, 1.0, 2.0**-18),
+    (8, 1, 128, 300, 4.0, 2.0**12), (4, 1, 64, 300, 1.0, 2.0**-18), (8, 2, 16, 300, 1.0, 2.0**12),
+    # all-zero values: every step 0, the output exactly 0
+    (4, 1, 128, 300, 1.0, 0.0), (4, 2, 256, 70, 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("Hq,group,d,T,qs,vs", SCALE_CASES)
+def test_kv4_attention_value_ranges(torch, Hq, group, d, T, qs, vs):
+    """The vector kernel over value and score ranges far from N(0, 1): the
+    value weights are scaled by a power of two per chunk before they are
+    split into fp16 parts, which must hold from subnormal steps to steps near
+    the top of fp16 and for weights that span the whole exponent range."""
+    G.log(f"[kv4 ranges] Hq={Hq} group={group} d={d} T={T} qscale={qs} vscale={vs}")
+    check_attention(torch, Hq, group, d, T, seed=11 + T, qscale=qs, vscale=vs)
 
 
 def test_kv4_attention_bench_size(torch):
@@ -200,7 +232,7 @@ def test_kv4_attention_varlen(torch, Hq, group, d, Tmax):
         step = np.abs(Vs[g, :T].view(np.float16).astype(np.float64))
         dev = np.abs(Vu[g, :T].astype(np.int16) - Vz[g, :T, None].astype(np.int16)).max(axis=-1)
         vmax = (step * dev).max()
-        tol = 2.0**-11 * np.abs(ref) + 2.0**-16 * vmax
+        tol = 2.0**-11 * np.abs(ref) + 2.0**-25 + 2.0**-16 * vmax
         err = np.abs(o[hq] - ref)
         worst = max(worst, float((err / tol).max()))
         assert (err <= tol).all(), (g, T, float((err / tol).max()))
