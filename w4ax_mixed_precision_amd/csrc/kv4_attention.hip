@@ -252,6 +252,26 @@ __device__ __forceinline__ float fdot2_bits(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(kv_half2, a), __builtin_bit_cast(kv_half2, b), c, false);
 }
 
+// Wave priority from progress through the workgroup's work (done of total
+// loop steps): 3 in the first quarter down to 0 in the last. All workgroups
+// of a launch start together, eight per CU, and with equal priorities the
+// oldest waves win the issue arbitration, so the last-dispatched workgroups
+// fell behind and ran their value loops alone at the end (LLaMA-7B decode
+// shape, 1024-token chunks: per-CU finishing times spread over 17 us of a
+// 56 us kernel); letting the waves that are behind go first brings the
+// spread to 8 us.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+    const int lv = (4 * done) / total;
+    if (lv == 0)
+        __builtin_amdgcn_s_setprio(3);
+    else if (lv == 1)
+        __builtin_amdgcn_s_setprio(2);
+    else if (lv == 2)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
 // channels of one token (d / CPL lanes share a token); each code is converted
 // once and feeds the G queries, so a grouped-query cache is read once for G
@@ -269,10 +289,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
     const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int chunk, int nsplit,
     float* __restrict__ part, float* __restrict__ ml, const int* __restrict__ Tk) {
     constexpr int NW = CPL / 8;                  // 32-bit code words per lane
-    // Steps whose loads are issued together: one for 16-byte slices (more
-    // steps in flight would hold more registers than the occupancy they cost
-    // is worth: LLaMA-7B / -70B decode shapes 81.4 / 87.3 us with one, 83-86 /
-    // 103-104 with two, 124 / 131 with four), four for the narrow slices.
+    // Token steps whose loads are issued together: two for 16-byte slices
+    // (the value loop takes two per step by construction; in the score loop
+    // two gave 72 us against 73.6 with one on the LLaMA-7B decode shape, four
+    // 62 against 61 with two, all at 64 registers), four for the narrow slices.
     constexpr int U = NW == 4 ? 2 : 4;
     if constexpr (kDim != 0) d = kDim;
     __shared__ float sc[G][kKvChunkMax];
@@ -342,7 +362,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
 
     // scores a_t = s_t (q . u_t - z_t sum q) / sqrt(d)
     float vmx = 0.0f;                            // the chunk's largest value step (NW == 4)
+    const int ptotal = (niter + U - 1) / U + (niter + 1) / 2;   // loop steps of the two loops (NW == 4)
     for (int it0 = 0; it0 < niter; it0 += U) {
+        if constexpr (NW == 4) progress_priority(it0 / U, ptotal);
         uint32_t w[U][NW];
         float st[U];
         int zt[U];
@@ -467,6 +489,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
         if (m[G] > 0.0f) frexpf(m[G], &ex);
         const float wsc = m[G] > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
         for (int it0 = 0; it0 < niter; it0 += 2) {
+            progress_priority((niter + U - 1) / U + it0 / 2, ptotal);
             uint32_t w[2][4];
             float st[2];
             int zt[2];
