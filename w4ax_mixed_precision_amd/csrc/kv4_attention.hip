@@ -243,35 +243,6 @@ __device__ __forceinline__ float stride_sum(float v, int n) {
     return v;
 }
 
-// c + a.x b.x + a.y b.y over fp16 pairs given as bits (v_dot2c_f32_f16, FP32
-// result). 4-bit codes enter as fp16 subnormals (a code u in the low bits is
-// the value u 2^-24, or 16 u 2^-24 for a high nibble left in place), so no
-// bias term has to cancel; the kernels run with fp16 denormals kept.
-typedef _Float16 kv_half2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float fdot2_bits(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(kv_half2, a), __builtin_bit_cast(kv_half2, b), c, false);
-}
-
-// Wave priority from progress through the workgroup's work (done of total
-// loop steps): 3 in the first quarter down to 0 in the last. All workgroups
-// of a launch start together, eight per CU, and with equal priorities the
-// oldest waves win the issue arbitration, so the last-dispatched workgroups
-// fell behind and ran their value loops alone at the end (LLaMA-7B decode
-// shape, 1024-token chunks: per-CU finishing times spread over 17 us of a
-// 56 us kernel); letting the waves that are behind go first brings the
-// spread to 8 us.
-__device__ __forceinline__ void progress_priority(int done, int total) {
-    const int lv = (4 * done) / total;
-    if (lv == 0)
-        __builtin_amdgcn_s_setprio(3);
-    else if (lv == 1)
-        __builtin_amdgcn_s_setprio(2);
-    else if (lv == 2)
-        __builtin_amdgcn_s_setprio(1);
-    else
-        __builtin_amdgcn_s_setprio(0);
-}
-
 // One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
 // channels of one token (d / CPL lanes share a token); each code is converted
 // once and feeds the G queries, so a grouped-query cache is read once for G
@@ -283,21 +254,21 @@ __device__ __forceinline__ int head_tokens(const int* Tk, int hk, int T) {
 }
 
 template <int CPL, int G, int kDim>              // kDim: d, or 0 for any d
-__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL == 32 && G == 1 ? 8 : 1))) void kv4_attn_chunk_kernel(
+__global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const uint8_t* __restrict__ vz, int group, int d, int T, int tcap, float scale, int chunk, int nsplit,
     float* __restrict__ part, float* __restrict__ ml, const int* __restrict__ Tk) {
     constexpr int NW = CPL / 8;                  // 32-bit code words per lane
-    // Token steps whose loads are issued together: two for 16-byte slices
-    // (the value loop takes two per step by construction; in the score loop
-    // two gave 72 us against 73.6 with one on the LLaMA-7B decode shape, four
-    // 62 against 61 with two, all at 64 registers), four for the narrow slices.
-    constexpr int U = NW == 4 ? 2 : 4;
+    // Steps whose loads are issued together: one for 16-byte slices (more
+    // steps in flight would hold more registers than the occupancy they cost
+    // is worth: LLaMA-7B / -70B decode shapes 81.4 / 87.3 us with one, 83-86 /
+    // 103-104 with two, 124 / 131 with four), four for the narrow slices.
+    constexpr int U = NW == 4 ? 1 : 4;
     if constexpr (kDim != 0) d = kDim;
     __shared__ float sc[G][kKvChunkMax];
     __shared__ float red[G * 512];
-    __shared__ float wred[G + 1][4];
+    __shared__ float wred[G][4];
     const int rq = group / G;                    // workgroups per kv head and chunk
     // chunk-major order: consecutive workgroups (which the dispatcher deals
     // round-robin to the XCDs) take the same chunk of different heads, so
@@ -329,60 +300,20 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
         for (int c = 0; c < CPL; ++c) a += qf[g][c];
         qs[g] = group_sum(a, D);
     }
-    // 32-channel slices (NW == 4): the query as fp16 pairs in the order the
-    // score loop takes the code pairs of a word: channels (0, 4), (2, 6),
-    // (1, 5), (3, 7) of each 8
-    uint32_t q2[G][NW == 4 ? 16 : 1];
-    if constexpr (NW == 4) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const uint16_t* qg = q + static_cast<size_t>(h0 + g) * d + CPL * j;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint4 v = *reinterpret_cast<const uint4*>(qg + 8 * k);
-                q2[g][4 * k + 0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-                q2[g][4 * k + 1] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-                q2[g][4 * k + 2] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-                q2[g][4 * k + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-            }
-        }
-    }
 
     const size_t base = static_cast<size_t>(hk) * tcap + t0;   // slot of the chunk's first token
     const int per_step = 4 * TPW;
     const int niter = (nt + per_step - 1) / per_step;
     const int first = wave * TPW + sub;
 
-    // 32-channel slices load through buffer resources over the chunk's nt
-    // tokens (past them a load reads 0), so those loops need no guards
-    const uint32_t nt32 = static_cast<uint32_t>(nt), rb32 = static_cast<uint32_t>(rb);
-    const Rsrc rkc = make_rsrc(kc + base * rb, nt32 * rb32), rvc = make_rsrc(vc + base * rb, nt32 * rb32);
-    const Rsrc rks = make_rsrc(ks + base, 2u * nt32), rvs = make_rsrc(vs + base, 2u * nt32);
-    const Rsrc rkz = make_rsrc(kz + base, nt32), rvz = make_rsrc(vz + base, nt32);
-
     // scores a_t = s_t (q . u_t - z_t sum q) / sqrt(d)
-    float vmx = 0.0f;                            // the chunk's largest value step (NW == 4)
-    const int ptotal = (niter + U - 1) / U + (niter + 1) / 2;   // loop steps of the two loops (NW == 4)
     for (int it0 = 0; it0 < niter; it0 += U) {
-        if constexpr (NW == 4) progress_priority(it0 / U, ptotal);
         uint32_t w[U][NW];
         float st[U];
         int zt[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            if constexpr (NW == 4) {
-                const uint32_t ti = static_cast<uint32_t>(i);
-                const uint4 v = buf_load16(rkc, ti * rb32 + 16u * j);
-                w[u][0] = v.x;
-                w[u][1] = v.y;
-                w[u][2] = v.z;
-                w[u][3] = v.w;
-                st[u] = h2f(__builtin_amdgcn_raw_buffer_load_b16(rks, 2u * ti, 0, 0));
-                zt[u] = __builtin_amdgcn_raw_buffer_load_b8(rkz, ti, 0, 0);
-                vmx = fmaxf(vmx, h2f(__builtin_amdgcn_raw_buffer_load_b16(rvs, 2u * ti, 0, 0)));
-                continue;
-            }
 #pragma unroll
             for (int k = 0; k < NW; ++k) w[u][k] = 0;
             st[u] = 0.0f;
@@ -397,39 +328,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            float dot[G];
+            float dot[G], x[CPL];
+            codes_to_float<NW>(w[u], x);
 #pragma unroll
             for (int g = 0; g < G; ++g) dot[g] = 0.0f;
-            if constexpr (NW == 4) {
-                // code pairs of a word (channels 0 + 4 and 2 + 6 from the low
-                // nibbles, 1 + 5 and 3 + 7 from the high ones, each pair two
-                // 16-bit fields), one dot product per pair and query; the
-                // high-nibble sums carry a factor 16
-                float dh[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) dh[g] = 0.0f;
+            for (int c = 0; c < CPL; ++c) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t wk = w[u][k], sk = wk >> 8;
-                    const uint32_t p4[4] = {wk & 0x000F000Fu, sk & 0x000F000Fu, wk & 0x00F000F0u, sk & 0x00F000F0u};
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        dot[g] = fdot2_bits(p4[0], q2[g][4 * k + 0], dot[g]);
-                        dot[g] = fdot2_bits(p4[1], q2[g][4 * k + 1], dot[g]);
-                        dh[g] = fdot2_bits(p4[2], q2[g][4 * k + 2], dh[g]);
-                        dh[g] = fdot2_bits(p4[3], q2[g][4 * k + 3], dh[g]);
-                    }
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) dot[g] = fmaf(dh[g], 0x1p20f, dot[g] * 0x1p24f);
-            } else {
-                float x[CPL];
-                codes_to_float<NW>(w[u], x);
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g) dot[g] = fmaf(qf[g][c], x[c], dot[g]);
-                }
+                for (int g = 0; g < G; ++g) dot[g] = fmaf(qf[g][c], x[c], dot[g]);
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) dot[g] = group_sum(dot[g], D);
@@ -441,15 +347,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
     }
     __syncthreads();
 
-    constexpr int GM = NW == 4 ? G + 1 : G;     // the value-step maximum rides along
-    float m[GM], l[G];
+    float m[G], l[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = -INFINITY;
         for (int i = threadIdx.x; i < nt; i += kKvThreads) m[g] = fmaxf(m[g], sc[g][i]);
     }
-    if constexpr (NW == 4) m[G] = vmx;
-    block_reduce<GM, true>(m, wred);
+    block_reduce<G, true>(m, wred);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         l[g] = 0.0f;
@@ -460,14 +364,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
         }
     }
     block_reduce<G, false>(l, wred);             // its barriers also publish sc
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (threadIdx.x == g) {
-            const size_t row = static_cast<size_t>(h0 + g) * nsplit + s;
-            ml[2 * row] = m[g];
-            ml[2 * row + 1] = l[g];
-        }
-    }
 
     // acc = sum_t p_t s_t u_t - sum_t p_t s_t z_t, the second sum once per token
     float acc[G][CPL], wz[G];
@@ -477,73 +373,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[g][c] = 0.0f;
     }
-    if constexpr (NW == 4) {
-        // Two tokens per step: a byte permute puts byte b of both tokens'
-        // word k in the two 16-bit fields of one register, two masks split
-        // it into the channel pairs 8k + 2b (low nibbles) and 8k + 2b + 1
-        // (high nibbles, x16), and one dot product per pair takes both
-        // tokens. The weights w = p s go in as two fp16 parts (hi + lo, to
-        // about 2^-20 relative) after a power-of-two scale that puts the
-        // chunk's largest step in [2^13, 2^14).
-        int ex = 0;
-        if (m[G] > 0.0f) frexpf(m[G], &ex);
-        const float wsc = m[G] > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-        for (int it0 = 0; it0 < niter; it0 += 2) {
-            progress_priority((niter + U - 1) / U + it0 / 2, ptotal);
-            uint32_t w[2][4];
-            float st[2];
-            int zt[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint32_t ti = static_cast<uint32_t>((it0 + u) * per_step + first);
-                const uint4 v = buf_load16(rvc, ti * rb32 + 16u * j);
-                w[u][0] = v.x;
-                w[u][1] = v.y;
-                w[u][2] = v.z;
-                w[u][3] = v.w;
-                st[u] = h2f(__builtin_amdgcn_raw_buffer_load_b16(rvs, 2u * ti, 0, 0));
-                zt[u] = __builtin_amdgcn_raw_buffer_load_b8(rvz, ti, 0, 0);
-            }
-            uint32_t hi[G], lo[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float wt[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int i = (it0 + u) * per_step + first;
-                    wt[u] = i < nt ? sc[g][i] * st[u] : 0.0f;
-                    wz[g] = fmaf(wt[u], static_cast<float>(zt[u]), wz[g]);
-                    wt[u] *= wsc;
-                }
-                const auto h = __builtin_amdgcn_cvt_pkrtz(wt[0], wt[1]);
-                const auto r = __builtin_amdgcn_cvt_pkrtz(wt[0] - static_cast<float>(h.x),
-                                                          wt[1] - static_cast<float>(h.y));
-                hi[g] = __builtin_bit_cast(uint32_t, h);
-                lo[g] = __builtin_bit_cast(uint32_t, r);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t x = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x0C000C00u | ((4u + b) << 16) | b);
-                    const uint32_t xe = x & 0x000F000Fu, xo = x & 0x00F000F0u;
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        acc[g][8 * k + 2 * b] = fdot2_bits(xe, hi[g], acc[g][8 * k + 2 * b]);
-                        acc[g][8 * k + 2 * b] = fdot2_bits(xe, lo[g], acc[g][8 * k + 2 * b]);
-                        acc[g][8 * k + 2 * b + 1] = fdot2_bits(xo, hi[g], acc[g][8 * k + 2 * b + 1]);
-                        acc[g][8 * k + 2 * b + 1] = fdot2_bits(xo, lo[g], acc[g][8 * k + 2 * b + 1]);
-                    }
-                }
-            }
-        }
-        // back to real units: x 2^24 (low nibbles) or 2^20 (high), / the scale
-        const float fe = 0x1p24f / wsc, fo = 0x1p20f / wsc;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[g][c] *= (c & 1) ? fo : fe;
-    } else
     for (int it0 = 0; it0 < niter; it0 += U) {
         uint32_t w[U][NW];
         float st[U];
@@ -604,6 +433,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(CPL 
     for (int i = threadIdx.x; i < G * d; i += kKvThreads) {
         const int g = i / d;
         part[(static_cast<size_t>(h0 + g) * nsplit + s) * d + (i - g * d)] = red[i];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (threadIdx.x == g) {
+            const size_t row = static_cast<size_t>(h0 + g) * nsplit + s;
+            ml[2 * row] = m[g];
+            ml[2 * row + 1] = l[g];
+        }
     }
 }
 
