@@ -152,7 +152,9 @@ ATT_CASES = [  # Hq, group, d, T
     # partial score tiles and value steps, 512-token chunks with one token in
     # the last
     (16, 16, 128, 300), (12, 12, 128, 33), (24, 3, 128, 1), (10, 5, 128, 257), (64, 8, 128, 1000),
-    (4096, 2, 128, 513)]
+    (4096, 2, 128, 513),
+    # more than 16 chunks per head (the combine step's LDS path), both kernels
+    (4, 1, 128, 5000), (16, 8, 128, 5000)]
 
 
 @pytest.mark.parametrize("Hq,group,d,T", ATT_CASES)
@@ -196,7 +198,9 @@ def test_kv4_attention_gqa_bench_size(torch):
 
 VARLEN_CASES = [  # Hq, group, d, T_max: the vector kernel (one and two query heads per
     # workgroup, narrow slices), the matrix kernel (256- and 512-token chunks)
-    (32, 1, 128, 1000), (16, 2, 64, 700), (8, 1, 16, 300), (64, 8, 128, 1000), (256, 8, 128, 2048)]
+    (32, 1, 128, 1000), (16, 2, 64, 700), (8, 1, 16, 300), (64, 8, 128, 1000), (256, 8, 128, 2048),
+    # more than 16 chunks at T_max, fewer in the shorter heads
+    (16, 1, 128, 5000)]
 
 
 @pytest.mark.parametrize("Hq,group,d,Tmax", VARLEN_CASES)
