@@ -243,6 +243,24 @@ __device__ __forceinline__ float stride_sum(float v, int n) {
     return v;
 }
 
+// 32-channel key slices on fp16 dot products (v_dot2c_f32_f16, FP32 sum):
+// a code word's 8 codes become four fp16 pairs of u - z, exact integers in
+// [-15, 15] (a byte permute places each code under the fp16 exponent of 1024,
+// 0x64NN = 1024 + NN, and a packed fp16 add of -(1024 + z) leaves u - z), in
+// the channel order (0, 2), (4, 6), (1, 3), (5, 7) that the query pairs are
+// held in. Both operands are normal fp16 numbers (or zero), whose products
+// the instruction sums to within about one FP32 rounding; the zero point is
+// inside the operand, so no z sum q term cancels afterwards.
+typedef _Float16 kv_half2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float fdot2_bits(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(kv_half2, a), __builtin_bit_cast(kv_half2, b), c, false);
+}
+__device__ __forceinline__ uint32_t pk_add_half2(uint32_t a, uint32_t b) {
+    const kv_half2 r = __builtin_bit_cast(kv_half2, a) + __builtin_bit_cast(kv_half2, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+constexpr uint32_t kCodeBias = 0x64646464u;   // fp16 bits 0x64NN = 1024 + NN for NN < 1024
+
 // One (kv head, G of its query heads, chunk of 256 tokens). A lane holds CPL
 // channels of one token (d / CPL lanes share a token); each code is converted
 // once and feeds the G queries, so a grouped-query cache is read once for G
@@ -289,16 +307,32 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
     const int nt = imin(chunk, Th - t0);         // >= 1
     const int rb = d >> 1;                       // bytes per cached vector
 
-    float qf[G][CPL], qs[G];
+    // the query: fp16 pairs for the dot products (32-channel slices), else
+    // floats and their sum for the zero points
+    constexpr bool kDot2 = NW == 4;
+    float qf[G][kDot2 ? 1 : CPL], qs[G];
+    uint32_t q2[G][kDot2 ? 16 : 1];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const uint16_t* qg = q + static_cast<size_t>(h0 + g) * d + CPL * j;
+        if constexpr (kDot2) {
 #pragma unroll
-        for (int k = 0; k < CPL / 8; ++k) unpack8(*reinterpret_cast<const uint4*>(qg + 8 * k), &qf[g][8 * k]);
-        float a = 0.0f;
+            for (int k = 0; k < 4; ++k) {
+                const uint4 v = *reinterpret_cast<const uint4*>(qg + 8 * k);
+                q2[g][4 * k + 0] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);   // channels 0, 2
+                q2[g][4 * k + 1] = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);   // 4, 6
+                q2[g][4 * k + 2] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);   // 1, 3
+                q2[g][4 * k + 3] = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);   // 5, 7
+            }
+            qs[g] = 0.0f;                        // the zero points are in the code pairs
+        } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) a += qf[g][c];
-        qs[g] = group_sum(a, D);
+            for (int k = 0; k < CPL / 8; ++k) unpack8(*reinterpret_cast<const uint4*>(qg + 8 * k), &qf[g][8 * k]);
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) a += qf[g][c];
+            qs[g] = group_sum(a, D);
+        }
     }
 
     const size_t base = static_cast<size_t>(hk) * tcap + t0;   // slot of the chunk's first token
@@ -328,14 +362,34 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            float dot[G], x[CPL];
-            codes_to_float<NW>(w[u], x);
+            float dot[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) dot[g] = 0.0f;
+            if constexpr (kDot2) {
+                const uint32_t nz = static_cast<uint32_t>(0xE400 + zt[u]) * 0x00010001u;   // -(1024 + z), twice
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t x = w[u][k] & 0x0F0F0F0Fu, y = (w[u][k] >> 4) & 0x0F0F0F0Fu;
+                    const uint32_t c0 = pk_add_half2(__builtin_amdgcn_perm(kCodeBias, x, 0x04010400u), nz);
+                    const uint32_t c1 = pk_add_half2(__builtin_amdgcn_perm(kCodeBias, x, 0x04030402u), nz);
+                    const uint32_t c2 = pk_add_half2(__builtin_amdgcn_perm(kCodeBias, y, 0x04010400u), nz);
+                    const uint32_t c3 = pk_add_half2(__builtin_amdgcn_perm(kCodeBias, y, 0x04030402u), nz);
 #pragma unroll
-                for (int g = 0; g < G; ++g) dot[g] = fmaf(qf[g][c], x[c], dot[g]);
+                    for (int g = 0; g < G; ++g) {
+                        dot[g] = fdot2_bits(c0, q2[g][4 * k + 0], dot[g]);
+                        dot[g] = fdot2_bits(c1, q2[g][4 * k + 1], dot[g]);
+                        dot[g] = fdot2_bits(c2, q2[g][4 * k + 2], dot[g]);
+                        dot[g] = fdot2_bits(c3, q2[g][4 * k + 3], dot[g]);
+                    }
+                }
+            } else {
+                float x[CPL];
+                codes_to_float<NW>(w[u], x);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) dot[g] = fmaf(qf[g][c], x[c], dot[g]);
+                }
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) dot[g] = group_sum(dot[g], D);
@@ -394,18 +448,25 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = (it0 + u) * per_step + first;
-            float wt[G], x[CPL];
-            codes_to_float<NW>(w[u], x);
+            float wt[G];
             const float zf = static_cast<float>(zt[u]);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 wt[g] = i < nt ? sc[g][i] * st[u] : 0.0f;
                 wz[g] = fmaf(wt[g], zf, wz[g]);
             }
+            // one code word (8 channels) at a time: 8 converted codes live
+            // instead of CPL (the one-query 32-channel form fits 64 VGPRs,
+            // eight waves per SIMD)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
+            for (int k = 0; k < NW; ++k) {
+                float x[8];
+                codes_to_float<1>(&w[u][k], x);
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g][c] = fmaf(wt[g], x[c], acc[g][c]);
+                for (int c = 0; c < 8; ++c) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) acc[g][8 * k + c] = fmaf(wt[g], x[c], acc[g][8 * k + c]);
+                }
             }
         }
     }
@@ -809,6 +870,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_attn_mfma_kernel(
 }
 
 inline int imin_host(int a, int b) { return a < b ? a : b; }
+constexpr unsigned kVarlenLdsPad = 17408;   // dynamic LDS of the per-length launch (see launch_kv4_attention)
 
 }  // namespace
 
@@ -871,13 +933,23 @@ int launch_kv4_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* k
     const float scale = 1.0f / sqrtf(static_cast<float>(d));
     const int cpl = imin_host(32, d);
     const int grid = (Hq / G) * nsplit;
+    // With per-head lengths, chunks past a head's tokens exit at once, and
+    // with all workgroups resident in one round (the one-query 32-channel
+    // form: 64 VGPRs, eight per CU) each CU keeps the live chunks it was dealt.
+    // Reserving LDS so that at most six share a CU (6160 bytes static + this
+    // pad = 23568; six take 141 KB of the 160, seven would need 165) leaves a
+    // second round that the dispatcher hands out as slots free up (LLaMA-7B
+    // decode shape, sequences of 635-3792 tokens: 43.7 against 45.6 us; the
+    // uniform call keeps all eight: 61.3 us, against 74.7 for the form with
+    // FP32 key products and all codes of a slice converted at once, 87 VGPRs).
+    const unsigned pad = (Tk != nullptr && cpl == 32 && G == 1) ? kVarlenLdsPad : 0u;
 #define COMET_KV4_CHUNK(C, GG)                                                                                 \
     do {                                                                                                       \
         if (d == 128)                                                                                          \
-            kv4_attn_chunk_kernel<C, GG, 128><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, \
+            kv4_attn_chunk_kernel<C, GG, 128><<<grid, kKvThreads, pad, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T, \
                                                                           tcap, scale, chunk, nsplit, part, ml, Tk); \
         else                                                                                                   \
-            kv4_attn_chunk_kernel<C, GG, 0><<<grid, kKvThreads, 0, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T,   \
+            kv4_attn_chunk_kernel<C, GG, 0><<<grid, kKvThreads, pad, st>>>(q, kc, ks, kz, vc, vs, vz, group, d, T,   \
                                                                         tcap, scale, chunk, nsplit, part, ml, Tk); \
     } while (0)
     if (G == 2) {
