@@ -1020,6 +1020,15 @@ __global__ __launch_bounds__(64 * kSplit) __attribute__((amdgpu_waves_per_eu(2))
     }
     unroll_seq([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        // wave priority from progress through the wave's blocks (3 in the
+        // first quarter down to 0): the workgroup waits for its slowest wave
+        // at the split-K sum, and with equal priorities the oldest waves win
+        // the issue arbitration. Measured to pay for the half-group units and
+        // four row tiles (LLaMA-70B decode, N = 10240: 12.1 to 11.8 us at
+        // M = 1, 19.3 to 18.3 at M = 64; N = 28672, M = 64: 39.8 to 37.7), not
+        // for the one-tile whole-group forms (N = 28672, M = 1: 24.9 to 26.5)
+        if constexpr ((H > 0 || MR == 4) && (i == 0 || 4 * i / NBW != 4 * (i - 1) / NBW))
+            __builtin_amdgcn_s_setprio(3 - (4 * i) / NBW);
         COMET_VMCNT((lds_g_loads_after<MR, G, kRA, kRR, kAsym>(i, NBW)));
         AuxSlotG<MR, G, kAsym>& sl = slot[i % kRA];
         stream_compute_lds_g<MR, G, kAsym, kDump>(b_begin + i < nb4, sl, my + (i % kRR) * G * kFragBytes, lane, y,
